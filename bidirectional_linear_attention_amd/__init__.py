@@ -1,0 +1,141 @@
+"""MI355X-native Gated Bidirectional Linear Attention (GBLA).
+
+Python binding of libgbla.so (C ABI in include/gbla.h). The functions named
+like the C entry points take torch tensors and pass their device pointers and
+the current HIP stream; the convenience wrappers `forward` / `backward` also
+allocate the outputs and the workspace. Every step of the layer runs in the
+library's HIP kernels; if the library is missing an error is raised.
+
+The layer is Eqs. (4)-(6) of "Gated Bidirectional Linear Attention for
+Generative Retrieval" (core method): causal depthwise Conv1d (kernel 4), per-head
+Q/K/V projections, phi = elu + 1, sigmoid key gate, global state
+S = sum_j g_j phi(k_j) v_j^T, z = sum_j g_j phi(k_j), readout
+y_i = phi(q_i)^T S / phi(q_i)^T z, on packed variable-length sequences.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import DTYPE_BF16, DTYPE_F32, GATE_SIGMOID, GblaError, GblaProblem
+
+__all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "gbla_forward",
+           "gbla_backward", "forward", "backward", "DTYPE_F32", "DTYPE_BF16"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float32:
+        return DTYPE_F32
+    if dt == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}: float32 or bfloat16")
+
+
+def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype) -> GblaProblem:
+    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code."""
+    code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
+    return GblaProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code,
+                       GATE_SIGMOID, 4)
+
+
+def saved_size(p: GblaProblem) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().gbla_saved_size(ctypes.byref(p), ctypes.byref(out)), "gbla_saved_size")
+    return out.value
+
+
+def workspace_size(p: GblaProblem, backward: bool) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().gbla_workspace_size(ctypes.byref(p), int(bool(backward)), ctypes.byref(out)),
+               "gbla_workspace_size")
+    return out.value
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("all tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, workspace,
+                 stream=None) -> None:
+    """Enqueue the forward pass (include/gbla.h: gbla_forward)."""
+    st = _lib.load().gbla_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
+                                  _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(y), _ptr(saved), _ptr(workspace),
+                                  ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
+    _lib.check(st, "gbla_forward")
+
+
+def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, dx, dconv_w, dw_q,
+                  dw_k, dw_v, dw_g, db_g, workspace, stream=None) -> None:
+    """Enqueue the backward pass (include/gbla.h: gbla_backward)."""
+    st = _lib.load().gbla_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
+                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(saved), _ptr(dy), _ptr(dx), _ptr(dconv_w),
+                                   _ptr(dw_q), _ptr(dw_k), _ptr(dw_v), _ptr(dw_g), _ptr(db_g), _ptr(workspace),
+                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
+    _lib.check(st, "gbla_backward")
+
+
+def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads):
+    torch = _torch()
+    T, d = x.shape
+    D = w_q.shape[1]
+    if D % num_heads:
+        raise ValueError("w_q columns must be a multiple of num_heads")
+    for name, t, shape in (("conv_w", conv_w, (d, 4)), ("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)),
+                           ("w_v", w_v, (d, D)), ("w_g", w_g, (num_heads, d))):
+        if tuple(t.shape) != shape or t.dtype != x.dtype:
+            raise ValueError(f"{name}: expected {shape} {x.dtype}, got {tuple(t.shape)} {t.dtype}")
+    if b_g.dtype != torch.float32 or tuple(b_g.shape) != (num_heads,):
+        raise ValueError("b_g must be float32 [num_heads]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be int32 [N+1]")
+    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype)
+
+
+def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, workspace=None):
+    """Allocate y, saved (and the workspace unless given) and run gbla_forward.
+    Returns (y [T, H*d_h], saved [N, H, d_h*d_h + d_h] float32)."""
+    torch = _torch()
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
+    dev = x.device
+    y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
+    saved = torch.empty((p.num_seqs, p.num_heads, p.head_dim * p.head_dim + p.head_dim), dtype=torch.float32,
+                        device=dev)
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, False), dtype=torch.uint8, device=dev)
+    gbla_forward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, workspace)
+    return y, saved
+
+
+def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, num_heads: int, workspace=None) -> dict:
+    """Allocate the gradients (and the workspace unless given) and run gbla_backward.
+    Returns dict dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g."""
+    torch = _torch()
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), dconv_w=torch.empty(conv_w.shape, **f32), dw_q=torch.empty(w_q.shape, **f32),
+             dw_k=torch.empty(w_k.shape, **f32), dw_v=torch.empty(w_v.shape, **f32),
+             dw_g=torch.empty(w_g.shape, **f32), db_g=torch.empty(b_g.shape, **f32))
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, True), dtype=torch.uint8, device=dev)
+    gbla_backward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, g["dx"], g["dconv_w"], g["dw_q"],
+                  g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace)
+    return g

@@ -1,0 +1,74 @@
+"""ctypes view of libgbla.so (include/gbla.h). Marshalling only: every step of
+the layer runs in the HIP library; there is no CPU or PyTorch fallback."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgbla.so")
+
+STATUS = {
+    0: "GBLA_OK", 1: "GBLA_ERR_NULL_ARG", 2: "GBLA_ERR_BAD_SHAPE", 3: "GBLA_ERR_UNSUPPORTED",
+    4: "GBLA_ERR_MISALIGNED", 5: "GBLA_ERR_WORKSPACE_TOO_SMALL", 6: "GBLA_ERR_HIP",
+}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+GATE_SIGMOID = 0
+
+
+class GblaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class GblaProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "gate", "conv_width")]
+
+
+class LionProblem(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "chunk", "reserved")]
+
+
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+_P = ctypes.POINTER(GblaProblem)
+_LP = ctypes.POINTER(LionProblem)
+
+_SIGNATURES = {
+    "gbla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gbla_version": (ctypes.c_int, []),
+    "gbla_saved_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
+    "gbla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
+    "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 10 + [_vp, _sz, _vp]),
+    "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 17 + [_vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def load():
+    """Load libgbla.so once. torch is imported first so the library binds to the
+    same HIP runtime instance as torch's device memory and streams."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m bidirectional_linear_attention_amd.build` (no fallback path exists)")
+    import torch  # noqa: F401  (shares the HIP runtime)
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        if not hasattr(lib, name):
+            continue
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def check(status: int, where: str):
+    if status != 0:
+        raise GblaError(status, where)

@@ -1,0 +1,182 @@
+// Device-side building blocks shared by the GBLA and LION-s kernels (gfx950).
+//
+// Conventions used by every kernel in this library:
+//  * activations and weights are stored either as float or as bfloat16 (the
+//    raw 16-bit pattern in a uint16_t); accumulation is always float;
+//  * MFMA lane layouts (wave64, 16x16 output tiles):
+//      - an A operand supplies row  i = lane % 16, a B operand column j = lane % 16;
+//      - each lane supplies the same set of k indices for A and B, so any
+//        consistent assignment of k to (lane / 16, element) gives the same sum;
+//      - the output tile C holds C[4 * (lane / 16) + r][lane % 16] in element r.
+//    A C tile can therefore be fed back as a K=16 operand (k = 4 * (lane / 16) + r)
+//    without moving data between lanes ("C-reuse"), which is how token-axis
+//    contractions are done on values already held in registers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gbla {
+
+typedef uint16_t bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_v;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// float -> bfloat16, round to nearest even (NaN stays NaN)
+__device__ __forceinline__ bf16 f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return f2bf(v); }
+
+// round a float to the storage precision of T, returned as float
+template <typename T> __device__ __forceinline__ float round_to(float v) { return to_f<T>(from_f<T>(v)); }
+
+// ---------------------------------------------------------------- 8-element fragments
+// Eight consecutive elements of one row along k: the per-lane MFMA operand for
+// a 32-wide k step (one 16x16x32 bf16 MFMA, or eight 16x16x4 f32 MFMAs).
+template <typename T> struct Frag8;
+template <> struct Frag8<bf16> { uint4 v; };
+template <> struct Frag8<float> { float4 lo, hi; };
+
+template <typename T> __device__ __forceinline__ Frag8<T> frag_zero();
+template <> __device__ __forceinline__ Frag8<bf16> frag_zero<bf16>() { Frag8<bf16> f; f.v = make_uint4(0, 0, 0, 0); return f; }
+template <> __device__ __forceinline__ Frag8<float> frag_zero<float>() {
+  Frag8<float> f; f.lo = make_float4(0.f, 0.f, 0.f, 0.f); f.hi = f.lo; return f;
+}
+
+template <typename T> __device__ __forceinline__ Frag8<T> frag_load(const T* p);
+template <> __device__ __forceinline__ Frag8<bf16> frag_load<bf16>(const bf16* p) {
+  Frag8<bf16> f; f.v = *reinterpret_cast<const uint4*>(p); return f;
+}
+template <> __device__ __forceinline__ Frag8<float> frag_load<float>(const float* p) {
+  Frag8<float> f; f.lo = reinterpret_cast<const float4*>(p)[0]; f.hi = reinterpret_cast<const float4*>(p)[1]; return f;
+}
+template <typename T> __device__ __forceinline__ void frag_store(T* p, const Frag8<T>& f);
+template <> __device__ __forceinline__ void frag_store<bf16>(bf16* p, const Frag8<bf16>& f) {
+  *reinterpret_cast<uint4*>(p) = f.v;
+}
+template <> __device__ __forceinline__ void frag_store<float>(float* p, const Frag8<float>& f) {
+  reinterpret_cast<float4*>(p)[0] = f.lo; reinterpret_cast<float4*>(p)[1] = f.hi;
+}
+
+// element access of a fragment as float
+__device__ __forceinline__ float frag_get(const Frag8<float>& f, int j) {
+  const float* p = reinterpret_cast<const float*>(&f);
+  return p[j];
+}
+__device__ __forceinline__ float frag_get(const Frag8<bf16>& f, int j) {
+  const bf16* p = reinterpret_cast<const bf16*>(&f.v);
+  return bf2f(p[j]);
+}
+
+// build a fragment from 8 floats (rounded to T)
+template <typename T> __device__ __forceinline__ Frag8<T> frag_from(const float* v);
+template <> __device__ __forceinline__ Frag8<float> frag_from<float>(const float* v) {
+  Frag8<float> f; f.lo = make_float4(v[0], v[1], v[2], v[3]); f.hi = make_float4(v[4], v[5], v[6], v[7]); return f;
+}
+template <> __device__ __forceinline__ Frag8<bf16> frag_from<bf16>(const float* v) {
+  Frag8<bf16> f;
+  f.v.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  f.v.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  f.v.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  f.v.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  return f;
+}
+
+// acc += A(16x32) * B(32x16); a, b: this lane's 8 k-elements
+__device__ __forceinline__ void mma8(f32x4& acc, const Frag8<bf16>& a, const Frag8<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_v, a.v), __builtin_bit_cast(bf16x8_v, b.v),
+                                                acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma8(f32x4& acc, const Frag8<float>& a, const Frag8<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.z, b.lo.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.w, b.lo.w, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.x, b.hi.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.y, b.hi.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.z, b.hi.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi.w, b.hi.w, acc, 0, 0, 0);
+}
+
+// acc += A(16x16) * B(16x16) with this lane's 4 k-elements given as floats
+// (rounded to T first). Used with C-reuse operands: k = 4 * (lane / 16) + j.
+template <typename T> __device__ __forceinline__ void mma4(f32x4& acc, const float* a, const float* b);
+template <> __device__ __forceinline__ void mma4<bf16>(f32x4& acc, const float* a, const float* b) {
+  s16x4_v av, bv;
+  av[0] = (short)f2bf(a[0]); av[1] = (short)f2bf(a[1]); av[2] = (short)f2bf(a[2]); av[3] = (short)f2bf(a[3]);
+  bv[0] = (short)f2bf(b[0]); bv[1] = (short)f2bf(b[1]); bv[2] = (short)f2bf(b[2]); bv[3] = (short)f2bf(b[3]);
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mma4<float>(f32x4& acc, const float* a, const float* b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// ---------------------------------------------------------------- small helpers
+__device__ __forceinline__ float sigmoidf_(float s) { return 1.f / (1.f + __expf(-s)); }
+// phi(u) = elu(u) + 1
+__device__ __forceinline__ float phi_elu1(float u) { return u > 0.f ? u + 1.f : __expf(u); }
+
+// Workgroup i runs on XCD i % 8. Give every XCD a contiguous range of logical
+// block ids so blocks that share inputs (the heads of one token tile) share an
+// L2. The grid must hold 8 * ceil(n / 8) blocks; ids >= n are idle.
+__device__ __forceinline__ int xcd_logical_block(int bid, int n) {
+  const int per = (n + 7) >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+__host__ __device__ inline int xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
+
+// sum over the 16 lanes that share lane / 16
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+// value held by lane 16 * (lane / 16) (column 0 of this lane's C-tile rows)
+__device__ __forceinline__ float col0_bcast(float v, int lane) { return __shfl(v, lane & 48, 64); }
+
+// position of token t inside its packed sequence (largest b with cu[b] <= t),
+// clamped so that t - pos >= 0 even for malformed offsets
+__device__ __forceinline__ int pos_in_seq(const int32_t* __restrict__ cu, int nseq, int t) {
+  int lo = 0, hi = nseq;  // invariant: cu[lo] <= t < cu[hi] for well-formed offsets
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  int p = t - cu[lo];
+  return p < 0 ? 0 : (p > t ? t : p);
+}
+// end (exclusive) of token t's sequence, clamped to [t + 1, T]
+__device__ __forceinline__ int seq_end_of(const int32_t* __restrict__ cu, int nseq, int t, int T) {
+  int lo = 0, hi = nseq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid; else hi = mid;
+  }
+  int e = cu[lo + 1];
+  return e <= t ? t + 1 : (e > T ? T : e);
+}
+
+// chunk table entry: one run of <= chunk tokens inside one sequence
+struct Chunk { int seq, start, end, pad; };
+
+}  // namespace gbla

@@ -1,0 +1,215 @@
+// C ABI of the GBLA library: argument validation, workspace carving and the
+// launch sequence of the forward and backward passes (see include/gbla.h).
+#include "gbla.h"
+
+#include <algorithm>
+
+#include "internal.h"
+
+using namespace gbla;
+
+namespace {
+
+// ---------------------------------------------------------------- workspace plan
+struct Carver {
+  size_t off = 0;
+  template <typename P> P* take(char* base, size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += (bytes + 255) & ~size_t(255);
+    return p;
+  }
+};
+
+struct Dims {
+  int N, T, d, H, dh, D, E, NP, Kp, slots, nsplit, conv_rb;
+  size_t esz;  // bytes per activation element
+};
+
+Dims dims_of(const gbla_problem* p) {
+  Dims m;
+  m.N = p->num_seqs; m.T = p->total_tokens; m.d = p->d_model; m.H = p->num_heads; m.dh = p->head_dim;
+  m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.NP = proj_cols(m.dh); m.Kp = grad_cols(m.H, m.dh);
+  m.slots = max_chunks(m.T, m.N);
+  const int tiles = ((m.d + 127) / 128) * ((m.Kp + 127) / 128);
+  int ns = (1024 + tiles - 1) / tiles;
+  ns = std::min(ns, std::max(1, (m.T + 511) / 512));
+  m.nsplit = std::max(1, std::min(ns, 64));
+  m.conv_rb = conv_bwd_row_blocks(m.T);
+  m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
+  return m;
+}
+
+struct FwdWs {
+  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* qa; void* ka; void* va; float* partial;
+};
+struct BwdWs {
+  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; void* qa; void* ka; void* va; float* ga; void* xt;
+  float* partial; float* dsz; float* dbg_part; void* G; float* dxt; float* dw_part; float* dconv_part;
+};
+
+size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
+  Carver c;
+  FwdWs t;
+  const size_t TD = (size_t)m.T * m.D * m.esz;
+  t.nchunks = c.take<int>(base, sizeof(int));
+  t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
+  t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
+  t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
+  t.qa = c.take<char>(base, TD);
+  t.ka = c.take<char>(base, TD);
+  t.va = c.take<char>(base, TD);
+  t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
+  if (w) *w = t;
+  return c.off;
+}
+
+size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
+  Carver c;
+  BwdWs t;
+  const size_t TD = (size_t)m.T * m.D * m.esz;
+  t.nchunks = c.take<int>(base, sizeof(int));
+  t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
+  t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
+  t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
+  t.wt = c.take<char>(base, (size_t)m.d * m.Kp * m.esz);
+  t.qa = c.take<char>(base, TD);
+  t.ka = c.take<char>(base, TD);
+  t.va = c.take<char>(base, TD);
+  t.ga = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
+  t.xt = c.take<char>(base, (size_t)m.T * m.d * m.esz);
+  t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
+  t.dsz = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H * m.E);
+  t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
+  t.G = c.take<char>(base, (size_t)m.T * m.Kp * m.esz);
+  t.dxt = c.take<float>(base, sizeof(float) * (size_t)m.T * m.d);
+  t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
+  t.dconv_part = c.take<float>(base, sizeof(float) * (size_t)std::max(1, m.conv_rb) * m.d * 4);
+  if (w) *w = t;
+  return c.off;
+}
+
+gbla_status check_problem(const gbla_problem* p) {
+  if (!p) return GBLA_ERR_NULL_ARG;
+  if (p->dtype != GBLA_DTYPE_F32 && p->dtype != GBLA_DTYPE_BF16) return GBLA_ERR_UNSUPPORTED;
+  if (p->head_dim != 32 && p->head_dim != 64) return GBLA_ERR_UNSUPPORTED;
+  if (p->gate != GBLA_GATE_SIGMOID || p->conv_width != 4) return GBLA_ERR_UNSUPPORTED;
+  if (p->num_seqs < 1 || p->total_tokens < 0 || p->num_heads < 1 || p->d_model < 8 || p->d_model % 8 != 0)
+    return GBLA_ERR_BAD_SHAPE;
+  const long long T = p->total_tokens;
+  const long long widest = std::max<long long>(p->d_model, grad_cols(p->num_heads, p->head_dim));
+  if (T * widest >= (1LL << 31) || (long long)p->num_heads * p->head_dim * 4 + 64 >= (1LL << 24) ||
+      (long long)p->num_seqs >= (1LL << 24))
+    return GBLA_ERR_BAD_SHAPE;
+  return GBLA_OK;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* gbla_status_string(int status) {
+  switch (status) {
+    case GBLA_OK: return "GBLA_OK";
+    case GBLA_ERR_NULL_ARG: return "GBLA_ERR_NULL_ARG: a required pointer is NULL";
+    case GBLA_ERR_BAD_SHAPE: return "GBLA_ERR_BAD_SHAPE: sizes out of the supported range";
+    case GBLA_ERR_UNSUPPORTED: return "GBLA_ERR_UNSUPPORTED: dtype, head_dim, gate or conv width not supported";
+    case GBLA_ERR_MISALIGNED: return "GBLA_ERR_MISALIGNED: pointer alignment violated";
+    case GBLA_ERR_WORKSPACE_TOO_SMALL: return "GBLA_ERR_WORKSPACE_TOO_SMALL: workspace below the size query";
+    case GBLA_ERR_HIP: return "GBLA_ERR_HIP: a HIP launch failed";
+    default: return "unknown gbla_status";
+  }
+}
+
+int gbla_version(void) { return 1; }
+
+gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes) {
+  if (!bytes) return GBLA_ERR_NULL_ARG;
+  const gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  *bytes = sizeof(float) * (size_t)p->num_seqs * p->num_heads * (p->head_dim * p->head_dim + p->head_dim);
+  return GBLA_OK;
+}
+
+gbla_status gbla_workspace_size(const gbla_problem* p, int backward, size_t* bytes) {
+  if (!bytes) return GBLA_ERR_NULL_ARG;
+  const gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  const Dims m = dims_of(p);
+  *bytes = backward ? plan_bwd(m, nullptr, nullptr) : plan_fwd(m, nullptr, nullptr);
+  return GBLA_OK;
+}
+
+gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                         const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                         void* y, float* saved, void* workspace, size_t workspace_bytes, void* stream) {
+  gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !workspace) return GBLA_ERR_NULL_ARG;
+  if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)y, (const void*)saved, (const void*)workspace})
+    if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
+  if (!aligned(b_g, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
+  const Dims m = dims_of(p);
+  FwdWs w;
+  if (workspace_bytes < plan_fwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+
+  (void)hipGetLastError();
+  launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s);
+  launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s);
+  if (m.T > 0)
+    launch_proj(dt, m.dh, false, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, nullptr,
+                nullptr, s);
+  launch_state_partial(dt, m.dh, w.ka, w.va, w.nchunks, w.tab, m.slots, m.H, w.partial, s);
+  launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s);
+  launch_readout(dt, m.dh, w.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s);
+  return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
+}
+
+gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                          const float* saved, const void* dy, void* dx, float* dconv_w, float* dw_q, float* dw_k,
+                          float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !dconv_w || !dw_q || !dw_k ||
+      !dw_v || !dw_g || !db_g || !workspace)
+    return GBLA_ERR_NULL_ARG;
+  if (p->total_tokens > 0 && (!x || !dy || !dx)) return GBLA_ERR_NULL_ARG;
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)saved, dy, (const void*)dx, (const void*)dw_q,
+                        (const void*)dw_k, (const void*)dw_v, (const void*)dw_g, (const void*)workspace})
+    if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
+  if (!aligned(b_g, 4) || !aligned(db_g, 4) || !aligned(dconv_w, 4) || !aligned(cu_seqlens, 4))
+    return GBLA_ERR_MISALIGNED;
+  const Dims m = dims_of(p);
+  BwdWs w;
+  if (workspace_bytes < plan_bwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+
+  (void)hipGetLastError();
+  launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s);
+  launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s);
+  launch_pack_wt(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s);
+  if (m.T > 0)
+    launch_proj(dt, m.dh, true, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, w.ga, w.xt,
+                s);
+  launch_bwd_dstate(dt, m.dh, w.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s);
+  launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s);
+  launch_bwd_token(dt, m.dh, w.ka, w.va, w.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s);
+  launch_dbg_reduce(w.dbg_part, w.nchunks, m.H, db_g, s);
+  if (m.T > 0) {
+    launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s);
+    launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s);
+  }
+  launch_gemm_dw(dt, w.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s);
+  launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_g, s);
+  launch_dconv_reduce(w.dconv_part, m.conv_rb, m.d, dconv_w, s);
+  return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -34,9 +34,15 @@ __all__ = ["Workload", "WORKLOADS", "make_inputs", "round_bf16", "small_variant"
 def round_bf16(a: np.ndarray) -> np.ndarray:
     """Round float32 values to the nearest bfloat16 (ties to even), returned as float32."""
     a = np.ascontiguousarray(a, dtype=np.float32)
-    bits = a.view(np.uint32).astype(np.uint64)
-    lsb = (bits >> 16) & 1
-    rounded = ((bits + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    try:  # torch's float32 -> bfloat16 cast is round-to-nearest-even and multi-threaded
+        import torch
+        return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    bits = a.view(np.uint32)
+    # finite values never overflow 32 bits here: |bits| <= 0xFF7FFFFF, + 0x8000
+    rounded = bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))
+    rounded &= np.uint32(0xFFFF0000)
     return rounded.view(np.float32).reshape(a.shape)
 
 
@@ -114,7 +120,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     T, d, H, dh = int(cu[-1]), w.d_model, w.num_heads, w.head_dim
     D = H * dh
 
-    x = rng.standard_normal((T, d), dtype=np.float64).astype(np.float32)
+    x = rng.standard_normal((T, d), dtype=np.float32)
     if w.dup_frac > 0:
         for b in range(len(lens)):
             s, L = int(cu[b]), int(lens[b])
@@ -132,7 +138,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     w_v = (rng.standard_normal((d, D)) * std).astype(np.float32)
     w_g = (rng.standard_normal((H, d)) * std).astype(np.float32)
     b_g = np.full((H,), w.gate_bias, dtype=np.float32)
-    dy = rng.standard_normal((T, D), dtype=np.float64).astype(np.float32)
+    dy = rng.standard_normal((T, D), dtype=np.float32)
 
     if w.dtype == "bf16":
         x, conv_w, w_q, w_k, w_v, w_g, dy = (round_bf16(a) for a in (x, conv_w, w_q, w_k, w_v, w_g, dy))

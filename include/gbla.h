@@ -1,0 +1,127 @@
+/*
+ * gbla.h -- C ABI of the MI355X (gfx950) Gated Bidirectional Linear Attention
+ * library (libgbla.so).
+ *
+ * The layer is the one of "Gated Bidirectional Linear Attention for Generative
+ * Retrieval", section "核心方法" (core method), Eqs. (4)-(6). For every packed
+ * sequence b (rows cu_seqlens[b] .. cu_seqlens[b+1]-1) and every head h:
+ *
+ *   x~      = causal depthwise Conv1d(x), kernel 4                (Eq. (4))
+ *   q, k, v = x~ W_Q^h, x~ W_K^h, x~ W_V^h                       (Eq. (4), per-head weights)
+ *   g_j     = sigmoid(x~_j . w_g^h + b_g^h)                      (key gate of Eq. (5))
+ *   S       = sum_j g_j phi(k_j) v_j^T,  z = sum_j g_j phi(k_j)  (Eq. (6), phi(u) = elu(u) + 1)
+ *   y_i     = phi(q_i)^T S / phi(q_i)^T z                        (Eq. (5), state-first order of Eq. (3))
+ *
+ * The conv restarts at every sequence start (zero left padding, tap 3 multiplies
+ * the current token, tap k the token 3-k steps back) and S, z cover only the
+ * sequence's own tokens. No 1/sqrt(d_h) scale, no epsilon, no projection bias;
+ * y concatenates the heads (head h in columns h*d_h .. h*d_h+d_h-1).
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers (HIP), row-major, owned by the
+ *    caller; the library allocates nothing and keeps no pointer after a call
+ *    returns. Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *    stream) and nothing synchronises with the host, so outputs are ready only
+ *    when that stream is.
+ *  - Activations, weights and y/dx use the problem's dtype (float32 or
+ *    bfloat16); accumulation is float32; b_g, saved state and all weight
+ *    gradients are float32.
+ *  - Argument errors are detected on the host before anything is enqueued and
+ *    returned as a gbla_status; GBLA_ERR_HIP reports a failed launch.
+ *  - cu_seqlens must satisfy cu[0] = 0, cu[b] <= cu[b+1], cu[N] = total_tokens.
+ *    It is read on the device only; if it is malformed, no token is scheduled
+ *    (outputs are unspecified but no memory outside the arguments is touched).
+ *  - Results are deterministic: every reduction runs in a fixed order with no
+ *    floating-point atomics, so repeated calls are bitwise identical.
+ *  - Large arrays must be 16-byte aligned; b_g, db_g, dconv_w and cu_seqlens
+ *    4-byte aligned.
+ *  - Sizes: total_tokens * max(d_model, 3*H*d_h + H + 64) < 2^31.
+ *  - Calls that share a workspace must not overlap in time.
+ */
+#ifndef GBLA_H_
+#define GBLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__) || defined(__clang__)
+#define GBLA_API __attribute__((visibility("default")))
+#else
+#define GBLA_API
+#endif
+
+typedef enum {
+  GBLA_OK = 0,
+  GBLA_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  GBLA_ERR_BAD_SHAPE = 2,           /* sizes out of the supported range */
+  GBLA_ERR_UNSUPPORTED = 3,         /* dtype, head_dim, gate or conv width not supported */
+  GBLA_ERR_MISALIGNED = 4,          /* pointer alignment violated */
+  GBLA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the size query */
+  GBLA_ERR_HIP = 6                  /* a HIP launch failed */
+} gbla_status;
+
+enum { GBLA_DTYPE_F32 = 0, GBLA_DTYPE_BF16 = 1 };
+enum { GBLA_GATE_SIGMOID = 0 };
+
+typedef struct {
+  int32_t num_seqs;     /* N >= 1 packed sequences (empty sequences allowed) */
+  int32_t total_tokens; /* T = cu_seqlens[N] >= 0 */
+  int32_t d_model;      /* d: multiple of 8, >= 8 */
+  int32_t num_heads;    /* H >= 1 */
+  int32_t head_dim;     /* d_h: 32 or 64 */
+  int32_t dtype;        /* GBLA_DTYPE_F32 or GBLA_DTYPE_BF16 */
+  int32_t gate;         /* GBLA_GATE_SIGMOID */
+  int32_t conv_width;   /* must be 4 */
+} gbla_problem;
+
+/* Human-readable name of a status code (static string). */
+GBLA_API const char* gbla_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+GBLA_API int gbla_version(void);
+
+/* Bytes of the `saved` buffer written by gbla_forward and read by
+ * gbla_backward: N * H * (d_h*d_h + d_h) float32 values, laid out
+ * [N][H][S (d_h x d_h, row i = key feature, column = value feature) | z (d_h)]. */
+GBLA_API gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes);
+
+/* Bytes of device workspace needed by gbla_forward (backward = 0) or
+ * gbla_backward (backward = 1). */
+GBLA_API gbla_status gbla_workspace_size(const gbla_problem* p, int backward, size_t* bytes);
+
+/* Forward pass, Eqs. (4)-(6).
+ *   x        [T, d]        input rows (dtype)
+ *   cu_seqlens [N+1] int32 sequence offsets
+ *   conv_w   [d, 4]        depthwise conv taps (dtype)
+ *   w_q, w_k, w_v [d, H*d_h] projections; head h owns columns h*d_h.. (dtype)
+ *   w_g      [H, d]        gate weights (dtype);  b_g [H] gate bias (float32)
+ *   y        [T, H*d_h]    output (dtype, overwritten)
+ *   saved    see gbla_saved_size (float32, overwritten): the states S and z
+ *   workspace, workspace_bytes: at least gbla_workspace_size(p, 0) bytes */
+GBLA_API gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                         const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                         void* y, float* saved, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass: gradients of sum(y * dy) for the forward above, obtained by
+ * the chain rule through Eqs. (4)-(6). Inputs as in gbla_forward plus
+ *   saved    the state written by gbla_forward for the same inputs (float32)
+ *   dy       [T, H*d_h]    upstream gradient (dtype)
+ * Outputs (all overwritten, never accumulated):
+ *   dx       [T, d] (dtype);  dconv_w [d, 4];  dw_q, dw_k, dw_v [d, H*d_h];
+ *   dw_g     [H, d];  db_g [H]   (all float32)
+ *   workspace, workspace_bytes: at least gbla_workspace_size(p, 1) bytes */
+GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                          const float* saved, const void* dy, void* dx, float* dconv_w, float* dw_q, float* dw_k,
+                          float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GBLA_H_ */

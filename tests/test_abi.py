@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function declared in include/*.h, and rejects bad arguments before it
+enqueues anything."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import bidirectional_linear_attention_amd as gb
+from bidirectional_linear_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M):
+            if not m.group(0).lstrip().startswith(("typedef", "#")):
+                names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert "gbla_forward" in declared and "gbla_backward" in declared
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_version():
+    lib = _lib.load()
+    for code in range(7):
+        assert lib.gbla_status_string(code).decode().startswith(_lib.STATUS[code])
+    assert lib.gbla_version() >= 1
+
+
+def _prob(**kw):
+    base = dict(num_seqs=2, total_tokens=100, d_model=64, num_heads=2, head_dim=64, dtype=gb.DTYPE_BF16)
+    base.update(kw)
+    return gb.GblaProblem(base["num_seqs"], base["total_tokens"], base["d_model"], base["num_heads"],
+                          base["head_dim"], base["dtype"], 0, 4)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(d_model=60), 2), (dict(num_seqs=0), 2),
+    (dict(total_tokens=-1), 2), (dict(num_heads=0), 2), (dict(total_tokens=1 << 30), 2),
+])
+def test_size_queries_reject_bad_problems(kw, status):
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    assert lib.gbla_workspace_size(ctypes.byref(_prob(**kw)), 0, ctypes.byref(out)) == status
+    assert lib.gbla_saved_size(ctypes.byref(_prob(**kw)), ctypes.byref(out)) == status
+
+
+def test_unsupported_gate_and_conv_width():
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    p = _prob()
+    p.gate = 1
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 3
+    p = _prob()
+    p.conv_width = 3
+    assert lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out)) == 3
+
+
+def test_size_queries_are_consistent():
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    p = _prob()
+    assert lib.gbla_saved_size(ctypes.byref(p), ctypes.byref(out)) == 0
+    assert out.value == 4 * 2 * 2 * (64 * 64 + 64)
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    fwd = out.value
+    assert lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out)) == 0
+    assert out.value > fwd > 0
+    assert lib.gbla_workspace_size(None, 0, ctypes.byref(out)) == 1
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, None) == 1
+
+
+def _fake(addr=0x10000):
+    return ctypes.c_void_p(addr)
+
+
+def test_forward_rejects_null_misaligned_and_small_workspace_without_launching():
+    lib = _lib.load()
+    p = _prob()
+    out = ctypes.c_size_t()
+    lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(10)]
+    # NULL weight
+    args = list(a)
+    args[4] = None
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    # misaligned x
+    args = list(a)
+    args[0] = _fake(0x10008)
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
+    # workspace one byte short
+    assert lib.gbla_forward(ctypes.byref(p), *a, _fake(0x900000), need - 1, None) == 5
+    # bad problem is reported first
+    bad = _prob(head_dim=16)
+    assert lib.gbla_forward(ctypes.byref(bad), *a, _fake(0x900000), need, None) == 3
+
+
+def test_backward_rejects_null_and_small_workspace_without_launching():
+    lib = _lib.load()
+    p = _prob()
+    out = ctypes.c_size_t()
+    lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(17)]
+    args = list(a)
+    args[16] = None   # db_g
+    assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    assert lib.gbla_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5

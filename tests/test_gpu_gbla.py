@@ -1,0 +1,175 @@
+"""GPU parity of the HIP GBLA path against the float64 oracle.
+
+Every case feeds the same seeded inputs (bf16-representable values for bf16
+workloads) to libgbla.so through the C ABI and to oracle.gbla, and compares
+each output tensor with the max-norm relative error
+    ||gpu - oracle||_inf / ||oracle||_inf
+against 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs with float32
+accumulation. y and the gradients of the backward are compared elementwise in
+that norm; the saved states S and z too.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bidirectional_linear_attention_amd as gb
+from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, small_variant
+from oracle import gbla as og
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GRADS = ("dx", "dconv_w", "dw_q", "dw_k", "dw_v", "dw_g", "db_g")
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    if ref.size == 0:
+        return 0.0
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(den, 1e-30))
+
+
+def to_dev(inp):
+    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
+
+    return dict(x=t(inp["x"]), cu=torch.from_numpy(inp["cu_seqlens"]).to("cuda"), conv_w=t(inp["conv_w"]),
+                w_q=t(inp["w_q"]), w_k=t(inp["w_k"]), w_v=t(inp["w_v"]), w_g=t(inp["w_g"]),
+                b_g=torch.from_numpy(inp["b_g"]).float().to("cuda"), dy=t(inp["dy"]))
+
+
+def run_gpu(inp, backward):
+    d = to_dev(inp)
+    H = inp["H"]
+    y, saved = gb.forward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"], H)
+    out = {"y": y, "saved": saved}
+    if backward:
+        out.update(gb.backward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"],
+                               saved, d["dy"], H))
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy() for k, v in out.items()}
+
+
+def oracle_args(inp):
+    return [inp[k] for k in ("x", "cu_seqlens", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g")]
+
+
+def compare(inp, backward, tol=None, label=""):
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    gpu = run_gpu(inp, backward)
+    y, S, z = og.forward(*oracle_args(inp), inp["H"])
+    N, H, dh = inp["N"], inp["H"], inp["dh"]
+    sv = gpu["saved"].reshape(N, H, dh * dh + dh)
+    errs = {"y": rel_err(gpu["y"], y),
+            "S": rel_err(sv[:, :, :dh * dh].reshape(N, H, dh, dh), S),
+            "z": rel_err(sv[:, :, dh * dh:], z)}
+    if backward:
+        g = og.backward(*oracle_args(inp), inp["dy"], inp["H"])
+        for k in GRADS:
+            errs[k] = rel_err(gpu[k], g[k])
+    print(f"\n[{label}] T={inp['T']} N={N} d={inp['d']} H={H} dh={dh} {inp['dtype']}: "
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"tolerance {tol} exceeded: {bad}"
+    return gpu
+
+
+# ------------------------------------------------------------ the float32 workload, exactly
+
+def test_f32_L256_d64_forward_exact_workload():
+    w = WORKLOADS["gbla_f32_L256_d64"]
+    compare(make_inputs(w), backward=False, label=w.name)
+
+
+# ------------------------------------------------------------ float32 parity of every kernel at 1e-4
+
+@pytest.mark.parametrize("lengths,d,H,dh", [
+    ((300, 1, 513, 77), 96, 3, 64),          # several tiles, ragged tails, a single-token sequence
+    ((129, 0, 255, 40, 2), 64, 2, 32),       # empty sequence, head_dim 32
+    ((700,), 40, 1, 64),                     # d not a multiple of the k chunk
+])
+def test_f32_forward_backward_multi_tile(lengths, d, H, dh):
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lengths, d_model=d, num_heads=H, head_dim=dh,
+                      dtype="f32", seed=11)
+    compare(make_inputs(w), backward=True, label="f32 " + str(lengths))
+
+
+# ------------------------------------------------------------ bf16, small versions of each workload
+
+def test_bf16_small_B32_recipe():
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (1024, 1024, 333, 1000), seed=21)
+    compare(make_inputs(w), backward=True, label="bf16 B32 recipe small")
+
+
+def test_bf16_small_long_history_recipe():
+    w = small_variant(WORKLOADS["gbla_bf16_B8_L8192_d512"], (2048, 1500), seed=22)
+    compare(make_inputs(w), backward=True, label="bf16 long-history recipe small")
+
+
+def test_bf16_small_ragged_recipe():
+    rng = np.random.default_rng(23)
+    lens = np.clip(np.rint(np.exp(rng.normal(np.log(600), 1.0, 12))), 16, 32768).astype(int)
+    w = small_variant(WORKLOADS["gbla_bf16_ragged_N256_d512"], lens, seed=23)
+    compare(make_inputs(w), backward=True, label="bf16 ragged recipe small")
+
+
+# ------------------------------------------------------------ full-size workloads (the bench configuration)
+
+def test_bf16_B32_L1024_d256_full():
+    w = WORKLOADS["gbla_bf16_B32_L1024_d256"]
+    compare(make_inputs(w), backward=True, label=w.name)
+
+
+def test_bf16_B8_L8192_d512_full():
+    w = WORKLOADS["gbla_bf16_B8_L8192_d512"]
+    compare(make_inputs(w), backward=True, label=w.name)
+
+
+def test_bf16_ragged_N256_d512_full():
+    w = WORKLOADS["gbla_bf16_ragged_N256_d512"]
+    compare(make_inputs(w), backward=True, label=w.name)
+
+
+# ------------------------------------------------------------ properties of the GPU path itself
+
+def _small_bf16():
+    w = small_variant(WORKLOADS["gbla_bf16_B8_L8192_d512"], (700, 300, 1, 0, 520), d_model=128, num_heads=2,
+                      seed=31)
+    return make_inputs(w)
+
+
+def test_bitwise_deterministic():
+    inp = _small_bf16()
+    a, b = run_gpu(inp, True), run_gpu(inp, True)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_packed_sequences_are_isolated():
+    """Changing one sequence's tokens leaves every other sequence's y and dx
+    bitwise unchanged (the state and the conv stay inside a sequence)."""
+    inp = _small_bf16()
+    a = run_gpu(inp, True)
+    cu = inp["cu_seqlens"]
+    inp2 = dict(inp, x=inp["x"].copy())
+    inp2["x"][cu[1]:cu[2]] = inp2["x"][cu[1]:cu[2]][::-1]
+    b = run_gpu(inp2, True)
+    keep = np.ones(inp["T"], bool)
+    keep[cu[1]:cu[2]] = False
+    for k in ("y", "dx"):
+        assert np.array_equal(a[k][keep], b[k][keep]), k
+        assert not np.array_equal(a[k][~keep], b[k][~keep]), k
+
+
+def test_no_tokens():
+    """T = 0: the states are zero and every weight gradient is zero."""
+    inp = make_inputs(small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (0, 0), d_model=64, num_heads=2,
+                                    seed=5))
+    out = run_gpu(inp, True)
+    assert out["y"].shape == (0, 128)
+    assert np.all(out["saved"] == 0)
+    for k in ("dconv_w", "dw_q", "dw_k", "dw_v", "dw_g", "db_g"):
+        assert np.all(out[k] == 0), k
