@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""GBLA forward+backward throughput on one MI355X.
+
+One step = one gbla_forward + one gbla_backward (every stage of the layer's hot
+path) over one synthetic batch of the long-history workload: 8 sequences x 8192
+tokens, d_model 512, 8 heads of 64, bf16 activations and weights with fp32
+accumulation, 10% repeated rows, gate bias +1. Inputs are resident in HBM
+before the timed region; x and dy rotate over three buffer sets (> 256 MB) so
+the 256 MB Infinity Cache does not serve a step from the previous step's data.
+
+Prints ONE JSON line: tokens/s (value), the roofline of the dominant stage
+measured live with the library's per-stage HIP events on the launch stream,
+and the float64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense MFMA, TFLOP/s
+WORKLOAD = "gbla_bf16_B8_L8192_d512"
+
+
+def stage_work(stage, T, N, d, H, dh, esz, nsplit=1):
+    """Algorithmic work of one launch of a stage: ("mfma", flops) or ("hbm", bytes).
+    Bytes count each compulsory operand once; flops count the dense contraction."""
+    D = H * dh
+    P3 = 3 * D + H
+    table = {
+        "proj_fwd": ("mfma", 2.0 * T * d * P3),
+        "proj_bwd": ("mfma", 2.0 * T * d * P3),
+        "gemm_dx": ("mfma", 2.0 * T * P3 * d),
+        "gemm_dw": ("mfma", 2.0 * T * d * P3),
+        "state_partial": ("hbm", 2.0 * T * D * esz),
+        "readout": ("hbm", 2.0 * T * D * esz),
+        "bwd_dstate": ("hbm", 3.0 * T * D * esz),
+        "bwd_token": ("hbm", 4.0 * T * D * esz + 4.0 * T * H + esz * T * H),
+        "conv_bwd": ("hbm", 4.0 * T * d + 2.0 * T * d * esz),
+    }
+    return table.get(stage)
+
+
+def layer_bytes_per_token(d, D, esz):
+    """Compulsory HBM bytes per token of one fwd+bwd: x read twice-free (once per
+    pass), y written, dy read, dx written (weights and states are negligible)."""
+    return esz * (d + D) + esz * (d + D + d)
+
+
+def traffic_for(stage, launches_per_step):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel's source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(stage)
+    except Exception:
+        return None
+    if not rec:
+        return None
+    src = os.path.join(ROOT, rec["source"])
+    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["bytes_per_launch"]
+
+
+def cpu_baseline(inp, sample_seqs):
+    """Time the float64 oracle (fwd+bwd) on the first `sample_seqs` sequences."""
+    import numpy as np
+    from oracle import gbla as og
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    cu = inp["cu_seqlens"]
+    S = min(sample_seqs, inp["N"])
+    T = int(cu[S])
+    sub = dict(inp, x=inp["x"][:T], dy=inp["dy"][:T], cu_seqlens=cu[:S + 1].copy())
+    args = [sub[k] for k in ("x", "cu_seqlens", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g")]
+    t0 = time.perf_counter()
+    og.forward(*args, inp["H"])
+    og.backward(*args, sub["dy"], inp["H"])
+    dt = time.perf_counter() - t0
+    del np
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 numpy oracle forward+backward on the first {S} of {inp['N']} sequences "
+                      f"({T} tokens) of the same batch, timed once ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is a design note, not an implemented path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bidirectional_linear_attention_amd as gb
+    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    esz = 2 if w.dtype == "bf16" else 4
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt).contiguous()
+
+    T, N, d, H, dh = inp["T"], inp["N"], inp["d"], inp["H"], inp["dh"]
+    D = H * dh
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    conv_w, w_q, w_k, w_v, w_g = (t(inp[k]) for k in ("conv_w", "w_q", "w_k", "w_v", "w_g"))
+    b_g = torch.from_numpy(inp["b_g"]).float().to(dev)
+    n_sets = 3
+    xs = [t(inp["x"]) for _ in range(n_sets)]
+    dys = [t(inp["dy"]) for _ in range(n_sets)]
+    p = gb.problem(N, T, d, H, dh, dt)
+    y = torch.empty((T, D), dtype=dt, device=dev)
+    saved = torch.empty((N, H, dh * dh + dh), dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty((T, d), dtype=dt, device=dev)
+    dconv = torch.empty((d, 4), **f32)
+    dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
+    dwg, dbg = torch.empty((H, d), **f32), torch.empty((H,), **f32)
+    ws = torch.empty(max(gb.workspace_size(p, False), gb.workspace_size(p, True)), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        x, dy = xs[i % n_sets], dys[i % n_sets]
+        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, ws)
+        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, dx, dconv, dwq, dwk, dwv, dwg, dbg, ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    gb.profile_begin(64 * max(1, args.steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stages = gb.profile_end()
+    elapsed = t1 - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+    tok_s = T * args.steps / elapsed
+
+    # dominant stage by total device time, and its roofline
+    per_step = {k: v[0] / args.steps for k, v in stages.items()}
+    timed = {k: v for k, v in stages.items() if stage_work(k, T, N, d, H, dh, esz)}
+    dom = max(timed, key=lambda k: timed[k][0])
+    bound, work = stage_work(dom, T, N, d, H, dh, esz)
+    dom_ms, dom_launches = stages[dom]
+    avg_s = dom_ms / dom_launches / 1e3
+    if bound == "mfma":
+        achieved, peak, unit = work / avg_s / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = work / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
+    roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, 1),
+            "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    bpt = layer_bytes_per_token(d, D, esz)
+    out = {
+        "metric": "GBLA fwd+bwd tokens/s at L=8192,H=8,d_h=64 bf16; % of HBM roofline",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "global_batch": N, "seq_len": T // N, "d_model": d, "num_heads": H,
+                   "head_dim": dh, "tokens_per_step": T, "parallelism": "none (1 GPU)"},
+        "hbm_roofline_frac_layer": round(bpt * tok_s / (HBM_PEAK_GBS * 1e9), 4),
+        "roofline": roof,
+        "stage_ms_per_step": {k: round(v, 4) for k, v in sorted(per_step.items(), key=lambda kv: -kv[1])},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_seqs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

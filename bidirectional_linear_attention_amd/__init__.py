@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import DTYPE_BF16, DTYPE_F32, GATE_SIGMOID, GblaError, GblaProblem
 
 __all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "gbla_forward",
-           "gbla_backward", "forward", "backward", "DTYPE_F32", "DTYPE_BF16"]
+           "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "DTYPE_F32", "DTYPE_BF16"]
 
 
 def _torch():
@@ -139,3 +139,18 @@ def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, num_head
     gbla_backward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, g["dx"], g["dconv_w"], g["dw_q"],
                   g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace)
     return g
+
+
+def profile_begin(max_records: int) -> None:
+    """Open the library's per-stage event-timing window (gbla_profile_begin)."""
+    _lib.check(_lib.load().gbla_profile_begin(int(max_records)), "gbla_profile_begin")
+
+
+def profile_end() -> dict:
+    """Close the timing window; returns {stage name: (total device ms, launches)}."""
+    lib = _lib.load()
+    ms = (ctypes.c_double * 64)()
+    n = (ctypes.c_int * 64)()
+    ns = ctypes.c_int()
+    _lib.check(lib.gbla_profile_end(ms, n, 64, ctypes.byref(ns)), "gbla_profile_end")
+    return {lib.gbla_profile_stage_name(i).decode(): (ms[i], n[i]) for i in range(ns.value) if n[i] > 0}

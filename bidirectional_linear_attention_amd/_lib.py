@@ -44,6 +44,10 @@ _SIGNATURES = {
     "gbla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
     "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 10 + [_vp, _sz, _vp]),
     "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 17 + [_vp, _sz, _vp]),
+    "gbla_profile_begin": (ctypes.c_int, [ctypes.c_int]),
+    "gbla_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
+                                        ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
+    "gbla_profile_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
 _lib = None

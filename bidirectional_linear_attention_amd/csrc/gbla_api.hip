@@ -158,14 +158,17 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
 
   (void)hipGetLastError();
-  launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s);
-  launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s);
-  if (m.T > 0)
+  { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
+  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s); }
+  if (m.T > 0) {
+    StageScope ps(ST_PROJ_FWD, s);
     launch_proj(dt, m.dh, false, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, nullptr,
                 nullptr, s);
-  launch_state_partial(dt, m.dh, w.ka, w.va, w.nchunks, w.tab, m.slots, m.H, w.partial, s);
-  launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s);
-  launch_readout(dt, m.dh, w.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s);
+  }
+  { StageScope ps(ST_STATE_PARTIAL, s);
+    launch_state_partial(dt, m.dh, w.ka, w.va, w.nchunks, w.tab, m.slots, m.H, w.partial, s); }
+  { StageScope ps(ST_COMBINE_STATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s); }
+  { StageScope ps(ST_READOUT, s); launch_readout(dt, m.dh, w.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 
@@ -192,23 +195,29 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
 
   (void)hipGetLastError();
-  launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s);
-  launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s);
-  launch_pack_wt(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s);
-  if (m.T > 0)
+  { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
+  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s); }
+  { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s); }
+  if (m.T > 0) {
+    StageScope ps(ST_PROJ_BWD, s);
     launch_proj(dt, m.dh, true, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, w.ga, w.xt,
                 s);
-  launch_bwd_dstate(dt, m.dh, w.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s);
-  launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s);
-  launch_bwd_token(dt, m.dh, w.ka, w.va, w.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s);
-  launch_dbg_reduce(w.dbg_part, w.nchunks, m.H, db_g, s);
-  if (m.T > 0) {
-    launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s);
-    launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s);
   }
-  launch_gemm_dw(dt, w.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s);
-  launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_g, s);
-  launch_dconv_reduce(w.dconv_part, m.conv_rb, m.d, dconv_w, s);
+  { StageScope ps(ST_BWD_DSTATE, s);
+    launch_bwd_dstate(dt, m.dh, w.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s); }
+  { StageScope ps(ST_COMBINE_DSTATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s); }
+  { StageScope ps(ST_BWD_TOKEN, s);
+    launch_bwd_token(dt, m.dh, w.ka, w.va, w.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s); }
+  { StageScope ps(ST_DBG_REDUCE, s); launch_dbg_reduce(w.dbg_part, w.nchunks, m.H, db_g, s); }
+  if (m.T > 0) {
+    { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }
+    { StageScope ps(ST_CONV_BWD, s);
+      launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s); }
+  }
+  { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, w.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
+  { StageScope ps(ST_DW_REDUCE, s);
+    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_g, s); }
+  { StageScope ps(ST_DCONV_REDUCE, s); launch_dconv_reduce(w.dconv_part, m.conv_rb, m.d, dconv_w, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 

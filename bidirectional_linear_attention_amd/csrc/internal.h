@@ -10,6 +10,27 @@ namespace gbla {
 
 enum DType { F32 = 0, BF16 = 1 };
 
+// stages timed by the optional profiling window (gbla_profile_begin/end)
+enum StageId {
+  ST_SCHEDULE, ST_PACK_PROJ, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
+  ST_PACK_WT, ST_PROJ_BWD, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN, ST_DBG_REDUCE,
+  ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
+  kNumStages
+};
+
+// brackets the launches of one stage with events while a profiling window is open
+class StageScope {
+ public:
+  StageScope(int stage_id, hipStream_t s);
+  ~StageScope();
+  StageScope(const StageScope&) = delete;
+  StageScope& operator=(const StageScope&) = delete;
+
+ private:
+  int rec_;
+  hipStream_t s_;
+};
+
 // tokens per chunk of the split-L reductions and per-token attention kernels
 constexpr int kChunk = 256;
 

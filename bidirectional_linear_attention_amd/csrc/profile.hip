@@ -1,0 +1,115 @@
+// Optional per-stage timing of the library's launches with HIP events.
+//
+// While a profiling window is open (gbla_profile_begin .. gbla_profile_end),
+// every stage of gbla_forward / gbla_backward records one event before and one
+// after its kernel(s) on the caller's stream, so the elapsed time between the
+// two is that stage's device time on that stream. gbla_profile_end waits for
+// the recorded events and returns per-stage totals. The window is process-wide
+// state meant for benchmarking; it is not meant for concurrent callers.
+#include <mutex>
+#include <vector>
+
+#include "gbla.h"
+#include "internal.h"
+
+namespace gbla {
+
+namespace {
+const char* kStageNames[kNumStages] = {
+    "schedule", "pack_proj", "proj_fwd", "state_partial", "combine_state", "readout",
+    "pack_wt", "proj_bwd", "bwd_dstate", "combine_dstate", "bwd_token", "dbg_reduce",
+    "gemm_dx", "conv_bwd", "gemm_dw", "dw_reduce", "dconv_reduce",
+};
+
+struct Profiler {
+  std::mutex mu;
+  bool active = false;
+  int capacity = 0;
+  int used = 0;
+  std::vector<hipEvent_t> ev;  // 2 per record
+  std::vector<int> stage;
+};
+Profiler& prof() {
+  static Profiler p;
+  return p;
+}
+}  // namespace
+
+StageScope::StageScope(int stage_id, hipStream_t s) : rec_(-1), s_(s) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.active || p.used >= p.capacity) return;
+  rec_ = p.used++;
+  p.stage[rec_] = stage_id;
+  (void)hipEventRecord(p.ev[2 * rec_], s_);
+}
+
+StageScope::~StageScope() {
+  if (rec_ < 0) return;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  (void)hipEventRecord(p.ev[2 * rec_ + 1], s_);
+}
+
+}  // namespace gbla
+
+using namespace gbla;
+
+extern "C" {
+
+GBLA_API gbla_status gbla_profile_begin(int max_records) {
+  if (max_records < 1 || max_records > (1 << 20)) return GBLA_ERR_BAD_SHAPE;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.assign(2 * (size_t)max_records, nullptr);
+  p.stage.assign(max_records, -1);
+  for (auto& e : p.ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      p.active = false;
+      return GBLA_ERR_HIP;
+    }
+  p.capacity = max_records;
+  p.used = 0;
+  p.active = true;
+  return GBLA_OK;
+}
+
+GBLA_API gbla_status gbla_profile_end(double* ms_per_stage, int* launches_per_stage, int max_stages, int* n_stages) {
+  if (!ms_per_stage || !launches_per_stage || !n_stages) return GBLA_ERR_NULL_ARG;
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> g(p.mu);
+  if (!p.active) return GBLA_ERR_BAD_SHAPE;
+  const int ns = max_stages < kNumStages ? max_stages : kNumStages;
+  for (int i = 0; i < ns; ++i) {
+    ms_per_stage[i] = 0.0;
+    launches_per_stage[i] = 0;
+  }
+  gbla_status st = GBLA_OK;
+  for (int r = 0; r < p.used; ++r) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.ev[2 * r + 1]) != hipSuccess ||
+        hipEventElapsedTime(&ms, p.ev[2 * r], p.ev[2 * r + 1]) != hipSuccess) {
+      st = GBLA_ERR_HIP;
+      continue;
+    }
+    const int sid = p.stage[r];
+    if (sid >= 0 && sid < ns) {
+      ms_per_stage[sid] += ms;
+      launches_per_stage[sid] += 1;
+    }
+  }
+  for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
+  p.ev.clear();
+  p.stage.clear();
+  p.active = false;
+  p.capacity = p.used = 0;
+  *n_stages = kNumStages;
+  return st;
+}
+
+GBLA_API const char* gbla_profile_stage_name(int stage) {
+  return stage >= 0 && stage < kNumStages ? kStageNames[stage] : "unknown";
+}
+
+}  // extern "C"

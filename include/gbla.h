@@ -120,6 +120,20 @@ GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const i
                           float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/* ---- Optional per-stage timing (benchmarking aid) ----------------------
+ * gbla_profile_begin opens a process-wide window of at most max_records
+ * stage launches. While it is open, every stage of gbla_forward/gbla_backward
+ * records a HIP event before and after its kernels on the caller's stream.
+ * gbla_profile_end waits for those events, writes per-stage total device
+ * milliseconds and launch counts for min(max_stages, *n_stages) stages
+ * (names: gbla_profile_stage_name), and closes the window. Launches beyond
+ * max_records are not timed. Not meant for concurrent callers.
+ * Errors: GBLA_ERR_BAD_SHAPE (max_records out of [1, 2^20], or end without
+ * begin), GBLA_ERR_NULL_ARG, GBLA_ERR_HIP (event creation/query failed). */
+GBLA_API gbla_status gbla_profile_begin(int max_records);
+GBLA_API gbla_status gbla_profile_end(double* ms_per_stage, int* launches_per_stage, int max_stages, int* n_stages);
+GBLA_API const char* gbla_profile_stage_name(int stage);
+
 #ifdef __cplusplus
 }
 #endif
