@@ -35,8 +35,9 @@ def stage_work(stage, T, N, d, H, dh, esz, nsplit=1):
     D = H * dh
     P3 = 3 * D + H
     table = {
-        "proj_fwd": ("mfma", 2.0 * T * d * P3),
-        "proj_bwd": ("mfma", 2.0 * T * d * P3),
+        "proj_fwd": ("mfma", 2.0 * T * d * 3 * D),
+        "proj_recompute": ("mfma", 2.0 * T * d * 3 * D),
+        "conv_fwd": ("hbm", 2.0 * T * d * esz + 4.0 * T * H),
         "gemm_dx": ("mfma", 2.0 * T * P3 * d),
         "gemm_dw": ("mfma", 2.0 * T * d * P3),
         "state_partial": ("hbm", 2.0 * T * D * esz),
@@ -141,11 +142,13 @@ def main():
     dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
     dwg, dbg = torch.empty((H, d), **f32), torch.empty((H,), **f32)
     ws = torch.empty(max(gb.workspace_size(p, False), gb.workspace_size(p, True)), dtype=torch.uint8, device=dev)
+    act = torch.empty(gb.activation_size(p), dtype=torch.uint8, device=dev)
 
     def step(i):
         x, dy = xs[i % n_sets], dys[i % n_sets]
-        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, ws)
-        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, dx, dconv, dwq, dwk, dwv, dwg, dbg, ws)
+        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws)
+        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
+                         dbg, ws)
 
     for i in range(args.warmup):
         step(i)

@@ -19,7 +19,7 @@ import ctypes
 from . import _lib
 from ._lib import DTYPE_BF16, DTYPE_F32, GATE_SIGMOID, GblaError, GblaProblem
 
-__all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "gbla_forward",
+__all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "activation_size", "gbla_forward",
            "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "DTYPE_F32", "DTYPE_BF16"]
 
 
@@ -57,6 +57,12 @@ def workspace_size(p: GblaProblem, backward: bool) -> int:
     return out.value
 
 
+def activation_size(p: GblaProblem) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().gbla_activation_size(ctypes.byref(p), ctypes.byref(out)), "gbla_activation_size")
+    return out.value
+
+
 def _ptr(t):
     if t is None:
         return None
@@ -73,20 +79,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, workspace,
+def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace,
                  stream=None) -> None:
-    """Enqueue the forward pass (include/gbla.h: gbla_forward)."""
+    """Enqueue the forward pass (include/gbla.h: gbla_forward); act may be None."""
     st = _lib.load().gbla_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
-                                  _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(y), _ptr(saved), _ptr(workspace),
+                                  _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(y), _ptr(saved), _ptr(act), _ptr(workspace),
                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _lib.check(st, "gbla_forward")
 
 
-def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, dx, dconv_w, dw_q,
-                  dw_k, dw_v, dw_g, db_g, workspace, stream=None) -> None:
-    """Enqueue the backward pass (include/gbla.h: gbla_backward)."""
+def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv_w,
+                  dw_q, dw_k, dw_v, dw_g, db_g, workspace, stream=None) -> None:
+    """Enqueue the backward pass (include/gbla.h: gbla_backward); act None recomputes."""
     st = _lib.load().gbla_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
-                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(saved), _ptr(dy), _ptr(dx), _ptr(dconv_w),
+                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(saved), _ptr(act), _ptr(dy), _ptr(dx),
+                                   _ptr(dconv_w),
                                    _ptr(dw_q), _ptr(dw_k), _ptr(dw_v), _ptr(dw_g), _ptr(db_g), _ptr(workspace),
                                    ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _lib.check(st, "gbla_backward")
@@ -109,23 +116,28 @@ def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads):
     return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype)
 
 
-def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, workspace=None):
-    """Allocate y, saved (and the workspace unless given) and run gbla_forward.
-    Returns (y [T, H*d_h], saved [N, H, d_h*d_h + d_h] float32)."""
+def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, workspace=None,
+            save_activations: bool = True):
+    """Allocate y, saved, the activation cache (if save_activations) and the
+    workspace (unless given) and run gbla_forward.
+    Returns (y [T, H*d_h], saved [N, H, d_h*d_h + d_h] float32, act or None)."""
     torch = _torch()
     p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
     dev = x.device
     y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
     saved = torch.empty((p.num_seqs, p.num_heads, p.head_dim * p.head_dim + p.head_dim), dtype=torch.float32,
                         device=dev)
+    act = torch.empty(activation_size(p), dtype=torch.uint8, device=dev) if save_activations else None
     if workspace is None:
         workspace = torch.empty(workspace_size(p, False), dtype=torch.uint8, device=dev)
-    gbla_forward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, workspace)
-    return y, saved
+    gbla_forward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace)
+    return y, saved, act
 
 
-def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, num_heads: int, workspace=None) -> dict:
-    """Allocate the gradients (and the workspace unless given) and run gbla_backward.
+def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num_heads: int,
+             workspace=None) -> dict:
+    """Allocate the gradients (and the workspace unless given) and run
+    gbla_backward; act is forward's activation cache or None (recompute).
     Returns dict dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g."""
     torch = _torch()
     p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
@@ -136,8 +148,8 @@ def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, num_head
              dw_g=torch.empty(w_g.shape, **f32), db_g=torch.empty(b_g.shape, **f32))
     if workspace is None:
         workspace = torch.empty(workspace_size(p, True), dtype=torch.uint8, device=dev)
-    gbla_backward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, dy, g["dx"], g["dconv_w"], g["dw_q"],
-                  g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace)
+    gbla_backward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, g["dx"], g["dconv_w"],
+                  g["dw_q"], g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace)
     return g
 
 

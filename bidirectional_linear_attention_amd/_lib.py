@@ -42,8 +42,9 @@ _SIGNATURES = {
     "gbla_version": (ctypes.c_int, []),
     "gbla_saved_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
     "gbla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
-    "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 10 + [_vp, _sz, _vp]),
-    "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 17 + [_vp, _sz, _vp]),
+    "gbla_activation_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
+    "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
+    "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 18 + [_vp, _sz, _vp]),
     "gbla_profile_begin": (ctypes.c_int, [ctypes.c_int]),
     "gbla_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),

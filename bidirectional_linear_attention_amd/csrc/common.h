@@ -129,6 +129,43 @@ template <> __device__ __forceinline__ void mma4<float>(f32x4& acc, const float*
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// ---------------------------------------------------------------- k-major LDS operands
+// tile is a k-major LDS tile (row = k, column = m or n; pitch ld elements).
+// Lane (g = lane / 16, i = lane % 16) receives tile[kb + m][cb + i] for
+// m = 0..3, where kb may differ between the four 16-lane groups.
+//
+// For 16-bit data this is one ds_read_b64_tr_b16: within each group of 16
+// lanes, lane j addresses the 4 elements tile[kb + j/4][cb + 4(j%4) .. +3] and
+// the hardware hands lane i the element (m, i%4) of the row loaded by lane
+// 4m + i/4, i.e. tile[kb + m][cb + i]. ld and cb must be multiples of 4.
+typedef short s16x4_tr __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_tr lds_s16x4_tr;
+
+__device__ __forceinline__ uint2 tr_read4(const bf16* tile, int ld, int kb, int cb, int lane) {
+  const int j = lane & 15;
+  const bf16* p = tile + (kb + (j >> 2)) * ld + cb + 4 * (j & 3);
+  const s16x4_tr r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tr*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
+// eight k values kb..kb+7 of column cb + lane % 16 as an MFMA fragment
+template <typename T> __device__ __forceinline__ Frag8<T> frag_kmajor(const T* tile, int ld, int kb, int cb, int lane);
+template <> __device__ __forceinline__ Frag8<bf16> frag_kmajor<bf16>(const bf16* tile, int ld, int kb, int cb,
+                                                                    int lane) {
+  const uint2 lo = tr_read4(tile, ld, kb, cb, lane), hi = tr_read4(tile, ld, kb + 4, cb, lane);
+  Frag8<bf16> f;
+  f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return f;
+}
+template <> __device__ __forceinline__ Frag8<float> frag_kmajor<float>(const float* tile, int ld, int kb, int cb,
+                                                                      int lane) {
+  const float* p = tile + kb * ld + cb + (lane & 15);
+  Frag8<float> f;
+  f.lo = make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]);
+  f.hi = make_float4(p[4 * ld], p[5 * ld], p[6 * ld], p[7 * ld]);
+  return f;
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ float sigmoidf_(float s) { return 1.f / (1.f + __expf(-s)); }
 // phi(u) = elu(u) + 1
@@ -175,6 +212,41 @@ __device__ __forceinline__ int seq_end_of(const int32_t* __restrict__ cu, int ns
   int e = cu[lo + 1];
   return e <= t ? t + 1 : (e > T ? T : e);
 }
+
+// Walks consecutive tokens t0, t0+1, ... tracking their sequence: pos(t) and
+// end(t) as pos_in_seq / seq_end_of, with one binary search at t0 and an
+// advance over the offsets only where a sequence boundary is crossed.
+// Must be queried with non-decreasing t.
+struct SeqCursor {
+  const int32_t* cu;
+  int nseq, T, b, start, stop;
+  __device__ SeqCursor(const int32_t* cu_, int nseq_, int t0, int T_) : cu(cu_), nseq(nseq_), T(T_) {
+    int lo = 0, hi = nseq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= t0) lo = mid; else hi = mid;
+    }
+    b = lo;
+    start = cu[b];
+    stop = cu[b + 1];
+  }
+  __device__ __forceinline__ void seek(int t) {
+    while (t >= stop && b + 1 < nseq) {
+      ++b;
+      start = stop;
+      stop = cu[b + 1];
+    }
+  }
+  __device__ __forceinline__ int pos(int t) {
+    seek(t);
+    const int p = t - start;
+    return p < 0 ? 0 : (p > t ? t : p);
+  }
+  __device__ __forceinline__ int end(int t) {
+    seek(t);
+    return stop <= t ? t + 1 : (stop > T ? T : stop);
+  }
+};
 
 // chunk table entry: one run of <= chunk tokens inside one sequence
 struct Chunk { int seq, start, end, pad; };

@@ -30,35 +30,55 @@ Dims dims_of(const gbla_problem* p) {
   m.N = p->num_seqs; m.T = p->total_tokens; m.d = p->d_model; m.H = p->num_heads; m.dh = p->head_dim;
   m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.NP = proj_cols(m.dh); m.Kp = grad_cols(m.H, m.dh);
   m.slots = max_chunks(m.T, m.N);
-  const int tiles = ((m.d + 127) / 128) * ((m.Kp + 127) / 128);
-  int ns = (1024 + tiles - 1) / tiles;
-  ns = std::min(ns, std::max(1, (m.T + 511) / 512));
+  const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+  const int tiles = dw_tiles(dt, m.d, m.Kp);
+  int ns = (256 + tiles - 1) / tiles;                     // about one dW block per CU
+  ns = std::min(ns, std::max(1, (m.T + 1023) / 1024));   // at least 1024 tokens per split
   m.nsplit = std::max(1, std::min(ns, 64));
   m.conv_rb = conv_bwd_row_blocks(m.T);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
   return m;
 }
 
+// activations kept from the forward for the backward
+struct Act { void* xt; void* qa; void* ka; void* va; float* ga; };
+
+Act carve_act(const Dims& m, Carver& c, char* base) {
+  Act a;
+  const size_t TD = (size_t)m.T * m.D * m.esz;
+  a.xt = c.take<char>(base, (size_t)m.T * m.d * m.esz);
+  a.qa = c.take<char>(base, TD);
+  a.ka = c.take<char>(base, TD);
+  a.va = c.take<char>(base, TD);
+  a.ga = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
+  return a;
+}
+
+size_t act_bytes(const Dims& m) {
+  Carver c;
+  carve_act(m, c, nullptr);
+  return c.off;
+}
+
 struct FwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* qa; void* ka; void* va; float* partial;
+  int* nchunks; int* chunk_off; Chunk* tab; void* wp; float* partial; Act act;
 };
 struct BwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; void* qa; void* ka; void* va; float* ga; void* xt;
-  float* partial; float* dsz; float* dbg_part; void* G; float* dxt; float* dw_part; float* dconv_part;
+  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
+  void* G; float* dxt; float* dw_part; float* dconv_part; Act act;
 };
 
+// The workspace always has room for the activations, so it suffices whether or
+// not the caller passes an activation cache.
 size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
   Carver c;
   FwdWs t;
-  const size_t TD = (size_t)m.T * m.D * m.esz;
   t.nchunks = c.take<int>(base, sizeof(int));
   t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
-  t.qa = c.take<char>(base, TD);
-  t.ka = c.take<char>(base, TD);
-  t.va = c.take<char>(base, TD);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
+  t.act = carve_act(m, c, base);
   if (w) *w = t;
   return c.off;
 }
@@ -66,17 +86,11 @@ size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
 size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   Carver c;
   BwdWs t;
-  const size_t TD = (size_t)m.T * m.D * m.esz;
   t.nchunks = c.take<int>(base, sizeof(int));
   t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
   t.wt = c.take<char>(base, (size_t)m.d * m.Kp * m.esz);
-  t.qa = c.take<char>(base, TD);
-  t.ka = c.take<char>(base, TD);
-  t.va = c.take<char>(base, TD);
-  t.ga = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
-  t.xt = c.take<char>(base, (size_t)m.T * m.d * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
   t.dsz = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H * m.E);
   t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
@@ -84,6 +98,7 @@ size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   t.dxt = c.take<float>(base, sizeof(float) * (size_t)m.T * m.d);
   t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
   t.dconv_part = c.take<float>(base, sizeof(float) * (size_t)std::max(1, m.conv_rb) * m.d * 4);
+  t.act = carve_act(m, c, base);
   if (w) *w = t;
   return c.off;
 }
@@ -122,7 +137,7 @@ const char* gbla_status_string(int status) {
   }
 }
 
-int gbla_version(void) { return 1; }
+int gbla_version(void) { return 2; }
 
 gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes) {
   if (!bytes) return GBLA_ERR_NULL_ARG;
@@ -141,41 +156,53 @@ gbla_status gbla_workspace_size(const gbla_problem* p, int backward, size_t* byt
   return GBLA_OK;
 }
 
+gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes) {
+  if (!bytes) return GBLA_ERR_NULL_ARG;
+  const gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  *bytes = act_bytes(dims_of(p));
+  return GBLA_OK;
+}
+
 gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                         void* y, float* saved, void* workspace, size_t workspace_bytes, void* stream) {
+                         void* y, float* saved, void* act, void* workspace, size_t workspace_bytes, void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
   if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !workspace) return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
-  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)y, (const void*)saved, (const void*)workspace})
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)y, (const void*)saved, (const void*)act,
+                        (const void*)workspace})
     if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
   if (!aligned(b_g, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
   const Dims m = dims_of(p);
   FwdWs w;
   if (workspace_bytes < plan_fwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
+  if (act) {
+    Carver c;
+    w.act = carve_act(m, c, static_cast<char*>(act));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+  const Act& A = w.act;
 
   (void)hipGetLastError();
   { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s); }
-  if (m.T > 0) {
-    StageScope ps(ST_PROJ_FWD, s);
-    launch_proj(dt, m.dh, false, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, nullptr,
-                nullptr, s);
-  }
+  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
+  { StageScope ps(ST_CONV_FWD, s);
+    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, A.xt, A.ga, s); }
+  { StageScope ps(ST_PROJ_FWD, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
   { StageScope ps(ST_STATE_PARTIAL, s);
-    launch_state_partial(dt, m.dh, w.ka, w.va, w.nchunks, w.tab, m.slots, m.H, w.partial, s); }
+    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, s); }
   { StageScope ps(ST_COMBINE_STATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s); }
-  { StageScope ps(ST_READOUT, s); launch_readout(dt, m.dh, w.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s); }
+  { StageScope ps(ST_READOUT, s); launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 
 gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                           const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                          const float* saved, const void* dy, void* dx, float* dconv_w, float* dw_q, float* dw_k,
-                          float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
+                          const float* saved, const void* act, const void* dy, void* dx, float* dconv_w, float* dw_q,
+                          float* dw_k, float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
                           void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
@@ -183,41 +210,47 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
       !dw_v || !dw_g || !db_g || !workspace)
     return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !dy || !dx)) return GBLA_ERR_NULL_ARG;
-  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)saved, dy, (const void*)dx, (const void*)dw_q,
-                        (const void*)dw_k, (const void*)dw_v, (const void*)dw_g, (const void*)workspace})
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)saved, act, dy, (const void*)dx,
+                        (const void*)dw_q, (const void*)dw_k, (const void*)dw_v, (const void*)dw_g,
+                        (const void*)workspace})
     if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
   if (!aligned(b_g, 4) || !aligned(db_g, 4) || !aligned(dconv_w, 4) || !aligned(cu_seqlens, 4))
     return GBLA_ERR_MISALIGNED;
   const Dims m = dims_of(p);
   BwdWs w;
   if (workspace_bytes < plan_bwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
+  if (act) {
+    Carver c;
+    w.act = carve_act(m, c, static_cast<char*>(const_cast<void*>(act)));
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+  const Act& A = w.act;
 
   (void)hipGetLastError();
   { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, w.wp, s); }
   { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s); }
-  if (m.T > 0) {
-    StageScope ps(ST_PROJ_BWD, s);
-    launch_proj(dt, m.dh, true, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w.wp, b_g, w.qa, w.ka, w.va, w.ga, w.xt,
-                s);
+  if (!act) {  // recompute x~, g, phi(q), phi(k), v into the workspace
+    { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
+    { StageScope ps(ST_CONV_RECOMPUTE, s);
+      launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, A.xt, A.ga, s); }
+    { StageScope ps(ST_PROJ_RECOMPUTE, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
   }
   { StageScope ps(ST_BWD_DSTATE, s);
-    launch_bwd_dstate(dt, m.dh, w.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s); }
+    launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s); }
   { StageScope ps(ST_COMBINE_DSTATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s); }
   { StageScope ps(ST_BWD_TOKEN, s);
-    launch_bwd_token(dt, m.dh, w.ka, w.va, w.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s); }
-  { StageScope ps(ST_DBG_REDUCE, s); launch_dbg_reduce(w.dbg_part, w.nchunks, m.H, db_g, s); }
+    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s); }
+  { StageScope ps(ST_DBG_REDUCE, s); launch_sum_parts(w.dbg_part, m.H, 0, w.nchunks, db_g, s); }
   if (m.T > 0) {
     { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }
     { StageScope ps(ST_CONV_BWD, s);
       launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s); }
   }
-  { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, w.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
+  { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, A.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
   { StageScope ps(ST_DW_REDUCE, s);
     launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_g, s); }
-  { StageScope ps(ST_DCONV_REDUCE, s); launch_dconv_reduce(w.dconv_part, m.conv_rb, m.d, dconv_w, s); }
+  { StageScope ps(ST_DCONV_REDUCE, s); launch_sum_parts(w.dconv_part, 4 * m.d, m.conv_rb, nullptr, dconv_w, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 

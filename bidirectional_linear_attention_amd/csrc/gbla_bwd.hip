@@ -12,12 +12,13 @@
 // and the conv chain rule.
 //
 // Kernels:
-//   (k_proj in backward mode recomputes phi(q), phi(k), v, g and writes x~)
+//   (without an activation cache, k_conv_fwd + k_proj recompute x~, g, phi(q), phi(k), v)
 //   k_bwd_dstate  per (chunk, head): y, dn, dden, dq -> G; partial [dS | dz]
 //   k_bwd_token   per (chunk, head): dk, dv, ds -> G; partial db_g
-//   k_gemm_nt     dX~ = G Wt^T (MFMA)
-//   k_gemm_tn     split-token partials of X~^T G (MFMA), then k_dw_reduce
-//   k_conv_bwd    dx and per-block partial dconv_w, then k_dconv_reduce
+//   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA)
+//   k_gemm_dw     split-token partials of X~^T G (pipelined MFMA), then k_dw_reduce
+//   k_conv_bwd    dx and per-block partial dconv_w (summed by k_sum_parts)
+#include "gemm.h"
 #include "internal.h"
 
 namespace gbla {
@@ -66,6 +67,13 @@ __device__ __forceinline__ void wave_reduce_state(float* red, const f32x4 (&acc)
 }
 
 // ============================================================== dS, dz and dq
+// Block = one chunk x one head; tiles of 64 tokens of q~ and dy are staged in
+// LDS with 16-byte loads, each wave then works on 16 of those tokens:
+//   [num | den] = q~ [S | z]             (MFMA, A rows from LDS)
+//   dn, dden from dy and y = num / den   (C-tile order, LDS reads)
+//   dq~ = dn S^T + dden z                (MFMA, dn staged back through LDS)
+//   dS += q~^T dn, dz += q~^T dden       (K=16 MFMAs on C-tile registers)
+// dq is staged in LDS over the wave's own q~ rows and written with 16-byte stores.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, const T* __restrict__ dy,
                                                     const float* __restrict__ saved, const int* __restrict__ nchunks,
@@ -76,9 +84,11 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   constexpr int LD = DH + 16 / (int)sizeof(T);
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
+  constexpr int ST = 64, V8 = DH / 8;
   __shared__ __align__(16) T Bsz[P * NR * LD];  // [S | z] as B of q~ [S|z]:  Bsz[n][i]
   __shared__ __align__(16) T Brm[P * DH * LD];  // S as B of dn S^T:          Brm[a][n] = S[a][n]
-  __shared__ __align__(16) T dns[4 * 16 * LD];  // per-wave dn rows
+  __shared__ __align__(16) T qs[ST * LD];       // q~ tile, then dq
+  __shared__ __align__(16) T ys[ST * LD];       // dy tile, then dn
   __shared__ float zs[DH];
   __shared__ float red[E];
 
@@ -99,7 +109,6 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   }
   stage_mat<T, DH, false>(Brm, LD, st, tid);
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
-  __syncthreads();
 
   f32x4 dS[FB][FB];
   float dz[FB];
@@ -109,15 +118,21 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
 #pragma unroll
     for (int b = 0; b < FB; ++b) dS[a][b] = zero4();
   }
-  T* dnw = dns + w * 16 * LD;
+  const int r0 = 16 * w;  // this wave's rows of the staged tile
 
-  for (int tb = ch.start; tb < ch.end; tb += 64) {  // uniform trip count (barriers inside)
-    const int t0 = tb + 16 * w;
-    const int ta = t0 + col;
+  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      const bool ok = t < ch.end;
+      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+      frag_store(qs + r * LD + c, ok ? frag_load(qa + o) : frag_zero<T>());
+      frag_store(ys + r * LD + c, ok ? frag_load(dy + o) : frag_zero<T>());
+    }
+    __syncthreads();
     Frag8<T> a[DH / 32];
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s)
-      a[s] = ta < ch.end ? frag_load(qa + (size_t)ta * D + h * DH + 32 * s + 8 * grp) : frag_zero<T>();
+    for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
     f32x4 acc[FB + 1];
 #pragma unroll
     for (int nt = 0; nt <= FB; ++nt) {
@@ -131,30 +146,30 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
     float qv[FB][4], dn[FB][4], dden[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * grp + r;
-      const bool ok = t < ch.end;
+      const int row = r0 + 4 * grp + r;
+      const bool ok = tb + row < ch.end;
       const float den = col0_bcast(acc[FB][r], lane);
       const float inv = ok ? 1.f / den : 0.f;
-      const size_t base = (size_t)(ok ? t : ch.start) * D + h * DH + col;
       float p = 0.f, dyv[FB];
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {
-        dyv[nt] = ok ? to_f<T>(dy[base + 16 * nt]) : 0.f;
-        qv[nt][r] = ok ? to_f<T>(qa[base + 16 * nt]) : 0.f;
+        dyv[nt] = to_f<T>(ys[row * LD + 16 * nt + col]);
+        qv[nt][r] = to_f<T>(qs[row * LD + 16 * nt + col]);
         p += dyv[nt] * (acc[nt][r] * inv);
       }
       p = row16_sum(p);
       dden[r] = -p * inv;
 #pragma unroll
-      for (int nt = 0; nt < FB; ++nt) {
-        dn[nt][r] = dyv[nt] * inv;
-        dnw[(4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dn[nt][r]);
-      }
+      for (int nt = 0; nt < FB; ++nt) dn[nt][r] = dyv[nt] * inv;
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) ys[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dn[nt][r]);
     __syncthreads();
     Frag8<T> dnf[DH / 32];
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s) dnf[s] = frag_load(dnw + col * LD + 32 * s + 8 * grp);
+    for (int s = 0; s < DH / 32; ++s) dnf[s] = frag_load(ys + (r0 + col) * LD + 32 * s + 8 * grp);
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
       f32x4 dq = zero4();
@@ -165,19 +180,20 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
           mma8(dq, dnf[s], frag_load(Brm + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
       const float za = zs[16 * nt + col];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = t0 + 4 * grp + r;
-        if (t < ch.end) {
-          const float v = (dq[r] + dden[r] * za) * fminf(1.f, qv[nt][r]);
-          G[(size_t)t * Kp + h * DH + 16 * nt + col] = from_f<T>(v);
-        }
-      }
+      for (int r = 0; r < 4; ++r)
+        qs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>((dq[r] + dden[r] * za) * fminf(1.f, qv[nt][r]));
     }
 #pragma unroll
     for (int ia = 0; ia < FB; ++ia) {
       dz[ia] += (dden[0] * qv[ia][0] + dden[1] * qv[ia][1]) + (dden[2] * qv[ia][2] + dden[3] * qv[ia][3]);
 #pragma unroll
       for (int nb = 0; nb < FB; ++nb) mma4<T>(dS[ia][nb], qv[ia], dn[nb]);
+    }
+    __syncthreads();
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      if (t < ch.end) frag_store(G + (size_t)t * Kp + h * DH + c, frag_load(qs + r * LD + c));
     }
     __syncthreads();
   }
@@ -202,6 +218,11 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 }
 
 // ============================================================== dk, dv, ds
+// Same tiling as k_bwd_dstate: phi(k), v and g of 64 tokens are staged in LDS;
+//   dk~ = v dS^T + dz,  dv = k~ dS      (MFMA, A rows from LDS, k~ = g phi(k))
+//   dg = phi(k) . dk~,  dk = g dk~ (.) phi'(k),  ds = dg g (1 - g)
+// dk and dv are staged over the wave's own phi(k) and v rows and written to G
+// with 16-byte stores.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, const T* __restrict__ va,
                                                    const float* __restrict__ ga, const float* __restrict__ dsz,
@@ -212,8 +233,12 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   constexpr int LD = DH + 16 / (int)sizeof(T);
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
+  constexpr int ST = 64, V8 = DH / 8;
   __shared__ __align__(16) T Srm[P * DH * LD];  // dS as B of v dS^T: Srm[i][n] = dS[i][n]
   __shared__ __align__(16) T Str[P * DH * LD];  // dS as B of k~ dS:  Str[n][i] = dS[i][n]
+  __shared__ __align__(16) T ks[ST * LD];       // phi(k) tile, then dk
+  __shared__ __align__(16) T vs[ST * LD];       // v tile, then dv
+  __shared__ float gs[ST];
   __shared__ float dzs[DH];
   __shared__ float wsum[4];
 
@@ -228,20 +253,27 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   stage_mat<T, DH, false>(Srm, LD, st, tid);
   stage_mat<T, DH, true>(Str, LD, st, tid);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
-  __syncthreads();
 
   float dbg = 0.f;
   const int gcol0 = 3 * D + H;  // first zero-pad column of G
-  for (int t0 = ch.start + 16 * w; t0 < ch.end; t0 += 64) {
-    const int ta = t0 + col;
-    const bool okA = ta < ch.end;
-    const float gA = okA ? ga[(size_t)ta * H + h] : 0.f;
+  const int r0 = 16 * w;
+  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      const bool ok = t < ch.end;
+      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+      frag_store(ks + r * LD + c, ok ? frag_load(ka + o) : frag_zero<T>());
+      frag_store(vs + r * LD + c, ok ? frag_load(va + o) : frag_zero<T>());
+    }
+    for (int r = tid; r < ST; r += 256) gs[r] = tb + r < ch.end ? ga[(size_t)(tb + r) * H + h] : 0.f;
+    __syncthreads();
+    const float gA = gs[r0 + col];
     Frag8<T> vf[DH / 32], kf[DH / 32];
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) {
-      const size_t o = (size_t)(okA ? ta : ch.start) * D + h * DH + 32 * s + 8 * grp;
-      vf[s] = okA ? frag_load(va + o) : frag_zero<T>();
-      const Frag8<T> pk = okA ? frag_load(ka + o) : frag_zero<T>();
+      vf[s] = frag_load(vs + (r0 + col) * LD + 32 * s + 8 * grp);
+      const Frag8<T> pk = frag_load(ks + (r0 + col) * LD + 32 * s + 8 * grp);
       float kt[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) kt[e] = gA * frag_get(pk, e);
@@ -260,36 +292,48 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
           mma8(dvv[nt], kf[s], frag_load(Str + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
         }
     }
+    float dkv[FB][4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = t0 + 4 * grp + r;
+      const int row = r0 + 4 * grp + r;
+      const int t = tb + row;
       const bool ok = t < ch.end;
-      const size_t base = (size_t)(ok ? t : ch.start) * D + h * DH + col;
-      const float g = ok ? ga[(size_t)t * H + h] : 0.f;
+      const float g = gs[row];
       float kv[FB], dk[FB], dg = 0.f;
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {
-        kv[nt] = ok ? to_f<T>(ka[base + 16 * nt]) : 0.f;
+        kv[nt] = to_f<T>(ks[row * LD + 16 * nt + col]);
         dk[nt] = dkt[nt][r] + dzs[16 * nt + col];
         dg += kv[nt] * dk[nt];
       }
       dg = row16_sum(dg);
-      if (ok) {
-        T* grow = G + (size_t)t * Kp;
 #pragma unroll
-        for (int nt = 0; nt < FB; ++nt) {
-          grow[D + h * DH + 16 * nt + col] = from_f<T>(g * dk[nt] * fminf(1.f, kv[nt]));
-          grow[2 * D + h * DH + 16 * nt + col] = from_f<T>(dvv[nt][r]);
-        }
-        const float ds = dg * g * (1.f - g);
-        if (col == 0) {
-          grow[3 * D + h] = from_f<T>(ds);
-          dbg += ds;
-        }
-        if (h == 0)
-          for (int c = gcol0 + col; c < Kp; c += 16) grow[c] = from_f<T>(0.f);
+      for (int nt = 0; nt < FB; ++nt) dkv[nt][r] = g * dk[nt] * fminf(1.f, kv[nt]);
+      const float ds = dg * g * (1.f - g);
+      if (ok && col == 0) {
+        G[(size_t)t * Kp + 3 * D + h] = from_f<T>(ds);
+        dbg += ds;
+      }
+      if (ok && h == 0)
+        for (int c = gcol0 + col; c < Kp; c += 16) G[(size_t)t * Kp + c] = from_f<T>(0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) {
+        ks[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dkv[nt][r]);
+        vs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dvv[nt][r]);
+      }
+    __syncthreads();
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      if (t < ch.end) {
+        frag_store(G + (size_t)t * Kp + D + h * DH + c, frag_load(ks + r * LD + c));
+        frag_store(G + (size_t)t * Kp + 2 * D + h * DH + c, frag_load(vs + r * LD + c));
       }
     }
+    __syncthreads();
   }
   dbg += __shfl_xor(dbg, 16, 64);
   dbg += __shfl_xor(dbg, 32, 64);
@@ -340,155 +384,98 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
 }
 
 // ============================================================== dX~ = G Wt^T
-// C[M][N] = A[M][K] B[N][K]^T, both operands k-contiguous; 128x128 block tile,
-// 2x2 waves of 64x64, fp32 output. Requires K % 8 == 0.
+// C[M=T][N=d] = G[T][Kp] Wt[d][Kp]^T, fp32 output; 256 x 256 tiles, 8 waves.
+template <typename T> struct DxCfg { using S = GemmShape<T, 256, 256, 32, 4, 2>; };
+template <> struct DxCfg<float> { using S = GemmShape<float, 64, 128, 32, 2, 2>; };
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_gemm_nt(const T* __restrict__ A, const T* __restrict__ B, int M, int N,
-                                                 int K, float* __restrict__ C) {
-  constexpr int BM = 128, BN = 128;
-  constexpr int BK = 128 / (int)sizeof(T), LD = BK + 16 / (int)sizeof(T), G8 = BK / 8;
-  __shared__ __align__(16) T As[BM * LD];
-  __shared__ __align__(16) T Bs[BN * LD];
-  const int mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
+__global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G, const T* __restrict__ wt,
+                                                                   int T_, int d, int Kp, float* __restrict__ dxt) {
+  using S = typename DxCfg<T>::S;
+  __shared__ __align__(16) T smem[2 * S::STAGE];
+  const int mtiles = (T_ + S::BM - 1) / S::BM, ntiles = (d + S::BN - 1) / S::BN;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * ntiles);
   if (lid >= mtiles * ntiles) return;
   const int mt = lid / ntiles, nt = lid - mt * ntiles;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
-  const int wm = w >> 1, wn = w & 1;
-  f32x4 acc[4][4];
+  const int m0 = mt * S::BM, n0 = nt * S::BN;
+  f32x4 acc[S::FM][S::FN];
+  gemm_nt_mainloop<T, S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp, min(S::BN, d - n0),
+                         Kp, smem, acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+  const int wm = w / S::WGN, wn = w % S::WGN;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    for (int it = tid; it < BM * G8; it += 256) {
-      const int r = it / G8, g8 = it - r * G8;
-      const int c = k0 + g8 * 8;
-      const bool okA = (m0 + r) < M && c < K;
-      frag_store(As + r * LD + g8 * 8, okA ? frag_load(A + (size_t)(m0 + r) * K + c) : frag_zero<T>());
-      const bool okB = (n0 + r) < N && c < K;
-      frag_store(Bs + r * LD + g8 * 8, okB ? frag_load(B + (size_t)(n0 + r) * K + c) : frag_zero<T>());
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      Frag8<T> a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = frag_load(As + (64 * wm + 16 * i + col) * LD + ks + 8 * grp);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = frag_load(Bs + (64 * wn + 16 * j + col) * LD + ks + 8 * grp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mma8(acc[i][j], a[i], b[j]);
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < S::FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * grp + r;
-      if (m >= M) continue;
+      const int m = m0 + wm * S::WTM + 16 * i + 4 * grp + r;
+      if (m >= T_) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + col;
-        if (n < N) C[(size_t)m * N + n] = acc[i][j][r];
+      for (int j = 0; j < S::FN; ++j) {
+        const int n = n0 + wn * S::WTN + 16 * j + col;
+        if (n < d) dxt[(size_t)m * d + n] = acc[i][j][r];
       }
     }
 }
 
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, float* dxt, hipStream_t s) {
-  const int n = ((T + 127) / 128) * ((d + 127) / 128);
-  if (dt == BF16)
-    hipLaunchKernelGGL(k_gemm_nt<bf16>, dim3(xcd_grid(n)), dim3(256), 0, s, (const bf16*)G, (const bf16*)wt, T, d,
-                       Kp, dxt);
-  else
-    hipLaunchKernelGGL(k_gemm_nt<float>, dim3(xcd_grid(n)), dim3(256), 0, s, (const float*)G, (const float*)wt, T,
-                       d, Kp, dxt);
+  if (dt == BF16) {
+    using S = DxCfg<bf16>::S;
+    const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
+    if (n) hipLaunchKernelGGL(k_gemm_dx<bf16>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const bf16*)G,
+                              (const bf16*)wt, T, d, Kp, dxt);
+  } else {
+    using S = DxCfg<float>::S;
+    const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
+    if (n) hipLaunchKernelGGL(k_gemm_dx<float>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const float*)G,
+                              (const float*)wt, T, d, Kp, dxt);
+  }
 }
 
 // ============================================================== dW = X~^T G (split over tokens)
-// part[ks][m][n] = sum over tokens t of split ks of A[t][m] B[t][n]. Both
-// operands are token-major, so the LDS tiles are written transposed (pairs of
-// tokens per 32-bit store) and read k-contiguous.
-template <typename T> __device__ __forceinline__ void store_pair(T* p, float a, float b);
-template <> __device__ __forceinline__ void store_pair<bf16>(bf16* p, float a, float b) {
-  *reinterpret_cast<uint32_t*>(p) = (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16);
-}
-template <> __device__ __forceinline__ void store_pair<float>(float* p, float a, float b) {
-  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+// part[ks][m][n] = sum over the tokens of split ks of X~[t][m] G[t][n]; both
+// operands are token-major and are transposed while staged in LDS.
+template <typename T> struct DwCfg { using S = GemmShapeTN<T, 256, 256, 32, 4, 2>; };
+template <> struct DwCfg<float> { using S = GemmShapeTN<float, 64, 128, 32, 2, 2>; };
+
+int dw_tiles(int dt, int d, int Kp) {
+  if (dt == BF16) {
+    using S = DwCfg<bf16>::S;
+    return ((d + S::BM - 1) / S::BM) * ((Kp + S::BN - 1) / S::BN);
+  }
+  using S = DwCfg<float>::S;
+  return ((d + S::BM - 1) / S::BM) * ((Kp + S::BN - 1) / S::BN);
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_gemm_tn(const T* __restrict__ A, const T* __restrict__ B, int Tn, int M,
-                                                 int N, int tok_per_split, int nsplit, float* __restrict__ part) {
-  constexpr int BM = 128, BN = 128, BKT = 32;
-  constexpr int LD = BKT + 16 / (int)sizeof(T);
-  __shared__ __align__(16) T As[BM * LD];
-  __shared__ __align__(16) T Bs[BN * LD];
-  const int mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
+__global__ __launch_bounds__((DwCfg<T>::S::NTHREADS)) void k_gemm_dw(const T* __restrict__ xt, const T* __restrict__ G,
+                                                                   int T_, int d, int Kp, int tok_per_split,
+                                                                   int nsplit, float* __restrict__ part) {
+  using S = typename DwCfg<T>::S;
+  __shared__ __align__(16) T smem[2 * S::STAGE];
+  const int mtiles = (d + S::BM - 1) / S::BM, ntiles = (Kp + S::BN - 1) / S::BN;
   const int total = mtiles * ntiles * nsplit;
   const int lid = xcd_logical_block(blockIdx.x, total);
   if (lid >= total) return;
   const int ks = lid / (mtiles * ntiles);
   const int rem = lid - ks * mtiles * ntiles;
   const int mt = rem / ntiles, nt = rem - mt * ntiles;
-  const int m0 = mt * BM, n0 = nt * BN;
-  const int tbeg = ks * tok_per_split, tend = min(Tn, tbeg + tok_per_split);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
-  const int wm = w >> 1, wn = w & 1;
-  const int pr = tid >> 4, c8 = tid & 15;  // loader: token pair pr, 8-column group c8
-
-  f32x4 acc[4][4];
+  const int m0 = mt * S::BM, n0 = nt * S::BN;
+  const int tbeg = ks * tok_per_split, tend = min(T_, tbeg + tok_per_split);
+  f32x4 acc[S::FM][S::FN];
+  gemm_tn_mainloop<T, S>(xt + m0, d, min(S::BM, d - m0), G + n0, Kp, min(S::BN, Kp - n0), tbeg, tend, smem, acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+  const int wm = w / S::WGN, wn = w % S::WGN;
+  float* out = part + (size_t)ks * d * Kp;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = zero4();
-
-  for (int t0 = tbeg; t0 < tend; t0 += BKT) {
-    const int ta = t0 + 2 * pr, tb = ta + 1;
-    {
-      const int m = m0 + 8 * c8;
-      const bool okc = m < M;
-      const Frag8<T> f0 = okc && ta < tend ? frag_load(A + (size_t)ta * M + m) : frag_zero<T>();
-      const Frag8<T> f1 = okc && tb < tend ? frag_load(A + (size_t)tb * M + m) : frag_zero<T>();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_pair<T>(As + (8 * c8 + j) * LD + 2 * pr, frag_get(f0, j), frag_get(f1, j));
-    }
-    {
-      const int n = n0 + 8 * c8;
-      const bool okc = n < N;
-      const Frag8<T> f0 = okc && ta < tend ? frag_load(B + (size_t)ta * N + n) : frag_zero<T>();
-      const Frag8<T> f1 = okc && tb < tend ? frag_load(B + (size_t)tb * N + n) : frag_zero<T>();
-#pragma unroll
-      for (int j = 0; j < 8; ++j) store_pair<T>(Bs + (8 * c8 + j) * LD + 2 * pr, frag_get(f0, j), frag_get(f1, j));
-    }
-    __syncthreads();
-    Frag8<T> a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = frag_load(As + (64 * wm + 16 * i + col) * LD + 8 * grp);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = frag_load(Bs + (64 * wn + 16 * j + col) * LD + 8 * grp);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mma8(acc[i][j], a[i], b[j]);
-    __syncthreads();
-  }
-  float* out = part + (size_t)ks * M * N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < S::FM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + 64 * wm + 16 * i + 4 * grp + r;
-      if (m >= M) continue;
+      const int m = m0 + wm * S::WTM + 16 * i + 4 * grp + r;
+      if (m >= d) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = n0 + 64 * wn + 16 * j + col;
-        if (n < N) out[(size_t)m * N + n] = acc[i][j][r];
+      for (int j = 0; j < S::FN; ++j) {
+        const int n = n0 + wn * S::WTN + 16 * j + col;
+        if (n < Kp) out[(size_t)m * Kp + n] = acc[i][j][r];
       }
     }
 }
@@ -496,13 +483,13 @@ __global__ __launch_bounds__(256) void k_gemm_tn(const T* __restrict__ A, const 
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s) {
   const int tps = ((T + nsplit - 1) / nsplit + 31) / 32 * 32;
-  const int n = ((d + 127) / 128) * ((Kp + 127) / 128) * nsplit;
+  const int n = dw_tiles(dt, d, Kp) * nsplit;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_gemm_tn<bf16>, dim3(xcd_grid(n)), dim3(256), 0, s, (const bf16*)xt, (const bf16*)G, T, d,
-                       Kp, tps, nsplit, part);
+    hipLaunchKernelGGL(k_gemm_dw<bf16>, dim3(xcd_grid(n)), dim3(DwCfg<bf16>::S::NTHREADS), 0, s, (const bf16*)xt,
+                       (const bf16*)G, T, d, Kp, tps, nsplit, part);
   else
-    hipLaunchKernelGGL(k_gemm_tn<float>, dim3(xcd_grid(n)), dim3(256), 0, s, (const float*)xt, (const float*)G, T,
-                       d, Kp, tps, nsplit, part);
+    hipLaunchKernelGGL(k_gemm_dw<float>, dim3(xcd_grid(n)), dim3(DwCfg<float>::S::NTHREADS), 0, s,
+                       (const float*)xt, (const float*)G, T, d, Kp, tps, nsplit, part);
 }
 
 __global__ void k_dw_reduce(const float* __restrict__ part, int nsplit, int d, int H, int dh, int Kp,
@@ -529,42 +516,38 @@ void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int K
   hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(256), 0, s, part, nsplit, d, H, dh, Kp, dw_q, dw_k, dw_v, dw_g);
 }
 
-__global__ void k_dbg_reduce(const float* __restrict__ part, const int* __restrict__ nchunks, int H,
-                             float* __restrict__ db_g) {
-  const int h = blockIdx.x * blockDim.x + threadIdx.x;
-  if (h >= H) return;
-  const int nc = *nchunks;
-  float s = 0.f;
-  for (int c = 0; c < nc; ++c) s += part[(size_t)c * H + h];
-  db_g[h] = s;
-}
-
-void launch_dbg_reduce(const float* dbg_part, const int* nchunks, int H, float* db_g, hipStream_t s) {
-  hipLaunchKernelGGL(k_dbg_reduce, dim3((H + 255) / 256), dim3(256), 0, s, dbg_part, nchunks, H, db_g);
-}
-
 // ============================================================== conv backward
-// Thread = 8 channels x 8 consecutive tokens; block = 64 channels x 256 tokens.
+// Thread = 8 channels x kConvRun consecutive tokens; block = 64 channel groups
+// (512 channels) x 4 runs. Both windows slide in registers: dx~ rows u..u+3
+// (for dx) and x rows u-3..u (for dconv_w); sequence bounds come from a cursor.
 //   dx_u[c]       = sum_k w[c][k] dx~_{u+3-k}[c]      (u+3-k inside u's sequence)
 //   dconv_w[c][k] = sum_t dx~_t[c] x_{t-3+k}[c]       (t-3+k inside t's sequence)
-constexpr int kConvRows = 256;
+constexpr int kConvRun = 32;
+constexpr int kConvRows = 4 * kConvRun;
 int conv_bwd_row_blocks(int T) { return (T + kConvRows - 1) / kConvRows; }
+
+__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_conv_bwd(const float* __restrict__ dxt, const T* __restrict__ x,
                                                   const int32_t* __restrict__ cu, int nseq, int T_, int d,
                                                   const T* __restrict__ conv_w, T* __restrict__ dx,
                                                   float* __restrict__ part) {
-  __shared__ float red[32][8 * 8 * 4 + 1];
+  __shared__ float red[4][64 * 32 + 1];
   const int rb = blockIdx.x, cb = blockIdx.y;
-  const int tid = threadIdx.x, c8 = tid & 7, run = tid >> 3;
-  const int c = cb * 64 + c8 * 8;
+  const int tid = threadIdx.x, cg = tid & 63, run = tid >> 6;
+  const int c = cb * 512 + cg * 8;
   float dw[8][4];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
     for (int k = 0; k < 4; ++k) dw[j][k] = 0.f;
-  if (c < d) {
+  const int u0 = rb * kConvRows + run * kConvRun;
+  const int u1 = min(u0 + kConvRun, T_);
+  if (c < d && u0 < u1) {
     float wv[8][4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -572,71 +555,78 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const float* __restrict__ dxt,
 #pragma unroll
       for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
     }
-    const int u0 = rb * kConvRows + run * 8;
-    for (int u = u0; u < min(u0 + 8, T_); ++u) {
-      const int end = seq_end_of(cu, nseq, u, T_);
-      const int pos = pos_in_seq(cu, nseq, u);
+    // forward window g[s] = dx~_{u+s}, s = 0..3; backward window xm[s] = x_{u-s}, s = 1..3
+    float g[4][8], xm[4][8];
+#pragma unroll
+    for (int sft = 0; sft < 4; ++sft) {
+      const int t = u0 + sft;
+      if (sft < 3 && t < T_) load8f(dxt + (size_t)t * d + c, g[sft]);
+      else
+#pragma unroll
+        for (int j = 0; j < 8; ++j) g[sft][j] = 0.f;
+      const int tb = u0 - sft;
+      if (sft >= 1 && tb >= 0) {
+        const Frag8<T> f = frag_load(x + (size_t)tb * d + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xm[sft][j] = frag_get(f, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xm[sft][j] = 0.f;
+      }
+    }
+    SeqCursor cur(cu, nseq, u0, T_);
+    for (int u = u0; u < u1; ++u) {
+      if (u + 3 < T_) load8f(dxt + (size_t)(u + 3) * d + c, g[3]);
+      {
+        const Frag8<T> f = frag_load(x + (size_t)u * d + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) xm[0][j] = frag_get(f, j);
+      }
+      const int end = cur.end(u);
+      const int pos = cur.pos(u);
       float o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) o[j] = 0.f;
-      float g[8];
-      const float4 g0 = *reinterpret_cast<const float4*>(dxt + (size_t)u * d + c);
-      const float4 g1 = *reinterpret_cast<const float4*>(dxt + (size_t)u * d + c + 4);
-      g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int sh = 3 - k;
-        // dx: output token u + sh reads x_u through tap k
-        if (u + sh < end) {
-          const float4 a = *reinterpret_cast<const float4*>(dxt + (size_t)(u + sh) * d + c);
-          const float4 b = *reinterpret_cast<const float4*>(dxt + (size_t)(u + sh) * d + c + 4);
-          o[0] += wv[0][k] * a.x; o[1] += wv[1][k] * a.y; o[2] += wv[2][k] * a.z; o[3] += wv[3][k] * a.w;
-          o[4] += wv[4][k] * b.x; o[5] += wv[5][k] * b.y; o[6] += wv[6][k] * b.z; o[7] += wv[7][k] * b.w;
-        }
-        // dconv_w: output token u read x_{u-sh} through tap k
-        if (sh <= pos) {
-          const Frag8<T> xv = frag_load(x + (size_t)(u - sh) * d + c);
+        if (u + sh < end)  // output token u + sh reads x_u through tap k
 #pragma unroll
-          for (int j = 0; j < 8; ++j) dw[j][k] += g[j] * frag_get(xv, j);
-        }
+          for (int j = 0; j < 8; ++j) o[j] += wv[j][k] * g[sh][j];
+        if (sh <= pos)     // output token u read x_{u-sh} through tap k
+#pragma unroll
+          for (int j = 0; j < 8; ++j) dw[j][k] += g[0][j] * xm[sh][j];
       }
       frag_store(dx + (size_t)u * d + c, frag_from<T>(o));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        g[0][j] = g[1][j]; g[1][j] = g[2][j]; g[2][j] = g[3][j]; g[3][j] = 0.f;
+        xm[3][j] = xm[2][j]; xm[2][j] = xm[1][j]; xm[1][j] = xm[0][j];
+      }
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) red[run][c8 * 32 + j * 4 + k] = dw[j][k];
+    for (int k = 0; k < 4; ++k) red[run][cg * 32 + j * 4 + k] = dw[j][k];
   __syncthreads();
-  // 64 channels x 4 taps = 256 outputs, one per thread, summed over the 32 runs in order
-  const int oc = tid >> 2, ok = tid & 3;
-  const int cc = cb * 64 + oc;
-  float s = 0.f;
-  for (int r = 0; r < 32; ++r) s += red[r][(oc >> 3) * 32 + (oc & 7) * 4 + ok];
-  if (cc < d) part[((size_t)rb * d + cc) * 4 + ok] = s;
+  // 512 channels x 4 taps, summed over the 4 runs in a fixed order
+  for (int e = tid; e < 512 * 4; e += 256) {
+    const int cc = cb * 512 + (e >> 2);
+    if (cc < d) part[((size_t)rb * d + cc) * 4 + (e & 3)] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+  }
 }
 
 void launch_conv_bwd(int dt, const float* dxt, const void* x, const int32_t* cu, int N, int T, int d,
                      const void* conv_w, void* dx, float* dconv_part, hipStream_t s) {
-  const dim3 grid(conv_bwd_row_blocks(T), (d + 63) / 64);
+  const dim3 grid(conv_bwd_row_blocks(T), (d + 511) / 512);
+  if (grid.x == 0) return;
   if (dt == BF16)
     hipLaunchKernelGGL(k_conv_bwd<bf16>, grid, dim3(256), 0, s, dxt, (const bf16*)x, cu, N, T, d,
                        (const bf16*)conv_w, (bf16*)dx, dconv_part);
   else
     hipLaunchKernelGGL(k_conv_bwd<float>, grid, dim3(256), 0, s, dxt, (const float*)x, cu, N, T, d,
                        (const float*)conv_w, (float*)dx, dconv_part);
-}
-
-__global__ void k_dconv_reduce(const float* __restrict__ part, int nparts, int d, float* __restrict__ out) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= d * 4) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += part[(size_t)p * d * 4 + e];
-  out[e] = s;
-}
-
-void launch_dconv_reduce(const float* dconv_part, int nparts, int d, float* dconv_w, hipStream_t s) {
-  hipLaunchKernelGGL(k_dconv_reduce, dim3((d * 4 + 255) / 256), dim3(256), 0, s, dconv_part, nparts, d, dconv_w);
 }
 
 }  // namespace gbla

@@ -10,11 +10,13 @@
 //
 // Kernels (all on the caller's stream, no host synchronisation):
 //   k_schedule      chunk table of <= kChunk-token runs inside each sequence, from cu_seqlens
-//   k_pack_proj     per-head packed weights [H][3*dh+16][d]: Q, K, V columns then the gate row
-//   k_proj          fused conv + projection GEMM (MFMA) + phi + gate epilogue
+//   k_pack_proj     per-head packed weights [H][3*dh][d]: Q, K, V columns, k contiguous
+//   k_conv_fwd      causal conv -> x~, and the gates g = sigmoid(x~ w_g + b_g) of every head
+//   k_proj          projection GEMM x~ [W_Q|W_K|W_V]^h (pipelined MFMA) with phi epilogue
 //   k_state_partial split-L partial [S | z] per (chunk, head), MFMA over the token axis
 //   k_combine       fixed-order sum of the partials of each (sequence, head)
 //   k_readout       y = phi(Q) [S | z] (MFMA), divide
+#include "gemm.h"
 #include "internal.h"
 
 namespace gbla {
@@ -77,200 +79,237 @@ void launch_schedule(const int32_t* cu, int N, int T, int max_slots, int* nchunk
 }
 
 // ============================================================== weight packing
+// wp[h][n][c]: rows n < dh are W_Q[:, h*dh + n], then W_K, then W_V (k = c contiguous)
 template <typename T>
-__global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
-                            const T* __restrict__ w_g, int d, int H, int dh, T* __restrict__ wp) {
-  const int NP = 3 * dh + 16, D = H * dh;
+__global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v, int d,
+                            int H, int dh, T* __restrict__ wp) {
+  const int NP = 3 * dh, D = H * dh;
   const long total = (long)H * NP * d;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
     const int c = (int)(e % d);
     const int n = (int)((e / d) % NP);
     const int h = (int)(e / ((long)d * NP));
-    T v = from_f<T>(0.f);
-    if (n < dh) v = w_q[(long)c * D + h * dh + n];
-    else if (n < 2 * dh) v = w_k[(long)c * D + h * dh + n - dh];
-    else if (n < 3 * dh) v = w_v[(long)c * D + h * dh + n - 2 * dh];
-    else if (n == 3 * dh) v = w_g[(long)h * d + c];
-    wp[e] = v;
+    const T* src = n < dh ? w_q : (n < 2 * dh ? w_k : w_v);
+    wp[e] = src[(long)c * D + h * dh + (n % dh)];
   }
 }
 
-void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_g, int d, int H,
-                      int dh, void* wp, hipStream_t s) {
+void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
+                      hipStream_t s) {
   const long total = (long)H * proj_cols(dh) * d;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_g, d, H, dh, (bf16*)wp);
+                       (const bf16*)w_v, d, H, dh, (bf16*)wp);
   else
     hipLaunchKernelGGL(k_pack_proj<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_g, d, H, dh, (float*)wp);
+                       (const float*)w_v, d, H, dh, (float*)wp);
 }
 
-// ============================================================== fused conv + projection
-// One block = 128 packed tokens x one head; four waves of 32 rows, each wave
-// holding all 3*dh/16 + 1 output tiles of its rows. k runs over d in chunks of
-// 128 bytes per row staged in LDS; the A chunk is produced by the causal conv
-// straight from x (never written to HBM in the forward).
-template <typename T> struct GemmCfg {
-  static constexpr int BK = 128 / (int)sizeof(T);   // k elements per LDS chunk
-  static constexpr int LD = BK + 16 / (int)sizeof(T);  // LDS row pitch (16 B pad)
-};
+// ============================================================== causal conv + gate
+// One wave per token row (16 consecutive rows per wave, 64 per block); lane l
+// owns channel groups c = 8 * (l + 64 m). The three previous rows slide in
+// registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
+// reduce-scatter butterfly: 8 head partials per lane become one head total per
+// 8 lanes in 4 + 2 + 1 + 3 shuffles.
+constexpr int kConvRowsPerWave = 16;
 
-template <typename T, int DH, bool BWD>
-__global__ __launch_bounds__(256) void k_proj(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
-                                              int T_, int d, int H, const T* __restrict__ conv_w,
-                                              const T* __restrict__ wp, const float* __restrict__ b_g,
-                                              T* __restrict__ q_out, T* __restrict__ k_out, T* __restrict__ v_out,
-                                              float* __restrict__ g_out, T* __restrict__ xt_out) {
-  constexpr int BM = 128;
-  constexpr int FB = DH / 16;          // 16-wide feature blocks per head
-  constexpr int NT = 3 * FB + 1;       // + gate tile
-  constexpr int NP = NT * 16;
-  constexpr int BK = GemmCfg<T>::BK, LD = GemmCfg<T>::LD;
-  constexpr int G8 = BK / 8;
-  constexpr int AIT = BM * G8 / 256;
-  __shared__ __align__(16) T As[BM * LD];
-  __shared__ __align__(16) T Bs[NP * LD];
+__device__ __forceinline__ float butterfly8(float (&v)[8], int lane) {
+  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+  float u[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float mine = b5 ? v[4 + i] : v[i], other = b5 ? v[i] : v[4 + i];
+    u[i] = mine + __shfl_xor(other, 32, 64);
+  }
+  float q[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float mine = b4 ? u[2 + i] : u[i], other = b4 ? u[i] : u[2 + i];
+    q[i] = mine + __shfl_xor(other, 16, 64);
+  }
+  float x = (b3 ? q[1] : q[0]) + __shfl_xor(b3 ? q[0] : q[1], 8, 64);
+  x += __shfl_xor(x, 4, 64);
+  x += __shfl_xor(x, 2, 64);
+  x += __shfl_xor(x, 1, 64);
+  return x;  // total of head (lane >> 3)
+}
 
-  const int mtiles = (T_ + BM - 1) / BM;
+template <typename T>
+__global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
+                                                  int T_, int d, int H, const T* __restrict__ conv_w,
+                                                  const T* __restrict__ w_g, const float* __restrict__ b_g,
+                                                  T* __restrict__ xt, float* __restrict__ g_out) {
+  __shared__ float sacc[4][kConvRowsPerWave][8];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t_begin = (blockIdx.x * 4 + w) * kConvRowsPerWave;
+  const int t_end = min(t_begin + kConvRowsPerWave, T_);
+  const int ngroups = d / 8;
+  for (int hg = 0; hg < H; hg += 8) {
+    for (int g8 = lane; g8 < ((ngroups + 63) / 64) * 64; g8 += 64) {
+      const bool okc = g8 < ngroups;
+      const int c = g8 * 8;
+      float wv[8][4], wg[8][8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Frag8<T> f = okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 8; ++hh) {
+        const Frag8<T> f = okc && hg + hh < H ? frag_load(w_g + (size_t)(hg + hh) * d + c) : frag_zero<T>();
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wg[hh][e] = frag_get(f, e);
+      }
+      Frag8<T> xm1 = frag_zero<T>(), xm2 = frag_zero<T>(), xm3 = frag_zero<T>();
+      if (okc && t_begin < t_end) {
+        if (t_begin >= 1) xm1 = frag_load(x + (size_t)(t_begin - 1) * d + c);
+        if (t_begin >= 2) xm2 = frag_load(x + (size_t)(t_begin - 2) * d + c);
+        if (t_begin >= 3) xm3 = frag_load(x + (size_t)(t_begin - 3) * d + c);
+      }
+      SeqCursor cur(cu, nseq, t_begin, T_);
+      for (int t = t_begin; t < t_end; ++t) {
+        const int pos = cur.pos(t);
+        const Frag8<T> x0 = okc ? frag_load(x + (size_t)t * d + c) : frag_zero<T>();
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float a = wv[j][3] * frag_get(x0, j);
+          if (pos >= 1) a += wv[j][2] * frag_get(xm1, j);
+          if (pos >= 2) a += wv[j][1] * frag_get(xm2, j);
+          if (pos >= 3) a += wv[j][0] * frag_get(xm3, j);
+          o[j] = a;
+        }
+        const Frag8<T> of = frag_from<T>(o);
+        if (okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
+        float sp[8];
+#pragma unroll
+        for (int hh = 0; hh < 8; ++hh) {
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a += wg[hh][j] * frag_get(of, j);  // the rounded x~ that Q, K, V see
+          sp[hh] = a;
+        }
+        const float tot = butterfly8(sp, lane);
+        if ((lane & 7) == 0) {
+          float& acc = sacc[w][t - t_begin][lane >> 3];
+          acc = g8 < 64 ? tot : acc + tot;
+        }
+        xm3 = xm2;
+        xm2 = xm1;
+        xm1 = x0;
+      }
+    }
+    __syncthreads();
+    // sacc[w][row][hh] now holds the full logits of heads hg..hg+7 for this wave's rows
+    for (int e = lane; e < kConvRowsPerWave * 8; e += 64) {
+      const int row = e >> 3, hh = e & 7;
+      const int t = t_begin + row, h = hg + hh;
+      if (t < t_end && h < H) g_out[(size_t)t * H + h] = sigmoidf_(sacc[w][row][hh] + b_g[h]);
+    }
+    __syncthreads();
+  }
+}
+
+void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
+                     const void* w_g, const float* b_g, void* xt, float* g, hipStream_t s) {
+  const int rows = 4 * kConvRowsPerWave;
+  const dim3 grid((T + rows - 1) / rows);
+  if (T == 0) return;
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_conv_fwd<bf16>, grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
+                       (const bf16*)conv_w, (const bf16*)w_g, b_g, (bf16*)xt, g);
+  else
+    hipLaunchKernelGGL(k_conv_fwd<float>, grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
+                       (const float*)conv_w, (const float*)w_g, b_g, (float*)xt, g);
+}
+
+// ============================================================== projection GEMM
+// Block = 256 tokens x one head's [Q | K | V] columns (3 dh), 8 waves (4 x 2).
+// Epilogue: phi on Q and K, identity on V.
+template <typename T, int DH> struct ProjCfg { using S = GemmShape<T, 256, 3 * DH, 32, 4, 2>; };
+// float32 tiles stay within 64 KB of LDS
+template <> struct ProjCfg<float, 64> { using S = GemmShape<float, 32, 192, 32, 1, 4>; };
+template <> struct ProjCfg<float, 32> { using S = GemmShape<float, 64, 96, 32, 2, 2>; };
+
+template <typename T, int DH>
+__global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T* __restrict__ xt,
+                                                                      const T* __restrict__ wp, int T_, int d, int H,
+                                                                      T* __restrict__ q_out, T* __restrict__ k_out,
+                                                                      T* __restrict__ v_out) {
+  using S = typename ProjCfg<T, DH>::S;
+  __shared__ __align__(16) T smem[2 * S::STAGE];
+  const int mtiles = (T_ + S::BM - 1) / S::BM;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * H);
   if (lid >= mtiles * H) return;
   const int mt = lid / H, h = lid - mt * H;
-  const int m0 = mt * BM;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
+  const int m0 = mt * S::BM;
+  f32x4 acc[S::FM][S::FN];
+  gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d, smem,
+                         acc);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
+  const int wm = w / S::WGN, wn = w % S::WGN;
   const int D = H * DH;
-
-  int arow[AIT], apos[AIT], ag8[AIT];
 #pragma unroll
-  for (int i = 0; i < AIT; ++i) {
-    const int it = tid + 256 * i;
-    arow[i] = it / G8;
-    ag8[i] = it % G8;
-    const int t = m0 + arow[i];
-    apos[i] = t < T_ ? pos_in_seq(cu, nseq, t) : -1;
-  }
-
-  f32x4 acc[2][NT];
+  for (int j = 0; j < S::FN; ++j) {
+    const int n = wn * S::WTN + 16 * j;  // first column of this 16-wide tile
+    const int kind = n / DH;             // 0: q, 1: k, 2: v
+    T* out = kind == 0 ? q_out : (kind == 1 ? k_out : v_out);
+    const int c = h * DH + (n % DH) + col;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+    for (int i = 0; i < S::FM; ++i)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[mi][nt] = zero4();
-
-  const T* wph = wp + (size_t)h * NP * d;
-  for (int k0 = 0; k0 < d; k0 += BK) {
-#pragma unroll
-    for (int i = 0; i < AIT; ++i) {
-      const int c = k0 + ag8[i] * 8;
-      const int t = m0 + arow[i];
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = 0.f;
-      if (apos[i] >= 0 && c < d) {
-        float wv[32];  // conv_w[c + j][k] at wv[4 * j + k]
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const Frag8<T> f = frag_load(conv_w + (size_t)c * 4 + 8 * m);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) wv[8 * m + e] = frag_get(f, e);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int sh = 3 - k;  // tap k reads the token sh steps back
-          if (sh > apos[i]) continue;
-          const Frag8<T> xv = frag_load(x + (size_t)(t - sh) * d + c);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] += wv[4 * j + k] * frag_get(xv, j);
+      for (int r = 0; r < 4; ++r) {
+        const int t = m0 + wm * S::WTM + 16 * i + 4 * grp + r;
+        if (t < T_) {
+          const float v = acc[i][j][r];
+          out[(size_t)t * D + c] = from_f<T>(kind == 2 ? v : phi_elu1(v));
         }
       }
-      const Frag8<T> f = frag_from<T>(o);
-      frag_store(As + arow[i] * LD + ag8[i] * 8, f);
-      if (BWD && h == 0 && t < T_ && c < d) frag_store(xt_out + (size_t)t * d + c, f);
-    }
-    for (int it = tid; it < NP * G8; it += 256) {
-      const int n = it / G8, g8 = it - n * G8;
-      const int c = k0 + g8 * 8;
-      const Frag8<T> f = c < d ? frag_load(wph + (size_t)n * d + c) : frag_zero<T>();
-      frag_store(Bs + n * LD + g8 * 8, f);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < BK; ks += 32) {
-      Frag8<T> a[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) a[mi] = frag_load(As + (32 * w + 16 * mi + col) * LD + ks + 8 * grp);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const Frag8<T> b = frag_load(Bs + (16 * nt + col) * LD + ks + 8 * grp);
-#pragma unroll
-        for (int mi = 0; mi < 2; ++mi) mma8(acc[mi][nt], a[mi], b);
-      }
-    }
-    __syncthreads();
-  }
-
-  const float bg = b_g[h];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-    const int rbase = m0 + 32 * w + 16 * mi + 4 * grp;
-    float g[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) g[r] = col0_bcast(sigmoidf_(acc[mi][NT - 1][r] + bg), lane);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = rbase + r;
-      if (t >= T_) continue;
-      T* qrow = q_out + (size_t)t * D + h * DH + col;
-      T* krow = k_out + (size_t)t * D + h * DH + col;
-      T* vrow = v_out + (size_t)t * D + h * DH + col;
-#pragma unroll
-      for (int f = 0; f < FB; ++f) {
-        qrow[16 * f] = from_f<T>(phi_elu1(acc[mi][f][r]));
-        const float kf = phi_elu1(acc[mi][FB + f][r]);
-        krow[16 * f] = from_f<T>(BWD ? kf : g[r] * kf);
-        vrow[16 * f] = from_f<T>(acc[mi][2 * FB + f][r]);
-      }
-      if (BWD && col == 0) g_out[(size_t)t * H + h] = g[r];
-    }
   }
 }
 
-template <typename T, int DH, bool BWD>
-static void proj_t(const void* x, const int32_t* cu, int N, int T_, int d, int H, const void* conv_w, const void* wp,
-                   const float* b_g, void* q, void* k, void* v, float* g, void* xt, hipStream_t s) {
-  const int n = ((T_ + 127) / 128) * H;
-  hipLaunchKernelGGL((k_proj<T, DH, BWD>), dim3(xcd_grid(n)), dim3(256), 0, s, (const T*)x, cu, N, T_, d, H,
-                     (const T*)conv_w, (const T*)wp, b_g, (T*)q, (T*)k, (T*)v, g, (T*)xt);
+template <typename T, int DH>
+static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, hipStream_t s) {
+  using S = typename ProjCfg<T, DH>::S;
+  const int n = ((T_ + S::BM - 1) / S::BM) * H;
+  if (n == 0) return;
+  hipLaunchKernelGGL((k_proj<T, DH>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
+                     (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v);
 }
 
-void launch_proj(int dt, int dh, bool bwd, const void* x, const int32_t* cu, int N, int T, int d, int H,
-                 const void* conv_w, const void* wp, const float* b_g, void* q_out, void* k_out, void* v_out,
-                 float* g_out, void* xt_out, hipStream_t s) {
-#define GBLA_PROJ(TT, DD, BB) proj_t<TT, DD, BB>(x, cu, N, T, d, H, conv_w, wp, b_g, q_out, k_out, v_out, g_out, xt_out, s)
+void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
+                 void* v_out, hipStream_t s) {
   if (dt == BF16) {
-    if (dh == 64) { if (bwd) GBLA_PROJ(bf16, 64, true); else GBLA_PROJ(bf16, 64, false); }
-    else          { if (bwd) GBLA_PROJ(bf16, 32, true); else GBLA_PROJ(bf16, 32, false); }
+    if (dh == 64) proj_t<bf16, 64>(xt, wp, T, d, H, q_out, k_out, v_out, s);
+    else proj_t<bf16, 32>(xt, wp, T, d, H, q_out, k_out, v_out, s);
   } else {
-    if (dh == 64) { if (bwd) GBLA_PROJ(float, 64, true); else GBLA_PROJ(float, 64, false); }
-    else          { if (bwd) GBLA_PROJ(float, 32, true); else GBLA_PROJ(float, 32, false); }
+    if (dh == 64) proj_t<float, 64>(xt, wp, T, d, H, q_out, k_out, v_out, s);
+    else proj_t<float, 32>(xt, wp, T, d, H, q_out, k_out, v_out, s);
   }
-#undef GBLA_PROJ
 }
 
 // ============================================================== split-L state reduction
-// Block = one chunk (<= kChunk tokens of one sequence) x one head. Each wave
-// takes 16 tokens at a time, loads g*phi(k) and v in C-tile order (lane holds
-// feature lane%16 of tokens 4*(lane/16)+0..3) and contracts over the tokens with
-// K=16 MFMAs, accumulating the whole dh x dh partial state. The four wave
-// partials are summed in a fixed order through LDS.
+// Block = one chunk (<= kChunk tokens of one sequence) x one head. Tiles of 64
+// tokens of k~ = g phi(k) and [v | 1] are staged in LDS in token-major order
+// exactly as loaded (16-byte vectors); the MFMA operands, which need 8
+// consecutive tokens per feature, are read with the transposing LDS read. The
+// appended ones column makes the last output column the normaliser z. Each wave
+// owns whole 16x16 output tiles, so no cross-wave reduction is needed.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka, const T* __restrict__ va,
-                                                       const int* __restrict__ nchunks,
+                                                       const float* __restrict__ ga, const int* __restrict__ nchunks,
                                                        const Chunk* __restrict__ tab, int max_slots, int H,
                                                        float* __restrict__ partial) {
-  constexpr int FB = DH / 16;
+  constexpr int FB = DH / 16, NB = FB + 1;     // key-feature blocks; value blocks + ones block
+  constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
+  constexpr int ST = 64;                       // tokens per staged tile
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LDK = DH + PAD, LDV = 16 * NB + PAD;
   constexpr int E = DH * DH + DH;
-  __shared__ float red[E];
+  __shared__ __align__(16) T ks[ST * LDK];
+  __shared__ __align__(16) T vs[ST * LDV];
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
@@ -278,93 +317,117 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
   const Chunk ch = tab[slot];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
+  for (int e = tid; e < ST * 16; e += 256) {  // ones column (z) and zero padding of the last block
+    const int r = e >> 4, c = e & 15;
+    vs[r * LDV + DH + c] = from_f<T>(c == 0 ? 1.f : 0.f);
+  }
+  f32x4 acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 
-  f32x4 sacc[FB][FB];
-  float zacc[FB];
-#pragma unroll
-  for (int a = 0; a < FB; ++a) {
-    zacc[a] = 0.f;
-#pragma unroll
-    for (int b = 0; b < FB; ++b) sacc[a][b] = zero4();
-  }
-  for (int t0 = ch.start + 16 * w; t0 < ch.end; t0 += 64) {
-    float kv[FB][4], vv[FB][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = t0 + 4 * grp + j;
+  constexpr int V8 = DH / 8;  // 8-feature vectors per token row
+  for (int tb = ch.start; tb < ch.end; tb += ST) {
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
       const bool ok = t < ch.end;
-      const size_t base = (size_t)(ok ? t : ch.start) * D + h * DH + col;
+      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+      const float g = ok ? ga[(size_t)t * H + h] : 0.f;
+      const Frag8<T> fk = ok ? frag_load(ka + o) : frag_zero<T>();
+      float kt[8];
 #pragma unroll
-      for (int b = 0; b < FB; ++b) {
-        kv[b][j] = ok ? to_f<T>(ka[base + 16 * b]) : 0.f;
-        vv[b][j] = ok ? to_f<T>(va[base + 16 * b]) : 0.f;
-      }
+      for (int j = 0; j < 8; ++j) kt[j] = g * frag_get(fk, j);  // rounded once, used by S and z alike
+      frag_store(ks + r * LDK + c, frag_from<T>(kt));
+      frag_store(vs + r * LDV + c, ok ? frag_load(va + o) : frag_zero<T>());
     }
+    __syncthreads();
 #pragma unroll
-    for (int a = 0; a < FB; ++a) {
-      zacc[a] += (kv[a][0] + kv[a][1]) + (kv[a][2] + kv[a][3]);
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = w + 4 * u;
+      if (tile < TILES) {
+        const int ib = tile / NB, nb = tile - ib * NB;
 #pragma unroll
-      for (int b = 0; b < FB; ++b) mma4<T>(sacc[a][b], kv[a], vv[b]);
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < FB; ++a) {
-    zacc[a] += __shfl_xor(zacc[a], 16, 64);
-    zacc[a] += __shfl_xor(zacc[a], 32, 64);
-  }
-  // fixed-order cross-wave sum: wave 0 stores, waves 1..3 add in turn
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
-#pragma unroll
-      for (int a = 0; a < FB; ++a) {
-#pragma unroll
-        for (int b = 0; b < FB; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int idx = (16 * a + 4 * grp + r) * DH + 16 * b + col;
-            red[idx] = ww == 0 ? sacc[a][b][r] : red[idx] + sacc[a][b][r];
-          }
-        if (grp == 0) {
-          const int idx = DH * DH + 16 * a + col;
-          red[idx] = ww == 0 ? zacc[a] : red[idx] + zacc[a];
+        for (int k0 = 0; k0 < ST; k0 += 32) {
+          const Frag8<T> a = frag_kmajor<T>(ks, LDK, k0 + 8 * grp, 16 * ib, lane);
+          const Frag8<T> b = frag_kmajor<T>(vs, LDV, k0 + 8 * grp, 16 * nb, lane);
+          mma8(acc[u], a, b);
         }
       }
     }
     __syncthreads();
   }
   float* out = partial + ((size_t)slot * H + h) * E;
-  for (int e = tid; e < E; e += 256) out[e] = red[e];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = w + 4 * u;
+    if (tile < TILES) {
+      const int ib = tile / NB, nb = tile - ib * NB;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ib + 4 * grp + r;
+        if (nb < FB) out[i * DH + 16 * nb + col] = acc[u][r];
+        else if (col == 0) out[DH * DH + i] = acc[u][r];
+      }
+    }
+  }
 }
 
-void launch_state_partial(int dt, int dh, const void* ka, const void* va, const int* nchunks, const Chunk* tab,
-                          int max_slots, int H, float* partial, hipStream_t s) {
+void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
+                          const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s) {
   const dim3 grid(xcd_grid(max_slots * H));
 #define GBLA_SP(TT, DD) hipLaunchKernelGGL((k_state_partial<TT, DD>), grid, dim3(256), 0, s, (const TT*)ka, \
-                                           (const TT*)va, nchunks, tab, max_slots, H, partial)
+                                           (const TT*)va, ga, nchunks, tab, max_slots, H, partial)
   if (dt == BF16) { if (dh == 64) GBLA_SP(bf16, 64); else GBLA_SP(bf16, 32); }
   else            { if (dh == 64) GBLA_SP(float, 64); else GBLA_SP(float, 32); }
 #undef GBLA_SP
 }
 
 // ============================================================== combine
-// out[b][h][e] = sum of partial[slot][h][e] over the chunks of sequence b, in
-// chunk order (deterministic).
+// out[b][h][e] = sum of partial[c][h][e] over the chunks c of sequence b. A
+// block covers 64 elements of one (sequence, head); its four waves take every
+// fourth chunk and the four sums are added in a fixed order (deterministic).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int* __restrict__ nchunks,
                                                  const int* __restrict__ chunk_off, int N, int H, int E,
                                                  float* __restrict__ out) {
-  const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+  __shared__ float red[4][64];
+  const int eblocks = (E + 63) / 64;
+  const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
+  const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int e = (blockIdx.x - bh * eblocks) * 64 + lane;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
-  for (int e = threadIdx.x; e < E; e += 256) {
-    float s = 0.f;
-    for (int c = c0; c < c1; ++c) s += partial[((size_t)c * H + h) * E + e];
-    out[((size_t)b * H + h) * E + e] = s;
-  }
+  float s = 0.f;
+  if (e < E)
+    for (int c = c0 + ph; c < c1; c += 4) s += partial[((size_t)c * H + h) * E + e];
+  red[ph][lane] = s;
+  __syncthreads();
+  if (ph == 0 && e < E) out[((size_t)b * H + h) * E + e] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
                     float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_combine, dim3(N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N, H, elems, out);
+  hipLaunchKernelGGL(k_combine, dim3(((elems + 63) / 64) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N,
+                     H, elems, out);
+}
+
+// out[e] = sum over p < P of in[p * E + e], P = *P_dev if given else P_host (fixed order)
+__global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ in, int E, int P_host,
+                                                   const int* __restrict__ P_dev, float* __restrict__ out) {
+  __shared__ float red[4][64];
+  const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
+  const int e = blockIdx.x * 64 + lane;
+  const int P = P_dev ? *P_dev : P_host;
+  float s = 0.f;
+  if (e < E)
+    for (int p = ph; p < P; p += 4) s += in[(size_t)p * E + e];
+  red[ph][lane] = s;
+  __syncthreads();
+  if (ph == 0 && e < E) out[e] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+}
+
+void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s) {
+  if (E <= 0) return;
+  hipLaunchKernelGGL(k_sum_parts, dim3((E + 63) / 64), dim3(256), 0, s, in, E, P_host, P_dev, out);
 }
 
 // ============================================================== readout
@@ -396,7 +459,9 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   constexpr int LD = DH + 16 / (int)sizeof(T);
   constexpr int P = SplitState<T>::parts;
   constexpr int E = DH * DH + DH;
+  constexpr int ST = 64, V8 = DH / 8;
   __shared__ __align__(16) T Bs[P * NR * LD];
+  __shared__ __align__(16) T qs[ST * LD];  // phi(q) tile, then y
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
@@ -406,14 +471,18 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
   stage_state_T<T, DH, NR>(Bs, LD, st, st + DH * DH, tid);
-  __syncthreads();
+  const int r0 = 16 * w;
 
-  for (int t0 = ch.start + 16 * w; t0 < ch.end; t0 += 64) {
-    const int ta = t0 + col;  // A-operand row of this lane
+  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      frag_store(qs + r * LD + c, t < ch.end ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>());
+    }
+    __syncthreads();
     Frag8<T> a[DH / 32];
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s)
-      a[s] = ta < ch.end ? frag_load(qa + (size_t)ta * D + h * DH + 32 * s + 8 * grp) : frag_zero<T>();
+    for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
     f32x4 acc[FB + 1];
 #pragma unroll
     for (int nt = 0; nt <= FB; ++nt) {
@@ -427,14 +496,17 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float den = col0_bcast(acc[FB][r], lane);
-      const int t = t0 + 4 * grp + r;
-      if (t < ch.end) {
-        const float inv = 1.f / den;
-        T* yrow = y + (size_t)t * D + h * DH + col;
+      const float inv = tb + r0 + 4 * grp + r < ch.end ? 1.f / den : 0.f;
 #pragma unroll
-        for (int nt = 0; nt < FB; ++nt) yrow[16 * nt] = from_f<T>(acc[nt][r] * inv);
-      }
+      for (int nt = 0; nt < FB; ++nt) qs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(acc[nt][r] * inv);
     }
+    __syncthreads();
+    for (int it = tid; it < ST * V8; it += 256) {
+      const int r = it / V8, c = (it % V8) * 8;
+      const int t = tb + r;
+      if (t < ch.end) frag_store(y + (size_t)t * D + h * DH + c, frag_load(qs + r * LD + c));
+    }
+    __syncthreads();
   }
 }
 

@@ -12,9 +12,9 @@ enum DType { F32 = 0, BF16 = 1 };
 
 // stages timed by the optional profiling window (gbla_profile_begin/end)
 enum StageId {
-  ST_SCHEDULE, ST_PACK_PROJ, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
-  ST_PACK_WT, ST_PROJ_BWD, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN, ST_DBG_REDUCE,
-  ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
+  ST_SCHEDULE, ST_PACK_PROJ, ST_CONV_FWD, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
+  ST_PACK_WT, ST_CONV_RECOMPUTE, ST_PROJ_RECOMPUTE, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN,
+  ST_DBG_REDUCE, ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
   kNumStages
 };
 
@@ -37,9 +37,8 @@ constexpr int kChunk = 256;
 // upper bound on the number of chunks for T tokens in N sequences
 inline int max_chunks(int T, int N) { return (T + kChunk - 1) / kChunk + N; }
 
-// output columns of the packed per-head projection: Q, K, V features and a
-// 16-wide tile whose column 0 is the gate
-inline int proj_cols(int dh) { return 3 * dh + 16; }
+// rows of the packed per-head projection weights: Q, K and V features
+inline int proj_cols(int dh) { return 3 * dh; }
 
 // columns of the gradient matrix [dQ | dK | dV | ds | 0-pad], padded to 64
 inline int grad_cols(int H, int dh) { return ((3 * H * dh + H) + 63) / 64 * 64; }
@@ -47,15 +46,17 @@ inline int grad_cols(int H, int dh) { return ((3 * H * dh + H) + 63) / 64 * 64; 
 // ---- forward / shared
 void launch_schedule(const int32_t* cu, int N, int T, int max_slots, int* nchunks, int* chunk_off, Chunk* tab,
                      hipStream_t s);
-void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_g, int d, int H,
-                      int dh, void* wp, hipStream_t s);
-void launch_proj(int dt, int dh, bool bwd, const void* x, const int32_t* cu, int N, int T, int d, int H,
-                 const void* conv_w, const void* wp, const float* b_g, void* q_out, void* k_out, void* v_out,
-                 float* g_out, void* xt_out, hipStream_t s);
-void launch_state_partial(int dt, int dh, const void* ka, const void* va, const int* nchunks, const Chunk* tab,
-                          int max_slots, int H, float* partial, hipStream_t s);
+void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
+                      hipStream_t s);
+void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
+                     const void* w_g, const float* b_g, void* xt, float* g, hipStream_t s);
+void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
+                 void* v_out, hipStream_t s);
+void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
+                          const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s);
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
                     float* out, hipStream_t s);
+void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s);
 void launch_readout(int dt, int dh, const void* qa, const float* saved, const int* nchunks, const Chunk* tab,
                     int max_slots, int H, void* y, hipStream_t s);
 
@@ -68,14 +69,13 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
                       hipStream_t s);
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, float* dxt, hipStream_t s);
+int dw_tiles(int dt, int d, int Kp);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_g, hipStream_t s);
-void launch_dbg_reduce(const float* dbg_part, const int* nchunks, int H, float* db_g, hipStream_t s);
 void launch_conv_bwd(int dt, const float* dxt, const void* x, const int32_t* cu, int N, int T, int d,
                      const void* conv_w, void* dx, float* dconv_part, hipStream_t s);
-void launch_dconv_reduce(const float* dconv_part, int nparts, int d, float* dconv_w, hipStream_t s);
 int conv_bwd_row_blocks(int T);
 
 }  // namespace gbla

@@ -90,8 +90,15 @@ GBLA_API int gbla_version(void);
 GBLA_API gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes);
 
 /* Bytes of device workspace needed by gbla_forward (backward = 0) or
- * gbla_backward (backward = 1). */
+ * gbla_backward (backward = 1); enough whether or not an activation cache is
+ * passed. */
 GBLA_API gbla_status gbla_workspace_size(const gbla_problem* p, int backward, size_t* bytes);
+
+/* Bytes of the optional activation cache `act`: the conv output, phi(q),
+ * phi(k), v (dtype) and the gates (float32) of every token, kept by
+ * gbla_forward so that gbla_backward needs no recomputation. Its layout is
+ * internal to the library. */
+GBLA_API gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes);
 
 /* Forward pass, Eqs. (4)-(6).
  *   x        [T, d]        input rows (dtype)
@@ -101,24 +108,29 @@ GBLA_API gbla_status gbla_workspace_size(const gbla_problem* p, int backward, si
  *   w_g      [H, d]        gate weights (dtype);  b_g [H] gate bias (float32)
  *   y        [T, H*d_h]    output (dtype, overwritten)
  *   saved    see gbla_saved_size (float32, overwritten): the states S and z
+ *   act      optional activation cache (gbla_activation_size bytes, overwritten)
+ *            for a later gbla_backward; NULL for inference
  *   workspace, workspace_bytes: at least gbla_workspace_size(p, 0) bytes */
 GBLA_API gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
-                         const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                         void* y, float* saved, void* workspace, size_t workspace_bytes, void* stream);
+                                  const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                                  void* y, float* saved, void* act, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Backward pass: gradients of sum(y * dy) for the forward above, obtained by
  * the chain rule through Eqs. (4)-(6). Inputs as in gbla_forward plus
  *   saved    the state written by gbla_forward for the same inputs (float32)
+ *   act      the activation cache written by that gbla_forward, or NULL to
+ *            recompute the activations from x (same results)
  *   dy       [T, H*d_h]    upstream gradient (dtype)
  * Outputs (all overwritten, never accumulated):
  *   dx       [T, d] (dtype);  dconv_w [d, 4];  dw_q, dw_k, dw_v [d, H*d_h];
  *   dw_g     [H, d];  db_g [H]   (all float32)
  *   workspace, workspace_bytes: at least gbla_workspace_size(p, 1) bytes */
 GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
-                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                          const float* saved, const void* dy, void* dx, float* dconv_w, float* dw_q, float* dw_k,
-                          float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
-                          void* stream);
+                                   const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                                   const float* saved, const void* act, const void* dy, void* dx, float* dconv_w,
+                                   float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /* ---- Optional per-stage timing (benchmarking aid) ----------------------
  * gbla_profile_begin opens a process-wide window of at most max_records

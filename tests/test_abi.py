@@ -81,6 +81,9 @@ def test_size_queries_are_consistent():
     assert out.value > fwd > 0
     assert lib.gbla_workspace_size(None, 0, ctypes.byref(out)) == 1
     assert lib.gbla_workspace_size(ctypes.byref(p), 0, None) == 1
+    assert lib.gbla_activation_size(ctypes.byref(p), ctypes.byref(out)) == 0
+    # x~, phi(q), phi(k), v in bf16 and the gates in float32
+    assert out.value >= 100 * (64 + 3 * 128) * 2 + 100 * 2 * 4
 
 
 def _fake(addr=0x10000):
@@ -93,7 +96,7 @@ def test_forward_rejects_null_misaligned_and_small_workspace_without_launching()
     out = ctypes.c_size_t()
     lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out))
     need = out.value
-    a = [_fake(0x10000 + 0x1000 * i) for i in range(10)]
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(11)]
     # NULL weight
     args = list(a)
     args[4] = None
@@ -115,8 +118,8 @@ def test_backward_rejects_null_and_small_workspace_without_launching():
     out = ctypes.c_size_t()
     lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
     need = out.value
-    a = [_fake(0x10000 + 0x1000 * i) for i in range(17)]
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(18)]
     args = list(a)
-    args[16] = None   # db_g
+    args[17] = None   # db_g
     assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
     assert lib.gbla_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5

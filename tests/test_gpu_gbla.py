@@ -41,14 +41,17 @@ def to_dev(inp):
                 b_g=torch.from_numpy(inp["b_g"]).float().to("cuda"), dy=t(inp["dy"]))
 
 
-def run_gpu(inp, backward):
+def run_gpu(inp, backward, keep_act=True):
+    """keep_act: pass forward's activation cache to the backward; False makes
+    the backward recompute the activations from x."""
     d = to_dev(inp)
     H = inp["H"]
-    y, saved = gb.forward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"], H)
+    y, saved, act = gb.forward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"], H,
+                               save_activations=keep_act)
     out = {"y": y, "saved": saved}
     if backward:
         out.update(gb.backward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"],
-                               saved, d["dy"], H))
+                               saved, act, d["dy"], H))
     torch.cuda.synchronize()
     return {k: v.float().cpu().numpy() for k, v in out.items()}
 
@@ -57,9 +60,9 @@ def oracle_args(inp):
     return [inp[k] for k in ("x", "cu_seqlens", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g")]
 
 
-def compare(inp, backward, tol=None, label=""):
+def compare(inp, backward, tol=None, label="", keep_act=True):
     tol = TOL[inp["dtype"]] if tol is None else tol
-    gpu = run_gpu(inp, backward)
+    gpu = run_gpu(inp, backward, keep_act)
     y, S, z = og.forward(*oracle_args(inp), inp["H"])
     N, H, dh = inp["N"], inp["H"], inp["dh"]
     sv = gpu["saved"].reshape(N, H, dh * dh + dh)
@@ -146,6 +149,22 @@ def test_bitwise_deterministic():
     a, b = run_gpu(inp, True), run_gpu(inp, True)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+def test_recompute_path_matches_cached_activations():
+    """Backward without the activation cache recomputes the same activations
+    with the same kernels, so every gradient is bitwise identical."""
+    inp = _small_bf16()
+    a, b = run_gpu(inp, True, keep_act=True), run_gpu(inp, True, keep_act=False)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_recompute_path_parity(dtype):
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (400, 3, 260), d_model=64, num_heads=2, dtype=dtype,
+                      seed=41)
+    compare(make_inputs(w), backward=True, label=f"recompute {dtype}", keep_act=False)
 
 
 def test_packed_sequences_are_isolated():
