@@ -248,6 +248,41 @@ struct SeqCursor {
   }
 };
 
+// Stage a dh x dh float matrix M (row-major, read coalesced) and a vector z as
+// MFMA B operands in LDS, split into a high and a low part for bfloat16 (P = 2)
+// so the staged matrix keeps about 16 mantissa bits:
+//   MT[p][n][i] = M[i][n] for n < DH; row DH holds z, rows DH+1 .. NR-1 are 0
+//   MR[p][i][n] = M[i][n]
+// Either destination may be null; part 1 of MT starts NR rows after part 0,
+// part 1 of MR starts DH rows after part 0 (pitch ld elements).
+template <typename T, int DH, int NR>
+__device__ __forceinline__ void stage_state(T* MT, T* MR, int ld, const float* __restrict__ M,
+                                            const float* __restrict__ z, int tid, int nthreads) {
+  constexpr bool SPLIT = sizeof(T) == 2;
+  for (int e = tid; e < DH * DH; e += nthreads) {
+    const int i = e / DH, n = e - i * DH;
+    const float v = M[e];
+    const T hi = from_f<T>(v);
+    const T lo = from_f<T>(v - to_f<T>(hi));
+    if (MT) {
+      MT[n * ld + i] = hi;
+      if (SPLIT) MT[NR * ld + n * ld + i] = lo;
+    }
+    if (MR) {
+      MR[i * ld + n] = hi;
+      if (SPLIT) MR[DH * ld + i * ld + n] = lo;
+    }
+  }
+  if (MT)
+    for (int e = tid; e < (NR - DH) * DH; e += nthreads) {
+      const int n = DH + e / DH, i = e % DH;
+      const float v = n == DH ? z[i] : 0.f;
+      const T hi = from_f<T>(v);
+      MT[n * ld + i] = hi;
+      if (SPLIT) MT[NR * ld + n * ld + i] = from_f<T>(v - to_f<T>(hi));
+    }
+}
+
 // chunk table entry: one run of <= chunk tokens inside one sequence
 struct Chunk { int seq, start, end, pad; };
 

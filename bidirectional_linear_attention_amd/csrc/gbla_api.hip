@@ -65,7 +65,7 @@ struct FwdWs {
 };
 struct BwdWs {
   int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
-  void* G; float* dxt; float* dw_part; float* dconv_part; Act act;
+  void* G; void* dxt; float* dw_part; float* dconv_part; Act act;
 };
 
 // The workspace always has room for the activations, so it suffices whether or
@@ -95,7 +95,7 @@ size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   t.dsz = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H * m.E);
   t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
   t.G = c.take<char>(base, (size_t)m.T * m.Kp * m.esz);
-  t.dxt = c.take<float>(base, sizeof(float) * (size_t)m.T * m.d);
+  t.dxt = c.take<char>(base, m.esz * (size_t)m.T * m.d);
   t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
   t.dconv_part = c.take<float>(base, sizeof(float) * (size_t)std::max(1, m.conv_rb) * m.d * 4);
   t.act = carve_act(m, c, base);

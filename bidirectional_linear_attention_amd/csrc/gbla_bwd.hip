@@ -15,7 +15,7 @@
 //   (without an activation cache, k_conv_fwd + k_proj recompute x~, g, phi(q), phi(k), v)
 //   k_bwd_dstate  per (chunk, head): y, dn, dden, dq -> G; partial [dS | dz]
 //   k_bwd_token   per (chunk, head): dk, dv, ds -> G; partial db_g
-//   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA)
+//   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA), stored in the activation dtype
 //   k_gemm_dw     split-token partials of X~^T G (pipelined MFMA), then k_dw_reduce
 //   k_conv_bwd    dx and per-block partial dconv_w (summed by k_sum_parts)
 #include "gemm.h"
@@ -25,20 +25,6 @@ namespace gbla {
 
 template <typename T> struct Parts { static constexpr int n = 2; };  // bf16: hi + lo split of fp32 matrices
 template <> struct Parts<float> { static constexpr int n = 1; };
-
-// Bs[p][row][col] (ld pitch) <- split(M[row][col]) for a dh x dh fp32 matrix,
-// transposed when TR (Bs[p][col][row] = M[row][col]).
-template <typename T, int DH, bool TR>
-__device__ __forceinline__ void stage_mat(T* __restrict__ Bs, int ld, const float* __restrict__ M, int tid) {
-  for (int e = tid; e < DH * DH; e += 256) {
-    const int r = e / DH, c = e - r * DH;
-    const float v = M[e];
-    const int o = TR ? c * ld + r : r * ld + c;
-    const T hi = from_f<T>(v);
-    Bs[o] = hi;
-    if (Parts<T>::n == 2) Bs[DH * ld + o] = from_f<T>(v - to_f<T>(hi));
-  }
-}
 
 // fixed-order sum of per-wave dh x dh C-tile accumulators (+ a per-lane vector) into red[]
 template <int DH>
@@ -100,14 +86,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  for (int e = tid; e < NR * DH; e += 256) {
-    const int n = e / DH, i = e - n * DH;
-    const float v = n < DH ? st[i * DH + n] : (n == DH ? st[DH * DH + i] : 0.f);
-    const T hi = from_f<T>(v);
-    Bsz[n * LD + i] = hi;
-    if (P == 2) Bsz[NR * LD + n * LD + i] = from_f<T>(v - to_f<T>(hi));
-  }
-  stage_mat<T, DH, false>(Brm, LD, st, tid);
+  stage_state<T, DH, NR>(Bsz, Brm, LD, st, st + DH * DH, tid, 256);
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
 
   f32x4 dS[FB][FB];
@@ -120,16 +99,30 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   }
   const int r0 = 16 * w;  // this wave's rows of the staged tile
 
-  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      const bool ok = t < ch.end;
+  constexpr int NV = (ST * V8 + 255) / 256;
+  Frag8<T> pq[NV], py[NV];
+  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
+      const bool ok = it < ST * V8 && t < ch.end;
       const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      frag_store(qs + r * LD + c, ok ? frag_load(qa + o) : frag_zero<T>());
-      frag_store(ys + r * LD + c, ok ? frag_load(dy + o) : frag_zero<T>());
+      pq[v] = ok ? frag_load(qa + o) : frag_zero<T>();
+      py[v] = ok ? frag_load(dy + o) : frag_zero<T>();
+    }
+  };
+  fetch(ch.start);
+  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      if (it < ST * V8) {
+        frag_store(qs + r * LD + c, pq[v]);
+        frag_store(ys + r * LD + c, py[v]);
+      }
     }
     __syncthreads();
+    if (tb + ST < ch.end) fetch(tb + ST);
     Frag8<T> a[DH / 32];
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
@@ -250,24 +243,39 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = dsz + ((size_t)ch.seq * H + h) * E;
-  stage_mat<T, DH, false>(Srm, LD, st, tid);
-  stage_mat<T, DH, true>(Str, LD, st, tid);
+  stage_state<T, DH, DH>(Str, Srm, LD, st, st + DH * DH, tid, 256);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
   const int gcol0 = 3 * D + H;  // first zero-pad column of G
   const int r0 = 16 * w;
-  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      const bool ok = t < ch.end;
+  constexpr int NV = (ST * V8 + 255) / 256;
+  Frag8<T> pk[NV], pv[NV];
+  float pg = 0.f;
+  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
+      const bool ok = it < ST * V8 && t < ch.end;
       const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      frag_store(ks + r * LD + c, ok ? frag_load(ka + o) : frag_zero<T>());
-      frag_store(vs + r * LD + c, ok ? frag_load(va + o) : frag_zero<T>());
+      pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
+      pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
     }
-    for (int r = tid; r < ST; r += 256) gs[r] = tb + r < ch.end ? ga[(size_t)(tb + r) * H + h] : 0.f;
+    if (tid < ST) pg = tb + tid < ch.end ? ga[(size_t)(tb + tid) * H + h] : 0.f;
+  };
+  fetch(ch.start);
+  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      if (it < ST * V8) {
+        frag_store(ks + r * LD + c, pk[v]);
+        frag_store(vs + r * LD + c, pv[v]);
+      }
+    }
+    if (tid < ST) gs[tid] = pg;
     __syncthreads();
+    if (tb + ST < ch.end) fetch(tb + ST);
     const float gA = gs[r0 + col];
     Frag8<T> vf[DH / 32], kf[DH / 32];
 #pragma unroll
@@ -389,8 +397,9 @@ template <typename T> struct DxCfg { using S = GemmShape<T, 256, 256, 32, 4, 2>;
 template <> struct DxCfg<float> { using S = GemmShape<float, 64, 128, 32, 2, 2>; };
 
 template <typename T>
-__global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G, const T* __restrict__ wt,
-                                                                   int T_, int d, int Kp, float* __restrict__ dxt) {
+__global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
+                                                                     const T* __restrict__ wt, int T_, int d, int Kp,
+                                                                     T* __restrict__ dxt) {
   using S = typename DxCfg<T>::S;
   __shared__ __align__(16) T smem[2 * S::STAGE];
   const int mtiles = (T_ + S::BM - 1) / S::BM, ntiles = (d + S::BN - 1) / S::BN;
@@ -401,33 +410,41 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
   f32x4 acc[S::FM][S::FN];
   gemm_nt_mainloop<T, S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp, min(S::BN, d - n0),
                          Kp, smem, acc);
+  // epilogue staged per wave through LDS, 16 rows at a time, 16-byte row stores
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
+  constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
+  constexpr int RP = 16, VPR = S::WTN / 8;
+  static_assert(S::NWAVES * RP * LDO <= 2 * S::STAGE, "epilogue staging must fit the main-loop LDS");
+  T* ws = smem + w * RP * LDO;
 #pragma unroll
-  for (int i = 0; i < S::FM; ++i)
+  for (int i = 0; i < S::FM; ++i) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * S::WTM + 16 * i + 4 * grp + r;
-      if (m >= T_) continue;
+    for (int j = 0; j < S::FN; ++j)
 #pragma unroll
-      for (int j = 0; j < S::FN; ++j) {
-        const int n = n0 + wn * S::WTN + 16 * j + col;
-        if (n < d) dxt[(size_t)m * d + n] = acc[i][j][r];
-      }
+      for (int r = 0; r < 4; ++r) ws[(4 * grp + r) * LDO + 16 * j + col] = from_f<T>(acc[i][j][r]);
+    __syncthreads();
+    for (int it = lane; it < RP * VPR; it += 64) {
+      const int r = it / VPR, c = (it % VPR) * 8;
+      const int m = m0 + wm * S::WTM + 16 * i + r;
+      const int n = n0 + wn * S::WTN + c;
+      if (m < T_ && n < d) frag_store(dxt + (size_t)m * d + n, frag_load(ws + r * LDO + c));
     }
+    __syncthreads();
+  }
 }
 
-void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, float* dxt, hipStream_t s) {
+void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s) {
   if (dt == BF16) {
     using S = DxCfg<bf16>::S;
     const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
     if (n) hipLaunchKernelGGL(k_gemm_dx<bf16>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const bf16*)G,
-                              (const bf16*)wt, T, d, Kp, dxt);
+                              (const bf16*)wt, T, d, Kp, (bf16*)dxt);
   } else {
     using S = DxCfg<float>::S;
     const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
     if (n) hipLaunchKernelGGL(k_gemm_dx<float>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const float*)G,
-                              (const float*)wt, T, d, Kp, dxt);
+                              (const float*)wt, T, d, Kp, (float*)dxt);
   }
 }
 
@@ -526,13 +543,15 @@ constexpr int kConvRun = 32;
 constexpr int kConvRows = 4 * kConvRun;
 int conv_bwd_row_blocks(int T) { return (T + kConvRows - 1) / kConvRows; }
 
-__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
-  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+template <typename T>
+__device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
+  const Frag8<T> f = frag_load(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = frag_get(f, j);
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_conv_bwd(const float* __restrict__ dxt, const T* __restrict__ x,
+__global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ dxt, const T* __restrict__ x,
                                                   const int32_t* __restrict__ cu, int nseq, int T_, int d,
                                                   const T* __restrict__ conv_w, T* __restrict__ dx,
                                                   float* __restrict__ part) {
@@ -617,15 +636,15 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const float* __restrict__ dxt,
   }
 }
 
-void launch_conv_bwd(int dt, const float* dxt, const void* x, const int32_t* cu, int N, int T, int d,
+void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,
                      const void* conv_w, void* dx, float* dconv_part, hipStream_t s) {
   const dim3 grid(conv_bwd_row_blocks(T), (d + 511) / 512);
   if (grid.x == 0) return;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_conv_bwd<bf16>, grid, dim3(256), 0, s, dxt, (const bf16*)x, cu, N, T, d,
+    hipLaunchKernelGGL(k_conv_bwd<bf16>, grid, dim3(256), 0, s, (const bf16*)dxt, (const bf16*)x, cu, N, T, d,
                        (const bf16*)conv_w, (bf16*)dx, dconv_part);
   else
-    hipLaunchKernelGGL(k_conv_bwd<float>, grid, dim3(256), 0, s, dxt, (const float*)x, cu, N, T, d,
+    hipLaunchKernelGGL(k_conv_bwd<float>, grid, dim3(256), 0, s, (const float*)dxt, (const float*)x, cu, N, T, d,
                        (const float*)conv_w, (float*)dx, dconv_part);
 }
 

@@ -248,25 +248,38 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
   f32x4 acc[S::FM][S::FN];
   gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d, smem,
                          acc);
+  // epilogue: phi on Q and K, staged per wave through LDS (the main loop ended
+  // with a barrier, so smem is free) and written as 16-byte row vectors
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
   const int D = H * DH;
+  constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
+  constexpr int RP = 16;                       // rows per pass
+  constexpr int VPR = S::WTN / 8;              // 8-element vectors per row
+  static_assert(S::NWAVES * RP * LDO <= 2 * S::STAGE, "epilogue staging must fit the main-loop LDS");
+  T* ws = smem + w * RP * LDO;
 #pragma unroll
-  for (int j = 0; j < S::FN; ++j) {
-    const int n = wn * S::WTN + 16 * j;  // first column of this 16-wide tile
-    const int kind = n / DH;             // 0: q, 1: k, 2: v
-    T* out = kind == 0 ? q_out : (kind == 1 ? k_out : v_out);
-    const int c = h * DH + (n % DH) + col;
+  for (int i = 0; i < S::FM; ++i) {
 #pragma unroll
-    for (int i = 0; i < S::FM; ++i)
+    for (int j = 0; j < S::FN; ++j) {
+      const int n = wn * S::WTN + 16 * j;
+      const bool lin = n / DH == 2;  // v columns stay linear
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int t = m0 + wm * S::WTM + 16 * i + 4 * grp + r;
-        if (t < T_) {
-          const float v = acc[i][j][r];
-          out[(size_t)t * D + c] = from_f<T>(kind == 2 ? v : phi_elu1(v));
-        }
+        const float v = acc[i][j][r];
+        ws[(4 * grp + r) * LDO + 16 * j + col] = from_f<T>(lin ? v : phi_elu1(v));
       }
+    }
+    __syncthreads();
+    for (int it = lane; it < RP * VPR; it += 64) {
+      const int r = it / VPR, c = (it % VPR) * 8;
+      const int t = m0 + wm * S::WTM + 16 * i + r;
+      const int n = wn * S::WTN + c;
+      const int kind = n / DH;
+      T* out = kind == 0 ? q_out : (kind == 1 ? k_out : v_out);
+      if (t < T_) frag_store(out + (size_t)t * D + h * DH + (n % DH), frag_load(ws + r * LDO + c));
+    }
+    __syncthreads();
   }
 }
 
@@ -326,21 +339,35 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
   for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 
   constexpr int V8 = DH / 8;  // 8-feature vectors per token row
-  for (int tb = ch.start; tb < ch.end; tb += ST) {
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      const bool ok = t < ch.end;
-      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      const float g = ok ? ga[(size_t)t * H + h] : 0.f;
-      const Frag8<T> fk = ok ? frag_load(ka + o) : frag_zero<T>();
-      float kt[8];
+  constexpr int NV = (ST * V8 + 255) / 256;
+  Frag8<T> pk[NV], pv[NV];
+  float pg[NV];
+  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
 #pragma unroll
-      for (int j = 0; j < 8; ++j) kt[j] = g * frag_get(fk, j);  // rounded once, used by S and z alike
-      frag_store(ks + r * LDK + c, frag_from<T>(kt));
-      frag_store(vs + r * LDV + c, ok ? frag_load(va + o) : frag_zero<T>());
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
+      const bool ok = it < ST * V8 && t < ch.end;
+      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+      pg[v] = ok ? ga[(size_t)t * H + h] : 0.f;
+      pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
+      pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
+    }
+  };
+  fetch(ch.start);
+  for (int tb = ch.start; tb < ch.end; tb += ST) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      if (it < ST * V8) {
+        float kt[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kt[j] = pg[v] * frag_get(pk[v], j);  // rounded once, used by S and z alike
+        frag_store(ks + r * LDK + c, frag_from<T>(kt));
+        frag_store(vs + r * LDV + c, pv[v]);
+      }
     }
     __syncthreads();
+    if (tb + ST < ch.end) fetch(tb + ST);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = w + 4 * u;
@@ -410,24 +437,45 @@ void launch_combine(const float* partial, const int* nchunks, const int* chunk_o
                      H, elems, out);
 }
 
-// out[e] = sum over p < P of in[p * E + e], P = *P_dev if given else P_host (fixed order)
+// out[e] = sum over p < P of in[p * E + e], P = *P_dev if given else P_host.
+// A block covers EB elements with 256 / EB phases; each thread keeps eight
+// independent partial sums so its loads stay in flight. Fixed summation order.
+template <int EB>
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ in, int E, int P_host,
                                                    const int* __restrict__ P_dev, float* __restrict__ out) {
-  __shared__ float red[4][64];
-  const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int e = blockIdx.x * 64 + lane;
+  constexpr int PH = 256 / EB;
+  __shared__ float red[PH][EB];
+  const int el = threadIdx.x % EB, ph = threadIdx.x / EB;
+  const int e = blockIdx.x * EB + el;
   const int P = P_dev ? *P_dev : P_host;
-  float s = 0.f;
-  if (e < E)
-    for (int p = ph; p < P; p += 4) s += in[(size_t)p * E + e];
-  red[ph][lane] = s;
+  float a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = 0.f;
+  if (e < E) {
+    int p = ph;
+    for (; p + 7 * PH < P; p += 8 * PH)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += in[(size_t)(p + u * PH) * E + e];
+    for (int u = 0; p < P; p += PH, ++u) a[u] += in[(size_t)p * E + e];
+  }
+  red[ph][el] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
   __syncthreads();
-  if (ph == 0 && e < E) out[e] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  if (ph == 0 && e < E) {
+    float t = 0.f;
+    for (int q = 0; q < PH; ++q) t += red[q][el];
+    out[e] = t;
+  }
 }
 
 void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s) {
   if (E <= 0) return;
-  hipLaunchKernelGGL(k_sum_parts, dim3((E + 63) / 64), dim3(256), 0, s, in, E, P_host, P_dev, out);
+#define GBLA_SUMP(EB) hipLaunchKernelGGL(k_sum_parts<EB>, dim3((E + EB - 1) / EB), dim3(256), 0, s, in, E, P_host, \
+                                         P_dev, out)
+  if (E >= 64) GBLA_SUMP(64);
+  else if (E > 16) GBLA_SUMP(32);
+  else if (E > 4) GBLA_SUMP(16);
+  else GBLA_SUMP(4);
+#undef GBLA_SUMP
 }
 
 // ============================================================== readout
@@ -436,19 +484,6 @@ void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, floa
 // state keeps ~16 mantissa bits; A = phi(q) rows straight from HBM.
 template <typename T> struct SplitState { static constexpr int parts = 2; };
 template <> struct SplitState<float> { static constexpr int parts = 1; };
-
-template <typename T, int DH, int NROWS>
-__device__ __forceinline__ void stage_state_T(T* __restrict__ Bs, int ld, const float* __restrict__ S,
-                                              const float* __restrict__ z, int tid) {
-  // Bs[part][n][i] = S[i][n] (n < DH), z[i] (n == DH), 0 (DH < n < NROWS)
-  for (int e = tid; e < NROWS * DH; e += 256) {
-    const int n = e / DH, i = e - n * DH;
-    const float v = n < DH ? S[i * DH + n] : (n == DH ? z[i] : 0.f);
-    const T hi = from_f<T>(v);
-    Bs[n * ld + i] = hi;
-    if (SplitState<T>::parts == 2) Bs[NROWS * ld + n * ld + i] = from_f<T>(v - to_f<T>(hi));
-  }
-}
 
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const float* __restrict__ saved,
@@ -470,16 +505,28 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state_T<T, DH, NR>(Bs, LD, st, st + DH * DH, tid);
+  stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid, 256);
   const int r0 = 16 * w;
 
+  // the next tile's loads are issued before the current tile is processed
+  constexpr int NV = (ST * V8 + 255) / 256;
+  Frag8<T> pf[NV];
+  auto fetch = [&](int tb) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
+      pf[v] = it < ST * V8 && t < ch.end ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>();
+    }
+  };
+  fetch(ch.start);
   for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      frag_store(qs + r * LD + c, t < ch.end ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>());
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v;
+      if (it < ST * V8) frag_store(qs + (it / V8) * LD + (it % V8) * 8, pf[v]);
     }
     __syncthreads();
+    if (tb + ST < ch.end) fetch(tb + ST);
     Frag8<T> a[DH / 32];
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);

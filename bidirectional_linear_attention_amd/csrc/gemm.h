@@ -18,6 +18,9 @@
 
 namespace gbla {
 
+// k chunks held in flight in registers by the main loops
+constexpr int kPrefetchDepth = 3;
+
 template <typename T, int BM_, int BN_, int BK_, int WGM_, int WGN_>
 struct GemmShape {
   static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
@@ -68,46 +71,55 @@ __device__ __forceinline__ void gemm_nt_mainloop(const T* __restrict__ A, int ld
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) acc[i][j] = zero4();
 
-  Frag8<T> ra[VA], rb[VB];
-  auto fetch = [&](int k0) {
+  // PF register sets: the loads of chunk c + PF - 1 are in flight while chunk c
+  // is multiplied, so each load has PF - 1 chunks of MFMA work to arrive.
+  constexpr int PF = kPrefetchDepth;
+  Frag8<T> ra[PF][VA], rb[PF][VB];
+  auto fetch = [&](int set, int k0) {
 #pragma unroll
     for (int v = 0; v < VA; ++v) {
       const int it = tid + v * S::NTHREADS;
       const int r = it / G8, c = k0 + (it % G8) * 8;
-      ra[v] = (it < S::BM * G8 && r < ma && c < K) ? frag_load(A + (size_t)r * lda + c) : frag_zero<T>();
+      ra[set][v] = (it < S::BM * G8 && r < ma && c < K) ? frag_load(A + (size_t)r * lda + c) : frag_zero<T>();
     }
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int it = tid + v * S::NTHREADS;
       const int r = it / G8, c = k0 + (it % G8) * 8;
-      rb[v] = (it < S::BN * G8 && r < nb && c < K) ? frag_load(B + (size_t)r * ldb + c) : frag_zero<T>();
+      rb[set][v] = (it < S::BN * G8 && r < nb && c < K) ? frag_load(B + (size_t)r * ldb + c) : frag_zero<T>();
     }
   };
-  auto stash = [&](T* buf) {
+  auto stash = [&](int set, T* buf) {
 #pragma unroll
     for (int v = 0; v < VA; ++v) {
       const int it = tid + v * S::NTHREADS;
-      if (it < S::BM * G8) frag_store(buf + (it / G8) * S::LD + (it % G8) * 8, ra[v]);
+      if (it < S::BM * G8) frag_store(buf + (it / G8) * S::LD + (it % G8) * 8, ra[set][v]);
     }
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int it = tid + v * S::NTHREADS;
-      if (it < S::BN * G8) frag_store(buf + S::BM * S::LD + (it / G8) * S::LD + (it % G8) * 8, rb[v]);
+      if (it < S::BN * G8) frag_store(buf + S::BM * S::LD + (it / G8) * S::LD + (it % G8) * 8, rb[set][v]);
     }
   };
 
-  fetch(0);
-  stash(smem);
+  const int nk = (K + S::BK - 1) / S::BK;
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < nk) fetch(p, p * S::BK);
+  stash(0, smem);
   __syncthreads();
-  int cur = 0;
-  for (int k0 = 0; k0 < K; k0 += S::BK) {
-    const bool more = k0 + S::BK < K;
-    if (more) fetch(k0 + S::BK);
-    const T* buf = smem + cur * S::STAGE;
-    mma_chunk<T, S>(buf, buf + S::BM * S::LD, wm, wn, col, grp, acc);
-    if (more) stash(smem + (cur ^ 1) * S::STAGE);
-    __syncthreads();
-    cur ^= 1;
+  for (int c0 = 0; c0 < nk; c0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {  // chunk c = c0 + p lives in register set p
+      const int c = c0 + p;
+      if (c < nk) {
+        if (c > 0 && c + PF - 1 < nk) fetch((p + PF - 1) % PF, (c + PF - 1) * S::BK);
+        const T* buf = smem + (c & 1) * S::STAGE;
+        mma_chunk<T, S>(buf, buf + S::BM * S::LD, wm, wn, col, grp, acc);
+        if (c + 1 < nk) stash((p + 1) % PF, smem + ((c + 1) & 1) * S::STAGE);
+        __syncthreads();
+      }
+    }
   }
 }
 
@@ -143,31 +155,32 @@ __device__ __forceinline__ void gemm_tn_mainloop(const T* __restrict__ A, int ld
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) acc[i][j] = zero4();
 
-  Frag8<T> ra[VA], rb[VB];
-  auto fetch = [&](int k0) {
+  constexpr int PF = kPrefetchDepth;
+  Frag8<T> ra[PF][VA], rb[PF][VB];
+  auto fetch = [&](int set, int k0) {
 #pragma unroll
     for (int v = 0; v < VA; ++v) {
       const int it = tid + v * S::NTHREADS;
       const int kr = it / CA, c = (it % CA) * 8, k = k0 + kr;
-      ra[v] = (it < CA * S::BK && c < ma && k < k_end) ? frag_load(A + (size_t)k * lda + c) : frag_zero<T>();
+      ra[set][v] = (it < CA * S::BK && c < ma && k < k_end) ? frag_load(A + (size_t)k * lda + c) : frag_zero<T>();
     }
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int it = tid + v * S::NTHREADS;
       const int kr = it / CB, c = (it % CB) * 8, k = k0 + kr;
-      rb[v] = (it < CB * S::BK && c < nb && k < k_end) ? frag_load(B + (size_t)k * ldb + c) : frag_zero<T>();
+      rb[set][v] = (it < CB * S::BK && c < nb && k < k_end) ? frag_load(B + (size_t)k * ldb + c) : frag_zero<T>();
     }
   };
-  auto stash = [&](T* buf) {
+  auto stash = [&](int set, T* buf) {
 #pragma unroll
     for (int v = 0; v < VA; ++v) {
       const int it = tid + v * S::NTHREADS;
-      if (it < CA * S::BK) frag_store(buf + (it / CA) * S::LDA + (it % CA) * 8, ra[v]);
+      if (it < CA * S::BK) frag_store(buf + (it / CA) * S::LDA + (it % CA) * 8, ra[set][v]);
     }
 #pragma unroll
     for (int v = 0; v < VB; ++v) {
       const int it = tid + v * S::NTHREADS;
-      if (it < CB * S::BK) frag_store(buf + S::BK * S::LDA + (it / CB) * S::LDB + (it % CB) * 8, rb[v]);
+      if (it < CB * S::BK) frag_store(buf + S::BK * S::LDA + (it / CB) * S::LDB + (it % CB) * 8, rb[set][v]);
     }
   };
   auto compute = [&](const T* buf) {
@@ -188,17 +201,23 @@ __device__ __forceinline__ void gemm_tn_mainloop(const T* __restrict__ A, int ld
   };
 
   if (k_begin >= k_end) return;
-  fetch(k_begin);
-  stash(smem);
+  const int nk = (k_end - k_begin + S::BK - 1) / S::BK;
+#pragma unroll
+  for (int p = 0; p < PF; ++p)
+    if (p < nk) fetch(p, k_begin + p * S::BK);
+  stash(0, smem);
   __syncthreads();
-  int cur = 0;
-  for (int k0 = k_begin; k0 < k_end; k0 += S::BK) {
-    const bool more = k0 + S::BK < k_end;
-    if (more) fetch(k0 + S::BK);
-    compute(smem + cur * S::STAGE);
-    if (more) stash(smem + (cur ^ 1) * S::STAGE);
-    __syncthreads();
-    cur ^= 1;
+  for (int c0 = 0; c0 < nk; c0 += PF) {
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {  // chunk c = c0 + p lives in register set p
+      const int c = c0 + p;
+      if (c < nk) {
+        if (c > 0 && c + PF - 1 < nk) fetch((p + PF - 1) % PF, k_begin + (c + PF - 1) * S::BK);
+        compute(smem + (c & 1) * S::STAGE);
+        if (c + 1 < nk) stash((p + 1) % PF, smem + ((c + 1) & 1) * S::STAGE);
+        __syncthreads();
+      }
+    }
   }
 }
 

@@ -68,13 +68,13 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
                       hipStream_t s);
-void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, float* dxt, hipStream_t s);
+void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s);
 int dw_tiles(int dt, int d, int Kp);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_g, hipStream_t s);
-void launch_conv_bwd(int dt, const float* dxt, const void* x, const int32_t* cu, int N, int T, int d,
+void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,
                      const void* conv_w, void* dx, float* dconv_part, hipStream_t s);
 int conv_bwd_row_blocks(int T);
 
