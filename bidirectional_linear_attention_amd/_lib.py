@@ -1,4 +1,4 @@
-"""ctypes view of libgbla.so (include/gbla.h). Marshalling only: every step of
+"""ctypes view of libgbla.so (include/gbla.h, include/lion.h). Marshalling only: every step of
 the layer runs in the HIP library; there is no CPU or PyTorch fallback."""
 from __future__ import annotations
 
@@ -49,6 +49,10 @@ _SIGNATURES = {
     "gbla_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "gbla_profile_stage_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "lion_workspace_size": (ctypes.c_int, [_LP, ctypes.c_int, ctypes.POINTER(_sz)]),
+    "lion_activation_size": (ctypes.c_int, [_LP, ctypes.POINTER(_sz)]),
+    "lion_forward": (ctypes.c_int, [_LP] + [_vp] * 9 + [_vp, _sz, _vp]),
+    "lion_backward": (ctypes.c_int, [_LP] + [_vp] * 16 + [_vp, _sz, _vp]),
 }
 
 _lib = None

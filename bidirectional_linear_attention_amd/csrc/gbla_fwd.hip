@@ -22,9 +22,9 @@
 namespace gbla {
 
 // ============================================================== schedule
-__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ cu, int N, int T, int max_slots,
-                                                   int* __restrict__ nchunks, int* __restrict__ chunk_off,
-                                                   Chunk* __restrict__ tab) {
+__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ cu, int N, int T, int chunk,
+                                                   int max_slots, int* __restrict__ nchunks,
+                                                   int* __restrict__ chunk_off, Chunk* __restrict__ tab) {
   __shared__ int scan[1024];
   __shared__ int bad;
   const int tid = threadIdx.x;
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ c
   for (int b0 = 0; b0 < N; b0 += 1024) {
     const int b = b0 + tid;
     int n = 0;
-    if (b < N) n = (cu[b + 1] - cu[b] + kChunk - 1) / kChunk;
+    if (b < N) n = (cu[b + 1] - cu[b] + chunk - 1) / chunk;
     scan[tid] = n;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
@@ -58,8 +58,8 @@ __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ c
       for (int c = 0; c < n && excl + c < max_slots; ++c) {
         Chunk ch;
         ch.seq = b;
-        ch.start = s + c * kChunk;
-        ch.end = min(s + (c + 1) * kChunk, e);
+        ch.start = s + c * chunk;
+        ch.end = min(s + (c + 1) * chunk, e);
         ch.pad = 0;
         tab[excl + c] = ch;
       }
@@ -73,9 +73,9 @@ __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ c
   }
 }
 
-void launch_schedule(const int32_t* cu, int N, int T, int max_slots, int* nchunks, int* chunk_off, Chunk* tab,
-                     hipStream_t s) {
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, cu, N, T, max_slots, nchunks, chunk_off, tab);
+void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
+                     Chunk* tab, hipStream_t s) {
+  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, cu, N, T, chunk, max_slots, nchunks, chunk_off, tab);
 }
 
 // ============================================================== weight packing
@@ -135,7 +135,12 @@ __device__ __forceinline__ float butterfly8(float (&v)[8], int lane) {
   return x;  // total of head (lane >> 3)
 }
 
-template <typename T>
+// log(sigmoid(z)) = -softplus(-z), stable for any z
+__device__ __forceinline__ float log_sigmoidf_(float z) { return fminf(z, 0.f) - log1pf(__expf(-fabsf(z))); }
+
+// CONV = true: GBLA, x~ = causal conv(x) is stored and g = sigmoid(x~ w_g + b_g).
+// CONV = false: LION-s decay, x~ = x (nothing stored) and g = log sigmoid(x w_lam + b_lam).
+template <typename T, bool CONV = true>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
@@ -152,7 +157,7 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
       float wv[8][4], wg[8][8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const Frag8<T> f = okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
+        const Frag8<T> f = CONV && okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
 #pragma unroll
         for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
       }
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         for (int e = 0; e < 8; ++e) wg[hh][e] = frag_get(f, e);
       }
       Frag8<T> xm1 = frag_zero<T>(), xm2 = frag_zero<T>(), xm3 = frag_zero<T>();
-      if (okc && t_begin < t_end) {
+      if (CONV && okc && t_begin < t_end) {
         if (t_begin >= 1) xm1 = frag_load(x + (size_t)(t_begin - 1) * d + c);
         if (t_begin >= 2) xm2 = frag_load(x + (size_t)(t_begin - 2) * d + c);
         if (t_begin >= 3) xm3 = frag_load(x + (size_t)(t_begin - 3) * d + c);
@@ -175,14 +180,14 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         float o[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          float a = wv[j][3] * frag_get(x0, j);
-          if (pos >= 1) a += wv[j][2] * frag_get(xm1, j);
-          if (pos >= 2) a += wv[j][1] * frag_get(xm2, j);
-          if (pos >= 3) a += wv[j][0] * frag_get(xm3, j);
+          float a = CONV ? wv[j][3] * frag_get(x0, j) : frag_get(x0, j);
+          if (CONV && pos >= 1) a += wv[j][2] * frag_get(xm1, j);
+          if (CONV && pos >= 2) a += wv[j][1] * frag_get(xm2, j);
+          if (CONV && pos >= 3) a += wv[j][0] * frag_get(xm3, j);
           o[j] = a;
         }
         const Frag8<T> of = frag_from<T>(o);
-        if (okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
+        if (CONV && okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
         float sp[8];
 #pragma unroll
         for (int hh = 0; hh < 8; ++hh) {
@@ -206,7 +211,10 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
     for (int e = lane; e < kConvRowsPerWave * 8; e += 64) {
       const int row = e >> 3, hh = e & 7;
       const int t = t_begin + row, h = hg + hh;
-      if (t < t_end && h < H) g_out[(size_t)t * H + h] = sigmoidf_(sacc[w][row][hh] + b_g[h]);
+      if (t < t_end && h < H) {
+        const float z = sacc[w][row][hh] + b_g[h];
+        g_out[(size_t)t * H + h] = CONV ? sigmoidf_(z) : log_sigmoidf_(z);
+      }
     }
     __syncthreads();
   }
@@ -218,11 +226,25 @@ void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int
   const dim3 grid((T + rows - 1) / rows);
   if (T == 0) return;
   if (dt == BF16)
-    hipLaunchKernelGGL(k_conv_fwd<bf16>, grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
+    hipLaunchKernelGGL((k_conv_fwd<bf16, true>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
                        (const bf16*)conv_w, (const bf16*)w_g, b_g, (bf16*)xt, g);
   else
-    hipLaunchKernelGGL(k_conv_fwd<float>, grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
+    hipLaunchKernelGGL((k_conv_fwd<float, true>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
                        (const float*)conv_w, (const float*)w_g, b_g, (float*)xt, g);
+}
+
+void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
+                      const float* b_lam, float* logl, hipStream_t s) {
+  const int rows = 4 * kConvRowsPerWave;
+  const dim3 grid((T + rows - 1) / rows);
+  if (T == 0) return;
+  // no conv in this mode: the conv-tap pointer is never dereferenced
+  if (dt == BF16)
+    hipLaunchKernelGGL((k_conv_fwd<bf16, false>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
+                       (const bf16*)w_lam, (const bf16*)w_lam, b_lam, (bf16*)nullptr, logl);
+  else
+    hipLaunchKernelGGL((k_conv_fwd<float, false>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
+                       (const float*)w_lam, (const float*)w_lam, b_lam, (float*)nullptr, logl);
 }
 
 // ============================================================== projection GEMM
@@ -233,7 +255,8 @@ template <typename T, int DH> struct ProjCfg { using S = GemmShape<T, 256, 3 * D
 template <> struct ProjCfg<float, 64> { using S = GemmShape<float, 32, 192, 32, 1, 4>; };
 template <> struct ProjCfg<float, 32> { using S = GemmShape<float, 64, 96, 32, 2, 2>; };
 
-template <typename T, int DH>
+// PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION-s)
+template <typename T, int DH, bool PHI = true>
 __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T* __restrict__ xt,
                                                                       const T* __restrict__ wp, int T_, int d, int H,
                                                                       T* __restrict__ q_out, T* __restrict__ k_out,
@@ -263,7 +286,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
       const int n = wn * S::WTN + 16 * j;
-      const bool lin = n / DH == 2;  // v columns stay linear
+      const bool lin = !PHI || n / DH == 2;  // v columns (and everything without phi) stay linear
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[i][j][r];
@@ -283,24 +306,22 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
   }
 }
 
-template <typename T, int DH>
+template <typename T, int DH, bool PHI>
 static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, hipStream_t s) {
   using S = typename ProjCfg<T, DH>::S;
   const int n = ((T_ + S::BM - 1) / S::BM) * H;
   if (n == 0) return;
-  hipLaunchKernelGGL((k_proj<T, DH>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
+  hipLaunchKernelGGL((k_proj<T, DH, PHI>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
                      (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v);
 }
 
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
-                 void* v_out, hipStream_t s) {
-  if (dt == BF16) {
-    if (dh == 64) proj_t<bf16, 64>(xt, wp, T, d, H, q_out, k_out, v_out, s);
-    else proj_t<bf16, 32>(xt, wp, T, d, H, q_out, k_out, v_out, s);
-  } else {
-    if (dh == 64) proj_t<float, 64>(xt, wp, T, d, H, q_out, k_out, v_out, s);
-    else proj_t<float, 32>(xt, wp, T, d, H, q_out, k_out, v_out, s);
-  }
+                 void* v_out, hipStream_t s, bool phi) {
+#define GBLA_PJ(TT, DD) (phi ? proj_t<TT, DD, true>(xt, wp, T, d, H, q_out, k_out, v_out, s) \
+                             : proj_t<TT, DD, false>(xt, wp, T, d, H, q_out, k_out, v_out, s))
+  if (dt == BF16) { if (dh == 64) GBLA_PJ(bf16, 64); else GBLA_PJ(bf16, 32); }
+  else            { if (dh == 64) GBLA_PJ(float, 64); else GBLA_PJ(float, 32); }
+#undef GBLA_PJ
 }
 
 // ============================================================== split-L state reduction

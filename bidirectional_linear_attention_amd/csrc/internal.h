@@ -15,6 +15,8 @@ enum StageId {
   ST_SCHEDULE, ST_PACK_PROJ, ST_CONV_FWD, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
   ST_PACK_WT, ST_CONV_RECOMPUTE, ST_PROJ_RECOMPUTE, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN,
   ST_DBG_REDUCE, ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
+  ST_LION_LOG_DECAY, ST_LION_PROJ, ST_LION_CHUNK_STATE, ST_LION_SCAN, ST_LION_READOUT,
+  ST_LION_BWD_STATE, ST_LION_BWD_SCAN, ST_LION_BWD_TOKEN, ST_LION_DA, ST_LION_DB_REDUCE,
   kNumStages
 };
 
@@ -34,8 +36,8 @@ class StageScope {
 // tokens per chunk of the split-L reductions and per-token attention kernels
 constexpr int kChunk = 256;
 
-// upper bound on the number of chunks for T tokens in N sequences
-inline int max_chunks(int T, int N) { return (T + kChunk - 1) / kChunk + N; }
+// upper bound on the number of chunks of `chunk` tokens for T tokens in N sequences
+inline int max_chunks(int T, int N, int chunk = kChunk) { return (T + chunk - 1) / chunk + N; }
 
 // rows of the packed per-head projection weights: Q, K and V features
 inline int proj_cols(int dh) { return 3 * dh; }
@@ -44,14 +46,16 @@ inline int proj_cols(int dh) { return 3 * dh; }
 inline int grad_cols(int H, int dh) { return ((3 * H * dh + H) + 63) / 64 * 64; }
 
 // ---- forward / shared
-void launch_schedule(const int32_t* cu, int N, int T, int max_slots, int* nchunks, int* chunk_off, Chunk* tab,
-                     hipStream_t s);
+void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
+                     Chunk* tab, hipStream_t s);
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
                       hipStream_t s);
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
                      const void* w_g, const float* b_g, void* xt, float* g, hipStream_t s);
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
-                 void* v_out, hipStream_t s);
+                 void* v_out, hipStream_t s, bool phi = true);
+void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
+                      const float* b_lam, float* logl, hipStream_t s);
 void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
                           const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s);
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,

@@ -1,0 +1,405 @@
+// LION-s chunkwise backward for gfx950.
+//
+// With P_ij = M_ij (q~_i . k~_j), r_i = sum_j P_ij, y_i = sum_j P_ij v_j / r_i and
+// the upstream gradient dy, let g^_i = [dy_i / r_i | -(dy_i . y_i) / r_i] (a
+// dh+1 vector, dN_i = its first dh entries) and v^_j = [v_j | 1]. Then
+//   dP_ij = g^_i . v^_j
+//   dq~_i = sum_j M_ij dP_ij k~_j,   dk~_j = sum_i M_ij dP_ij q~_i,   dv_j = sum_i P_ij dN_i
+// and for the decay (M_ij = exp(-|A_i - A_j|), A non-increasing), with E_ij = dP_ij P_ij,
+//   dA_t = sum_{j<t} (E_tj + E_jt) - sum_{j>t} (E_tj + E_jt),
+//   dlog lambda_k = sum_{t>=k} dA_t (within the sequence),  da = dlog lambda (1 - lambda).
+// Each sum over j splits like the forward into the chunk itself and the chunks
+// before / after it. The inter-chunk parts use the forward states SF, SB for
+// dq~ and the states HF, HB of sum_i decay q~_i g^_i^T (same recurrences) for dk~
+// and dv; the inter-chunk parts of dA are dot products of q~ and k~ with those
+// inter-chunk gradients (e.g. sum_{j before c} E_tj = q~_t . dq~_t(from SF)).
+//
+// k_lion_bwd_token   per (chunk, head): dq, dk, dv (through the feature-map
+//                    vector-Jacobian product) into G, and chunk-local suffix
+//                    sums of dA
+// k_lion_da          per (sequence, head): adds the suffix of later chunks,
+//                    writes da into G and a partial sum for db_lam
+#include "internal.h"
+#include "lion_internal.h"
+
+namespace gbla {
+
+// phi(u) = (SiLU(u) + 0.5) / n: given p = phi(u), n and d = dphi, returns du
+__device__ __forceinline__ float phi_lion_vjp(float u, float p, float inv_n, float d, float dot) {
+  const float sg = sigmoidf_(u);
+  return (d - p * dot) * inv_n * (sg * (1.f + u * (1.f - sg)));
+}
+
+// stage a state [dh x dh] (row a = row feature, column n = column feature) as a
+// row-major LDS tile [a][n] (pitch ld) and its extra column (index dh) as floats
+template <typename T, int DH>
+__device__ __forceinline__ void stage_state_rows(T* R, int ld, float* extra, const float* __restrict__ S, int tid) {
+  for (int e = tid; e < DH * DH; e += 256) {
+    const int a = e / DH, n = e - a * DH;
+    R[a * ld + n] = from_f<T>(S[e]);
+  }
+  if (tid < DH) extra[tid] = S[DH * DH + tid];
+}
+
+// Block = (chunk, head), 4 waves; wave w owns rows 16 w .. 16 w + 15 of the chunk
+// (query rows in phase 1, key rows in phase 2). The extra column of [v | 1] and
+// of g^ enters every contraction as a rank-1 term, so all MFMA widths are dh.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void k_lion_bwd_token(
+    const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vr, const float* __restrict__ logl,
+    const T* __restrict__ yv, const T* __restrict__ dy, const float* __restrict__ rsum, const float* __restrict__ st,
+    const float* __restrict__ hst, const int* __restrict__ nchunks, const Chunk* __restrict__ tab, int max_slots,
+    int H, int Kp, T* __restrict__ G, float* __restrict__ dA_loc, float* __restrict__ dA_tot) {
+  constexpr int C = kLionChunk;
+  constexpr int FB = DH / 16;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LDR = DH + PAD, LDP = C + PAD;
+  constexpr int E = DH * DH + DH;
+  constexpr int V8 = DH / 8, NV = (C * V8 + 255) / 256;
+  __shared__ __align__(16) T Qs[C * LDR];   // phi(q); dk on output
+  __shared__ __align__(16) T Ks[C * LDR];   // phi(k); dq on output
+  __shared__ __align__(16) T Vs[C * LDR];   // v; dv on output
+  __shared__ __align__(16) T Gs[C * LDR];   // dy / r
+  __shared__ __align__(16) T Pt[C * LDP];   // P
+  __shared__ __align__(16) T Dt[C * LDP];   // dP (.) M
+  __shared__ __align__(16) T SFs[DH * LDR];  // SF, then HF
+  __shared__ __align__(16) T SBs[DH * LDR];  // SB, then HB
+  __shared__ float xF[DH], xB[DH];          // extra columns of the staged states
+  __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C];
+  __shared__ float colpart[4][C];
+  __shared__ float Ls;
+
+  const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
+  if (lid >= max_slots * H) return;
+  const int slot = lid / H, h = lid - slot * H;
+  if (slot >= *nchunks) return;
+  const Chunk ch = tab[slot];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
+  const int D = H * DH;
+  const int r0 = 16 * w;
+
+  // ---------------- phase 0: staging
+  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
+  const float* sp = st + ((size_t)slot * H + h) * 2 * E;
+  stage_state_rows<T, DH>(SFs, LDR, xF, sp, tid);
+  stage_state_rows<T, DH>(SBs, LDR, xB, sp + E, tid);
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int it = tid + 256 * v;
+    if (it >= C * V8) continue;
+    const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
+    const bool ok = t < ch.end;
+    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+    float u[8], p[8];
+    Frag8<T> f = ok ? frag_load(qr + o) : frag_zero<T>();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    float n = phi_lion8<V8>(u, p, ok);
+    frag_store(Qs + r * LDR + c, frag_from<T>(p));
+    if (c == 0) nq[r] = ok ? n : 1.f;
+    f = ok ? frag_load(kr + o) : frag_zero<T>();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    n = phi_lion8<V8>(u, p, ok);
+    frag_store(Ks + r * LDR + c, frag_from<T>(p));
+    if (c == 0) nk[r] = ok ? n : 1.f;
+    frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
+    const Frag8<T> fd = ok ? frag_load(dy + o) : frag_zero<T>();
+    const Frag8<T> fy = ok ? frag_load(yv + o) : frag_zero<T>();
+    const float inv = ok ? 1.f / rsum[(size_t)t * H + h] : 0.f;
+    float g[8], dd = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      g[j] = frag_get(fd, j) * inv;
+      dd += frag_get(fd, j) * frag_get(fy, j);
+    }
+#pragma unroll
+    for (int m = 1; m < V8; m <<= 1) dd += __shfl_xor(dd, m, 64);
+    frag_store(Gs + r * LDR + c, frag_from<T>(g));
+    if (c == 0) {
+      gden[r] = -dd * inv;
+      vone[r] = ok ? 1.f : 0.f;
+    }
+  }
+  __syncthreads();
+  const float L = Ls;
+
+  // ---------------- phase 1: query rows i = r0 + 4 grp + r
+  float dqo[FB][4];
+  {
+    Frag8<T> aq[DH / 32], ag[DH / 32];
+#pragma unroll
+    for (int s = 0; s < DH / 32; ++s) {
+      aq[s] = frag_load(Qs + (r0 + col) * LDR + 32 * s + 8 * grp);
+      ag[s] = frag_load(Gs + (r0 + col) * LDR + 32 * s + 8 * grp);
+    }
+    float gd[4], ef[4], eb[4], sgn[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = As[r0 + 4 * grp + r];
+      gd[r] = gden[r0 + 4 * grp + r];
+      ef[r] = __expf(a);
+      eb[r] = __expf(L - a);
+    }
+#pragma unroll
+    for (int nt = 0; nt < C / 16; ++nt) {
+      f32x4 g = zero4(), dp = zero4();
+#pragma unroll
+      for (int s = 0; s < DH / 32; ++s) {
+        mma8(g, aq[s], frag_load(Ks + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(dp, ag[s], frag_load(Vs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+      }
+      const int j = 16 * nt + col;
+      const float aj = As[j], oj = vone[j];
+      float cp = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 4 * grp + r;
+        const float m = __expf(-fabsf(As[i] - aj));
+        const float dpf = dp[r] + gd[r] * oj;
+        const float P = g[r] * m, e = dpf * P;
+        Pt[i * LDP + j] = from_f<T>(P);
+        Dt[i * LDP + j] = from_f<T>(dpf * m);
+        sgn[r] += j < i ? e : (j > i ? -e : 0.f);  // towards dA_i
+        cp += i < j ? e : (i > j ? -e : 0.f);      // towards dA_j
+      }
+      cp += __shfl_xor(cp, 16, 64);
+      cp += __shfl_xor(cp, 32, 64);
+      if (grp == 0) colpart[w][j] = cp;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sgn[r] = row16_sum(sgn[r]);
+    __syncthreads();  // Pt, Dt complete
+
+    f32x4 dq[FB];
+    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < FB; ++nt) {
+      f32x4 in = zero4(), fw = zero4(), bw = zero4();
+#pragma unroll
+      for (int s = 0; s < C / 32; ++s)
+        mma8(in, frag_load(Dt + (r0 + col) * LDP + 32 * s + 8 * grp),
+             frag_kmajor<T>(Ks, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+#pragma unroll
+      for (int s = 0; s < DH / 32; ++s) {
+        mma8(fw, ag[s], frag_load(SFs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(bw, ag[s], frag_load(SBs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+      }
+      const float zf = xF[16 * nt + col], zb = xB[16 * nt + col];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 4 * grp + r;
+        const float f = ef[r] * (fw[r] + gd[r] * zf), b = eb[r] * (bw[r] + gd[r] * zb);
+        dq[nt][r] = in[r] + f + b;
+        const float p = to_f<T>(Qs[i * LDR + 16 * nt + col]);
+        inter[r] += p * (f - b);
+        dot[r] += p * dq[nt][r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      inter[r] = row16_sum(inter[r]);
+      dot[r] = row16_sum(dot[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = r0 + 4 * grp + r;
+      const int t = ch.start + i;
+      const bool ok = t < ch.end;
+      const float inv_n = 1.f / nq[i];
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) {
+        const float u = ok ? to_f<T>(qr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;
+        const float p = to_f<T>(Qs[i * LDR + 16 * nt + col]);
+        dqo[nt][r] = ok ? phi_lion_vjp(u, p, inv_n, dq[nt][r], dot[r]) : 0.f;
+      }
+      if (col == 0) dAq[i] = ok ? sgn[r] + inter[r] : 0.f;
+    }
+  }
+  __syncthreads();  // every wave is done with SF / SB
+
+  // ---------------- phase 2: key rows j = r0 + 4 grp + r
+  const float* hp = hst + ((size_t)slot * H + h) * 2 * E;
+  stage_state_rows<T, DH>(SFs, LDR, xF, hp, tid);
+  stage_state_rows<T, DH>(SBs, LDR, xB, hp + E, tid);
+  if (tid < C) dAk[tid] = (colpart[0][tid] + colpart[1][tid]) + (colpart[2][tid] + colpart[3][tid]);
+  __syncthreads();
+  float dko[FB][4];
+  f32x4 dv[FB];
+  {
+    Frag8<T> ak[DH / 32], av[DH / 32];
+#pragma unroll
+    for (int s = 0; s < DH / 32; ++s) {
+      ak[s] = frag_load(Ks + (r0 + col) * LDR + 32 * s + 8 * grp);
+      av[s] = frag_load(Vs + (r0 + col) * LDR + 32 * s + 8 * grp);
+    }
+    float ef[4], eb[4], oj[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float a = As[r0 + 4 * grp + r];
+      ef[r] = __expf(a);
+      eb[r] = __expf(L - a);
+      oj[r] = vone[r0 + 4 * grp + r];
+    }
+    f32x4 dk[FB];
+    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < FB; ++nt) {
+      f32x4 ik = zero4(), iv = zero4(), fk = zero4(), bk = zero4(), fv = zero4(), bv = zero4();
+#pragma unroll
+      for (int s = 0; s < C / 32; ++s) {
+        mma8(ik, frag_kmajor<T>(Dt, LDP, 32 * s + 8 * grp, r0, lane),
+             frag_kmajor<T>(Qs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(iv, frag_kmajor<T>(Pt, LDP, 32 * s + 8 * grp, r0, lane),
+             frag_kmajor<T>(Gs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+      }
+#pragma unroll
+      for (int s = 0; s < DH / 32; ++s) {
+        mma8(fk, av[s], frag_load(SFs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(bk, av[s], frag_load(SBs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(fv, ak[s], frag_kmajor<T>(SFs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(bv, ak[s], frag_kmajor<T>(SBs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+      }
+      const float hf = xF[16 * nt + col], hb = xB[16 * nt + col];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = r0 + 4 * grp + r;
+        const float f = ef[r] * (fk[r] + oj[r] * hf), b = eb[r] * (bk[r] + oj[r] * hb);
+        dk[nt][r] = ik[r] + f + b;
+        dv[nt][r] = iv[r] + ef[r] * fv[r] + eb[r] * bv[r];
+        const float p = to_f<T>(Ks[j * LDR + 16 * nt + col]);
+        inter[r] += p * (f - b);
+        dot[r] += p * dk[nt][r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      inter[r] = row16_sum(inter[r]);
+      dot[r] = row16_sum(dot[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = r0 + 4 * grp + r;
+      const int t = ch.start + j;
+      const bool ok = t < ch.end;
+      const float inv_n = 1.f / nk[j];
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) {
+        const float u = ok ? to_f<T>(kr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;
+        const float p = to_f<T>(Ks[j * LDR + 16 * nt + col]);
+        dko[nt][r] = ok ? phi_lion_vjp(u, p, inv_n, dk[nt][r], dot[r]) : 0.f;
+      }
+      if (col == 0) dAk[j] = ok ? dAk[j] + inter[r] : 0.f;
+    }
+  }
+  __syncthreads();  // every wave is done reading the tiles; reuse them for the outputs
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = r0 + 4 * grp + r;
+#pragma unroll
+    for (int nt = 0; nt < FB; ++nt) {
+      Ks[i * LDR + 16 * nt + col] = from_f<T>(dqo[nt][r]);
+      Qs[i * LDR + 16 * nt + col] = from_f<T>(dko[nt][r]);
+      Vs[i * LDR + 16 * nt + col] = from_f<T>(dv[nt][r]);
+    }
+  }
+  __syncthreads();
+
+  // ---------------- outputs
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int it = tid + 256 * v;
+    if (it >= C * V8) continue;
+    const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
+    if (t < ch.end) {
+      T* g = G + (size_t)t * Kp + h * DH + c;
+      frag_store(g, frag_load(Ks + r * LDR + c));
+      frag_store(g + D, frag_load(Qs + r * LDR + c));
+      frag_store(g + 2 * D, frag_load(Vs + r * LDR + c));
+    }
+  }
+  if (tid < C) {  // chunk-local suffix sums of dA
+    const bool ok = ch.start + tid < ch.end;
+    float a = ok ? dAq[tid] + dAk[tid] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_down(a, off, 64);
+      if (tid + off < 64) a += o;
+    }
+    if (ok) dA_loc[(size_t)(ch.start + tid) * H + h] = a;
+    if (tid == 0) dA_tot[(size_t)slot * H + h] = a;
+  }
+}
+
+void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
+                           const void* y, const void* dy, const float* rsum, const float* st, const float* hst,
+                           const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G,
+                           float* dA_loc, float* dA_tot, hipStream_t s) {
+  const dim3 grid(xcd_grid(max_slots * H));
+#define LION_BT(TT, DD) hipLaunchKernelGGL((k_lion_bwd_token<TT, DD>), grid, dim3(256), 0, s, (const TT*)q,         \
+                                           (const TT*)k, (const TT*)v, logl, (const TT*)y, (const TT*)dy, rsum, st, \
+                                           hst, nchunks, tab, max_slots, H, Kp, (TT*)G, dA_loc, dA_tot)
+  if (dt == BF16) { if (dh == 64) LION_BT(bf16, 64); else LION_BT(bf16, 32); }
+  else            { if (dh == 64) LION_BT(float, 64); else LION_BT(float, 32); }
+#undef LION_BT
+}
+
+// ---------------------------------------------------------------- decay gradient
+// Block = (sequence, head). dlog lambda_t = dA_loc[t] + (dA of all later chunks),
+// da_t = dlog lambda_t (1 - lambda_t) -> G column 3 D + h; the block's sum of
+// da (fixed order) -> db_part[b][h]. Blocks of head 0 also clear the G padding.
+template <typename T>
+__global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl, const float* __restrict__ dA_loc,
+                                                 float* __restrict__ dA_tot, const int* __restrict__ nchunks,
+                                                 const int* __restrict__ chunk_off, const Chunk* __restrict__ tab,
+                                                 int N, int H, int D, int Kp, T* __restrict__ G,
+                                                 float* __restrict__ db_part) {
+  __shared__ float wsum[4];
+  const int b = blockIdx.x / H, h = blockIdx.x - b * H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nc = *nchunks;
+  const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
+  if (tid == 0) {  // exclusive suffix sums over the chunks, in place (from the last chunk)
+    float acc = 0.f;
+    for (int c = c1 - 1; c >= c0; --c) {
+      float* p = dA_tot + (size_t)c * H + h;
+      const float v = *p;
+      *p = acc;
+      acc += v;
+    }
+  }
+  __syncthreads();
+  float sum = 0.f;
+  const int gpad = 3 * D + H;
+  for (int c = c0; c < c1; ++c) {
+    const Chunk ch = tab[c];
+    const float carry = dA_tot[(size_t)c * H + h];
+    for (int t = ch.start + tid; t < ch.end; t += 256) {
+      const float ll = logl[(size_t)t * H + h];
+      const float da = (dA_loc[(size_t)t * H + h] + carry) * -expm1f(ll);
+      G[(size_t)t * Kp + 3 * D + h] = from_f<T>(da);
+      sum += da;
+      if (h == 0)
+        for (int cc = gpad; cc < Kp; ++cc) G[(size_t)t * Kp + cc] = from_f<T>(0.f);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane == 0) wsum[w] = sum;
+  __syncthreads();
+  if (tid == 0) db_part[(size_t)b * H + h] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+}
+
+void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks,
+                    const int* chunk_off, const Chunk* tab, int N, int T, int H, int D, int Kp, int dt, void* G,
+                    float* db_part, hipStream_t s) {
+  (void)T;
+  float* tot = const_cast<float*>(dA_tot);
+  if (dt == BF16)
+    hipLaunchKernelGGL(k_lion_da<bf16>, dim3(N * H), dim3(256), 0, s, logl, dA_loc, tot, nchunks, chunk_off, tab, N,
+                       H, D, Kp, (bf16*)G, db_part);
+  else
+    hipLaunchKernelGGL(k_lion_da<float>, dim3(N * H), dim3(256), 0, s, logl, dA_loc, tot, nchunks, chunk_off, tab, N,
+                       H, D, Kp, (float*)G, db_part);
+}
+
+}  // namespace gbla

@@ -1,0 +1,69 @@
+// LION-s chunkwise kernels: launchers and device helpers shared by the forward and backward (internal).
+#pragma once
+#include "internal.h"
+
+namespace gbla {
+
+// tokens per chunk of the chunkwise LION-s evaluation (one per lane of a wave)
+constexpr int kLionChunk = 64;
+
+// ---------------------------------------------------------------- tile staging helpers
+// Rows of 8-element vectors: thread it handles row it / V8, columns 8 (it % V8)
+// .. + 7, and the V8 threads of one row are consecutive lanes.
+
+// phi(u) = (SiLU(u) + 0.5) / ||SiLU(u) + 0.5||_2 of one row, given this thread's 8
+// raw values; returns the row norm. `valid` rows produce zeros.
+template <int V8>
+__device__ __forceinline__ float phi_lion8(const float (&u)[8], float (&out)[8], bool valid) {
+  float f[8], ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    f[j] = u[j] * sigmoidf_(u[j]) + 0.5f;
+    ss += f[j] * f[j];
+  }
+#pragma unroll
+  for (int m = 1; m < V8; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  const float n = sqrtf(ss);
+  const float inv = valid ? 1.f / n : 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) out[j] = f[j] * inv;
+  return n;
+}
+
+// log-decay of the chunk's tokens -> inclusive prefix A~ (LDS), the chunk total
+// L (LDS), and validity; tokens past the chunk end count as log lambda = 0.
+// Called by all threads; uses wave 0.
+template <int C>
+__device__ __forceinline__ void chunk_decay_prefix(const float* __restrict__ logl, const Chunk& ch, int H, int h,
+                                                   float* As, float* Ls, int tid) {
+  static_assert(C == 64, "one token per lane of wave 0");
+  if (tid < 64) {
+    const int t = ch.start + tid;
+    float a = t < ch.end ? logl[(size_t)t * H + h] : 0.f;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(a, off, 64);
+      if (tid >= off) a += o;
+    }
+    As[tid] = a;
+    if (tid == 63) *Ls = a;
+  }
+}
+
+void launch_lion_chunk_state(int dt, int dh, int mode, const void* rsrc, const void* vsrc, const void* ysrc,
+                             const float* rsum, const float* logl, const int* nchunks, const Chunk* tab,
+                             int max_slots, int H, float* out, float* lam_out, hipStream_t s);
+void launch_lion_scan(float* st, const float* lam, const int* nchunks, const int* chunk_off, int N, int H, int E,
+                      hipStream_t s);
+void launch_lion_readout(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
+                         const float* st, const int* nchunks, const Chunk* tab, int max_slots, int H, void* y,
+                         float* rsum, hipStream_t s);
+void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
+                           const void* y, const void* dy, const float* rsum, const float* st, const float* hst,
+                           const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G,
+                           float* dA_loc, float* dA_tot, hipStream_t s);
+void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks,
+                    const int* chunk_off, const Chunk* tab, int N, int T, int H, int D, int Kp, int dt, void* G,
+                    float* db_part, hipStream_t s);
+
+}  // namespace gbla

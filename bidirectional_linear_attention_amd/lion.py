@@ -1,0 +1,142 @@
+"""LION-s layer of libgbla.so (C ABI in include/lion.h).
+
+Selective-decay bidirectional linear attention of "Linear Attention for
+Efficient Bidirectional Sequence Modeling" (method details: bidirectional mask
+M = M^F + M^B - I, chunkwise form; Lion-s row of the model table; feature map
+(SiLU + 0.5) / ||.||): q, k, v = x W, lambda = sigmoid(x w_lam + b_lam),
+y = Scale((phi(Q) phi(K)^T) (.) M) V with row normalisation, per packed
+sequence and head. `lion_forward` / `lion_backward` mirror the C entry points
+(device pointers and the current HIP stream only); `forward` / `backward`
+allocate outputs, cache and workspace. Every step runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _lib
+from ._lib import DTYPE_BF16, DTYPE_F32, LionProblem
+
+__all__ = ["LionProblem", "problem", "workspace_size", "activation_size", "lion_forward", "lion_backward",
+           "forward", "backward"]
+
+CHUNK = 64
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype) -> LionProblem:
+    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code."""
+    if isinstance(dtype, int):
+        code = dtype
+    else:
+        torch = _torch()
+        if dtype == torch.float32:
+            code = DTYPE_F32
+        elif dtype == torch.bfloat16:
+            code = DTYPE_BF16
+        else:
+            raise TypeError(f"unsupported dtype {dtype}: float32 or bfloat16")
+    return LionProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code, CHUNK, 0)
+
+
+def workspace_size(p: LionProblem, backward: bool) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().lion_workspace_size(ctypes.byref(p), int(bool(backward)), ctypes.byref(out)),
+               "lion_workspace_size")
+    return out.value
+
+
+def activation_size(p: LionProblem) -> int:
+    out = ctypes.c_size_t()
+    _lib.check(_lib.load().lion_activation_size(ctypes.byref(p), ctypes.byref(out)), "lion_activation_size")
+    return out.value
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("all tensors must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("all tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _nbytes(t):
+    return ctypes.c_size_t(t.numel() * t.element_size())
+
+
+def lion_forward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, y, act, workspace, stream=None) -> None:
+    """Enqueue the forward pass (include/lion.h: lion_forward); act may be None."""
+    st = _lib.load().lion_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                  _ptr(w_lam), _ptr(b_lam), _ptr(y), _ptr(act), _ptr(workspace), _nbytes(workspace),
+                                  _stream(stream))
+    _lib.check(st, "lion_forward")
+
+
+def lion_backward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, dx, dw_q, dw_k, dw_v,
+                  dw_lam, db_lam, workspace, stream=None) -> None:
+    """Enqueue the backward pass (include/lion.h: lion_backward)."""
+    st = _lib.load().lion_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(w_q), _ptr(w_k), _ptr(w_v),
+                                   _ptr(w_lam), _ptr(b_lam), _ptr(act), _ptr(y), _ptr(dy), _ptr(dx), _ptr(dw_q),
+                                   _ptr(dw_k), _ptr(dw_v), _ptr(dw_lam), _ptr(db_lam), _ptr(workspace),
+                                   _nbytes(workspace), _stream(stream))
+    _lib.check(st, "lion_backward")
+
+
+def _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads):
+    torch = _torch()
+    T, d = x.shape
+    D = w_q.shape[1]
+    if D % num_heads:
+        raise ValueError("w_q columns must be a multiple of num_heads")
+    for name, t, shape in (("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)), ("w_v", w_v, (d, D)),
+                           ("w_lam", w_lam, (num_heads, d))):
+        if tuple(t.shape) != shape or t.dtype != x.dtype:
+            raise ValueError(f"{name}: expected {shape} {x.dtype}, got {tuple(t.shape)} {t.dtype}")
+    if b_lam.dtype != torch.float32 or tuple(b_lam.shape) != (num_heads,):
+        raise ValueError("b_lam must be float32 [num_heads]")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be int32 [N+1]")
+    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype)
+
+
+def forward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads: int, workspace=None,
+            save_activations: bool = True):
+    """Allocate y, the activation cache (if save_activations) and the workspace
+    (unless given) and run lion_forward. Returns (y [T, H*d_h], act or None)."""
+    torch = _torch()
+    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads)
+    dev = x.device
+    y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
+    act = torch.empty(activation_size(p), dtype=torch.uint8, device=dev) if save_activations else None
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, False), dtype=torch.uint8, device=dev)
+    lion_forward(p, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, y, act, workspace)
+    return y, act
+
+
+def backward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, num_heads: int, workspace=None) -> dict:
+    """Allocate the gradients (and the workspace unless given) and run
+    lion_backward. Returns dict dx, dw_q, dw_k, dw_v, dw_lam, db_lam."""
+    torch = _torch()
+    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads)
+    dev = x.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    g = dict(dx=torch.empty_like(x), dw_q=torch.empty(w_q.shape, **f32), dw_k=torch.empty(w_k.shape, **f32),
+             dw_v=torch.empty(w_v.shape, **f32), dw_lam=torch.empty(w_lam.shape, **f32),
+             db_lam=torch.empty(b_lam.shape, **f32))
+    if workspace is None:
+        workspace = torch.empty(workspace_size(p, True), dtype=torch.uint8, device=dev)
+    lion_backward(p, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, g["dx"], g["dw_q"], g["dw_k"],
+                  g["dw_v"], g["dw_lam"], g["db_lam"], workspace)
+    return g

@@ -123,3 +123,74 @@ def test_backward_rejects_null_and_small_workspace_without_launching():
     args[17] = None   # db_g
     assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
     assert lib.gbla_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5
+
+
+# ---------------------------------------------------------------- LION-s entry points
+def _lprob(**kw):
+    base = dict(num_seqs=2, total_tokens=100, d_model=64, num_heads=2, head_dim=64, dtype=gb.DTYPE_BF16,
+                chunk=64, reserved=0)
+    base.update(kw)
+    return _lib.LionProblem(*(base[k] for k in ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim",
+                                                "dtype", "chunk", "reserved")))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(chunk=32), 3), (dict(reserved=1), 3),
+    (dict(d_model=60), 2), (dict(num_seqs=0), 2), (dict(total_tokens=-1), 2), (dict(num_heads=0), 2),
+    (dict(total_tokens=1 << 30), 2),
+])
+def test_lion_size_queries_reject_bad_problems(kw, status):
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    assert lib.lion_workspace_size(ctypes.byref(_lprob(**kw)), 0, ctypes.byref(out)) == status
+    assert lib.lion_activation_size(ctypes.byref(_lprob(**kw)), ctypes.byref(out)) == status
+
+
+def test_lion_size_queries_are_consistent():
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    p = _lprob()
+    assert lib.lion_activation_size(ctypes.byref(p), ctypes.byref(out)) == 0
+    act = out.value
+    # raw q, k, v (bf16), log lambda and row sums, and two carried states per chunk slot and head
+    slots = (100 + 63) // 64 + 2
+    assert act >= 3 * 100 * 128 * 2 + 2 * 100 * 2 * 4 + slots * 2 * 2 * (64 * 64 + 64) * 4
+    assert lib.lion_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    assert out.value >= act
+    assert lib.lion_workspace_size(ctypes.byref(p), 1, ctypes.byref(out)) == 0
+    assert out.value > 0
+    assert lib.lion_workspace_size(None, 0, ctypes.byref(out)) == 1
+    assert lib.lion_activation_size(ctypes.byref(p), None) == 1
+
+
+def test_lion_forward_rejects_bad_arguments_without_launching():
+    lib = _lib.load()
+    p = _lprob()
+    out = ctypes.c_size_t()
+    lib.lion_workspace_size(ctypes.byref(p), 0, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(9)]
+    args = list(a)
+    args[5] = None  # w_lam
+    assert lib.lion_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    args = list(a)
+    args[2] = _fake(0x12004)  # misaligned w_q
+    assert lib.lion_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
+    assert lib.lion_forward(ctypes.byref(p), *a, _fake(0x900000), need - 1, None) == 5
+    assert lib.lion_forward(ctypes.byref(_lprob(chunk=128)), *a, _fake(0x900000), need, None) == 3
+
+
+def test_lion_backward_requires_the_activation_cache():
+    lib = _lib.load()
+    p = _lprob()
+    out = ctypes.c_size_t()
+    lib.lion_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(16)]
+    args = list(a)
+    args[7] = None  # act
+    assert lib.lion_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    args = list(a)
+    args[15] = _fake(0x1f002)  # misaligned db_lam
+    assert lib.lion_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
+    assert lib.lion_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5

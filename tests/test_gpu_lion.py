@@ -1,0 +1,181 @@
+"""GPU parity of the HIP LION-s path (chunkwise, 64-token chunks) against the
+float64 oracle's full masked-matrix form.
+
+Every case feeds the same seeded inputs (bf16-representable values for bf16
+workloads) to libgbla.so through the C ABI (include/lion.h) and to oracle.lion,
+and compares each output with the max-norm relative error
+    ||gpu - oracle||_inf / ||oracle||_inf
+against 1e-4 for float32 inputs and 2e-2 for bfloat16 inputs with float32
+accumulation. At the full 16 x 4096 size the oracle evaluates sampled
+sequences (y and dx of a sequence depend only on that sequence), and the
+weight gradients are checked through an identity that holds at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bidirectional_linear_attention_amd import lion as gl
+from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, small_variant
+from oracle import lion as ol
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+GRADS = ("dx", "dw_q", "dw_k", "dw_v", "dw_lam", "db_lam")
+LION = WORKLOADS["lion_s_bf16_B16_L4096_d512"]
+
+
+def rel_err(got, ref):
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    den = np.max(np.abs(ref))
+    return float(np.max(np.abs(np.asarray(got, np.float64) - ref)) / max(den, 1e-30))
+
+
+def to_dev(inp):
+    dt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dt).contiguous()
+
+    return dict(x=t(inp["x"]), cu=torch.from_numpy(inp["cu_seqlens"]).to("cuda"), w_q=t(inp["w_q"]),
+                w_k=t(inp["w_k"]), w_v=t(inp["w_v"]), w_lam=t(inp["w_lam"]),
+                b_lam=torch.from_numpy(inp["b_lam"]).float().to("cuda"), dy=t(inp["dy"]))
+
+
+def run_gpu(inp, backward=True):
+    d = to_dev(inp)
+    H = inp["H"]
+    y, act = gl.forward(d["x"], d["cu"], d["w_q"], d["w_k"], d["w_v"], d["w_lam"], d["b_lam"], H,
+                        save_activations=backward)
+    out = {"y": y}
+    if backward:
+        out.update(gl.backward(d["x"], d["cu"], d["w_q"], d["w_k"], d["w_v"], d["w_lam"], d["b_lam"], act, y,
+                               d["dy"], H))
+    torch.cuda.synchronize()
+    return {k: v.float().cpu().numpy() for k, v in out.items()}
+
+
+def oracle_args(inp):
+    return [inp[k] for k in ("x", "cu_seqlens", "w_q", "w_k", "w_v", "w_lam", "b_lam")]
+
+
+def compare(inp, backward=True, tol=None, label=""):
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    gpu = run_gpu(inp, backward)
+    errs = {"y": rel_err(gpu["y"], ol.forward_full(*oracle_args(inp), inp["H"]))}
+    if backward:
+        g = ol.backward_full(*oracle_args(inp), inp["dy"], inp["H"])
+        for k in GRADS:
+            errs[k] = rel_err(gpu[k], g[k])
+    print(f"\n[{label}] T={inp['T']} N={inp['N']} d={inp['d']} H={inp['H']} dh={inp['dh']} {inp['dtype']}: "
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"tolerance {tol} exceeded: {bad}"
+    return gpu
+
+
+# ------------------------------------------------------------ float32 parity at 1e-4
+
+@pytest.mark.parametrize("lengths,d,H,dh", [
+    ((300, 1, 130, 64, 65), 96, 3, 64),     # several chunks, ragged tails, one-token and exact-chunk sequences
+    ((129, 0, 255, 40, 2), 64, 2, 32),      # empty sequence, head_dim 32
+    ((512,), 40, 1, 64),                    # d not a multiple of the GEMM k chunk
+])
+def test_f32_forward_backward_multi_chunk(lengths, d, H, dh):
+    w = small_variant(LION, lengths, d_model=d, num_heads=H, head_dim=dh, dtype="f32", seed=51)
+    compare(make_inputs(w), label="f32 " + str(lengths))
+
+
+@pytest.mark.parametrize("bias", [-3.0, 12.0])
+def test_f32_strong_and_vanishing_decay(bias):
+    """bias -3: lambda ~ 0.05, the mask decays to ~0 within a few tokens (every
+    exponent stays <= 0, nothing overflows); bias 12: lambda ~ 1 - 6e-6, almost
+    the all-ones mask of Lion-lit."""
+    w = small_variant(LION, (400, 70), d_model=64, num_heads=2, dtype="f32", seed=52)
+    inp = make_inputs(w)
+    inp["b_lam"] = np.full_like(inp["b_lam"], bias)
+    compare(inp, label=f"f32 bias {bias}")
+
+
+# ------------------------------------------------------------ bf16, the workload recipe at L <= 512
+
+def test_bf16_small_recipe_L512():
+    w = small_variant(LION, (512, 512, 200, 77), seed=53)
+    compare(make_inputs(w), label="bf16 LION-s recipe L<=512")
+
+
+def test_bf16_small_ragged():
+    w = small_variant(LION, (1, 63, 64, 65, 127, 128, 129, 450), d_model=128, num_heads=2, seed=54)
+    compare(make_inputs(w), label="bf16 ragged chunks")
+
+
+# ------------------------------------------------------------ full size: 16 x 4096, d 512, 8 heads
+
+@pytest.mark.timeout(400)  # the float64 oracle needs about a minute for one 4096-token sequence
+def test_bf16_full_size_sampled_sequence_and_identity():
+    inp = make_inputs(LION)
+    gpu = run_gpu(inp)
+    cu = inp["cu_seqlens"]
+    for b in (11,):  # a sampled sequence: its y and dx depend on it alone
+        s, e = int(cu[b]), int(cu[b + 1])
+        sub = dict(inp, x=inp["x"][s:e], dy=inp["dy"][s:e], cu_seqlens=np.array([0, e - s], np.int32))
+        y = ol.forward_full(*oracle_args(sub), inp["H"])
+        g = ol.backward_full(*oracle_args(sub), sub["dy"], inp["H"])
+        errs = {"y": rel_err(gpu["y"][s:e], y), "dx": rel_err(gpu["dx"][s:e], g["dx"])}
+        print(f"\n[full size, sequence {b}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+        assert max(errs.values()) <= TOL["bf16"], errs
+    # y is linear in W_V (the attention weights do not depend on it), so
+    # <W_V, dW_V> = <y, dy> for the whole batch.
+    lhs = float(np.sum(inp["w_v"].astype(np.float64) * gpu["dw_v"]))
+    rhs = float(np.sum(gpu["y"].astype(np.float64) * inp["dy"]))
+    print(f"[full size] <W_V, dW_V> = {lhs:.6e}, <y, dy> = {rhs:.6e}", flush=True)
+    assert abs(lhs - rhs) <= 2e-2 * max(abs(rhs), np.sqrt(np.sum(gpu["y"].astype(np.float64) ** 2)))
+    for k in GRADS:
+        assert np.all(np.isfinite(gpu[k])), k
+
+
+# ------------------------------------------------------------ properties of the GPU path itself
+
+def _small_bf16():
+    return make_inputs(small_variant(LION, (300, 65, 1, 0, 200), d_model=128, num_heads=2, seed=55))
+
+
+def test_bitwise_deterministic():
+    inp = _small_bf16()
+    a, b = run_gpu(inp), run_gpu(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_packed_sequences_are_isolated():
+    """Changing one sequence's tokens leaves every other sequence's y and dx
+    bitwise unchanged."""
+    inp = _small_bf16()
+    a = run_gpu(inp)
+    cu = inp["cu_seqlens"]
+    inp2 = dict(inp, x=inp["x"].copy())
+    inp2["x"][cu[0]:cu[1]] = inp2["x"][cu[0]:cu[1]][::-1]
+    b = run_gpu(inp2)
+    keep = np.ones(inp["T"], bool)
+    keep[cu[0]:cu[1]] = False
+    for k in ("y", "dx"):
+        assert np.array_equal(a[k][keep], b[k][keep]), k
+        assert not np.array_equal(a[k][~keep], b[k][~keep]), k
+
+
+def test_single_token_sequence_returns_v():
+    """L = 1: the only attention weight is the token itself, so y = v."""
+    inp = make_inputs(small_variant(LION, (1, 1, 1), d_model=64, num_heads=2, dtype="f32", seed=56))
+    gpu = run_gpu(inp, backward=False)
+    v = inp["x"].astype(np.float64) @ inp["w_v"].astype(np.float64)
+    assert rel_err(gpu["y"], v) <= 1e-5
+
+
+def test_no_tokens():
+    inp = make_inputs(small_variant(LION, (0, 0), d_model=64, num_heads=2, seed=57))
+    out = run_gpu(inp)
+    assert out["y"].shape == (0, 128)
+    for k in ("dw_q", "dw_k", "dw_v", "dw_lam", "db_lam"):
+        assert np.all(out[k] == 0), k
