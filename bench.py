@@ -11,6 +11,11 @@ the 256 MB Infinity Cache does not serve a step from the previous step's data.
 Prints ONE JSON line: tokens/s (value), the roofline of the dominant stage
 measured live with the library's per-stage HIP events on the launch stream,
 and the float64 CPU oracle timed on a bounded sample of the same workload.
+The same line carries a secondary measurement of the LION-s layer (16 x 4096
+tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under "lion_s".
+
+--copy-calibration instead times a plain device-to-device copy of a known size
+(for scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
 """
 from __future__ import annotations
 
@@ -44,7 +49,7 @@ def stage_work(stage, T, N, d, H, dh, esz, nsplit=1):
         "readout": ("hbm", 2.0 * T * D * esz),
         "bwd_dstate": ("hbm", 3.0 * T * D * esz),
         "bwd_token": ("hbm", 4.0 * T * D * esz + 4.0 * T * H + esz * T * H),
-        "conv_bwd": ("hbm", 4.0 * T * d + 2.0 * T * d * esz),
+        "conv_bwd": ("hbm", 3.0 * T * d * esz),
     }
     return table.get(stage)
 
@@ -55,9 +60,11 @@ def layer_bytes_per_token(d, D, esz):
     return esz * (d + D) + esz * (d + D + d)
 
 
-def traffic_for(stage, launches_per_step):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
-    if there is none or the kernel's source changed since it was taken."""
+def traffic_for(stage):
+    """HBM bytes per launch of the stage's kernel from the committed rocprofv3
+    counter summary (profiles/traffic.json: FETCH_SIZE and WRITE_SIZE scaled by
+    the factors measured on a copy of known size), or None if there is none or
+    any source file of the kernel changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -67,8 +74,13 @@ def traffic_for(stage, launches_per_step):
         return None
     if not rec:
         return None
-    src = os.path.join(ROOT, rec["source"])
-    if not os.path.exists(src) or hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        full = os.path.join(ROOT, src)
+        if not os.path.exists(full):
+            return None
+        h.update(open(full, "rb").read())
+    if h.hexdigest() != rec["sources_sha256"]:
         return None
     return rec["bytes_per_launch"]
 
@@ -97,6 +109,80 @@ def cpu_baseline(inp, sample_seqs):
                       f"({T} tokens) of the same batch, timed once ({dt:.1f} s)"}
 
 
+def copy_calibration(mib=1024, reps=3):
+    """Copy `mib` MiB device to device `reps` times; the copy kernel reads and
+    writes exactly mib MiB per launch."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda:0").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 2, "bytes_written_per_launch": n * 2,
+                                           "launches": reps, "gb_per_s": round(2 * n * 2 / dt / 1e9, 1)}}),
+          flush=True)
+
+
+def lion_leg(steps, warmup):
+    """LION-s forward+backward on its 16 x 4096 workload: tokens/s and stage times."""
+    import numpy as np
+    import torch
+
+    from bidirectional_linear_attention_amd import lion as gl
+    from bidirectional_linear_attention_amd import profile_begin, profile_end
+    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS["lion_s_bf16_B16_L4096_d512"]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt).contiguous()
+
+    T, N, d, H, dh = inp["T"], inp["N"], inp["d"], inp["H"], inp["dh"]
+    D = H * dh
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    w_q, w_k, w_v, w_lam = (t(inp[k]) for k in ("w_q", "w_k", "w_v", "w_lam"))
+    b_lam = torch.from_numpy(inp["b_lam"]).float().to(dev)
+    n_sets = 3
+    xs = [t(inp["x"]) for _ in range(n_sets)]
+    dys = [t(inp["dy"]) for _ in range(n_sets)]
+    p = gl.problem(N, T, d, H, dh, dt)
+    f32 = dict(dtype=torch.float32, device=dev)
+    y = torch.empty((T, D), dtype=dt, device=dev)
+    dx = torch.empty((T, d), dtype=dt, device=dev)
+    dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
+    dwl, dbl = torch.empty((H, d), **f32), torch.empty((H,), **f32)
+    ws = torch.empty(max(gl.workspace_size(p, False), gl.workspace_size(p, True)), dtype=torch.uint8, device=dev)
+    act = torch.empty(gl.activation_size(p), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        x, dy = xs[i % n_sets], dys[i % n_sets]
+        gl.lion_forward(p, x, cu, w_q, w_k, w_v, w_lam, b_lam, y, act, ws)
+        gl.lion_backward(p, x, cu, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, dx, dwq, dwk, dwv, dwl, dbl, ws)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    profile_begin(64 * max(1, steps))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    stages = profile_end()
+    return {"workload": w.name, "tokens_per_step": T, "steps": steps, "warmup": warmup,
+            "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(1e3 * elapsed / steps, 4),
+            "stage_ms_per_step": {k: round(v[0] / steps, 4)
+                                  for k, v in sorted(stages.items(), key=lambda kv: -kv[1][0])}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -104,11 +190,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lion-steps", type=int, default=10, help="LION-s steps timed after the main run (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               "(multi-GPU sharding is a design note, not an implemented path)", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     import numpy as np
     import torch
@@ -177,7 +268,7 @@ def main():
     else:
         achieved, peak, unit = work / avg_s / 1e9, HBM_PEAK_GBS, "GB/s"
     roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom, 1),
+            "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
             "avg_launch_us": round(avg_s * 1e6, 2)}
 
     bpt = layer_bytes_per_token(d, D, esz)
@@ -200,6 +291,10 @@ def main():
         "roofline": roof,
         "stage_ms_per_step": {k: round(v, 4) for k, v in sorted(per_step.items(), key=lambda kv: -kv[1])},
     }
+    if args.lion_steps > 0:
+        del xs, dys, ws, act
+        torch.cuda.empty_cache()
+        out["lion_s"] = lion_leg(args.lion_steps, min(args.warmup, 3))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_seqs)
     print(json.dumps(out), flush=True)
