@@ -254,33 +254,70 @@ struct SeqCursor {
 //   MT[p][n][i] = M[i][n] for n < DH; row DH holds z, rows DH+1 .. NR-1 are 0
 //   MR[p][i][n] = M[i][n]
 // Either destination may be null; part 1 of MT starts NR rows after part 0,
-// part 1 of MR starts DH rows after part 0 (pitch ld elements).
-template <typename T, int DH, int NR>
+// part 1 of MR starts DH rows after part 0 (pitch ld elements, a multiple of 4).
+// M and z must be 16-byte aligned. Every thread of the NT-thread block issues
+// all of its 16-byte loads before its first LDS store.
+template <typename T, int DH, int NR, int NT = 256>
 __device__ __forceinline__ void stage_state(T* MT, T* MR, int ld, const float* __restrict__ M,
-                                            const float* __restrict__ z, int tid, int nthreads) {
+                                            const float* __restrict__ z, int tid) {
   constexpr bool SPLIT = sizeof(T) == 2;
-  for (int e = tid; e < DH * DH; e += nthreads) {
-    const int i = e / DH, n = e - i * DH;
-    const float v = M[e];
-    const T hi = from_f<T>(v);
-    const T lo = from_f<T>(v - to_f<T>(hi));
+  constexpr int V4 = DH * DH / 4, PER = (V4 + NT - 1) / NT;
+  constexpr int XR = (NR - DH) * DH / 4;  // extra rows of MT, in 4-vectors
+  constexpr int XPER = XR > 0 ? (XR + NT - 1) / NT : 1;
+  float4 r[PER], x[XPER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e4 = tid + k * NT;
+    r[k] = e4 < V4 ? reinterpret_cast<const float4*>(M)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < XPER; ++k) {
+    const int e4 = tid + k * NT;
+    x[k] = MT && e4 < DH / 4 ? reinterpret_cast<const float4*>(z)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e4 = tid + k * NT;
+    if (e4 >= V4) continue;
+    const int i = (4 * e4) / DH, n = (4 * e4) % DH;
+    const float v[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+    T hi[4], lo[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      hi[j] = from_f<T>(v[j]);
+      lo[j] = from_f<T>(v[j] - to_f<T>(hi[j]));
+    }
     if (MT) {
-      MT[n * ld + i] = hi;
-      if (SPLIT) MT[NR * ld + n * ld + i] = lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        MT[(n + j) * ld + i] = hi[j];
+        if (SPLIT) MT[NR * ld + (n + j) * ld + i] = lo[j];
+      }
     }
     if (MR) {
-      MR[i * ld + n] = hi;
-      if (SPLIT) MR[DH * ld + i * ld + n] = lo;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        MR[i * ld + n + j] = hi[j];
+        if (SPLIT) MR[DH * ld + i * ld + n + j] = lo[j];
+      }
     }
   }
-  if (MT)
-    for (int e = tid; e < (NR - DH) * DH; e += nthreads) {
-      const int n = DH + e / DH, i = e % DH;
-      const float v = n == DH ? z[i] : 0.f;
-      const T hi = from_f<T>(v);
-      MT[n * ld + i] = hi;
-      if (SPLIT) MT[NR * ld + n * ld + i] = from_f<T>(v - to_f<T>(hi));
+  if (MT) {
+#pragma unroll
+    for (int k = 0; k < XPER; ++k) {  // rows DH.. of MT: z in row DH (from x), zeros below
+      const int e4 = tid + k * NT;
+      if (e4 >= XR) continue;
+      const int n = DH + (4 * e4) / DH, i = (4 * e4) % DH;
+      const float v[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float u = n == DH ? v[j] : 0.f;
+        const T hi = from_f<T>(u);
+        MT[n * ld + i + j] = hi;
+        if (SPLIT) MT[NR * ld + n * ld + i + j] = from_f<T>(u - to_f<T>(hi));
+      }
     }
+  }
 }
 
 // chunk table entry: one run of <= chunk tokens inside one sequence

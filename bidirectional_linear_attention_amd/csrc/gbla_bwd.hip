@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, NR>(Bsz, Brm, LD, st, st + DH * DH, tid, 256);
+  stage_state<T, DH, NR>(Bsz, Brm, LD, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
 
   f32x4 dS[FB][FB];
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = dsz + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, DH>(Str, Srm, LD, st, st + DH * DH, tid, 256);
+  stage_state<T, DH, DH>(Str, Srm, LD, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;

@@ -526,7 +526,7 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid, 256);
+  stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid);
   const int r0 = 16 * w;
 
   // the next tile's loads are issued before the current tile is processed

@@ -89,7 +89,7 @@ size_t plan_bwd(const LDims& m, char* base, LBwdWs* w) {
   t.hst = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * 2 * m.E);
   t.dA_loc = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
   t.dA_tot = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
-  t.db_part = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H);
+  t.db_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
   t.G = c.take<char>(base, (size_t)m.T * m.Kp * m.esz);
   t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
   if (w) *w = t;
@@ -208,9 +208,9 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
     launch_lion_bwd_token(dt, m.dh, A.q, A.k, A.v, A.logl, y, dy, A.rsum, A.st, w.hst, w.nchunks, w.tab, m.slots,
                           m.H, m.Kp, w.G, w.dA_loc, w.dA_tot, s); }
   { StageScope ps(ST_LION_DA, s);
-    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.T, m.H, m.D, m.Kp, dt, w.G,
+    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.slots, m.H, m.D, m.Kp, dt, w.G,
                    w.db_part, s); }
-  { StageScope ps(ST_LION_DB_REDUCE, s); launch_sum_parts(w.db_part, m.H, m.N, nullptr, db_lam, s); }
+  { StageScope ps(ST_LION_DB_REDUCE, s); launch_sum_parts(w.db_part, m.H, 0, w.nchunks, db_lam, s); }
   if (m.T > 0) {
     StageScope ps(ST_GEMM_DX, s);
     launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, dx, s);

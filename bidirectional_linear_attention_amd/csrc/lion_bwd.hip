@@ -30,15 +30,32 @@ __device__ __forceinline__ float phi_lion_vjp(float u, float p, float inv_n, flo
   return (d - p * dot) * inv_n * (sg * (1.f + u * (1.f - sg)));
 }
 
-// stage a state [dh x dh] (row a = row feature, column n = column feature) as a
-// row-major LDS tile [a][n] (pitch ld) and its extra column (index dh) as floats
+// stage a carried state, stored transposed ([n][a]: row n = column feature n,
+// dh values of the row feature a; row dh = the extra column), as the LDS tile
+// [n][a] for n < dh (pitch ld, a multiple of 4) plus the extra row as floats;
+// S is 16-byte aligned and every load is issued before the first LDS store
 template <typename T, int DH>
 __device__ __forceinline__ void stage_state_rows(T* R, int ld, float* extra, const float* __restrict__ S, int tid) {
-  for (int e = tid; e < DH * DH; e += 256) {
-    const int a = e / DH, n = e - a * DH;
-    R[a * ld + n] = from_f<T>(S[e]);
+  constexpr int V4 = DH * DH / 4, PER = (V4 + 255) / 256;
+  float4 r[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e4 = tid + 256 * k;
+    r[k] = e4 < V4 ? reinterpret_cast<const float4*>(S)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  if (tid < DH) extra[tid] = S[DH * DH + tid];
+  const float xv = tid < DH ? S[DH * DH + tid] : 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int e4 = tid + 256 * k;
+    if (e4 >= V4) continue;
+    const int n = (4 * e4) / DH, a = (4 * e4) % DH;
+    T* dst = R + n * ld + a;
+    dst[0] = from_f<T>(r[k].x);
+    dst[1] = from_f<T>(r[k].y);
+    dst[2] = from_f<T>(r[k].z);
+    dst[3] = from_f<T>(r[k].w);
+  }
+  if (tid < DH) extra[tid] = xv;
 }
 
 // Block = (chunk, head), 4 waves; wave w owns rows 16 w .. 16 w + 15 of the chunk
@@ -62,8 +79,8 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
   __shared__ __align__(16) T Gs[C * LDR];   // dy / r
   __shared__ __align__(16) T Pt[C * LDP];   // P
   __shared__ __align__(16) T Dt[C * LDP];   // dP (.) M
-  __shared__ __align__(16) T SFs[DH * LDR];  // SF, then HF
-  __shared__ __align__(16) T SBs[DH * LDR];  // SB, then HB
+  __shared__ __align__(16) T SFs[DH * LDR];  // SF, then HF: [n][a]
+  __shared__ __align__(16) T SBs[DH * LDR];  // SB, then HB: [n][a]
   __shared__ float xF[DH], xB[DH];          // extra columns of the staged states
   __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C];
   __shared__ float colpart[4][C];
@@ -182,8 +199,8 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
              frag_kmajor<T>(Ks, LDR, 32 * s + 8 * grp, 16 * nt, lane));
 #pragma unroll
       for (int s = 0; s < DH / 32; ++s) {
-        mma8(fw, ag[s], frag_load(SFs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
-        mma8(bw, ag[s], frag_load(SBs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(fw, ag[s], frag_kmajor<T>(SFs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(bw, ag[s], frag_kmajor<T>(SBs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
       }
       const float zf = xF[16 * nt + col], zb = xB[16 * nt + col];
 #pragma unroll
@@ -255,10 +272,10 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
       }
 #pragma unroll
       for (int s = 0; s < DH / 32; ++s) {
-        mma8(fk, av[s], frag_load(SFs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
-        mma8(bk, av[s], frag_load(SBs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
-        mma8(fv, ak[s], frag_kmajor<T>(SFs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
-        mma8(bv, ak[s], frag_kmajor<T>(SBs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(fk, av[s], frag_kmajor<T>(SFs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(bk, av[s], frag_kmajor<T>(SBs, LDR, 32 * s + 8 * grp, 16 * nt, lane));
+        mma8(fv, ak[s], frag_load(SFs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+        mma8(bv, ak[s], frag_load(SBs + (16 * nt + col) * LDR + 32 * s + 8 * grp));
       }
       const float hf = xF[16 * nt + col], hb = xB[16 * nt + col];
 #pragma unroll
@@ -345,61 +362,78 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
 }
 
 // ---------------------------------------------------------------- decay gradient
-// Block = (sequence, head). dlog lambda_t = dA_loc[t] + (dA of all later chunks),
-// da_t = dlog lambda_t (1 - lambda_t) -> G column 3 D + h; the block's sum of
-// da (fixed order) -> db_part[b][h]. Blocks of head 0 also clear the G padding.
-template <typename T>
-__global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl, const float* __restrict__ dA_loc,
-                                                 float* __restrict__ dA_tot, const int* __restrict__ nchunks,
-                                                 const int* __restrict__ chunk_off, const Chunk* __restrict__ tab,
-                                                 int N, int H, int D, int Kp, T* __restrict__ G,
-                                                 float* __restrict__ db_part) {
-  __shared__ float wsum[4];
-  const int b = blockIdx.x / H, h = blockIdx.x - b * H;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+// dlog lambda_t = dA_loc[t] (the suffix inside t's chunk) + the dA of all later
+// chunks of t's sequence; da_t = dlog lambda_t (1 - lambda_t) goes to G column
+// 3 D + h. Two launches:
+//   k_lion_dsuffix  one wave per (sequence, head): chunk totals -> exclusive
+//                   suffix sums over the sequence's chunks, in place
+//   k_lion_da       one block per chunk: da for every token and head, the zero
+//                   padding of G, and the chunk's per-head sum of da (db partial)
+__global__ __launch_bounds__(256) void k_lion_dsuffix(float* __restrict__ dA_tot, const int* __restrict__ nchunks,
+                                                      const int* __restrict__ chunk_off, int N, int H) {
+  const int lane = threadIdx.x & 63;
+  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (bh >= N * H) return;
+  const int b = bh / H, h = bh - b * H;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
-  if (tid == 0) {  // exclusive suffix sums over the chunks, in place (from the last chunk)
-    float acc = 0.f;
-    for (int c = c1 - 1; c >= c0; --c) {
-      float* p = dA_tot + (size_t)c * H + h;
-      const float v = *p;
-      *p = acc;
-      acc += v;
+  float carry = 0.f;
+  for (int top = c1; top > c0; top -= 64) {  // lane l takes chunk top - 1 - l
+    const int c = top - 1 - lane;
+    const bool ok = c >= c0;
+    const float v = ok ? dA_tot[(size_t)c * H + h] : 0.f;
+    float inc = v;  // inclusive sum over lanes <= l = chunks c .. top - 1
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float o = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += o;
     }
+    if (ok) dA_tot[(size_t)c * H + h] = carry + inc - v;
+    carry += __shfl(inc, 63, 64);
   }
-  __syncthreads();
-  float sum = 0.f;
-  const int gpad = 3 * D + H;
-  for (int c = c0; c < c1; ++c) {
-    const Chunk ch = tab[c];
-    const float carry = dA_tot[(size_t)c * H + h];
-    for (int t = ch.start + tid; t < ch.end; t += 256) {
-      const float ll = logl[(size_t)t * H + h];
-      const float da = (dA_loc[(size_t)t * H + h] + carry) * -expm1f(ll);
-      G[(size_t)t * Kp + 3 * D + h] = from_f<T>(da);
-      sum += da;
-      if (h == 0)
-        for (int cc = gpad; cc < Kp; ++cc) G[(size_t)t * Kp + cc] = from_f<T>(0.f);
-    }
-  }
-  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (lane == 0) wsum[w] = sum;
-  __syncthreads();
-  if (tid == 0) db_part[(size_t)b * H + h] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
 }
 
-void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks,
-                    const int* chunk_off, const Chunk* tab, int N, int T, int H, int D, int Kp, int dt, void* G,
-                    float* db_part, hipStream_t s) {
-  (void)T;
-  float* tot = const_cast<float*>(dA_tot);
+template <typename T>
+__global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl, const float* __restrict__ dA_loc,
+                                                 const float* __restrict__ dA_tot, const int* __restrict__ nchunks,
+                                                 const Chunk* __restrict__ tab, int H, int D, int Kp,
+                                                 T* __restrict__ G, float* __restrict__ db_part) {
+  constexpr int C = kLionChunk;
+  const int slot = blockIdx.x;
+  if (slot >= *nchunks) return;
+  const Chunk ch = tab[slot];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = ch.start + lane;
+  const bool ok = t < ch.end;
+  for (int h = w; h < H; h += 4) {  // lane = token of the chunk
+    float da = 0.f;
+    if (ok) {
+      const float ll = logl[(size_t)t * H + h];
+      da = (dA_loc[(size_t)t * H + h] + dA_tot[(size_t)slot * H + h]) * -expm1f(ll);
+      G[(size_t)t * Kp + 3 * D + h] = from_f<T>(da);
+    }
+    float sum = da;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) db_part[(size_t)slot * H + h] = sum;
+  }
+  const int g0 = 3 * D + H, P = Kp - g0;  // zero padding of G
+  for (int e = tid; e < C * P; e += 256) {
+    const int r = e / P, c = g0 + e % P;
+    if (ch.start + r < ch.end) G[(size_t)(ch.start + r) * Kp + c] = from_f<T>(0.f);
+  }
+}
+
+void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
+                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, void* G, float* db_part,
+                    hipStream_t s) {
+  hipLaunchKernelGGL(k_lion_dsuffix, dim3((N * H + 3) / 4), dim3(256), 0, s, dA_tot, nchunks, chunk_off, N, H);
   if (dt == BF16)
-    hipLaunchKernelGGL(k_lion_da<bf16>, dim3(N * H), dim3(256), 0, s, logl, dA_loc, tot, nchunks, chunk_off, tab, N,
-                       H, D, Kp, (bf16*)G, db_part);
+    hipLaunchKernelGGL(k_lion_da<bf16>, dim3(max_slots), dim3(256), 0, s, logl, dA_loc, dA_tot, nchunks, tab, H, D,
+                       Kp, (bf16*)G, db_part);
   else
-    hipLaunchKernelGGL(k_lion_da<float>, dim3(N * H), dim3(256), 0, s, logl, dA_loc, tot, nchunks, chunk_off, tab, N,
-                       H, D, Kp, (float*)G, db_part);
+    hipLaunchKernelGGL(k_lion_da<float>, dim3(max_slots), dim3(256), 0, s, logl, dA_loc, dA_tot, nchunks, tab, H, D,
+                       Kp, (float*)G, db_part);
 }
 
 }  // namespace gbla

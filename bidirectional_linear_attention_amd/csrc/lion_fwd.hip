@@ -33,7 +33,8 @@ namespace gbla {
 // MODE 0 (forward):  rows R = phi(k) [dh], columns V = [v | 1 | 0..]       (NC = dh + 16)
 // MODE 1 (backward): rows R = phi(q) [dh], columns V = g^ = [dy / r | -(dy . y) / r | 0..]
 // out[slot][h][0][E] = U = sum_j exp(L - A~_j) R_j V_j^T,  out[..][1][E] = W = sum_j exp(A~_j) R_j V_j^T,
-// laid out as [dh x dh] followed by the extra column (index dh) as a dh-vector.
+// each stored transposed: E = (dh + 1) rows n of dh values a, element [n][a] = (R^T V)[a][n];
+// row dh is the extra column (index dh of V).
 template <typename T, int DH, int MODE>
 __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ rsrc, const T* __restrict__ vsrc,
                                                           const T* __restrict__ ysrc, const float* __restrict__ rsum,
@@ -127,6 +128,8 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
       mma8(accW[u], frag_from<T>(aw), b);
     }
   }
+  // states are stored transposed, [n][a] (n = column feature, row n = dh is the
+  // extra column): this lane's 4 rows a of column n are contiguous
   float* o = out + ((size_t)slot * H + h) * 2 * E;
   const int col = lane & 15;
 #pragma unroll
@@ -134,16 +137,11 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
     const int tile = w + 4 * u;
     if (tile >= TILES) continue;
     const int ib = tile / NB, nb = tile - ib * NB;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * ib + 4 * grp + r;
-      if (nb < FB) {
-        o[i * DH + 16 * nb + col] = accU[u][r];
-        o[E + i * DH + 16 * nb + col] = accW[u][r];
-      } else if (col == 0) {
-        o[DH * DH + i] = accU[u][r];
-        o[E + DH * DH + i] = accW[u][r];
-      }
+    const int n = nb < FB ? 16 * nb + col : DH;
+    if (nb < FB || col == 0) {
+      float* p = o + n * DH + 16 * ib + 4 * grp;
+      *reinterpret_cast<float4*>(p) = make_float4(accU[u][0], accU[u][1], accU[u][2], accU[u][3]);
+      *reinterpret_cast<float4*>(p + E) = make_float4(accW[u][0], accW[u][1], accW[u][2], accW[u][3]);
     }
   }
   if (MODE == 0 && lam_out && tid == 0) lam_out[(size_t)slot * H + h] = Ls;
@@ -169,28 +167,57 @@ void launch_lion_chunk_state(int dt, int dh, int mode, const void* rsrc, const v
 // ---------------------------------------------------------------- scan over chunks
 // For every (sequence, head, element e): replace U_c by SF_c (the state that
 // enters chunk c from the left) and W_c by SB_c (from the right), in chunk order.
+// The loads of kScanBatch chunks are issued together before the carry walks
+// over them, so the walk pays one memory latency per batch.
+constexpr int kScanBatch = 16;
+
 __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const float* __restrict__ lam,
                                                    const int* __restrict__ nchunks, const int* __restrict__ chunk_off,
                                                    int N, int H, int E) {
+  constexpr int B = kScanBatch;
   const int eblocks = (E + 255) / 256;
   const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
   const int e = (blockIdx.x - bh * eblocks) * 256 + threadIdx.x;
   if (b >= N || e >= E) return;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
+  const size_t cs = (size_t)H * 2 * E;  // stride between consecutive chunks
+  float* base = st + (size_t)h * 2 * E + e;
   float sf = 0.f;
-  for (int c = c0; c < c1; ++c) {
-    float* p = st + ((size_t)c * H + h) * 2 * E + e;
-    const float u = *p;
-    *p = sf;
-    sf = __expf(lam[(size_t)c * H + h]) * sf + u;
+  for (int cb = c0; cb < c1; cb += B) {
+    float u[B], g[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int c = cb + j;
+      u[j] = c < c1 ? base[(size_t)c * cs] : 0.f;
+      g[j] = c < c1 ? lam[(size_t)c * H + h] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int c = cb + j;
+      if (c < c1) {
+        base[(size_t)c * cs] = sf;
+        sf = __expf(g[j]) * sf + u[j];
+      }
+    }
   }
   float sb = 0.f;
-  for (int c = c1 - 1; c >= c0; --c) {
-    float* p = st + ((size_t)c * H + h) * 2 * E + E + e;
-    const float w = *p;
-    *p = sb;
-    sb = __expf(lam[(size_t)c * H + h]) * sb + w;
+  for (int cb = c1 - 1; cb >= c0; cb -= B) {
+    float w[B], g[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int c = cb - j;
+      w[j] = c >= c0 ? base[(size_t)c * cs + E] : 0.f;
+      g[j] = c >= c0 ? lam[(size_t)c * H + h] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int c = cb - j;
+      if (c >= c0) {
+        base[(size_t)c * cs + E] = sb;
+        sb = __expf(g[j]) * sb + w[j];
+      }
+    }
   }
 }
 
@@ -201,7 +228,28 @@ void launch_lion_scan(float* st, const float* lam, const int* nchunks, const int
 }
 
 // ---------------------------------------------------------------- readout
-// Block = (chunk, head); wave w owns query rows 16 w .. 16 w + 15 of the chunk.
+// Block = (chunk, head), 4 waves.
+//  Phase 1: wave w forms rows 16 w .. 16 w + 15 of P = (q~ k~^T) (.) exp(-|A~_i - A~_j|)
+//           in LDS, with their row sums, and the dots q~_i . z of both carried
+//           states; together they give the denominators r_i.
+//  Phase 2: wave w produces output columns 16 ct .. 16 ct + 15 for its row tiles:
+//           P V plus e^{A~_i} q~_i^T SF + e^{L - A~_i} q~_i^T SB, over r_i. Its slice of
+//           SF and SB ([n][a] in HBM, n = 16 ct + lane % 16) is loaded straight into
+//           MFMA B fragments (split into high and low bf16 parts for bf16).
+
+// 8 floats -> high and low parts (bf16: ~16 mantissa bits together; float: exact, low = 0)
+__device__ __forceinline__ void split8(const float (&v)[8], Frag8<bf16>& hi, Frag8<bf16>& lo) {
+  float l[8];
+  hi = frag_from<bf16>(v);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) l[m] = v[m] - frag_get(hi, m);
+  lo = frag_from<bf16>(l);
+}
+__device__ __forceinline__ void split8(const float (&v)[8], Frag8<float>& hi, Frag8<float>& lo) {
+  hi = frag_from<float>(v);
+  lo = frag_zero<float>();
+}
+
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, const T* __restrict__ kr,
                                                       const T* __restrict__ vr, const float* __restrict__ logl,
@@ -209,19 +257,22 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
                                                       const Chunk* __restrict__ tab, int max_slots, int H,
                                                       T* __restrict__ y, float* __restrict__ rsum) {
   constexpr int C = kLionChunk;
-  constexpr int FB = DH / 16, NB = FB + 1, NR = DH + 16;
+  constexpr int FB = DH / 16;    // 16-wide column tiles of the output
+  constexpr int WPC = 4 / FB;    // waves per column tile
+  constexpr int RTW = 4 / WPC;   // row tiles per wave in phase 2
+  constexpr int KS = DH / 32;    // 32-wide k steps over the features
   constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LDR = DH + PAD, LDC = 16 * NB + PAD, LDP = C + PAD;
+  constexpr int LDR = DH + PAD, LDP = C + PAD;
   constexpr int P2 = sizeof(T) == 2 ? 2 : 1;
   constexpr int E = DH * DH + DH;
   constexpr int V8 = DH / 8, NV = (C * V8 + 255) / 256;
+  static_assert(FB * WPC == 4 && RTW * WPC == 4, "4 waves cover the 4 x FB output tiles");
   __shared__ __align__(16) T Qs[C * LDR];
-  __shared__ __align__(16) T Ks[C * LDR];
-  __shared__ __align__(16) T Vs[C * LDC];
-  __shared__ __align__(16) T Ps[4 * 16 * LDP];
-  __shared__ __align__(16) T SF[P2 * NR * LDR];
-  __shared__ __align__(16) T SB[P2 * NR * LDR];
-  __shared__ float As[C];
+  __shared__ __align__(16) T Ks[C * LDR];  // phi(k); y on output
+  __shared__ __align__(16) T Vs[C * LDR];
+  __shared__ __align__(16) T Ps[C * LDP];
+  __shared__ __align__(16) float zS[2][DH];
+  __shared__ float As[C], rowsum[C], zpart[C];
   __shared__ float Ls;
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
@@ -230,15 +281,24 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
   const Chunk ch = tab[slot];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
+  const int ct = w / WPC, rt0 = (w % WPC) * RTW;
 
-  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
+  // this wave's slice of the carried states: column n = 16 ct + col, rows a = 32 s + 8 grp .. + 7
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
-  stage_state<T, DH, NR>(SF, nullptr, LDR, sp, sp + DH * DH, tid, 256);
-  stage_state<T, DH, NR>(SB, nullptr, LDR, sp + E, sp + E + DH * DH, tid, 256);
-  for (int e = tid; e < C * 16; e += 256) {
-    const int r = e >> 4, c = e & 15;
-    Vs[r * LDC + DH + c] = from_f<T>(c == 0 && ch.start + r < ch.end ? 1.f : 0.f);
+  float4 sv[2][KS][2];
+#pragma unroll
+  for (int dir = 0; dir < 2; ++dir)
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const float4* p = reinterpret_cast<const float4*>(sp + dir * E + (16 * ct + col) * DH + 32 * s + 8 * grp);
+      sv[dir][s][0] = p[0];
+      sv[dir][s][1] = p[1];
+    }
+  if (tid < DH / 2) {  // the extra rows (z) of both states
+    const int dir = tid / (DH / 4), e4 = tid % (DH / 4);
+    reinterpret_cast<float4*>(zS[dir])[e4] = reinterpret_cast<const float4*>(sp + dir * E + DH * DH)[e4];
   }
+  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = tid + 256 * v;
@@ -257,71 +317,114 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
     for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
     phi_lion8<V8>(u, p, ok);
     frag_store(Ks + r * LDR + c, frag_from<T>(p));
-    frag_store(Vs + r * LDC + c, ok ? frag_load(vr + o) : frag_zero<T>());
+    frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
   }
   __syncthreads();
+  const float L = Ls;
 
-  const int r0 = 16 * w;
-  Frag8<T> aq[DH / 32];
+  // ---------------- phase 1: rows r0 .. r0 + 15 of P, row sums, q~ . z
+  {
+    const int r0 = 16 * w;
+    Frag8<T> aq[KS];
 #pragma unroll
-  for (int s = 0; s < DH / 32; ++s) aq[s] = frag_load(Qs + (r0 + col) * LDR + 32 * s + 8 * grp);
-  // intra-chunk similarities, masked by the decay: P = (q~ k~^T) (.) exp(-|A~_i - A~_j|)
-  T* Pw = Ps + w * 16 * LDP;
+    for (int s = 0; s < KS; ++s) aq[s] = frag_load(Qs + (r0 + col) * LDR + 32 * s + 8 * grp);
+    float zf = 0.f, zb = 0.f;  // partial dots of row r0 + col with the two z rows
 #pragma unroll
-  for (int nt = 0; nt < C / 16; ++nt) {
-    f32x4 g = zero4();
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s) mma8(g, aq[s], frag_load(Ks + (16 * nt + col) * LDR + 32 * s + 8 * grp));
-    const int j = 16 * nt + col;
+      for (int m = 0; m < 8; ++m) {
+        const float q = frag_get(aq[s], m);
+        zf += q * zS[0][32 * s + 8 * grp + m];
+        zb += q * zS[1][32 * s + 8 * grp + m];
+      }
+    zf += __shfl_xor(zf, 16, 64);
+    zf += __shfl_xor(zf, 32, 64);
+    zb += __shfl_xor(zb, 16, 64);
+    zb += __shfl_xor(zb, 32, 64);
+    if (grp == 0) {
+      const float a = As[r0 + col];
+      zpart[r0 + col] = __expf(a) * zf + __expf(L - a) * zb;
+    }
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nt = 0; nt < C / 16; ++nt) {
+      f32x4 g = zero4();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) mma8(g, aq[s], frag_load(Ks + (16 * nt + col) * LDR + 32 * s + 8 * grp));
+      const int j = 16 * nt + col;
+      const float aj = As[j];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 4 * grp + r;
+        const T pv = from_f<T>(g[r] * __expf(-fabsf(As[i] - aj)));
+        Ps[i * LDP + j] = pv;
+        rs[r] += to_f<T>(pv);  // the denominator sums the same rounded weights the numerator uses
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = r0 + 4 * grp + r;
-      Pw[(4 * grp + r) * LDP + j] = from_f<T>(g[r] * __expf(-fabsf(As[i] - As[j])));
+      rs[r] = row16_sum(rs[r]);
+      if (col == 0) rowsum[r0 + 4 * grp + r] = rs[r];
     }
   }
   __syncthreads();
-  f32x4 num[NB], fw[NB], bw[NB];
+  if (tid < C && ch.start + tid < ch.end) rsum[(size_t)(ch.start + tid) * H + h] = rowsum[tid] + zpart[tid];
+
+  // ---------------- phase 2: columns 16 ct .. 16 ct + 15, row tiles rt0 .. rt0 + RTW - 1
+  Frag8<T> bF[P2][KS], bB[P2][KS], vb[C / 32];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    num[nb] = fw[nb] = bw[nb] = zero4();
+  for (int s = 0; s < KS; ++s) {
+    float f[8], b[8];
+    f[0] = sv[0][s][0].x; f[1] = sv[0][s][0].y; f[2] = sv[0][s][0].z; f[3] = sv[0][s][0].w;
+    f[4] = sv[0][s][1].x; f[5] = sv[0][s][1].y; f[6] = sv[0][s][1].z; f[7] = sv[0][s][1].w;
+    b[0] = sv[1][s][0].x; b[1] = sv[1][s][0].y; b[2] = sv[1][s][0].z; b[3] = sv[1][s][0].w;
+    b[4] = sv[1][s][1].x; b[5] = sv[1][s][1].y; b[6] = sv[1][s][1].z; b[7] = sv[1][s][1].w;
+    Frag8<T> hi, lo;
+    split8(f, hi, lo);
+    bF[0][s] = hi;
+    if (P2 == 2) bF[P2 - 1][s] = lo;
+    split8(b, hi, lo);
+    bB[0][s] = hi;
+    if (P2 == 2) bB[P2 - 1][s] = lo;
+  }
 #pragma unroll
-    for (int s = 0; s < C / 32; ++s)
-      mma8(num[nb], frag_load(Pw + col * LDP + 32 * s + 8 * grp), frag_kmajor<T>(Vs, LDC, 32 * s + 8 * grp, 16 * nb, lane));
+  for (int s = 0; s < C / 32; ++s) vb[s] = frag_kmajor<T>(Vs, LDR, 32 * s + 8 * grp, 16 * ct, lane);
+  float yv[RTW][4];
 #pragma unroll
-    for (int p = 0; p < P2; ++p)
+  for (int q = 0; q < RTW; ++q) {
+    const int rt = rt0 + q;
+    f32x4 in = zero4(), fw = zero4(), bw = zero4();
 #pragma unroll
-      for (int s = 0; s < DH / 32; ++s) {
-        mma8(fw[nb], aq[s], frag_load(SF + p * NR * LDR + (16 * nb + col) * LDR + 32 * s + 8 * grp));
-        mma8(bw[nb], aq[s], frag_load(SB + p * NR * LDR + (16 * nb + col) * LDR + 32 * s + 8 * grp));
+    for (int s = 0; s < C / 32; ++s) mma8(in, frag_load(Ps + (16 * rt + col) * LDP + 32 * s + 8 * grp), vb[s]);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const Frag8<T> a = frag_load(Qs + (16 * rt + col) * LDR + 32 * s + 8 * grp);
+#pragma unroll
+      for (int p = 0; p < P2; ++p) {
+        mma8(fw, a, bF[p][s]);
+        mma8(bw, a, bB[p][s]);
       }
-  }
-  const float L = Ls;
-  float ef[4], eb[4];
+    }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float a = As[r0 + 4 * grp + r];
-    ef[r] = __expf(a);
-    eb[r] = __expf(L - a);
+    for (int r = 0; r < 4; ++r) {
+      const int i = 16 * rt + 4 * grp + r;
+      const float a = As[i];
+      const float den = rowsum[i] + zpart[i];
+      yv[q][r] = ch.start + i < ch.end ? (in[r] + __expf(a) * fw[r] + __expf(L - a) * bw[r]) / den : 0.f;
+    }
   }
-  __syncthreads();  // every wave is done with Qs (A operands above); reuse its rows for y
+  // Ks is free since phase 1 (every wave passed the barrier after its last read)
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = r0 + 4 * grp + r;
-    const float den = col0_bcast(num[FB][r] + ef[r] * fw[FB][r] + eb[r] * bw[FB][r], lane);
-    const bool ok = ch.start + i < ch.end;
-    const float inv = ok ? 1.f / den : 0.f;
+  for (int q = 0; q < RTW; ++q)
 #pragma unroll
-    for (int nb = 0; nb < FB; ++nb)
-      Qs[i * LDR + 16 * nb + col] = from_f<T>((num[nb][r] + ef[r] * fw[nb][r] + eb[r] * bw[nb][r]) * inv);
-    if (ok && col == 0) rsum[(size_t)(ch.start + i) * H + h] = den;
-  }
+    for (int r = 0; r < 4; ++r) Ks[(16 * (rt0 + q) + 4 * grp + r) * LDR + 16 * ct + col] = from_f<T>(yv[q][r]);
   __syncthreads();
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = tid + 256 * v;
     if (it >= C * V8) continue;
     const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
-    if (t < ch.end) frag_store(y + (size_t)t * D + h * DH + c, frag_load(Qs + r * LDR + c));
+    if (t < ch.end) frag_store(y + (size_t)t * D + h * DH + c, frag_load(Ks + r * LDR + c));
   }
 }
 

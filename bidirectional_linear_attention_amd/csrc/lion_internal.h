@@ -62,8 +62,10 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
                            const void* y, const void* dy, const float* rsum, const float* st, const float* hst,
                            const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G,
                            float* dA_loc, float* dA_tot, hipStream_t s);
-void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks,
-                    const int* chunk_off, const Chunk* tab, int N, int T, int H, int D, int Kp, int dt, void* G,
-                    float* db_part, hipStream_t s);
+// da into G (and its zero padding) and per-chunk partial sums of da [slot][H]
+// (sum them over the first *nchunks slots); dA_tot is overwritten
+void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
+                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, void* G, float* db_part,
+                    hipStream_t s);
 
 }  // namespace gbla
