@@ -24,13 +24,21 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays NaN)
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
+typedef float f32x2_v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// float -> bfloat16, round to nearest even (the gfx950 conversion instruction)
+__device__ __forceinline__ bf16 f2bf(float f) { return __builtin_bit_cast(bf16, (__bf16)f); }
+// two floats -> a packed bfloat16 pair, a in the low half (one instruction)
+__device__ __forceinline__ uint32_t f2bf2(float a, float b) {
+  const f32x2_v v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
 }
+
+// hardware reciprocal and reciprocal square root (about 1 ulp): used where a
+// result is normalised or squashed, never where a value is accumulated
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsqrt(float x) { return __builtin_amdgcn_rsqf(x); }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
@@ -88,10 +96,7 @@ template <> __device__ __forceinline__ Frag8<float> frag_from<float>(const float
 }
 template <> __device__ __forceinline__ Frag8<bf16> frag_from<bf16>(const float* v) {
   Frag8<bf16> f;
-  f.v.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-  f.v.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-  f.v.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
-  f.v.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  f.v = make_uint4(f2bf2(v[0], v[1]), f2bf2(v[2], v[3]), f2bf2(v[4], v[5]), f2bf2(v[6], v[7]));
   return f;
 }
 
@@ -115,10 +120,10 @@ __device__ __forceinline__ void mma8(f32x4& acc, const Frag8<float>& a, const Fr
 // (rounded to T first). Used with C-reuse operands: k = 4 * (lane / 16) + j.
 template <typename T> __device__ __forceinline__ void mma4(f32x4& acc, const float* a, const float* b);
 template <> __device__ __forceinline__ void mma4<bf16>(f32x4& acc, const float* a, const float* b) {
-  s16x4_v av, bv;
-  av[0] = (short)f2bf(a[0]); av[1] = (short)f2bf(a[1]); av[2] = (short)f2bf(a[2]); av[3] = (short)f2bf(a[3]);
-  bv[0] = (short)f2bf(b[0]); bv[1] = (short)f2bf(b[1]); bv[2] = (short)f2bf(b[2]); bv[3] = (short)f2bf(b[3]);
-  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, acc, 0, 0, 0);
+  const uint2 ap = make_uint2(f2bf2(a[0], a[1]), f2bf2(a[2], a[3]));
+  const uint2 bp = make_uint2(f2bf2(b[0], b[1]), f2bf2(b[2], b[3]));
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, ap), __builtin_bit_cast(s16x4_v, bp),
+                                                  acc, 0, 0, 0);
 }
 template <> __device__ __forceinline__ void mma4<float>(f32x4& acc, const float* a, const float* b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], acc, 0, 0, 0);
@@ -167,7 +172,7 @@ template <> __device__ __forceinline__ Frag8<float> frag_kmajor<float>(const flo
 }
 
 // ---------------------------------------------------------------- small helpers
-__device__ __forceinline__ float sigmoidf_(float s) { return 1.f / (1.f + __expf(-s)); }
+__device__ __forceinline__ float sigmoidf_(float s) { return fast_rcp(1.f + __expf(-s)); }
 // phi(u) = elu(u) + 1
 __device__ __forceinline__ float phi_elu1(float u) { return u > 0.f ? u + 1.f : __expf(u); }
 

@@ -142,7 +142,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       const int row = r0 + 4 * grp + r;
       const bool ok = tb + row < ch.end;
       const float den = col0_bcast(acc[FB][r], lane);
-      const float inv = ok ? 1.f / den : 0.f;
+      const float inv = ok ? fast_rcp(den) : 0.f;
       float p = 0.f, dyv[FB];
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {

@@ -564,7 +564,7 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float den = col0_bcast(acc[FB][r], lane);
-      const float inv = tb + r0 + 4 * grp + r < ch.end ? 1.f / den : 0.f;
+      const float inv = tb + r0 + 4 * grp + r < ch.end ? fast_rcp(den) : 0.f;
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) qs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(acc[nt][r] * inv);
     }

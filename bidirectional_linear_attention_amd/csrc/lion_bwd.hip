@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
     frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
     const Frag8<T> fd = ok ? frag_load(dy + o) : frag_zero<T>();
     const Frag8<T> fy = ok ? frag_load(yv + o) : frag_zero<T>();
-    const float inv = ok ? 1.f / rsum[(size_t)t * H + h] : 0.f;
+    const float inv = ok ? fast_rcp(rsum[(size_t)t * H + h]) : 0.f;
     float g[8], dd = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
       const int i = r0 + 4 * grp + r;
       const int t = ch.start + i;
       const bool ok = t < ch.end;
-      const float inv_n = 1.f / nq[i];
+      const float inv_n = fast_rcp(nq[i]);
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {
         const float u = ok ? to_f<T>(qr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
       const int j = r0 + 4 * grp + r;
       const int t = ch.start + j;
       const bool ok = t < ch.end;
-      const float inv_n = 1.f / nk[j];
+      const float inv_n = fast_rcp(nk[j]);
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {
         const float u = ok ? to_f<T>(kr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
     } else {  // g^ from dy (vsrc), y (ysrc) and the row sum r
       const Frag8<T> fd = ok ? frag_load(vsrc + o) : frag_zero<T>();
       const Frag8<T> fy = ok ? frag_load(ysrc + o) : frag_zero<T>();
-      const float inv = ok ? 1.f / rsum[(size_t)t * H + h] : 0.f;
+      const float inv = ok ? fast_rcp(rsum[(size_t)t * H + h]) : 0.f;
       float g[8], dd = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -410,7 +410,7 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
       const int i = 16 * rt + 4 * grp + r;
       const float a = As[i];
       const float den = rowsum[i] + zpart[i];
-      yv[q][r] = ch.start + i < ch.end ? (in[r] + __expf(a) * fw[r] + __expf(L - a) * bw[r]) / den : 0.f;
+      yv[q][r] = ch.start + i < ch.end ? (in[r] + __expf(a) * fw[r] + __expf(L - a) * bw[r]) * fast_rcp(den) : 0.f;
     }
   }
   // Ks is free since phase 1 (every wave passed the barrier after its last read)

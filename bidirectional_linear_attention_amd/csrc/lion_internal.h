@@ -23,8 +23,9 @@ __device__ __forceinline__ float phi_lion8(const float (&u)[8], float (&out)[8],
   }
 #pragma unroll
   for (int m = 1; m < V8; m <<= 1) ss += __shfl_xor(ss, m, 64);
-  const float n = sqrtf(ss);
-  const float inv = valid ? 1.f / n : 0.f;
+  const float rn = fast_rsqrt(ss);  // ss > 0: SiLU(u) + 0.5 >= 0.22 for every u
+  const float n = ss * rn;
+  const float inv = valid ? rn : 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) out[j] = f[j] * inv;
   return n;
