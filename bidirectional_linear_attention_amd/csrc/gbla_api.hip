@@ -31,10 +31,7 @@ Dims dims_of(const gbla_problem* p) {
   m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.NP = proj_cols(m.dh); m.Kp = grad_cols(m.H, m.dh);
   m.slots = max_chunks(m.T, m.N);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
-  const int tiles = dw_tiles(dt, m.d, m.Kp);
-  int ns = (256 + tiles - 1) / tiles;                     // about one dW block per CU
-  ns = std::min(ns, std::max(1, (m.T + 1023) / 1024));   // at least 1024 tokens per split
-  m.nsplit = std::max(1, std::min(ns, 64));
+  m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
   m.conv_rb = conv_bwd_row_blocks(m.T);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
   return m;

@@ -19,6 +19,8 @@
 //   k_gemm_dw     split-token partials of X~^T G (pipelined MFMA), then k_dw_reduce
 //   k_conv_bwd    dx and per-block partial dconv_w (summed by k_sum_parts)
 #include "gemm.h"
+#include <algorithm>
+
 #include "internal.h"
 
 namespace gbla {
@@ -393,29 +395,36 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
 
 // ============================================================== dX~ = G Wt^T
 // C[M=T][N=d] = G[T][Kp] Wt[d][Kp]^T, fp32 output; 256 x 256 tiles, 8 waves.
-template <typename T> struct DxCfg { using S = GemmShape<T, 256, 256, 32, 4, 2>; };
-template <> struct DxCfg<float> { using S = GemmShape<float, 64, 128, 32, 2, 2>; };
+template <typename T> struct DxCfg;
+template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; };
+template <> struct DxCfg<float> { using S = GemmShape<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; };
 
 template <typename T>
 __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
                                                                      const T* __restrict__ wt, int T_, int d, int Kp,
                                                                      T* __restrict__ dxt) {
   using S = typename DxCfg<T>::S;
-  __shared__ __align__(16) T smem[2 * S::STAGE];
+  constexpr bool DL = DxCfg<T>::DL;
+  __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
+  __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
   const int mtiles = (T_ + S::BM - 1) / S::BM, ntiles = (d + S::BN - 1) / S::BN;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * ntiles);
   if (lid >= mtiles * ntiles) return;
   const int mt = lid / ntiles, nt = lid - mt * ntiles;
   const int m0 = mt * S::BM, n0 = nt * S::BN;
   f32x4 acc[S::FM][S::FN];
-  gemm_nt_mainloop<T, S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp, min(S::BN, d - n0),
-                         Kp, smem, acc);
+  if constexpr (DL)
+    gemm_nt_dl<S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp, min(S::BN, d - n0), Kp,
+                  smem, smem1, smem1, smem1, acc);
+  else
+    gemm_nt_mainloop<T, S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp,
+                           min(S::BN, d - n0), Kp, smem, acc);
   // epilogue staged per wave through LDS, 16 rows at a time, 16-byte row stores
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
   constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
   constexpr int RP = 16, VPR = S::WTN / 8;
-  static_assert(S::NWAVES * RP * LDO <= 2 * S::STAGE, "epilogue staging must fit the main-loop LDS");
+  static_assert(S::NWAVES * RP * LDO <= S::STAGE, "epilogue staging must fit the main-loop LDS");
   T* ws = smem + w * RP * LDO;
 #pragma unroll
   for (int i = 0; i < S::FM; ++i) {
@@ -451,8 +460,9 @@ void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp,
 // ============================================================== dW = X~^T G (split over tokens)
 // part[ks][m][n] = sum over the tokens of split ks of X~[t][m] G[t][n]; both
 // operands are token-major and are transposed while staged in LDS.
-template <typename T> struct DwCfg { using S = GemmShapeTN<T, 256, 256, 32, 4, 2>; };
-template <> struct DwCfg<float> { using S = GemmShapeTN<float, 64, 128, 32, 2, 2>; };
+template <typename T> struct DwCfg;
+template <> struct DwCfg<bf16> { using S = DlShapeTN<128, 128, 64, 2, 2, 2>; static constexpr bool DL = true; };
+template <> struct DwCfg<float> { using S = GemmShapeTN<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; };
 
 int dw_tiles(int dt, int d, int Kp) {
   if (dt == BF16) {
@@ -463,12 +473,23 @@ int dw_tiles(int dt, int d, int Kp) {
   return ((d + S::BM - 1) / S::BM) * ((Kp + S::BN - 1) / S::BN);
 }
 
+// token splits of the dW GEMM: as many as fill two rounds of two resident
+// blocks on each of the 256 CUs, at least 1024 tokens per split, at most 64
+int dw_splits(int dt, int d, int Kp, int T) {
+  const int tiles = dw_tiles(dt, d, Kp);
+  int ns = std::max(1, 1024 / tiles);
+  ns = std::min(ns, std::max(1, (T + 1023) / 1024));
+  return std::max(1, std::min(ns, 64));
+}
+
 template <typename T>
 __global__ __launch_bounds__((DwCfg<T>::S::NTHREADS)) void k_gemm_dw(const T* __restrict__ xt, const T* __restrict__ G,
                                                                    int T_, int d, int Kp, int tok_per_split,
                                                                    int nsplit, float* __restrict__ part) {
   using S = typename DwCfg<T>::S;
-  __shared__ __align__(16) T smem[2 * S::STAGE];
+  constexpr bool DL = DwCfg<T>::DL;
+  __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
+  __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
   const int mtiles = (d + S::BM - 1) / S::BM, ntiles = (Kp + S::BN - 1) / S::BN;
   const int total = mtiles * ntiles * nsplit;
   const int lid = xcd_logical_block(blockIdx.x, total);
@@ -479,7 +500,11 @@ __global__ __launch_bounds__((DwCfg<T>::S::NTHREADS)) void k_gemm_dw(const T* __
   const int m0 = mt * S::BM, n0 = nt * S::BN;
   const int tbeg = ks * tok_per_split, tend = min(T_, tbeg + tok_per_split);
   f32x4 acc[S::FM][S::FN];
-  gemm_tn_mainloop<T, S>(xt + m0, d, min(S::BM, d - m0), G + n0, Kp, min(S::BN, Kp - n0), tbeg, tend, smem, acc);
+  if constexpr (DL)
+    gemm_tn_dl<S>(xt + m0, d, min(S::BM, d - m0), G + n0, Kp, min(S::BN, Kp - n0), tbeg, tend, smem, smem1, smem1,
+                  smem1, acc);
+  else
+    gemm_tn_mainloop<T, S>(xt + m0, d, min(S::BM, d - m0), G + n0, Kp, min(S::BN, Kp - n0), tbeg, tend, smem, acc);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
   float* out = part + (size_t)ks * d * Kp;

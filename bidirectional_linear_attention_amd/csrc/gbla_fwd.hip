@@ -248,12 +248,15 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
 }
 
 // ============================================================== projection GEMM
-// Block = 256 tokens x one head's [Q | K | V] columns (3 dh), 8 waves (4 x 2).
+// Block = 256 tokens x one head's [Q | K | V] columns (3 dh). bf16 runs the
+// direct-to-LDS main loop, float the register-staged one.
 // Epilogue: phi on Q and K, identity on V.
-template <typename T, int DH> struct ProjCfg { using S = GemmShape<T, 256, 3 * DH, 32, 4, 2>; };
+template <typename T, int DH> struct ProjCfg;
+template <> struct ProjCfg<bf16, 64> { using S = DlShape<256, 192, 64, 4, 2, 2>; static constexpr bool DL = true; };
+template <> struct ProjCfg<bf16, 32> { using S = DlShape<256, 96, 64, 4, 1, 2>; static constexpr bool DL = true; };
 // float32 tiles stay within 64 KB of LDS
-template <> struct ProjCfg<float, 64> { using S = GemmShape<float, 32, 192, 32, 1, 4>; };
-template <> struct ProjCfg<float, 32> { using S = GemmShape<float, 64, 96, 32, 2, 2>; };
+template <> struct ProjCfg<float, 64> { using S = GemmShape<float, 32, 192, 32, 1, 4>; static constexpr bool DL = false; };
+template <> struct ProjCfg<float, 32> { using S = GemmShape<float, 64, 96, 32, 2, 2>; static constexpr bool DL = false; };
 
 // PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION-s)
 template <typename T, int DH, bool PHI = true>
@@ -262,15 +265,21 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
                                                                       T* __restrict__ q_out, T* __restrict__ k_out,
                                                                       T* __restrict__ v_out) {
   using S = typename ProjCfg<T, DH>::S;
-  __shared__ __align__(16) T smem[2 * S::STAGE];
+  constexpr bool DL = ProjCfg<T, DH>::DL;
+  __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
+  __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
   const int mtiles = (T_ + S::BM - 1) / S::BM;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * H);
   if (lid >= mtiles * H) return;
   const int mt = lid / H, h = lid - mt * H;
   const int m0 = mt * S::BM;
   f32x4 acc[S::FM][S::FN];
-  gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d, smem,
-                         acc);
+  if constexpr (DL)
+    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d, smem, smem1,
+                  smem1, smem1, acc);
+  else
+    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d,
+                           smem, acc);
   // epilogue: phi on Q and K, staged per wave through LDS (the main loop ended
   // with a barrier, so smem is free) and written as 16-byte row vectors
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
@@ -279,7 +288,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
   constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
   constexpr int RP = 16;                       // rows per pass
   constexpr int VPR = S::WTN / 8;              // 8-element vectors per row
-  static_assert(S::NWAVES * RP * LDO <= 2 * S::STAGE, "epilogue staging must fit the main-loop LDS");
+  static_assert(S::NWAVES * RP * LDO <= S::STAGE, "epilogue staging must fit the main-loop LDS");
   T* ws = smem + w * RP * LDO;
 #pragma unroll
   for (int i = 0; i < S::FM; ++i) {

@@ -221,4 +221,235 @@ __device__ __forceinline__ void gemm_tn_mainloop(const T* __restrict__ A, int ld
   }
 }
 
+// ---------------------------------------------------------------- NT main loop, direct-to-LDS (bf16)
+// Same contract as gemm_nt_mainloop for bf16, built for gfx950:
+//  * global -> LDS with buffer_load ... lds (16 bytes per lane, no register
+//    round trip); rows past ma / nb and k past K read as zero through the
+//    buffer range check (out-of-range lanes get an offset beyond the range);
+//  * LDS rows are unpadded (BK bf16) and the 16-byte chunks of row r are
+//    XOR-swizzled so that 16 lanes reading one chunk of 16 consecutive rows hit
+//    16 distinct 4-bank groups;
+//  * NS stages, one barrier per k chunk: wait for this wave's loads of chunk c,
+//    barrier (every wave's loads of chunk c are in LDS and every wave is done
+//    with chunk c - 1), issue the loads of chunk c + NS - 1 into the stage of
+//    chunk c - 1, multiply chunk c. (A second barrier per chunk, to issue
+//    before waiting, measured slower.)
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int NS_>
+struct DlShape {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, NS = NS_;
+  static constexpr int NWAVES = WGM * WGN, NTHREADS = NWAVES * 64;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
+  static constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
+  static constexpr int RPL = 64 / CPR;      // rows written by one 1 KB wave load
+  static constexpr int LA = BM / RPL, LB = BN / RPL;
+  static constexpr int LPW = (LA + LB) / NWAVES;  // wave loads per wave per chunk
+  static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
+  static_assert(BK == 32 || BK == 64, "16 or 8 rows per wave load");
+  static_assert(BM % RPL == 0 && BN % RPL == 0 && (LA + LB) % NWAVES == 0, "whole wave loads per wave");
+  static_assert(WTM % 16 == 0 && WTN % 16 == 0 && NS >= 2 && NS <= 4, "tile shape");
+  static_assert(LPW * (NS - 1) < 64, "vmcnt range");
+};
+
+// physical 16-byte chunk of logical chunk c in LDS row r (CPR chunks per row)
+template <int CPR>
+__device__ __forceinline__ int dl_swizzle(int r, int c) { return c ^ ((r / (16 / CPR)) % CPR); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations are outstanding
+__host__ __device__ constexpr int dl_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+typedef __attribute__((address_space(3))) void dl_lds_void;
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// st[s] are NS distinct LDS arrays of S::STAGE elements (distinct objects let the
+// compiler tell the stages apart when it orders LDS reads after LDS-DMA loads)
+template <class S>
+__device__ __forceinline__ void gemm_nt_dl(const bf16* __restrict__ A, int lda, int ma, const bf16* __restrict__ B,
+                                           int ldb, int nb, int K, bf16* st0, bf16* st1, bf16* st2, bf16* st3,
+                                           f32x4 (&acc)[S::FM][S::FN]) {
+  constexpr int CPR = S::CPR, RPL = S::RPL, NS = S::NS;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / S::WGN, wn = w % S::WGN;
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j) acc[i][j] = zero4();
+
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, ma > 0 ? (ma - 1) * lda * 2 + K * 2 : 0, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, nb > 0 ? (nb - 1) * ldb * 2 + K * 2 : 0, kBufferRsrcWord3);
+  const int rr = lane / CPR, pp = lane % CPR;  // this lane's row in a wave load and physical chunk
+  auto stage = [&](int s) -> bf16* { return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : st3)); };
+  auto issue = [&](int s, int k0) {
+    bf16* base = stage(s);
+#pragma unroll
+    for (int j = 0; j < S::LPW; ++j) {
+      const int li = w + S::NWAVES * j;  // wave-uniform
+      const bool isA = li < S::LA;
+      const int r = (isA ? li : li - S::LA) * RPL + rr;
+      const int c = dl_swizzle<CPR>(r, pp);
+      const int k = k0 + 8 * c;
+      const int ld = isA ? lda : ldb, rows = isA ? ma : nb;
+      const unsigned off = (r < rows && k < K) ? (unsigned)(r * ld + k) * 2u : 0x80000000u;
+      bf16* dst = base + (isA ? li * RPL * S::BK : S::BM * S::BK + (li - S::LA) * RPL * S::BK);
+      if (isA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dl_lds_void*)dst, 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (dl_lds_void*)dst, 16, off, 0, 0, 0);
+    }
+  };
+  auto compute = [&](const bf16* buf) {
+    const bf16* As = buf;
+    const bf16* Bs = buf + S::BM * S::BK;
+#pragma unroll
+    for (int ks = 0; ks < S::BK / 32; ++ks) {
+      Frag8<bf16> a[S::FM];
+#pragma unroll
+      for (int i = 0; i < S::FM; ++i) {
+        const int r = wm * S::WTM + 16 * i + col;
+        a[i] = frag_load(As + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
+      }
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j) {
+        const int r = wn * S::WTN + 16 * j + col;
+        const Frag8<bf16> b = frag_load(Bs + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) mma8(acc[i][j], a[i], b);
+      }
+    }
+  };
+
+  const int nk = (K + S::BK - 1) / S::BK;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)  // chunks 0 .. NS - 2 in flight before the loop
+    if (p < nk) issue(p, p * S::BK);
+  for (int c = 0; c < nk; ++c) {
+    if (c + NS - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(dl_vmcnt(S::LPW * (NS - 2)));  // this wave's loads of chunk c are done
+    else
+      __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
+    __syncthreads();  // every wave's loads of chunk c are in LDS and every wave is done with chunk c - 1
+    if (c + NS - 1 < nk) issue((c + NS - 1) % NS, (c + NS - 1) * S::BK);
+    compute(stage(c % NS));
+  }
+  __syncthreads();  // the stages may be reused by the caller
+}
+
+// ---------------------------------------------------------------- TN main loop, direct-to-LDS (bf16)
+// Same contract as gemm_tn_mainloop for bf16: A [K][lda] and B [K][ldb] are
+// k-major (token-major). LDS tiles keep that layout (row = k, BM or BN columns,
+// unpadded) and the MFMA operands are read with the transposing LDS read. A
+// transposing read fetches, per 16-lane group, 4 rows x 32 bytes; the 16-byte
+// chunk q of row r is stored at chunk q ^ 2 g(r), g(r) = (r & 3) | ((r >> 1) & 4),
+// so the 8 rows r and r + 8 read by two groups land in 16 distinct bank groups.
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_, int NS_>
+struct DlShapeTN {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_, NS = NS_;
+  static constexpr int NWAVES = WGM * WGN, NTHREADS = NWAVES * 64;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN, FM = WTM / 16, FN = WTN / 16;
+  static constexpr int CA = BM / 8, CB = BN / 8;          // 16-byte chunks per k row
+  static constexpr int LA = BK * CA / 64, LB = BK * CB / 64;  // 1 KB wave loads per stage
+  static constexpr int LPW = (LA + LB) / NWAVES;
+  static constexpr int STAGE = BK * (BM + BN);
+  static_assert(CA % 16 == 0 && CB % 16 == 0, "the swizzle permutes chunks within groups of 16");
+  static_assert((BK * CA) % 64 == 0 && (BK * CB) % 64 == 0 && (LA + LB) % NWAVES == 0, "whole wave loads");
+  static_assert(BK % 32 == 0 && WTM % 16 == 0 && WTN % 16 == 0 && NS >= 2 && NS <= 4, "tile shape");
+  static_assert(LPW * (NS - 1) < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ int dl_tn_swizzle(int r, int q) { return q ^ (2 * ((r & 3) | ((r >> 1) & 4))); }
+
+// k-major operand (8 consecutive k of column cb + lane % 16) from a swizzled tile of W columns
+template <int W>
+__device__ __forceinline__ Frag8<bf16> frag_kmajor_swz(const bf16* tile, int kb, int cb, int lane) {
+  const int j = lane & 15;
+  uint2 part[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = kb + 4 * h + (j >> 2), c = cb + 4 * (j & 3);
+    const bf16* p = tile + r * W + 8 * dl_tn_swizzle(r, c >> 3) + (c & 7);
+    part[h] = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_tr*)p));
+  }
+  Frag8<bf16> f;
+  f.v = make_uint4(part[0].x, part[0].y, part[1].x, part[1].y);
+  return f;
+}
+
+template <class S>
+__device__ __forceinline__ void gemm_tn_dl(const bf16* __restrict__ A, int lda, int ma, const bf16* __restrict__ B,
+                                           int ldb, int nb, int k_begin, int k_end, bf16* st0, bf16* st1, bf16* st2,
+                                           bf16* st3, f32x4 (&acc)[S::FM][S::FN]) {
+  constexpr int NS = S::NS;
+  const int lane = threadIdx.x & 63, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / S::WGN, wn = w % S::WGN;
+#pragma unroll
+  for (int i = 0; i < S::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j) acc[i][j] = zero4();
+  if (k_begin >= k_end) return;
+
+  // the ranges cover rows k_begin .. k_end - 1 of each operand, columns 0 .. ma (nb) - 1
+  const bf16* A0 = A + (size_t)k_begin * lda;
+  const bf16* B0 = B + (size_t)k_begin * ldb;
+  const int kn = k_end - k_begin;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)A0, 0, ((kn - 1) * lda + ma) * 2, kBufferRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)B0, 0, ((kn - 1) * ldb + nb) * 2, kBufferRsrcWord3);
+  auto stage = [&](int s) -> bf16* { return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : st3)); };
+  auto issue = [&](int s, int k0) {  // k0 relative to k_begin
+    bf16* base = stage(s);
+#pragma unroll
+    for (int j = 0; j < S::LPW; ++j) {
+      const int li = w + S::NWAVES * j;  // wave-uniform
+      const bool isA = li < S::LA;
+      const int C = isA ? S::CA : S::CB;   // chunks per row
+      const int e = (isA ? li : li - S::LA) * 64 + lane;  // chunk slot in the operand's stage tile
+      const int r = e / C, p = e % C;      // k row and physical chunk
+      const int q = dl_tn_swizzle(r, p);   // logical chunk held there
+      const int k = k0 + r, col = 8 * q;
+      const int ld = isA ? lda : ldb, cols = isA ? ma : nb;
+      const unsigned off = (k < kn && col < cols) ? (unsigned)(k * ld + col) * 2u : 0x80000000u;
+      bf16* dst = base + (isA ? li * 512 : S::BK * S::BM + (li - S::LA) * 512);
+      if (isA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dl_lds_void*)dst, 16, off, 0, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (dl_lds_void*)dst, 16, off, 0, 0, 0);
+    }
+  };
+  auto compute = [&](const bf16* buf) {
+    const bf16* As = buf;
+    const bf16* Bs = buf + S::BK * S::BM;
+#pragma unroll
+    for (int ks = 0; ks < S::BK; ks += 32) {
+      Frag8<bf16> a[S::FM];
+#pragma unroll
+      for (int i = 0; i < S::FM; ++i) a[i] = frag_kmajor_swz<S::BM>(As, ks + 8 * grp, wm * S::WTM + 16 * i, lane);
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j) {
+        const Frag8<bf16> b = frag_kmajor_swz<S::BN>(Bs, ks + 8 * grp, wn * S::WTN + 16 * j, lane);
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) mma8(acc[i][j], a[i], b);
+      }
+    }
+  };
+
+  const int nk = (kn + S::BK - 1) / S::BK;
+#pragma unroll
+  for (int p = 0; p < NS - 1; ++p)
+    if (p < nk) issue(p, p * S::BK);
+  for (int c = 0; c < nk; ++c) {
+    if (c + NS - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(dl_vmcnt(S::LPW * (NS - 2)));
+    else
+      __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
+    __syncthreads();
+    if (c + NS - 1 < nk) issue((c + NS - 1) % NS, (c + NS - 1) * S::BK);
+    compute(stage(c % NS));
+  }
+  __syncthreads();
+}
+
 }  // namespace gbla

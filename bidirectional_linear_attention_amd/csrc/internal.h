@@ -74,6 +74,7 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
                       hipStream_t s);
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s);
 int dw_tiles(int dt, int d, int Kp);
+int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,

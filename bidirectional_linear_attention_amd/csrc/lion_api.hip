@@ -31,10 +31,7 @@ LDims dims_of(const lion_problem* p) {
   m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.Kp = grad_cols(m.H, m.dh);
   m.slots = max_chunks(m.T, m.N, kLionChunk);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
-  const int tiles = dw_tiles(dt, m.d, m.Kp);
-  int ns = (256 + tiles - 1) / tiles;
-  ns = std::min(ns, std::max(1, (m.T + 1023) / 1024));
-  m.nsplit = std::max(1, std::min(ns, 64));
+  m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
   return m;
 }
