@@ -248,15 +248,24 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
 }
 
 // ============================================================== projection GEMM
-// Block = 256 tokens x one head's [Q | K | V] columns (3 dh). bf16 runs the
-// direct-to-LDS main loop, float the register-staged one.
+// Block = 256 tokens x the [Q | K | V] columns (3 dh each) of HPB consecutive
+// heads (the packed per-head panels are contiguous, so HPB heads are one B
+// operand). bf16 runs the direct-to-LDS main loop, float the register-staged one.
 // Epilogue: phi on Q and K, identity on V.
 template <typename T, int DH> struct ProjCfg;
-template <> struct ProjCfg<bf16, 64> { using S = DlShape<256, 192, 64, 4, 2, 2>; static constexpr bool DL = true; };
-template <> struct ProjCfg<bf16, 32> { using S = DlShape<256, 96, 64, 4, 1, 2>; static constexpr bool DL = true; };
+template <> struct ProjCfg<bf16, 64> {
+  using S = DlShape<256, 384, 32, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+};
+template <> struct ProjCfg<bf16, 32> {
+  using S = DlShape<256, 192, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+};
 // float32 tiles stay within 64 KB of LDS
-template <> struct ProjCfg<float, 64> { using S = GemmShape<float, 32, 192, 32, 1, 4>; static constexpr bool DL = false; };
-template <> struct ProjCfg<float, 32> { using S = GemmShape<float, 64, 96, 32, 2, 2>; static constexpr bool DL = false; };
+template <> struct ProjCfg<float, 64> {
+  using S = GemmShape<float, 32, 192, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
+};
+template <> struct ProjCfg<float, 32> {
+  using S = GemmShape<float, 64, 96, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
+};
 
 // PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION-s)
 template <typename T, int DH, bool PHI = true>
@@ -266,19 +275,22 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
                                                                       T* __restrict__ v_out) {
   using S = typename ProjCfg<T, DH>::S;
   constexpr bool DL = ProjCfg<T, DH>::DL;
+  constexpr int HPB = ProjCfg<T, DH>::HPB;
+  static_assert(S::BN == HPB * 3 * DH, "a block covers whole heads");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
-  const int mtiles = (T_ + S::BM - 1) / S::BM;
-  const int lid = xcd_logical_block(blockIdx.x, mtiles * H);
-  if (lid >= mtiles * H) return;
-  const int mt = lid / H, h = lid - mt * H;
+  const int mtiles = (T_ + S::BM - 1) / S::BM, hgroups = (H + HPB - 1) / HPB;
+  const int lid = xcd_logical_block(blockIdx.x, mtiles * hgroups);
+  if (lid >= mtiles * hgroups) return;
+  const int mt = lid / hgroups, h0 = (lid - mt * hgroups) * HPB;
   const int m0 = mt * S::BM;
+  const int nb = min(HPB, H - h0) * 3 * DH;  // valid weight rows (a last odd head)
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
-    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d, smem, smem1,
+    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * 3 * DH * d, d, nb, d, smem, smem1,
                   smem1, smem1, acc);
   else
-    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h * S::BN * d, d, S::BN, d,
+    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * 3 * DH * d, d, nb, d,
                            smem, acc);
   // epilogue: phi on Q and K, staged per wave through LDS (the main loop ended
   // with a barrier, so smem is free) and written as 16-byte row vectors
@@ -295,7 +307,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
       const int n = wn * S::WTN + 16 * j;
-      const bool lin = !PHI || n / DH == 2;  // v columns (and everything without phi) stay linear
+      const bool lin = !PHI || (n % (3 * DH)) / DH == 2;  // v columns (and everything without phi) stay linear
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[i][j][r];
@@ -307,9 +319,9 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
       const int r = it / VPR, c = (it % VPR) * 8;
       const int t = m0 + wm * S::WTM + 16 * i + r;
       const int n = wn * S::WTN + c;
-      const int kind = n / DH;
+      const int h = h0 + n / (3 * DH), nn = n % (3 * DH), kind = nn / DH;
       T* out = kind == 0 ? q_out : (kind == 1 ? k_out : v_out);
-      if (t < T_) frag_store(out + (size_t)t * D + h * DH + (n % DH), frag_load(ws + r * LDO + c));
+      if (t < T_ && h < H) frag_store(out + (size_t)t * D + h * DH + (nn % DH), frag_load(ws + r * LDO + c));
     }
     __syncthreads();
   }
@@ -318,7 +330,8 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
 template <typename T, int DH, bool PHI>
 static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, hipStream_t s) {
   using S = typename ProjCfg<T, DH>::S;
-  const int n = ((T_ + S::BM - 1) / S::BM) * H;
+  constexpr int HPB = ProjCfg<T, DH>::HPB;
+  const int n = ((T_ + S::BM - 1) / S::BM) * ((H + HPB - 1) / HPB);
   if (n == 0) return;
   hipLaunchKernelGGL((k_proj<T, DH, PHI>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
                      (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v);

@@ -112,6 +112,14 @@ def test_bf16_small_long_history_recipe():
     compare(make_inputs(w), backward=True, label="bf16 long-history recipe small")
 
 
+@pytest.mark.parametrize("dh", [64, 32])
+def test_bf16_odd_head_count(dh):
+    """Three heads: the projection's two-head blocks end with a one-head block."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (300, 77, 513), d_model=96, num_heads=3, head_dim=dh,
+                      seed=24)
+    compare(make_inputs(w), backward=True, label=f"bf16 H=3 dh={dh}")
+
+
 def test_bf16_small_ragged_recipe():
     rng = np.random.default_rng(23)
     lens = np.clip(np.rint(np.exp(rng.normal(np.log(600), 1.0, 12))), 16, 32768).astype(int)

@@ -106,6 +106,11 @@ def test_bf16_small_recipe_L512():
     compare(make_inputs(w), label="bf16 LION-s recipe L<=512")
 
 
+def test_bf16_odd_head_count():
+    w = small_variant(LION, (300, 77, 130), d_model=96, num_heads=3, seed=58)
+    compare(make_inputs(w), label="bf16 LION-s H=3")
+
+
 def test_bf16_small_ragged():
     w = small_variant(LION, (1, 63, 64, 65, 127, 128, 129, 450), d_model=128, num_heads=2, seed=54)
     compare(make_inputs(w), label="bf16 ragged chunks")
