@@ -9,8 +9,10 @@ before the timed region; x and dy rotate over three buffer sets (> 256 MB) so
 the 256 MB Infinity Cache does not serve a step from the previous step's data.
 
 Prints ONE JSON line: tokens/s (value), the roofline of the dominant stage
-measured live with the library's per-stage HIP events on the launch stream,
-and the float64 CPU oracle timed on a bounded sample of the same workload.
+measured live with the library's HIP events on the launch stream, recorded in
+the timed region around that stage only (a pass before it, with events around
+every stage, gives stage_ms_per_step and picks the dominant stage), and the
+float64 CPU oracle timed on a bounded sample of the same workload.
 The same line carries a secondary measurement of the LION-s layer (16 x 4096
 tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under "lion_s".
 
@@ -109,6 +111,34 @@ def cpu_baseline(inp, sample_seqs):
                       f"({T} tokens) of the same batch, timed once ({dt:.1f} s)"}
 
 
+def timed_passes(gb, torch, step, steps, warmup, stage_filter):
+    """Warm up, then (1) an untimed pass with every stage's events for the
+    breakdown, (2) the timed region: `steps` steps bracketed by synchronize,
+    with events recorded only around the stages stage_filter(breakdown) picks
+    (each recorded event costs device time). Returns (elapsed seconds,
+    breakdown {stage: (ms, launches)} per pass-1 step, timed-region stages)."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    nb = max(1, min(steps, 10))
+    gb.profile_begin(64 * nb)
+    for i in range(nb):
+        step(i)
+    torch.cuda.synchronize()
+    br = gb.profile_end()
+    breakdown = {k: (v[0] / nb, v[1] / nb) for k, v in br.items()}
+    sel = stage_filter(breakdown)
+    gb.profile_begin(64 * max(1, steps), stages=sel)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timed = gb.profile_end()
+    return t1 - t0, breakdown, timed
+
+
 def copy_calibration(mib=1024, reps=3):
     """Copy `mib` MiB device to device `reps` times; the copy kernel reads and
     writes exactly mib MiB per launch."""
@@ -133,7 +163,6 @@ def lion_leg(steps, warmup):
     import torch
 
     from bidirectional_linear_attention_amd import lion as gl
-    from bidirectional_linear_attention_amd import profile_begin, profile_end
     from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
 
     w = WORKLOADS["lion_s_bf16_B16_L4096_d512"]
@@ -166,21 +195,11 @@ def lion_leg(steps, warmup):
         gl.lion_forward(p, x, cu, w_q, w_k, w_v, w_lam, b_lam, y, act, ws)
         gl.lion_backward(p, x, cu, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, dx, dwq, dwk, dwv, dwl, dbl, ws)
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    profile_begin(64 * max(1, steps))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    stages = profile_end()
+    import bidirectional_linear_attention_amd as gb
+    elapsed, breakdown, _ = timed_passes(gb, torch, step, steps, warmup, lambda br: [])
     return {"workload": w.name, "tokens_per_step": T, "steps": steps, "warmup": warmup,
             "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(1e3 * elapsed / steps, 4),
-            "stage_ms_per_step": {k: round(v[0] / steps, 4)
-                                  for k, v in sorted(stages.items(), key=lambda kv: -kv[1][0])}}
+            "stage_ms_per_step": {k: round(v[0], 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])}}
 
 
 def main():
@@ -241,27 +260,18 @@ def main():
         gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
                          dbg, ws)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    gb.profile_begin(64 * max(1, args.steps))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    stages = gb.profile_end()
-    elapsed = t1 - t0
+    def dominant(br):
+        timed = {k: v for k, v in br.items() if stage_work(k, T, N, d, H, dh, esz)}
+        return [max(timed, key=lambda k: timed[k][0])]
+
+    elapsed, breakdown, timed = timed_passes(gb, torch, step, args.steps, args.warmup, dominant)
     ms_per_step = 1e3 * elapsed / args.steps
     tok_s = T * args.steps / elapsed
 
-    # dominant stage by total device time, and its roofline
-    per_step = {k: v[0] / args.steps for k, v in stages.items()}
-    timed = {k: v for k, v in stages.items() if stage_work(k, T, N, d, H, dh, esz)}
-    dom = max(timed, key=lambda k: timed[k][0])
+    # roofline of the dominant stage from its events inside the timed region
+    dom = dominant(breakdown)[0]
     bound, work = stage_work(dom, T, N, d, H, dh, esz)
-    dom_ms, dom_launches = stages[dom]
+    dom_ms, dom_launches = timed[dom]
     avg_s = dom_ms / dom_launches / 1e3
     if bound == "mfma":
         achieved, peak, unit = work / avg_s / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
@@ -270,6 +280,7 @@ def main():
     roof = {"bound": bound, "kernel": dom, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
             "avg_launch_us": round(avg_s * 1e6, 2)}
+    per_step = {k: v[0] for k, v in breakdown.items()}
 
     bpt = layer_bytes_per_token(d, D, esz)
     out = {

@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import DTYPE_BF16, DTYPE_F32, GATE_SIGMOID, GblaError, GblaProblem
 
 __all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "activation_size", "gbla_forward",
-           "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "DTYPE_F32", "DTYPE_BF16"]
+           "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "stage_names", "DTYPE_F32", "DTYPE_BF16"]
 
 
 def _torch():
@@ -153,9 +153,30 @@ def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num
     return g
 
 
-def profile_begin(max_records: int) -> None:
-    """Open the library's per-stage event-timing window (gbla_profile_begin)."""
-    _lib.check(_lib.load().gbla_profile_begin(int(max_records)), "gbla_profile_begin")
+def stage_names() -> list:
+    """Names of the profiled stages, in stage-id order."""
+    lib = _lib.load()
+    names = []
+    for i in range(64):
+        n = lib.gbla_profile_stage_name(i).decode()
+        if n == "unknown":
+            break
+        names.append(n)
+    return names
+
+
+def profile_begin(max_records: int, stages=None) -> None:
+    """Open the library's per-stage event-timing window; stages: iterable of
+    stage names to time (None: all), see stage_names()."""
+    lib = _lib.load()
+    if stages is None:
+        _lib.check(lib.gbla_profile_begin(int(max_records)), "gbla_profile_begin")
+        return
+    ids = {n: i for i, n in enumerate(stage_names())}
+    mask = 0
+    for n in stages:
+        mask |= 1 << ids[n]
+    _lib.check(lib.gbla_profile_begin_stages(int(max_records), ctypes.c_uint64(mask)), "gbla_profile_begin_stages")
 
 
 def profile_end() -> dict:

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
     "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 18 + [_vp, _sz, _vp]),
     "gbla_profile_begin": (ctypes.c_int, [ctypes.c_int]),
+    "gbla_profile_begin_stages": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64]),
     "gbla_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),
                                         ctypes.c_int, ctypes.POINTER(ctypes.c_int)]),
     "gbla_profile_stage_name": (ctypes.c_char_p, [ctypes.c_int]),

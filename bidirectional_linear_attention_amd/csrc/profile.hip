@@ -1,8 +1,8 @@
 // Optional per-stage timing of the library's launches with HIP events.
 //
 // While a profiling window is open (gbla_profile_begin .. gbla_profile_end),
-// every stage of gbla_forward / gbla_backward records one event before and one
-// after its kernel(s) on the caller's stream, so the elapsed time between the
+// every selected stage of the forward / backward entry points records one event
+// before and one after its kernel(s) on the caller's stream, so the elapsed time between the
 // two is that stage's device time on that stream. gbla_profile_end waits for
 // the recorded events and returns per-stage totals. The window is process-wide
 // state meant for benchmarking; it is not meant for concurrent callers.
@@ -26,6 +26,7 @@ const char* kStageNames[kNumStages] = {
 struct Profiler {
   std::mutex mu;
   bool active = false;
+  uint64_t mask = ~0ull;  // stages that record events
   int capacity = 0;
   int used = 0;
   std::vector<hipEvent_t> ev;  // 2 per record
@@ -40,7 +41,7 @@ Profiler& prof() {
 StageScope::StageScope(int stage_id, hipStream_t s) : rec_(-1), s_(s) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
-  if (!p.active || p.used >= p.capacity) return;
+  if (!p.active || p.used >= p.capacity || !((p.mask >> stage_id) & 1ull)) return;
   rec_ = p.used++;
   p.stage[rec_] = stage_id;
   (void)hipEventRecord(p.ev[2 * rec_], s_);
@@ -59,10 +60,13 @@ using namespace gbla;
 
 extern "C" {
 
-GBLA_API gbla_status gbla_profile_begin(int max_records) {
+GBLA_API gbla_status gbla_profile_begin(int max_records) { return gbla_profile_begin_stages(max_records, ~0ull); }
+
+GBLA_API gbla_status gbla_profile_begin_stages(int max_records, uint64_t stage_mask) {
   if (max_records < 1 || max_records > (1 << 20)) return GBLA_ERR_BAD_SHAPE;
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
+  p.mask = stage_mask;
   for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
   p.ev.assign(2 * (size_t)max_records, nullptr);
   p.stage.assign(max_records, -1);

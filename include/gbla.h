@@ -134,8 +134,9 @@ GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const i
 
 /* ---- Optional per-stage timing (benchmarking aid) ----------------------
  * gbla_profile_begin opens a process-wide window of at most max_records
- * stage launches. While it is open, every stage of gbla_forward/gbla_backward
- * records a HIP event before and after its kernels on the caller's stream.
+ * stage launches. While it is open, every stage of the forward and backward
+ * entry points (GBLA and LION-s) records a HIP event before and after its
+ * kernels on the caller's stream.
  * gbla_profile_end waits for those events, writes per-stage total device
  * milliseconds and launch counts for min(max_stages, *n_stages) stages
  * (names: gbla_profile_stage_name), and closes the window. Launches beyond
@@ -143,6 +144,10 @@ GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const i
  * Errors: GBLA_ERR_BAD_SHAPE (max_records out of [1, 2^20], or end without
  * begin), GBLA_ERR_NULL_ARG, GBLA_ERR_HIP (event creation/query failed). */
 GBLA_API gbla_status gbla_profile_begin(int max_records);
+/* Same window, but only the stages whose bit (1 << stage) is set in stage_mask
+ * record events (each recorded event costs device time, so a narrow mask keeps
+ * the timed work close to an unprofiled run). */
+GBLA_API gbla_status gbla_profile_begin_stages(int max_records, uint64_t stage_mask);
 GBLA_API gbla_status gbla_profile_end(double* ms_per_stage, int* launches_per_stage, int max_stages, int* n_stages);
 GBLA_API const char* gbla_profile_stage_name(int stage);
 
