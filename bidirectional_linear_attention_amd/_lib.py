@@ -6,7 +6,8 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgbla.so")
+# GBLA_LIBRARY may name another build of the same library (e.g. to compare two builds)
+LIB_PATH = os.environ.get("GBLA_LIBRARY") or os.path.join(_PKG, "libgbla.so")
 
 STATUS = {
     0: "GBLA_OK", 1: "GBLA_ERR_NULL_ARG", 2: "GBLA_ERR_BAD_SHAPE", 3: "GBLA_ERR_UNSUPPORTED",

@@ -565,6 +565,7 @@ void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int K
 //   dx_u[c]       = sum_k w[c][k] dx~_{u+3-k}[c]      (u+3-k inside u's sequence)
 //   dconv_w[c][k] = sum_t dx~_t[c] x_{t-3+k}[c]       (t-3+k inside t's sequence)
 constexpr int kConvRun = 32;
+constexpr int kConvBatch = 4;  // tokens per unrolled, prefetched batch
 constexpr int kConvRows = 4 * kConvRun;
 int conv_bwd_row_blocks(int T) { return (T + kConvRows - 1) / kConvRows; }
 
@@ -580,7 +581,8 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ dxt, con
                                                   const int32_t* __restrict__ cu, int nseq, int T_, int d,
                                                   const T* __restrict__ conv_w, T* __restrict__ dx,
                                                   float* __restrict__ part) {
-  __shared__ float red[4][64 * 32 + 1];
+  constexpr int B = kConvBatch, RP = 33;  // tokens per unrolled batch; padded pitch of red[]
+  __shared__ float red[4][64 * RP];
   const int rb = blockIdx.x, cb = blockIdx.y;
   const int tid = threadIdx.x, cg = tid & 63, run = tid >> 6;
   const int c = cb * 512 + cg * 8;
@@ -599,65 +601,83 @@ __global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ dxt, con
 #pragma unroll
       for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
     }
-    // forward window g[s] = dx~_{u+s}, s = 0..3; backward window xm[s] = x_{u-s}, s = 1..3
-    float g[4][8], xm[4][8];
+    // sliding windows: gw[s] = dx~_{u+s} (s = 0..2), xw[s] = x_{u-1-s} (s = 0..2); zero outside [0, T)
+    float gw[3][8], xw[3][8];
 #pragma unroll
-    for (int sft = 0; sft < 4; ++sft) {
-      const int t = u0 + sft;
-      if (sft < 3 && t < T_) load8f(dxt + (size_t)t * d + c, g[sft]);
+    for (int s = 0; s < 3; ++s) {
+      const int tg = u0 + s, tx = u0 - 1 - s;
+      if (tg < T_) load8f(dxt + (size_t)tg * d + c, gw[s]);
       else
 #pragma unroll
-        for (int j = 0; j < 8; ++j) g[sft][j] = 0.f;
-      const int tb = u0 - sft;
-      if (sft >= 1 && tb >= 0) {
-        const Frag8<T> f = frag_load(x + (size_t)tb * d + c);
+        for (int j = 0; j < 8; ++j) gw[s][j] = 0.f;
+      if (tx >= 0) load8f(x + (size_t)tx * d + c, xw[s]);
+      else
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xm[sft][j] = frag_get(f, j);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xm[sft][j] = 0.f;
-      }
+        for (int j = 0; j < 8; ++j) xw[s][j] = 0.f;
     }
+    // the rows of a batch (dx~_{u+3}, x_u for its B tokens u) are loaded together, one batch ahead
+    Frag8<T> fa[2][B], fb[2][B];
+    auto fetch = [&](int buf, int ub) {
+#pragma unroll
+      for (int i = 0; i < B; ++i) {
+        const int tg = ub + 3 + i, tx = ub + i;
+        fa[buf][i] = tg < T_ ? frag_load(dxt + (size_t)tg * d + c) : frag_zero<T>();
+        fb[buf][i] = tx < u1 ? frag_load(x + (size_t)tx * d + c) : frag_zero<T>();
+      }
+    };
     SeqCursor cur(cu, nseq, u0, T_);
-    for (int u = u0; u < u1; ++u) {
-      if (u + 3 < T_) load8f(dxt + (size_t)(u + 3) * d + c, g[3]);
-      {
-        const Frag8<T> f = frag_load(x + (size_t)u * d + c);
+    auto compute = [&](int buf, int ub) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xm[0][j] = frag_get(f, j);
+      for (int i = 0; i < B; ++i) {
+        const int u = ub + i;
+        if (u >= u1) break;
+        float g3[8], x0[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          g3[j] = frag_get(fa[buf][i], j);
+          x0[j] = frag_get(fb[buf][i], j);
+        }
+        const int end = cur.end(u), pos = cur.pos(u);
+        float o[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          // output token u + 3 - k reads x_u through tap k; token u read x_{u-sh} through tap 3 - sh
+          float a = u + 3 < end ? wv[j][0] * g3[j] : 0.f;
+          if (u + 2 < end) a += wv[j][1] * gw[2][j];
+          if (u + 1 < end) a += wv[j][2] * gw[1][j];
+          a += wv[j][3] * gw[0][j];
+          o[j] = a;
+          dw[j][3] += gw[0][j] * x0[j];
+          if (pos >= 1) dw[j][2] += gw[0][j] * xw[0][j];
+          if (pos >= 2) dw[j][1] += gw[0][j] * xw[1][j];
+          if (pos >= 3) dw[j][0] += gw[0][j] * xw[2][j];
+        }
+        frag_store(dx + (size_t)u * d + c, frag_from<T>(o));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          gw[0][j] = gw[1][j]; gw[1][j] = gw[2][j]; gw[2][j] = g3[j];
+          xw[2][j] = xw[1][j]; xw[1][j] = xw[0][j]; xw[0][j] = x0[j];
+        }
       }
-      const int end = cur.end(u);
-      const int pos = cur.pos(u);
-      float o[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o[j] = 0.f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int sh = 3 - k;
-        if (u + sh < end)  // output token u + sh reads x_u through tap k
-#pragma unroll
-          for (int j = 0; j < 8; ++j) o[j] += wv[j][k] * g[sh][j];
-        if (sh <= pos)     // output token u read x_{u-sh} through tap k
-#pragma unroll
-          for (int j = 0; j < 8; ++j) dw[j][k] += g[0][j] * xm[sh][j];
-      }
-      frag_store(dx + (size_t)u * d + c, frag_from<T>(o));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        g[0][j] = g[1][j]; g[1][j] = g[2][j]; g[2][j] = g[3][j]; g[3][j] = 0.f;
-        xm[3][j] = xm[2][j]; xm[2][j] = xm[1][j]; xm[1][j] = xm[0][j];
-      }
+    };
+    fetch(0, u0);
+    for (int ub = u0; ub < u1; ub += 2 * B) {
+      if (ub + B < u1) fetch(1, ub + B);
+      compute(0, ub);
+      if (ub + 2 * B < u1) fetch(0, ub + 2 * B);
+      if (ub + B < u1) compute(1, ub + B);
     }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) red[run][cg * 32 + j * 4 + k] = dw[j][k];
+    for (int k = 0; k < 4; ++k) red[run][cg * RP + j * 4 + k] = dw[j][k];
   __syncthreads();
   // 512 channels x 4 taps, summed over the 4 runs in a fixed order
   for (int e = tid; e < 512 * 4; e += 256) {
     const int cc = cb * 512 + (e >> 2);
-    if (cc < d) part[((size_t)rb * d + cc) * 4 + (e & 3)] = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+    const int li = (e >> 5) * RP + (e & 31);  // channel group e / 32, element (channel % 8) * 4 + tap
+    if (cc < d) part[((size_t)rb * d + cc) * 4 + (e & 3)] = (red[0][li] + red[1][li]) + (red[2][li] + red[3][li]);
   }
 }
 

@@ -114,6 +114,25 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 // 8 lanes in 4 + 2 + 1 + 3 shuffles.
 constexpr int kConvRowsPerWave = 16;
 
+// sum of the 8 products of two fragments (bf16: four packed dot2 instructions)
+template <typename T> __device__ __forceinline__ float gate_dot8(const Frag8<T>& a, const Frag8<T>& b);
+template <> __device__ __forceinline__ float gate_dot8<float>(const Frag8<float>& a, const Frag8<float>& b) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += frag_get(a, j) * frag_get(b, j);
+  return s;
+}
+typedef __bf16 gate_bf16x2 __attribute__((ext_vector_type(2)));
+template <> __device__ __forceinline__ float gate_dot8<bf16>(const Frag8<bf16>& a, const Frag8<bf16>& b) {
+  const uint32_t av[4] = {a.v.x, a.v.y, a.v.z, a.v.w}, bv[4] = {b.v.x, b.v.y, b.v.z, b.v.w};
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(gate_bf16x2, av[j]), __builtin_bit_cast(gate_bf16x2, bv[j]),
+                                        s, false);
+  return s;
+}
+
 __device__ __forceinline__ float butterfly8(float (&v)[8], int lane) {
   const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
   float u[4];
@@ -154,7 +173,8 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
     for (int g8 = lane; g8 < ((ngroups + 63) / 64) * 64; g8 += 64) {
       const bool okc = g8 < ngroups;
       const int c = g8 * 8;
-      float wv[8][4], wg[8][8];
+      float wv[8][4];
+      Frag8<T> wgf[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const Frag8<T> f = CONV && okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
@@ -162,21 +182,25 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
       }
 #pragma unroll
-      for (int hh = 0; hh < 8; ++hh) {
-        const Frag8<T> f = okc && hg + hh < H ? frag_load(w_g + (size_t)(hg + hh) * d + c) : frag_zero<T>();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wg[hh][e] = frag_get(f, e);
-      }
+      for (int hh = 0; hh < 8; ++hh)
+        wgf[hh] = okc && hg + hh < H ? frag_load(w_g + (size_t)(hg + hh) * d + c) : frag_zero<T>();
       Frag8<T> xm1 = frag_zero<T>(), xm2 = frag_zero<T>(), xm3 = frag_zero<T>();
       if (CONV && okc && t_begin < t_end) {
         if (t_begin >= 1) xm1 = frag_load(x + (size_t)(t_begin - 1) * d + c);
         if (t_begin >= 2) xm2 = frag_load(x + (size_t)(t_begin - 2) * d + c);
         if (t_begin >= 3) xm3 = frag_load(x + (size_t)(t_begin - 3) * d + c);
       }
+      Frag8<T> xr[kConvRowsPerWave];  // every row of this wave, loaded together
+#pragma unroll
+      for (int i = 0; i < kConvRowsPerWave; ++i)
+        xr[i] = okc && t_begin + i < t_end ? frag_load(x + (size_t)(t_begin + i) * d + c) : frag_zero<T>();
       SeqCursor cur(cu, nseq, t_begin, T_);
-      for (int t = t_begin; t < t_end; ++t) {
+#pragma unroll
+      for (int i = 0; i < kConvRowsPerWave; ++i) {
+        const int t = t_begin + i;
+        if (t >= t_end) break;
         const int pos = cur.pos(t);
-        const Frag8<T> x0 = okc ? frag_load(x + (size_t)t * d + c) : frag_zero<T>();
+        const Frag8<T> x0 = xr[i];
         float o[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -190,15 +214,10 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         if (CONV && okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
         float sp[8];
 #pragma unroll
-        for (int hh = 0; hh < 8; ++hh) {
-          float a = 0.f;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a += wg[hh][j] * frag_get(of, j);  // the rounded x~ that Q, K, V see
-          sp[hh] = a;
-        }
+        for (int hh = 0; hh < 8; ++hh) sp[hh] = gate_dot8<T>(of, wgf[hh]);  // the rounded x~ that Q, K, V see
         const float tot = butterfly8(sp, lane);
         if ((lane & 7) == 0) {
-          float& acc = sacc[w][t - t_begin][lane >> 3];
+          float& acc = sacc[w][i][lane >> 3];
           acc = g8 < 64 ? tot : acc + tot;
         }
         xm3 = xm2;
