@@ -171,6 +171,65 @@ template <> __device__ __forceinline__ Frag8<float> frag_kmajor<float>(const flo
   return f;
 }
 
+// ---------------------------------------------------------------- 4-element quads (K = 16 MFMA operands)
+// Four consecutive k elements of one lane for a 16x16x16 MFMA (bf16: one 8-byte
+// register pair; float: four 16x16x4 MFMAs). With the C-reuse assignment
+// k = 4 * (lane / 16) + m, the 4 values a lane holds in a 16x16 C tile form
+// a quad, so a C tile feeds the next contraction without leaving registers.
+template <typename T> struct Quad;
+template <> struct Quad<bf16> { uint2 v; };
+template <> struct Quad<float> { float4 v; };
+
+template <typename T> __device__ __forceinline__ Quad<T> quad_from4(const float* f);
+template <> __device__ __forceinline__ Quad<bf16> quad_from4<bf16>(const float* f) {
+  Quad<bf16> q; q.v = make_uint2(f2bf2(f[0], f[1]), f2bf2(f[2], f[3])); return q;
+}
+template <> __device__ __forceinline__ Quad<float> quad_from4<float>(const float* f) {
+  Quad<float> q; q.v = make_float4(f[0], f[1], f[2], f[3]); return q;
+}
+__device__ __forceinline__ float quad_get(const Quad<float>& q, int m) { return reinterpret_cast<const float*>(&q.v)[m]; }
+__device__ __forceinline__ float quad_get(const Quad<bf16>& q, int m) {
+  return bf2f(reinterpret_cast<const bf16*>(&q.v)[m]);
+}
+// 4 consecutive elements at p (8-byte aligned for bf16, 16-byte for float)
+template <typename T> __device__ __forceinline__ Quad<T> quad_load(const T* p);
+template <> __device__ __forceinline__ Quad<bf16> quad_load<bf16>(const bf16* p) {
+  Quad<bf16> q; q.v = *reinterpret_cast<const uint2*>(p); return q;
+}
+template <> __device__ __forceinline__ Quad<float> quad_load<float>(const float* p) {
+  Quad<float> q; q.v = *reinterpret_cast<const float4*>(p); return q;
+}
+template <typename T> __device__ __forceinline__ void quad_store(T* p, const Quad<T>& q);
+template <> __device__ __forceinline__ void quad_store<bf16>(bf16* p, const Quad<bf16>& q) {
+  *reinterpret_cast<uint2*>(p) = q.v;
+}
+template <> __device__ __forceinline__ void quad_store<float>(float* p, const Quad<float>& q) {
+  *reinterpret_cast<float4*>(p) = q.v;
+}
+// acc += A(16x16) B(16x16) with this lane's quads of A (row lane % 16) and B (column lane % 16)
+__device__ __forceinline__ void mma_q(f32x4& acc, const Quad<bf16>& a, const Quad<bf16>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, a.v), __builtin_bit_cast(s16x4_v, b.v),
+                                                  acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_q(f32x4& acc, const Quad<float>& a, const Quad<float>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.x, b.v.x, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.y, b.v.y, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.z, b.v.z, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v.w, b.v.w, acc, 0, 0, 0);
+}
+
+// k-major quad: lane (g = lane / 16, i = lane % 16) receives tile[kb + m][cb + i], m = 0..3
+// (kb may differ between the groups; bf16: one transposing LDS read)
+template <typename T> __device__ __forceinline__ Quad<T> quad_kmajor(const T* tile, int ld, int kb, int cb, int lane);
+template <> __device__ __forceinline__ Quad<bf16> quad_kmajor<bf16>(const bf16* tile, int ld, int kb, int cb, int lane) {
+  Quad<bf16> q; q.v = tr_read4(tile, ld, kb, cb, lane); return q;
+}
+template <> __device__ __forceinline__ Quad<float> quad_kmajor<float>(const float* tile, int ld, int kb, int cb,
+                                                                      int lane) {
+  const float* p = tile + kb * ld + cb + (lane & 15);
+  Quad<float> q; q.v = make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]); return q;
+}
+
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ float sigmoidf_(float s) { return fast_rcp(1.f + __expf(-s)); }
 // phi(u) = elu(u) + 1

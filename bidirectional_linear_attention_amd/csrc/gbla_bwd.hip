@@ -56,29 +56,33 @@ __device__ __forceinline__ void wave_reduce_state(float* red, const f32x4 (&acc)
 
 // ============================================================== dS, dz and dq
 // Block = one chunk x one head; tiles of 64 tokens of q~ and dy are staged in
-// LDS with 16-byte loads, each wave then works on 16 of those tokens:
-//   [num | den] = q~ [S | z]             (MFMA, A rows from LDS)
-//   dn, dden from dy and y = num / den   (C-tile order, LDS reads)
-//   dq~ = dn S^T + dden z                (MFMA, dn staged back through LDS)
-//   dS += q~^T dn, dz += q~^T dden       (K=16 MFMAs on C-tile registers)
-// dq is staged in LDS over the wave's own q~ rows and written with 16-byte stores.
+// LDS with 16-byte loads, wave w works on tokens 16 w .. 16 w + 15 of a tile in
+// the transposed orientation (C rows = features, C columns = tokens), so each
+// lane holds 4 consecutive features of one token:
+//   [num | den]^T = [S | z]^T q~^T        (MFMA, A = the staged transposed state)
+//   dn = dy / den, dden = -(dy . y) / den (dy read as 8-byte quads)
+//   dq~^T = S dn^T (+ z dden)             (K=16 MFMAs: dn stays in registers, A =
+//                                          transposing reads of the staged state)
+//   dq = dq~ (.) phi'(q) -> G             (8-byte stores)
+//   [dS | dz] += q~^T [dn | dden]         (MFMA over the tile's tokens; each wave
+//                                          owns a fixed set of output tiles)
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, const T* __restrict__ dy,
                                                     const float* __restrict__ saved, const int* __restrict__ nchunks,
                                                     const Chunk* __restrict__ tab, int max_slots, int H, int Kp,
                                                     float* __restrict__ partial, T* __restrict__ G) {
-  constexpr int FB = DH / 16;
-  constexpr int NR = DH + 16;
-  constexpr int LD = DH + 16 / (int)sizeof(T);
+  constexpr int FB = DH / 16, NB = FB + 1, NR = DH + 16;
+  constexpr int PAD = 16 / (int)sizeof(T);
+  constexpr int LD = DH + PAD, LDN = DH + 16 + PAD;
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
-  constexpr int ST = 64, V8 = DH / 8;
-  __shared__ __align__(16) T Bsz[P * NR * LD];  // [S | z] as B of q~ [S|z]:  Bsz[n][i]
-  __shared__ __align__(16) T Brm[P * DH * LD];  // S as B of dn S^T:          Brm[a][n] = S[a][n]
-  __shared__ __align__(16) T qs[ST * LD];       // q~ tile, then dq
-  __shared__ __align__(16) T ys[ST * LD];       // dy tile, then dn
+  constexpr int ST = 64, V8 = DH / 8, KS = DH / 32;
+  constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
+  __shared__ __align__(16) T Sst[P * NR * LD];  // [S | z]^T: row n (row dh = z, rows > dh zero), column a
+  __shared__ __align__(16) T qs[ST * LD];       // q~ tile (token-major)
+  __shared__ __align__(16) T ys[ST * LD];       // dy tile
+  __shared__ __align__(16) T dns[ST * LDN];     // [dn | dden | 0] (token-major)
   __shared__ float zs[DH];
-  __shared__ float red[E];
 
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
@@ -88,18 +92,14 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, NR>(Bsz, Brm, LD, st, st + DH * DH, tid);
+  stage_state<T, DH, NR>(Sst, nullptr, LD, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
+  for (int e = tid; e < ST * 16; e += 256) dns[(e >> 4) * LDN + DH + (e & 15)] = from_f<T>(0.f);
 
-  f32x4 dS[FB][FB];
-  float dz[FB];
+  f32x4 accS[TPW];
 #pragma unroll
-  for (int a = 0; a < FB; ++a) {
-    dz[a] = 0.f;
-#pragma unroll
-    for (int b = 0; b < FB; ++b) dS[a][b] = zero4();
-  }
-  const int r0 = 16 * w;  // this wave's rows of the staged tile
+  for (int u = 0; u < TPW; ++u) accS[u] = zero4();
+  const int r0 = 16 * w;
 
   constexpr int NV = (ST * V8 + 255) / 256;
   Frag8<T> pq[NV], py[NV];
@@ -125,81 +125,93 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
     }
     __syncthreads();
     if (tb + ST < ch.end) fetch(tb + ST);
-    Frag8<T> a[DH / 32];
+
+    // [num | den]^T for tokens r0 .. r0 + 15: C[4 grp + r][col] = num[token r0 + col][16 nt + 4 grp + r]
+    Frag8<T> bq[KS];
 #pragma unroll
-    for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
-    f32x4 acc[FB + 1];
+    for (int s = 0; s < KS; ++s) bq[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
+    f32x4 num[NB];
 #pragma unroll
-    for (int nt = 0; nt <= FB; ++nt) {
-      acc[nt] = zero4();
+    for (int nt = 0; nt < NB; ++nt) {
+      num[nt] = zero4();
 #pragma unroll
       for (int p = 0; p < P; ++p)
 #pragma unroll
-        for (int s = 0; s < DH / 32; ++s)
-          mma8(acc[nt], a[s], frag_load(Bsz + p * NR * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
+        for (int s = 0; s < KS; ++s)
+          mma8(num[nt], frag_load(Sst + p * NR * LD + (16 * nt + col) * LD + 32 * s + 8 * grp), bq[s]);
     }
-    float qv[FB][4], dn[FB][4], dden[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r0 + 4 * grp + r;
-      const bool ok = tb + row < ch.end;
-      const float den = col0_bcast(acc[FB][r], lane);
-      const float inv = ok ? fast_rcp(den) : 0.f;
-      float p = 0.f, dyv[FB];
-#pragma unroll
-      for (int nt = 0; nt < FB; ++nt) {
-        dyv[nt] = to_f<T>(ys[row * LD + 16 * nt + col]);
-        qv[nt][r] = to_f<T>(qs[row * LD + 16 * nt + col]);
-        p += dyv[nt] * (acc[nt][r] * inv);
-      }
-      p = row16_sum(p);
-      dden[r] = -p * inv;
-#pragma unroll
-      for (int nt = 0; nt < FB; ++nt) dn[nt][r] = dyv[nt] * inv;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int nt = 0; nt < FB; ++nt) ys[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dn[nt][r]);
-    __syncthreads();
-    Frag8<T> dnf[DH / 32];
-#pragma unroll
-    for (int s = 0; s < DH / 32; ++s) dnf[s] = frag_load(ys + (r0 + col) * LD + 32 * s + 8 * grp);
+    const int tok = r0 + col;
+    const bool ok = tb + tok < ch.end;
+    const float den = __shfl(num[FB][0], col, 64);  // row dh (z) sits in group 0, element 0
+    const float inv = ok ? fast_rcp(den) : 0.f;
+    float dyv[FB][4], pdot = 0.f;
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
+      const Quad<T> q = quad_load(ys + tok * LD + 16 * nt + 4 * grp);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dyv[nt][r] = quad_get(q, r);
+        pdot += dyv[nt][r] * (num[nt][r] * inv);
+      }
+    }
+    pdot += __shfl_xor(pdot, 16, 64);
+    pdot += __shfl_xor(pdot, 32, 64);
+    const float dden = -pdot * inv;
+    Quad<T> dnq[FB];
+#pragma unroll
+    for (int nt = 0; nt < FB; ++nt) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = dyv[nt][r] * inv;
+      dnq[nt] = quad_from4<T>(v);
+      quad_store(dns + tok * LDN + 16 * nt + 4 * grp, dnq[nt]);
+    }
+    if (grp == 0) dns[tok * LDN + DH] = from_f<T>(dden);
+
+    // dq~^T tile at: C[4 grp + r][col] = sum_n S[16 at + 4 grp + r][n] dn[tok][n]
+#pragma unroll
+    for (int at = 0; at < FB; ++at) {
       f32x4 dq = zero4();
 #pragma unroll
-      for (int p = 0; p < P; ++p)
+      for (int nt = 0; nt < FB; ++nt)
 #pragma unroll
-        for (int s = 0; s < DH / 32; ++s)
-          mma8(dq, dnf[s], frag_load(Brm + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
-      const float za = zs[16 * nt + col];
+        for (int p = 0; p < P; ++p)
+          mma_q(dq, quad_kmajor<T>(Sst + p * NR * LD, LD, 16 * nt + 4 * grp, 16 * at, lane), dnq[nt]);
+      const Quad<T> qv = quad_load(qs + tok * LD + 16 * at + 4 * grp);
+      float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        qs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>((dq[r] + dden[r] * za) * fminf(1.f, qv[nt][r]));
+        o[r] = (dq[r] + dden * zs[16 * at + 4 * grp + r]) * fminf(1.f, quad_get(qv, r));
+      if (ok) quad_store(G + (size_t)(tb + tok) * Kp + h * DH + 16 * at + 4 * grp, quad_from4<T>(o));
     }
+    __syncthreads();  // [dn | dden] of all 64 tokens are in LDS
+
+    // [dS | dz] tiles of this wave, contracted over the tile's tokens
 #pragma unroll
-    for (int ia = 0; ia < FB; ++ia) {
-      dz[ia] += (dden[0] * qv[ia][0] + dden[1] * qv[ia][1]) + (dden[2] * qv[ia][2] + dden[3] * qv[ia][3]);
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = w + 4 * u;
+      if (tile >= TILES) continue;
+      const int ia = tile / NB, nb = tile - ia * NB;
 #pragma unroll
-      for (int nb = 0; nb < FB; ++nb) mma4<T>(dS[ia][nb], qv[ia], dn[nb]);
+      for (int s = 0; s < ST / 32; ++s)
+        mma8(accS[u], frag_kmajor<T>(qs, LD, 32 * s + 8 * grp, 16 * ia, lane),
+             frag_kmajor<T>(dns, LDN, 32 * s + 8 * grp, 16 * nb, lane));
     }
-    __syncthreads();
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      if (t < ch.end) frag_store(G + (size_t)t * Kp + h * DH + c, frag_load(qs + r * LD + c));
-    }
-    __syncthreads();
+    __syncthreads();  // the tiles are rewritten next
   }
-#pragma unroll
-  for (int a = 0; a < FB; ++a) {
-    dz[a] += __shfl_xor(dz[a], 16, 64);
-    dz[a] += __shfl_xor(dz[a], 32, 64);
-  }
-  wave_reduce_state<DH>(red, dS, dz, w, grp, col);
   float* out = partial + ((size_t)slot * H + h) * E;
-  for (int e = tid; e < E; e += 256) out[e] = red[e];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) {
+    const int tile = w + 4 * u;
+    if (tile >= TILES) continue;
+    const int ia = tile / NB, nb = tile - ia * NB;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int a = 16 * ia + 4 * grp + r;
+      if (nb < FB) out[a * DH + 16 * nb + col] = accS[u][r];
+      else if (col == 0) out[DH * DH + a] = accS[u][r];
+    }
+  }
 }
 
 void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const float* saved, const int* nchunks,
