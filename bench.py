@@ -13,8 +13,9 @@ measured live with the library's HIP events on the launch stream, recorded in
 the timed region around that stage only (a pass before it, with events around
 every stage, gives stage_ms_per_step and picks the dominant stage), and the
 float64 CPU oracle timed on a bounded sample of the same workload.
-The same line carries a secondary measurement of the LION-s layer (16 x 4096
-tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under "lion_s".
+The same line carries secondary measurements of the LION layers (16 x 4096
+tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under "lion_s",
+"lion_d" and "lion_lit" (selective, fixed per-head and no decay).
 
 --copy-calibration instead times a plain device-to-device copy of a known size
 (for scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
@@ -157,8 +158,10 @@ def copy_calibration(mib=1024, reps=3):
           flush=True)
 
 
-def lion_leg(steps, warmup):
-    """LION-s forward+backward on its 16 x 4096 workload: tokens/s and stage times."""
+def lion_leg(steps, warmup, decay="s"):
+    """LION forward+backward on the 16 x 4096 workload: tokens/s and stage times.
+    decay "s" (Lion-s), "d" (Lion-d: the workload's b_lam as the per-head logit)
+    or "lit" (Lion-lit)."""
     import numpy as np
     import torch
 
@@ -181,12 +184,16 @@ def lion_leg(steps, warmup):
     n_sets = 3
     xs = [t(inp["x"]) for _ in range(n_sets)]
     dys = [t(inp["dy"]) for _ in range(n_sets)]
-    p = gl.problem(N, T, d, H, dh, dt)
+    p = gl.problem(N, T, d, H, dh, dt, decay)
     f32 = dict(dtype=torch.float32, device=dev)
     y = torch.empty((T, D), dtype=dt, device=dev)
     dx = torch.empty((T, d), dtype=dt, device=dev)
     dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
     dwl, dbl = torch.empty((H, d), **f32), torch.empty((H,), **f32)
+    if decay != "s":
+        w_lam, dwl = None, None
+    if decay == "lit":
+        b_lam, dbl = None, None
     ws = torch.empty(max(gl.workspace_size(p, False), gl.workspace_size(p, True)), dtype=torch.uint8, device=dev)
     act = torch.empty(gl.activation_size(p), dtype=torch.uint8, device=dev)
 
@@ -197,7 +204,8 @@ def lion_leg(steps, warmup):
 
     import bidirectional_linear_attention_amd as gb
     elapsed, breakdown, _ = timed_passes(gb, torch, step, steps, warmup, lambda br: [])
-    return {"workload": w.name, "tokens_per_step": T, "steps": steps, "warmup": warmup,
+    return {"workload": w.name, "decay": {"s": "Lion-s", "d": "Lion-d", "lit": "Lion-lit"}[decay],
+            "tokens_per_step": T, "steps": steps, "warmup": warmup,
             "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(1e3 * elapsed / steps, 4),
             "stage_ms_per_step": {k: round(v[0], 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])}}
 
@@ -306,6 +314,8 @@ def main():
         del xs, dys, ws, act
         torch.cuda.empty_cache()
         out["lion_s"] = lion_leg(args.lion_steps, min(args.warmup, 3))
+        for dec in ("d", "lit"):
+            out["lion_" + dec] = lion_leg(args.lion_steps, min(args.warmup, 3), dec)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_sample_seqs)
     print(json.dumps(out), flush=True)

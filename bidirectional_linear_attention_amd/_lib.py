@@ -14,6 +14,7 @@ STATUS = {
     4: "GBLA_ERR_MISALIGNED", 5: "GBLA_ERR_WORKSPACE_TOO_SMALL", 6: "GBLA_ERR_HIP",
 }
 DTYPE_F32, DTYPE_BF16 = 0, 1
+LION_DECAY = {"s": 0, "d": 1, "lit": 2}  # selective, fixed per head, none
 GATE_SIGMOID = 0
 
 
@@ -30,7 +31,7 @@ class GblaProblem(ctypes.Structure):
 
 class LionProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "chunk", "reserved")]
+                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "chunk", "decay")]
 
 
 _vp = ctypes.c_void_p

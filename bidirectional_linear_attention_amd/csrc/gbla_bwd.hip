@@ -388,7 +388,7 @@ __global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, 
     if (n < D) v = w_q[(long)c * D + n];
     else if (n < 2 * D) v = w_k[(long)c * D + n - D];
     else if (n < 3 * D) v = w_v[(long)c * D + n - 2 * D];
-    else if (n < 3 * D + H) v = w_g[(long)(n - 3 * D) * d + c];
+    else if (n < 3 * D + H && w_g) v = w_g[(long)(n - 3 * D) * d + c];  // no w_g: zero rows
     wt[e] = v;
   }
 }
@@ -559,7 +559,7 @@ __global__ void k_dw_reduce(const float* __restrict__ part, int nsplit, int d, i
     if (n < D) dw_q[(long)c * D + n] = s;
     else if (n < 2 * D) dw_k[(long)c * D + n - D] = s;
     else if (n < 3 * D) dw_v[(long)c * D + n - 2 * D] = s;
-    else dw_g[(long)(n - 3 * D) * d + c] = s;
+    else if (dw_g) dw_g[(long)(n - 3 * D) * d + c] = s;
   }
 }
 

@@ -266,6 +266,20 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
                        (const float*)w_lam, (const float*)w_lam, b_lam, (float*)nullptr, logl);
 }
 
+__global__ __launch_bounds__(256) void k_const_log_decay(int T_, int H, const float* __restrict__ b_lam,
+                                                         float* __restrict__ logl) {
+  const long total = (long)T_ * H;
+  for (long e = blockIdx.x * 256L + threadIdx.x; e < total; e += (long)gridDim.x * 256L)
+    logl[e] = b_lam ? log_sigmoidf_(b_lam[e % H]) : 0.f;
+}
+
+void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipStream_t s) {
+  const long total = (long)T * H;
+  if (total == 0) return;
+  const int grid = (int)std::min<long>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_const_log_decay, dim3(grid), dim3(256), 0, s, T, H, b_lam, logl);
+}
+
 // ============================================================== projection GEMM
 // Block = 256 tokens x the [Q | K | V] columns (3 dh each) of HPB consecutive
 // heads (the packed per-head panels are contiguous, so HPB heads are one B

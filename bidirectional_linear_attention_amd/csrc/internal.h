@@ -56,6 +56,9 @@ void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, i
                  void* v_out, hipStream_t s, bool phi = true);
 void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
                       const float* b_lam, float* logl, hipStream_t s);
+// log lambda of every token for a decay that does not depend on the token:
+// log sigmoid(b_lam[h]) (b_lam non-null) or 0 (b_lam null)
+void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipStream_t s);
 void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
                           const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s);
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
@@ -65,6 +68,7 @@ void launch_readout(int dt, int dh, const void* qa, const float* saved, const in
                     int max_slots, int H, void* y, hipStream_t s);
 
 // ---- backward
+// w_g may be null (its rows of Wt are zero)
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_g, int d, int H,
                     int dh, int Kp, void* wt, hipStream_t s);
 void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const float* saved, const int* nchunks,
@@ -77,6 +81,7 @@ int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
+// dw_g may be null (its columns are not written)
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_g, hipStream_t s);
 void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,

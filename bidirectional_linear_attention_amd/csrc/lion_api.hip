@@ -97,7 +97,9 @@ gbla_status check_problem(const lion_problem* p) {
   if (!p) return GBLA_ERR_NULL_ARG;
   if (p->dtype != GBLA_DTYPE_F32 && p->dtype != GBLA_DTYPE_BF16) return GBLA_ERR_UNSUPPORTED;
   if (p->head_dim != 32 && p->head_dim != 64) return GBLA_ERR_UNSUPPORTED;
-  if (p->chunk != kLionChunk || p->reserved != 0) return GBLA_ERR_UNSUPPORTED;
+  if (p->chunk != kLionChunk) return GBLA_ERR_UNSUPPORTED;
+  if (p->decay != LION_DECAY_SELECTIVE && p->decay != LION_DECAY_FIXED && p->decay != LION_DECAY_NONE)
+    return GBLA_ERR_UNSUPPORTED;
   if (p->num_seqs < 1 || p->total_tokens < 0 || p->num_heads < 1 || p->d_model < 8 || p->d_model % 8 != 0)
     return GBLA_ERR_BAD_SHAPE;
   const long long T = p->total_tokens;
@@ -139,7 +141,9 @@ gbla_status lion_forward(const lion_problem* p, const void* x, const int32_t* cu
                          void* workspace, size_t workspace_bytes, void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
-  if (!cu_seqlens || !w_q || !w_k || !w_v || !w_lam || !b_lam || !workspace) return GBLA_ERR_NULL_ARG;
+  const bool sel = p->decay == LION_DECAY_SELECTIVE, fixed = p->decay == LION_DECAY_FIXED;
+  if (!cu_seqlens || !w_q || !w_k || !w_v || !workspace || (sel && !w_lam) || ((sel || fixed) && !b_lam))
+    return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
   for (const void* a : {x, w_q, w_k, w_v, w_lam, (const void*)y, (const void*)act, (const void*)workspace})
     if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
@@ -160,7 +164,8 @@ gbla_status lion_forward(const lion_problem* p, const void* x, const int32_t* cu
     launch_schedule(cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
   { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
   { StageScope ps(ST_LION_LOG_DECAY, s);
-    launch_log_decay(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, w_lam, b_lam, A.logl, s); }
+    if (sel) launch_log_decay(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, w_lam, b_lam, A.logl, s);
+    else launch_const_log_decay(m.T, m.H, fixed ? b_lam : nullptr, A.logl, s); }
   { StageScope ps(ST_LION_PROJ, s); launch_proj(dt, m.dh, x, w.wp, m.T, m.d, m.H, A.q, A.k, A.v, s, false); }
   { StageScope ps(ST_LION_CHUNK_STATE, s);
     launch_lion_chunk_state(dt, m.dh, 0, A.k, A.v, nullptr, nullptr, A.logl, w.nchunks, w.tab, m.slots, m.H, A.st,
@@ -177,8 +182,9 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
                           float* dw_lam, float* db_lam, void* workspace, size_t workspace_bytes, void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
-  if (!cu_seqlens || !w_q || !w_k || !w_v || !w_lam || !b_lam || !act || !dw_q || !dw_k || !dw_v || !dw_lam ||
-      !db_lam || !workspace)
+  const bool sel = p->decay == LION_DECAY_SELECTIVE, fixed = p->decay == LION_DECAY_FIXED;
+  if (!cu_seqlens || !w_q || !w_k || !w_v || !act || !dw_q || !dw_k || !dw_v || !workspace ||
+      (sel && (!w_lam || !dw_lam)) || ((sel || fixed) && (!b_lam || !db_lam)))
     return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !y || !dy || !dx)) return GBLA_ERR_NULL_ARG;
   for (const void* a : {x, w_q, w_k, w_v, w_lam, act, y, dy, (const void*)dx, (const void*)dw_q, (const void*)dw_k,
@@ -196,7 +202,8 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
   (void)hipGetLastError();
   { StageScope ps(ST_SCHEDULE, s);
     launch_schedule(cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_lam, m.d, m.H, m.dh, m.Kp, w.wt, s); }
+  { StageScope ps(ST_PACK_WT, s);
+    launch_pack_wt(dt, w_q, w_k, w_v, sel ? w_lam : nullptr, m.d, m.H, m.dh, m.Kp, w.wt, s); }
   { StageScope ps(ST_LION_BWD_STATE, s);
     launch_lion_chunk_state(dt, m.dh, 1, A.q, dy, y, A.rsum, A.logl, w.nchunks, w.tab, m.slots, m.H, w.hst, nullptr,
                             s); }
@@ -205,16 +212,19 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
     launch_lion_bwd_token(dt, m.dh, A.q, A.k, A.v, A.logl, y, dy, A.rsum, A.st, w.hst, w.nchunks, w.tab, m.slots,
                           m.H, m.Kp, w.G, w.dA_loc, w.dA_tot, s); }
   { StageScope ps(ST_LION_DA, s);
-    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.slots, m.H, m.D, m.Kp, dt, w.G,
-                   w.db_part, s); }
-  { StageScope ps(ST_LION_DB_REDUCE, s); launch_sum_parts(w.db_part, m.H, 0, w.nchunks, db_lam, s); }
+    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.slots, m.H, m.D, m.Kp, dt, sel,
+                   w.G, w.db_part, s); }
+  if (sel || fixed) {
+    StageScope ps(ST_LION_DB_REDUCE, s);
+    launch_sum_parts(w.db_part, m.H, 0, w.nchunks, db_lam, s);
+  }
   if (m.T > 0) {
     StageScope ps(ST_GEMM_DX, s);
     launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, dx, s);
   }
   { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, x, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
   { StageScope ps(ST_DW_REDUCE, s);
-    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_lam, s); }
+    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, sel ? dw_lam : nullptr, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 

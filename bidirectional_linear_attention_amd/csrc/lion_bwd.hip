@@ -367,8 +367,9 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
 // 3 D + h. Two launches:
 //   k_lion_dsuffix  one wave per (sequence, head): chunk totals -> exclusive
 //                   suffix sums over the sequence's chunks, in place
-//   k_lion_da       one block per chunk: da for every token and head, the zero
-//                   padding of G, and the chunk's per-head sum of da (db partial)
+//   k_lion_da       one block per chunk: da for every token and head (written to G
+//                   when the decay depends on x, else 0), the zero padding of G,
+//                   and the chunk's per-head sum of da (db partial)
 __global__ __launch_bounds__(256) void k_lion_dsuffix(float* __restrict__ dA_tot, const int* __restrict__ nchunks,
                                                       const int* __restrict__ chunk_off, int N, int H) {
   const int lane = threadIdx.x & 63;
@@ -397,7 +398,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl, const float* __restrict__ dA_loc,
                                                  const float* __restrict__ dA_tot, const int* __restrict__ nchunks,
                                                  const Chunk* __restrict__ tab, int H, int D, int Kp,
-                                                 T* __restrict__ G, float* __restrict__ db_part) {
+                                                 int write_da, T* __restrict__ G, float* __restrict__ db_part) {
   constexpr int C = kLionChunk;
   const int slot = blockIdx.x;
   if (slot >= *nchunks) return;
@@ -410,7 +411,7 @@ __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl,
     if (ok) {
       const float ll = logl[(size_t)t * H + h];
       da = (dA_loc[(size_t)t * H + h] + dA_tot[(size_t)slot * H + h]) * -expm1f(ll);
-      G[(size_t)t * Kp + 3 * D + h] = from_f<T>(da);
+      G[(size_t)t * Kp + 3 * D + h] = from_f<T>(write_da ? da : 0.f);
     }
     float sum = da;
 #pragma unroll
@@ -425,15 +426,15 @@ __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl,
 }
 
 void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
-                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, void* G, float* db_part,
-                    hipStream_t s) {
+                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G,
+                    float* db_part, hipStream_t s) {
   hipLaunchKernelGGL(k_lion_dsuffix, dim3((N * H + 3) / 4), dim3(256), 0, s, dA_tot, nchunks, chunk_off, N, H);
   if (dt == BF16)
     hipLaunchKernelGGL(k_lion_da<bf16>, dim3(max_slots), dim3(256), 0, s, logl, dA_loc, dA_tot, nchunks, tab, H, D,
-                       Kp, (bf16*)G, db_part);
+                       Kp, (int)write_da, (bf16*)G, db_part);
   else
     hipLaunchKernelGGL(k_lion_da<float>, dim3(max_slots), dim3(256), 0, s, logl, dA_loc, dA_tot, nchunks, tab, H, D,
-                       Kp, (float*)G, db_part);
+                       Kp, (int)write_da, (float*)G, db_part);
 }
 
 }  // namespace gbla

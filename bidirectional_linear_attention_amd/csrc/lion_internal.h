@@ -66,7 +66,7 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
 // da into G (and its zero padding) and per-chunk partial sums of da [slot][H]
 // (sum them over the first *nchunks slots); dA_tot is overwritten
 void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
-                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, void* G, float* db_part,
-                    hipStream_t s);
+                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G,
+                    float* db_part, hipStream_t s);
 
 }  // namespace gbla

@@ -1,11 +1,12 @@
-"""LION-s layer of libgbla.so (C ABI in include/lion.h).
+"""LION layers of libgbla.so (C ABI in include/lion.h).
 
-Selective-decay bidirectional linear attention of "Linear Attention for
+Bidirectional linear attention with a decay mask, from "Linear Attention for
 Efficient Bidirectional Sequence Modeling" (method details: bidirectional mask
-M = M^F + M^B - I, chunkwise form; Lion-s row of the model table; feature map
-(SiLU + 0.5) / ||.||): q, k, v = x W, lambda = sigmoid(x w_lam + b_lam),
-y = Scale((phi(Q) phi(K)^T) (.) M) V with row normalisation, per packed
-sequence and head. `lion_forward` / `lion_backward` mirror the C entry points
+M = M^F + M^B - I, chunkwise form; the model table's Lion-s, Lion-d and
+Lion-lit; feature map (SiLU + 0.5) / ||.||): q, k, v = x W, lambda =
+sigmoid(x w_lam + b_lam) (decay "s"), sigmoid(b_lam) per head (decay "d") or 1
+(decay "lit"), y = Scale((phi(Q) phi(K)^T) (.) M) V with row normalisation, per
+packed sequence and head. `lion_forward` / `lion_backward` mirror the C entry points
 (device pointers and the current HIP stream only); `forward` / `backward`
 allocate outputs, cache and workspace. Every step runs in the HIP library.
 """
@@ -14,7 +15,7 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import DTYPE_BF16, DTYPE_F32, LionProblem
+from ._lib import DTYPE_BF16, DTYPE_F32, LION_DECAY, LionProblem
 
 __all__ = ["LionProblem", "problem", "workspace_size", "activation_size", "lion_forward", "lion_backward",
            "forward", "backward"]
@@ -27,8 +28,10 @@ def _torch():
     return torch
 
 
-def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype) -> LionProblem:
-    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code."""
+def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype,
+            decay: str = "s") -> LionProblem:
+    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code; decay is
+    "s" (Lion-s), "d" (Lion-d) or "lit" (Lion-lit)."""
     if isinstance(dtype, int):
         code = dtype
     else:
@@ -39,7 +42,8 @@ def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head
             code = DTYPE_BF16
         else:
             raise TypeError(f"unsupported dtype {dtype}: float32 or bfloat16")
-    return LionProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code, CHUNK, 0)
+    return LionProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code, CHUNK,
+                       LION_DECAY[decay])
 
 
 def workspace_size(p: LionProblem, backward: bool) -> int:
@@ -93,29 +97,32 @@ def lion_backward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, ac
     _lib.check(st, "lion_backward")
 
 
-def _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads):
+def _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads, decay):
     torch = _torch()
     T, d = x.shape
     D = w_q.shape[1]
     if D % num_heads:
         raise ValueError("w_q columns must be a multiple of num_heads")
-    for name, t, shape in (("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)), ("w_v", w_v, (d, D)),
-                           ("w_lam", w_lam, (num_heads, d))):
-        if tuple(t.shape) != shape or t.dtype != x.dtype:
-            raise ValueError(f"{name}: expected {shape} {x.dtype}, got {tuple(t.shape)} {t.dtype}")
-    if b_lam.dtype != torch.float32 or tuple(b_lam.shape) != (num_heads,):
+    checks = [("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)), ("w_v", w_v, (d, D))]
+    if decay == "s":
+        checks.append(("w_lam", w_lam, (num_heads, d)))
+    for name, t, shape in checks:
+        if t is None or tuple(t.shape) != shape or t.dtype != x.dtype:
+            raise ValueError(f"{name}: expected {shape} {x.dtype}")
+    if decay in ("s", "d") and (b_lam is None or b_lam.dtype != torch.float32 or tuple(b_lam.shape) != (num_heads,)):
         raise ValueError("b_lam must be float32 [num_heads]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be int32 [N+1]")
-    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype)
+    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype, decay)
 
 
 def forward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads: int, workspace=None,
-            save_activations: bool = True):
+            save_activations: bool = True, decay: str = "s"):
     """Allocate y, the activation cache (if save_activations) and the workspace
-    (unless given) and run lion_forward. Returns (y [T, H*d_h], act or None)."""
+    (unless given) and run lion_forward. w_lam is used by decay "s" only, b_lam
+    by "s" and "d" (pass None otherwise). Returns (y [T, H*d_h], act or None)."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads)
+    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads, decay)
     dev = x.device
     y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
     act = torch.empty(activation_size(p), dtype=torch.uint8, device=dev) if save_activations else None
@@ -125,18 +132,21 @@ def forward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads: int, workspac
     return y, act
 
 
-def backward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, num_heads: int, workspace=None) -> dict:
+def backward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, num_heads: int, workspace=None,
+             decay: str = "s") -> dict:
     """Allocate the gradients (and the workspace unless given) and run
-    lion_backward. Returns dict dx, dw_q, dw_k, dw_v, dw_lam, db_lam."""
+    lion_backward. Returns dict dx, dw_q, dw_k, dw_v and, as the decay has
+    them, dw_lam ("s") and db_lam ("s", "d")."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads)
+    p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads, decay)
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty_like(x), dw_q=torch.empty(w_q.shape, **f32), dw_k=torch.empty(w_k.shape, **f32),
-             dw_v=torch.empty(w_v.shape, **f32), dw_lam=torch.empty(w_lam.shape, **f32),
-             db_lam=torch.empty(b_lam.shape, **f32))
+             dw_v=torch.empty(w_v.shape, **f32),
+             dw_lam=torch.empty((num_heads, x.shape[1]), **f32) if decay == "s" else None,
+             db_lam=torch.empty((num_heads,), **f32) if decay in ("s", "d") else None)
     if workspace is None:
         workspace = torch.empty(workspace_size(p, True), dtype=torch.uint8, device=dev)
     lion_backward(p, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, g["dx"], g["dw_q"], g["dw_k"],
                   g["dw_v"], g["dw_lam"], g["db_lam"], workspace)
-    return g
+    return {k: v for k, v in g.items() if v is not None}

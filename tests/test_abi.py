@@ -128,14 +128,14 @@ def test_backward_rejects_null_and_small_workspace_without_launching():
 # ---------------------------------------------------------------- LION-s entry points
 def _lprob(**kw):
     base = dict(num_seqs=2, total_tokens=100, d_model=64, num_heads=2, head_dim=64, dtype=gb.DTYPE_BF16,
-                chunk=64, reserved=0)
+                chunk=64, decay=0)
     base.update(kw)
     return _lib.LionProblem(*(base[k] for k in ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim",
-                                                "dtype", "chunk", "reserved")))
+                                                "dtype", "chunk", "decay")))
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(chunk=32), 3), (dict(reserved=1), 3),
+    (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(chunk=32), 3), (dict(decay=3), 3), (dict(decay=-1), 3),
     (dict(d_model=60), 2), (dict(num_seqs=0), 2), (dict(total_tokens=-1), 2), (dict(num_heads=0), 2),
     (dict(total_tokens=1 << 30), 2),
 ])
@@ -194,3 +194,26 @@ def test_lion_backward_requires_the_activation_cache():
     args[15] = _fake(0x1f002)  # misaligned db_lam
     assert lib.lion_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
     assert lib.lion_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5
+
+
+@pytest.mark.parametrize("decay,null_ok,null_bad", [
+    (1, [5], [6]),        # Lion-d: no w_lam; b_lam (the per-head logit) required
+    (2, [5, 6], []),      # Lion-lit: neither
+])
+def test_lion_fixed_and_no_decay_argument_rules(decay, null_ok, null_bad):
+    """w_lam (argument 5) and b_lam (6) may be NULL where the decay does not use
+    them; the forward then only fails on the workspace size (nothing launched)."""
+    lib = _lib.load()
+    p = _lprob(decay=decay)
+    out = ctypes.c_size_t()
+    assert lib.lion_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(9)]
+    args = list(a)
+    for i in null_ok:
+        args[i] = None
+    assert lib.lion_forward(ctypes.byref(p), *args, _fake(0x900000), need - 1, None) == 5
+    for i in null_bad:
+        bad = list(a)
+        bad[i] = None
+        assert lib.lion_forward(ctypes.byref(p), *bad, _fake(0x900000), need, None) == 1

@@ -184,3 +184,41 @@ def test_no_tokens():
     assert out["y"].shape == (0, 128)
     for k in ("dw_q", "dw_k", "dw_v", "dw_lam", "db_lam"):
         assert np.all(out[k] == 0), k
+
+
+# ------------------------------------------------------------ Lion-d and Lion-lit (the other two decays)
+
+def run_gpu_decay(inp, decay, b):
+    """decay "d": lambda^h = sigmoid(b[h]); "lit": lambda = 1. No w_lam."""
+    d = to_dev(inp)
+    H = inp["H"]
+    bl = torch.from_numpy(b).float().to("cuda") if b is not None else None
+    y, act = gl.forward(d["x"], d["cu"], d["w_q"], d["w_k"], d["w_v"], None, bl, H, decay=decay)
+    g = gl.backward(d["x"], d["cu"], d["w_q"], d["w_k"], d["w_v"], None, bl, act, y, d["dy"], H, decay=decay)
+    torch.cuda.synchronize()
+    out = {"y": y}
+    out.update(g)
+    return {k: v.float().cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("decay", ["d", "lit"])
+def test_fixed_and_no_decay_match_the_oracle(decay, dtype):
+    """Lion-d is the oracle's selective form with w_lam = 0 (the logit is b_lam
+    for every token: M_ij = lambda^|i-j|); Lion-lit is lambda = 1 (b_lam = +inf,
+    M = 1). Compared: y, dx, dW_Q, dW_K, dW_V and, for Lion-d, db_lam."""
+    w = small_variant(LION, (300, 65, 1, 130), d_model=96, num_heads=3, dtype=dtype, seed=59)
+    inp = make_inputs(w)
+    H = inp["H"]
+    b = np.random.default_rng(60).uniform(0.0, 4.0, size=H).astype(np.float32) if decay == "d" else None
+    gpu = run_gpu_decay(inp, decay, b)
+    ob = b if decay == "d" else np.full(H, np.inf, np.float32)
+    args = [inp["x"], inp["cu_seqlens"], inp["w_q"], inp["w_k"], inp["w_v"], np.zeros_like(inp["w_lam"]), ob]
+    errs = {"y": rel_err(gpu["y"], ol.forward_full(*args, H))}
+    g = ol.backward_full(*args, inp["dy"], H)
+    for k in ("dx", "dw_q", "dw_k", "dw_v") + (("db_lam",) if decay == "d" else ()):
+        errs[k] = rel_err(gpu[k], g[k])
+    print(f"\n[Lion-{decay} {dtype}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    assert set(gpu) == {"y", "dx", "dw_q", "dw_k", "dw_v"} | ({"db_lam"} if decay == "d" else set())
+    bad = {k: v for k, v in errs.items() if not v <= TOL[dtype]}
+    assert not bad, bad
