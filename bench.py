@@ -13,9 +13,10 @@ measured live with the library's HIP events on the launch stream, recorded in
 the timed region around that stage only (a pass before it, with events around
 every stage, gives stage_ms_per_step and picks the dominant stage), and the
 float64 CPU oracle timed on a bounded sample of the same workload.
-The same line carries secondary measurements of the LION layers (16 x 4096
-tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under "lion_s",
-"lion_d" and "lion_lit" (selective, fixed per-head and no decay).
+The same line carries secondary measurements: the same GBLA workload with the
+softmax-over-the-sequence key gate under "gbla_softmax", and the LION layers
+(16 x 4096 tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under
+"lion_s", "lion_d" and "lion_lit" (selective, fixed per-head and no decay).
 
 --copy-calibration instead times a plain device-to-device copy of a known size
 (for scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
@@ -158,6 +159,65 @@ def copy_calibration(mib=1024, reps=3):
           flush=True)
 
 
+def gbla_setup(torch, gb, gate):
+    """Device buffers and the step function of the GBLA workload (x and dy
+    rotate over three buffer sets)."""
+    import numpy as np
+
+    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
+
+    w = WORKLOADS[WORKLOAD]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    esz = 2 if w.dtype == "bf16" else 4
+
+    def t(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt).contiguous()
+
+    T, N, d, H, dh = inp["T"], inp["N"], inp["d"], inp["H"], inp["dh"]
+    D = H * dh
+    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+    conv_w, w_q, w_k, w_v, w_g = (t(inp[k]) for k in ("conv_w", "w_q", "w_k", "w_v", "w_g"))
+    b_g = torch.from_numpy(inp["b_g"]).float().to(dev)
+    n_sets = 3
+    xs = [t(inp["x"]) for _ in range(n_sets)]
+    dys = [t(inp["dy"]) for _ in range(n_sets)]
+    p = gb.problem(N, T, d, H, dh, dt, gate)
+    y = torch.empty((T, D), dtype=dt, device=dev)
+    saved = torch.empty(gb.saved_size(p) // 4, dtype=torch.float32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty((T, d), dtype=dt, device=dev)
+    dconv = torch.empty((d, 4), **f32)
+    dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
+    dwg, dbg = torch.empty((H, d), **f32), torch.empty((H,), **f32)
+    ws = torch.empty(max(gb.workspace_size(p, False), gb.workspace_size(p, True)), dtype=torch.uint8, device=dev)
+    act = torch.empty(gb.activation_size(p), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        x, dy = xs[i % n_sets], dys[i % n_sets]
+        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws)
+        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
+                         dbg, ws)
+
+    return dict(w=w, inp=inp, step=step, T=T, N=N, d=d, H=H, dh=dh, esz=esz)
+
+
+def gbla_softmax_leg(steps, warmup):
+    """The same GBLA workload with the softmax-over-the-sequence key gate."""
+    import torch
+
+    import bidirectional_linear_attention_amd as gb
+
+    g = gbla_setup(torch, gb, "softmax")
+    elapsed, breakdown, _ = timed_passes(gb, torch, g["step"], steps, warmup, lambda br: [])
+    T = g["T"]
+    return {"workload": g["w"].name, "gate": "softmax over the sequence", "tokens_per_step": T, "steps": steps,
+            "warmup": warmup, "tokens_per_s": round(T * steps / elapsed, 1),
+            "ms_per_step": round(1e3 * elapsed / steps, 4),
+            "stage_ms_per_step": {k: round(v[0], 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])}}
+
+
 def lion_leg(steps, warmup, decay="s"):
     """LION forward+backward on the 16 x 4096 workload: tokens/s and stage times.
     decay "s" (Lion-s), "d" (Lion-d: the workload's b_lam as the per-head logit)
@@ -217,7 +277,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-sample-seqs", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--lion-steps", type=int, default=10, help="LION-s steps timed after the main run (0: skip)")
+    ap.add_argument("--lion-steps", type=int, default=10,
+                    help="steps of each secondary leg (softmax-gate GBLA, Lion-s/d/lit) after the main run (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -228,45 +289,14 @@ def main():
         copy_calibration()
         return
 
-    import numpy as np
     import torch
 
     import bidirectional_linear_attention_amd as gb
-    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
 
-    w = WORKLOADS[WORKLOAD]
-    inp = make_inputs(w)
-    dev = torch.device("cuda:0")
-    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    esz = 2 if w.dtype == "bf16" else 4
-
-    def t(a):
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt).contiguous()
-
-    T, N, d, H, dh = inp["T"], inp["N"], inp["d"], inp["H"], inp["dh"]
+    g = gbla_setup(torch, gb, "sigmoid")
+    w, inp, step = g["w"], g["inp"], g["step"]
+    T, N, d, H, dh, esz = (g[k] for k in ("T", "N", "d", "H", "dh", "esz"))
     D = H * dh
-    cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
-    conv_w, w_q, w_k, w_v, w_g = (t(inp[k]) for k in ("conv_w", "w_q", "w_k", "w_v", "w_g"))
-    b_g = torch.from_numpy(inp["b_g"]).float().to(dev)
-    n_sets = 3
-    xs = [t(inp["x"]) for _ in range(n_sets)]
-    dys = [t(inp["dy"]) for _ in range(n_sets)]
-    p = gb.problem(N, T, d, H, dh, dt)
-    y = torch.empty((T, D), dtype=dt, device=dev)
-    saved = torch.empty((N, H, dh * dh + dh), dtype=torch.float32, device=dev)
-    f32 = dict(dtype=torch.float32, device=dev)
-    dx = torch.empty((T, d), dtype=dt, device=dev)
-    dconv = torch.empty((d, 4), **f32)
-    dwq, dwk, dwv = (torch.empty((d, D), **f32) for _ in range(3))
-    dwg, dbg = torch.empty((H, d), **f32), torch.empty((H,), **f32)
-    ws = torch.empty(max(gb.workspace_size(p, False), gb.workspace_size(p, True)), dtype=torch.uint8, device=dev)
-    act = torch.empty(gb.activation_size(p), dtype=torch.uint8, device=dev)
-
-    def step(i):
-        x, dy = xs[i % n_sets], dys[i % n_sets]
-        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws)
-        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
-                         dbg, ws)
 
     def dominant(br):
         timed = {k: v for k, v in br.items() if stage_work(k, T, N, d, H, dh, esz)}
@@ -311,7 +341,9 @@ def main():
         "stage_ms_per_step": {k: round(v, 4) for k, v in sorted(per_step.items(), key=lambda kv: -kv[1])},
     }
     if args.lion_steps > 0:
-        del xs, dys, ws, act
+        del g, step
+        torch.cuda.empty_cache()
+        out["gbla_softmax"] = gbla_softmax_leg(args.lion_steps, min(args.warmup, 3))
         torch.cuda.empty_cache()
         out["lion_s"] = lion_leg(args.lion_steps, min(args.warmup, 3))
         for dec in ("d", "lit"):

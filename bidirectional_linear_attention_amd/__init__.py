@@ -8,7 +8,8 @@ library's HIP kernels; if the library is missing an error is raised.
 
 The layer is Eqs. (4)-(6) of "Gated Bidirectional Linear Attention for
 Generative Retrieval" (core method): causal depthwise Conv1d (kernel 4), per-head
-Q/K/V projections, phi = elu + 1, sigmoid key gate, global state
+Q/K/V projections, phi = elu + 1, key gate (per-token sigmoid, or the softmax
+over the sequence that Eq. (5) writes), global state
 S = sum_j g_j phi(k_j) v_j^T, z = sum_j g_j phi(k_j), readout
 y_i = phi(q_i)^T S / phi(q_i)^T z, on packed variable-length sequences.
 """
@@ -17,7 +18,7 @@ from __future__ import annotations
 import ctypes
 
 from . import _lib
-from ._lib import DTYPE_BF16, DTYPE_F32, GATE_SIGMOID, GblaError, GblaProblem
+from ._lib import DTYPE_BF16, DTYPE_F32, GATES, GblaError, GblaProblem
 
 __all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "activation_size", "gbla_forward",
            "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "stage_names", "DTYPE_F32", "DTYPE_BF16"]
@@ -37,11 +38,13 @@ def _dtype_code(dt) -> int:
     raise TypeError(f"unsupported dtype {dt}: float32 or bfloat16")
 
 
-def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype) -> GblaProblem:
-    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code."""
+def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype,
+            gate: str = "sigmoid") -> GblaProblem:
+    """Problem descriptor; dtype is a torch dtype or a DTYPE_* code, gate
+    "sigmoid" or "softmax"."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return GblaProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code,
-                       GATE_SIGMOID, 4)
+                       GATES[gate], 4)
 
 
 def saved_size(p: GblaProblem) -> int:
@@ -99,7 +102,7 @@ def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g
     _lib.check(st, "gbla_backward")
 
 
-def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads):
+def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate):
     torch = _torch()
     T, d = x.shape
     D = w_q.shape[1]
@@ -113,20 +116,23 @@ def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads):
         raise ValueError("b_g must be float32 [num_heads]")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be int32 [N+1]")
-    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype)
+    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype, gate)
 
 
 def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, workspace=None,
-            save_activations: bool = True):
+            save_activations: bool = True, gate: str = "sigmoid"):
     """Allocate y, saved, the activation cache (if save_activations) and the
     workspace (unless given) and run gbla_forward.
-    Returns (y [T, H*d_h], saved [N, H, d_h*d_h + d_h] float32, act or None)."""
+    Returns (y [T, H*d_h], saved, act or None); saved is float32
+    [N, H, d_h*d_h + d_h] for the sigmoid gate and flat (states, then the N*H
+    logit maxima, as gbla_saved_size describes) for the softmax gate."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate)
     dev = x.device
     y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
-    saved = torch.empty((p.num_seqs, p.num_heads, p.head_dim * p.head_dim + p.head_dim), dtype=torch.float32,
-                        device=dev)
+    E = p.head_dim * p.head_dim + p.head_dim
+    shape = (p.num_seqs, p.num_heads, E) if gate == "sigmoid" else (p.num_seqs * p.num_heads * (E + 1),)
+    saved = torch.empty(shape, dtype=torch.float32, device=dev)
     act = torch.empty(activation_size(p), dtype=torch.uint8, device=dev) if save_activations else None
     if workspace is None:
         workspace = torch.empty(workspace_size(p, False), dtype=torch.uint8, device=dev)
@@ -135,12 +141,14 @@ def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, work
 
 
 def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num_heads: int,
-             workspace=None) -> dict:
+             workspace=None, gate: str = "sigmoid") -> dict:
     """Allocate the gradients (and the workspace unless given) and run
     gbla_backward; act is forward's activation cache or None (recompute).
     Returns dict dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads)
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate)
+    if saved.numel() * 4 != saved_size(p):
+        raise ValueError("saved does not match the problem (gate?)")
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty_like(x), dconv_w=torch.empty(conv_w.shape, **f32), dw_q=torch.empty(w_q.shape, **f32),

@@ -16,6 +16,8 @@ STATUS = {
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LION_DECAY = {"s": 0, "d": 1, "lit": 2}  # selective, fixed per head, none
 GATE_SIGMOID = 0
+GATE_SOFTMAX = 1
+GATES = {"sigmoid": GATE_SIGMOID, "softmax": GATE_SOFTMAX}
 
 
 class GblaError(RuntimeError):

@@ -22,7 +22,8 @@ struct Carver {
 
 struct Dims {
   int N, T, d, H, dh, D, E, NP, Kp, slots, nsplit, conv_rb;
-  size_t esz;  // bytes per activation element
+  bool softmax;  // softmax key gate: the gate array holds logits, saved ends with the logit maxima
+  size_t esz;    // bytes per activation element
 };
 
 Dims dims_of(const gbla_problem* p) {
@@ -34,6 +35,7 @@ Dims dims_of(const gbla_problem* p) {
   m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
   m.conv_rb = conv_bwd_row_blocks(m.T);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
+  m.softmax = p->gate == GBLA_GATE_SOFTMAX;
   return m;
 }
 
@@ -58,7 +60,7 @@ size_t act_bytes(const Dims& m) {
 }
 
 struct FwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wp; float* partial; Act act;
+  int* nchunks; int* chunk_off; Chunk* tab; void* wp; float* partial; float* mpart; Act act;
 };
 struct BwdWs {
   int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
@@ -75,6 +77,7 @@ size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
+  t.mpart = m.softmax ? c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H) : nullptr;
   t.act = carve_act(m, c, base);
   if (w) *w = t;
   return c.off;
@@ -104,7 +107,8 @@ gbla_status check_problem(const gbla_problem* p) {
   if (!p) return GBLA_ERR_NULL_ARG;
   if (p->dtype != GBLA_DTYPE_F32 && p->dtype != GBLA_DTYPE_BF16) return GBLA_ERR_UNSUPPORTED;
   if (p->head_dim != 32 && p->head_dim != 64) return GBLA_ERR_UNSUPPORTED;
-  if (p->gate != GBLA_GATE_SIGMOID || p->conv_width != 4) return GBLA_ERR_UNSUPPORTED;
+  if ((p->gate != GBLA_GATE_SIGMOID && p->gate != GBLA_GATE_SOFTMAX) || p->conv_width != 4)
+    return GBLA_ERR_UNSUPPORTED;
   if (p->num_seqs < 1 || p->total_tokens < 0 || p->num_heads < 1 || p->d_model < 8 || p->d_model % 8 != 0)
     return GBLA_ERR_BAD_SHAPE;
   const long long T = p->total_tokens;
@@ -134,13 +138,14 @@ const char* gbla_status_string(int status) {
   }
 }
 
-int gbla_version(void) { return 2; }
+int gbla_version(void) { return 3; }
 
 gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes) {
   if (!bytes) return GBLA_ERR_NULL_ARG;
   const gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
-  *bytes = sizeof(float) * (size_t)p->num_seqs * p->num_heads * (p->head_dim * p->head_dim + p->head_dim);
+  const size_t NH = (size_t)p->num_seqs * p->num_heads;
+  *bytes = sizeof(float) * NH * (p->head_dim * p->head_dim + p->head_dim + (p->gate == GBLA_GATE_SOFTMAX ? 1 : 0));
   return GBLA_OK;
 }
 
@@ -187,11 +192,13 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
   { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
   { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
   { StageScope ps(ST_CONV_FWD, s);
-    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, A.xt, A.ga, s); }
+    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
   { StageScope ps(ST_PROJ_FWD, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
   { StageScope ps(ST_STATE_PARTIAL, s);
-    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, s); }
-  { StageScope ps(ST_COMBINE_STATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s); }
+    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, w.mpart, s); }
+  { StageScope ps(ST_COMBINE_STATE, s);  // softmax gate: the logit maxima follow the N*H states
+    launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
+                   m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr); }
   { StageScope ps(ST_READOUT, s); launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
@@ -230,14 +237,15 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
   if (!act) {  // recompute x~, g, phi(q), phi(k), v into the workspace
     { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
     { StageScope ps(ST_CONV_RECOMPUTE, s);
-      launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, A.xt, A.ga, s); }
+      launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
     { StageScope ps(ST_PROJ_RECOMPUTE, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
   }
   { StageScope ps(ST_BWD_DSTATE, s);
     launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s); }
   { StageScope ps(ST_COMBINE_DSTATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s); }
   { StageScope ps(ST_BWD_TOKEN, s);
-    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part, s); }
+    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part,
+                     m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
   { StageScope ps(ST_DBG_REDUCE, s); launch_sum_parts(w.dbg_part, m.H, 0, w.nchunks, db_g, s); }
   if (m.T > 0) {
     { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }

@@ -230,12 +230,12 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 //   dg = phi(k) . dk~,  dk = g dk~ (.) phi'(k),  ds = dg g (1 - g)
 // dk and dv are staged over the wave's own phi(k) and v rows and written to G
 // with 16-byte stores.
-template <typename T, int DH>
+template <typename T, int DH, bool SOFTMAX>
 __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, const T* __restrict__ va,
                                                    const float* __restrict__ ga, const float* __restrict__ dsz,
                                                    const int* __restrict__ nchunks, const Chunk* __restrict__ tab,
                                                    int max_slots, int H, int Kp, T* __restrict__ G,
-                                                   float* __restrict__ dbg_part) {
+                                                   float* __restrict__ dbg_part, const float* __restrict__ gmax) {
   constexpr int FB = DH / 16;
   constexpr int LD = DH + 16 / (int)sizeof(T);
   constexpr int P = Parts<T>::n;
@@ -275,9 +275,10 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
       pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
       pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
     }
-    if (tid < ST) pg = tb + tid < ch.end ? ga[(size_t)(tb + tid) * H + h] : 0.f;
+    if (tid < ST) pg = tb + tid < ch.end ? ga[(size_t)(tb + tid) * H + h] : 0.f;  // gate or softmax logit
   };
   fetch(ch.start);
+  const float gm = SOFTMAX ? gmax[(size_t)ch.seq * H + h] : 0.f;  // softmax gate: exp(s - largest logit)
   for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
         frag_store(vs + r * LD + c, pv[v]);
       }
     }
-    if (tid < ST) gs[tid] = pg;
+    if (tid < ST) gs[tid] = SOFTMAX ? (tb + tid < ch.end ? __expf(pg - gm) : 0.f) : pg;
     __syncthreads();
     if (tb + ST < ch.end) fetch(tb + ST);
     const float gA = gs[r0 + col];
@@ -331,7 +332,9 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
       dg = row16_sum(dg);
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) dkv[nt][r] = g * dk[nt] * fminf(1.f, kv[nt]);
-      const float ds = dg * g * (1.f - g);
+      // sigmoid gate: dg g (1 - g); softmax gate (unnormalised g, the output is
+      // invariant to the normaliser): dg g
+      const float ds = SOFTMAX ? dg * g : dg * g * (1.f - g);
       if (ok && col == 0) {
         G[(size_t)t * Kp + 3 * D + h] = from_f<T>(ds);
         dbg += ds;
@@ -366,10 +369,17 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
 
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
-                      hipStream_t s) {
+                      const float* gmax, hipStream_t s) {
   const dim3 grid(xcd_grid(max_slots * H));
-#define GBLA_BT(TT, DD) hipLaunchKernelGGL((k_bwd_token<TT, DD>), grid, dim3(256), 0, s, (const TT*)ka, \
-                                           (const TT*)va, ga, dsz, nchunks, tab, max_slots, H, Kp, (TT*)G, dbg_part)
+#define GBLA_BT(TT, DD)                                                                                      \
+  do {                                                                                                       \
+    if (gmax)                                                                                                \
+      hipLaunchKernelGGL((k_bwd_token<TT, DD, true>), grid, dim3(256), 0, s, (const TT*)ka, (const TT*)va, ga, \
+                         dsz, nchunks, tab, max_slots, H, Kp, (TT*)G, dbg_part, gmax);                       \
+    else                                                                                                     \
+      hipLaunchKernelGGL((k_bwd_token<TT, DD, false>), grid, dim3(256), 0, s, (const TT*)ka, (const TT*)va,   \
+                         ga, dsz, nchunks, tab, max_slots, H, Kp, (TT*)G, dbg_part, gmax);                   \
+  } while (0)
   if (dt == BF16) { if (dh == 64) GBLA_BT(bf16, 64); else GBLA_BT(bf16, 32); }
   else            { if (dh == 64) GBLA_BT(float, 64); else GBLA_BT(float, 32); }
 #undef GBLA_BT

@@ -157,13 +157,16 @@ __device__ __forceinline__ float butterfly8(float (&v)[8], int lane) {
 // log(sigmoid(z)) = -softplus(-z), stable for any z
 __device__ __forceinline__ float log_sigmoidf_(float z) { return fminf(z, 0.f) - log1pf(__expf(-fabsf(z))); }
 
-// CONV = true: GBLA, x~ = causal conv(x) is stored and g = sigmoid(x~ w_g + b_g).
-// CONV = false: LION-s decay, x~ = x (nothing stored) and g = log sigmoid(x w_lam + b_lam).
+// CONV = true: GBLA, x~ = causal conv(x) is stored; CONV = false: LION-s, x~ = x
+// (nothing stored). With z = x~ w_g + b_g, g_out gets sigmoid(z) (gmode 0, the
+// sigmoid key gate), z itself (gmode 1, the logit of the softmax key gate) or
+// log sigmoid(z) (gmode 2, the LION-s log decay).
+enum GateMode { kGateSigmoid = 0, kGateLogit = 1, kGateLogSigmoid = 2 };
 template <typename T, bool CONV = true>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
-                                                  T* __restrict__ xt, float* __restrict__ g_out) {
+                                                  int gmode, T* __restrict__ xt, float* __restrict__ g_out) {
   __shared__ float sacc[4][kConvRowsPerWave][8];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_begin = (blockIdx.x * 4 + w) * kConvRowsPerWave;
@@ -232,7 +235,8 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
       const int t = t_begin + row, h = hg + hh;
       if (t < t_end && h < H) {
         const float z = sacc[w][row][hh] + b_g[h];
-        g_out[(size_t)t * H + h] = CONV ? sigmoidf_(z) : log_sigmoidf_(z);
+        g_out[(size_t)t * H + h] =
+            gmode == kGateSigmoid ? sigmoidf_(z) : (gmode == kGateLogit ? z : log_sigmoidf_(z));
       }
     }
     __syncthreads();
@@ -240,16 +244,17 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
 }
 
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
-                     const void* w_g, const float* b_g, void* xt, float* g, hipStream_t s) {
+                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s) {
+  const int gmode = softmax_gate ? kGateLogit : kGateSigmoid;
   const int rows = 4 * kConvRowsPerWave;
   const dim3 grid((T + rows - 1) / rows);
   if (T == 0) return;
   if (dt == BF16)
     hipLaunchKernelGGL((k_conv_fwd<bf16, true>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
-                       (const bf16*)conv_w, (const bf16*)w_g, b_g, (bf16*)xt, g);
+                       (const bf16*)conv_w, (const bf16*)w_g, b_g, gmode, (bf16*)xt, g);
   else
     hipLaunchKernelGGL((k_conv_fwd<float, true>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
-                       (const float*)conv_w, (const float*)w_g, b_g, (float*)xt, g);
+                       (const float*)conv_w, (const float*)w_g, b_g, gmode, (float*)xt, g);
 }
 
 void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
@@ -260,10 +265,10 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
   // no conv in this mode: the conv-tap pointer is never dereferenced
   if (dt == BF16)
     hipLaunchKernelGGL((k_conv_fwd<bf16, false>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
-                       (const bf16*)w_lam, (const bf16*)w_lam, b_lam, (bf16*)nullptr, logl);
+                       (const bf16*)w_lam, (const bf16*)w_lam, b_lam, (int)kGateLogSigmoid, (bf16*)nullptr, logl);
   else
     hipLaunchKernelGGL((k_conv_fwd<float, false>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
-                       (const float*)w_lam, (const float*)w_lam, b_lam, (float*)nullptr, logl);
+                       (const float*)w_lam, (const float*)w_lam, b_lam, (int)kGateLogSigmoid, (float*)nullptr, logl);
 }
 
 __global__ __launch_bounds__(256) void k_const_log_decay(int T_, int H, const float* __restrict__ b_lam,
@@ -386,11 +391,14 @@ void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, i
 // consecutive tokens per feature, are read with the transposing LDS read. The
 // appended ones column makes the last output column the normaliser z. Each wave
 // owns whole 16x16 output tiles, so no cross-wave reduction is needed.
-template <typename T, int DH>
+// With the softmax key gate, ga holds the logits s: the chunk's largest logit m
+// goes to mpart and the partial uses exp(s - m) (every exponent <= 0); the
+// combine rescales the partials to the sequence's largest logit.
+template <typename T, int DH, bool SOFTMAX>
 __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka, const T* __restrict__ va,
                                                        const float* __restrict__ ga, const int* __restrict__ nchunks,
                                                        const Chunk* __restrict__ tab, int max_slots, int H,
-                                                       float* __restrict__ partial) {
+                                                       float* __restrict__ partial, float* __restrict__ mpart) {
   constexpr int FB = DH / 16, NB = FB + 1;     // key-feature blocks; value blocks + ones block
   constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
   constexpr int ST = 64;                       // tokens per staged tile
@@ -424,20 +432,33 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
       const bool ok = it < ST * V8 && t < ch.end;
       const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      pg[v] = ok ? ga[(size_t)t * H + h] : 0.f;
+      pg[v] = ok ? ga[(size_t)t * H + h] : 0.f;  // the gate, or the softmax gate's logit
       pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
       pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
     }
   };
   fetch(ch.start);
+  float gmax = 0.f;  // softmax gate: largest logit of the chunk (reduced while the first tile loads)
+  if constexpr (SOFTMAX) {
+    __shared__ float wmax[4];
+    float m = -INFINITY;
+    for (int t = ch.start + tid; t < ch.end; t += 256) m = fmaxf(m, ga[(size_t)t * H + h]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (lane == 0) wmax[w] = m;
+    __syncthreads();
+    gmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (tid == 0) mpart[(size_t)slot * H + h] = gmax;
+  }
   for (int tb = ch.start; tb < ch.end; tb += ST) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
       if (it < ST * V8) {
+        const float g = SOFTMAX ? (tb + r < ch.end ? __expf(pg[v] - gmax) : 0.f) : pg[v];
         float kt[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kt[j] = pg[v] * frag_get(pk[v], j);  // rounded once, used by S and z alike
+        for (int j = 0; j < 8; ++j) kt[j] = g * frag_get(pk[v], j);  // rounded once, used by S and z alike
         frag_store(ks + r * LDK + c, frag_from<T>(kt));
         frag_store(vs + r * LDV + c, pv[v]);
       }
@@ -476,10 +497,17 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
 }
 
 void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
-                          const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s) {
+                          const Chunk* tab, int max_slots, int H, float* partial, float* mpart, hipStream_t s) {
   const dim3 grid(xcd_grid(max_slots * H));
-#define GBLA_SP(TT, DD) hipLaunchKernelGGL((k_state_partial<TT, DD>), grid, dim3(256), 0, s, (const TT*)ka, \
-                                           (const TT*)va, ga, nchunks, tab, max_slots, H, partial)
+#define GBLA_SP(TT, DD)                                                                                  \
+  do {                                                                                                   \
+    if (mpart)                                                                                           \
+      hipLaunchKernelGGL((k_state_partial<TT, DD, true>), grid, dim3(256), 0, s, (const TT*)ka,          \
+                         (const TT*)va, ga, nchunks, tab, max_slots, H, partial, mpart);                 \
+    else                                                                                                 \
+      hipLaunchKernelGGL((k_state_partial<TT, DD, false>), grid, dim3(256), 0, s, (const TT*)ka,         \
+                         (const TT*)va, ga, nchunks, tab, max_slots, H, partial, mpart);                 \
+  } while (0)
   if (dt == BF16) { if (dh == 64) GBLA_SP(bf16, 64); else GBLA_SP(bf16, 32); }
   else            { if (dh == 64) GBLA_SP(float, 64); else GBLA_SP(float, 32); }
 #undef GBLA_SP
@@ -489,9 +517,13 @@ void launch_state_partial(int dt, int dh, const void* ka, const void* va, const 
 // out[b][h][e] = sum of partial[c][h][e] over the chunks c of sequence b. A
 // block covers 64 elements of one (sequence, head); its four waves take every
 // fourth chunk and the four sums are added in a fixed order (deterministic).
+// With chunk maxima mpart (softmax key gate), partial c is scaled by
+// exp(mpart[c] - M), M the largest of the sequence's chunk maxima, which goes to
+// mout[b][h] (0 for an empty sequence).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int* __restrict__ nchunks,
                                                  const int* __restrict__ chunk_off, int N, int H, int E,
-                                                 float* __restrict__ out) {
+                                                 const float* __restrict__ mpart, float* __restrict__ out,
+                                                 float* __restrict__ mout) {
   __shared__ float red[4][64];
   const int eblocks = (E + 63) / 64;
   const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
@@ -499,18 +531,30 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
   const int e = (blockIdx.x - bh * eblocks) * 64 + lane;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
+  float M = 0.f;
+  if (mpart) {  // every wave reduces the same maximum, its lanes striding over the chunks
+    M = -INFINITY;
+    for (int c = c0 + lane; c < c1; c += 64) M = fmaxf(M, mpart[(size_t)c * H + h]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    if (c0 == c1) M = 0.f;
+    if (mout && blockIdx.x == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
+  }
   float s = 0.f;
   if (e < E)
-    for (int c = c0 + ph; c < c1; c += 4) s += partial[((size_t)c * H + h) * E + e];
+    for (int c = c0 + ph; c < c1; c += 4) {
+      const float p = partial[((size_t)c * H + h) * E + e];
+      s += mpart ? __expf(mpart[(size_t)c * H + h] - M) * p : p;
+    }
   red[ph][lane] = s;
   __syncthreads();
   if (ph == 0 && e < E) out[((size_t)b * H + h) * E + e] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
 }
 
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
-                    float* out, hipStream_t s) {
+                    float* out, hipStream_t s, const float* mpart, float* mout) {
   hipLaunchKernelGGL(k_combine, dim3(((elems + 63) / 64) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N,
-                     H, elems, out);
+                     H, elems, mpart, out, mout);
 }
 
 // out[e] = sum over p < P of in[p * E + e], P = *P_dev if given else P_host.

@@ -50,8 +50,9 @@ void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, 
                      Chunk* tab, hipStream_t s);
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
                       hipStream_t s);
+// g gets sigmoid(x~ w_g + b_g), or the logit itself for the softmax key gate
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
-                     const void* w_g, const float* b_g, void* xt, float* g, hipStream_t s);
+                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s);
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
                  void* v_out, hipStream_t s, bool phi = true);
 void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
@@ -59,10 +60,12 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
 // log lambda of every token for a decay that does not depend on the token:
 // log sigmoid(b_lam[h]) (b_lam non-null) or 0 (b_lam null)
 void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipStream_t s);
+// mpart non-null: softmax key gate (ga holds logits; chunk maxima go to mpart)
 void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
-                          const Chunk* tab, int max_slots, int H, float* partial, hipStream_t s);
+                          const Chunk* tab, int max_slots, int H, float* partial, float* mpart, hipStream_t s);
+// mpart non-null: rescale the partials to the sequence's largest chunk maximum (written to mout)
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
-                    float* out, hipStream_t s);
+                    float* out, hipStream_t s, const float* mpart = nullptr, float* mout = nullptr);
 void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s);
 void launch_readout(int dt, int dh, const void* qa, const float* saved, const int* nchunks, const Chunk* tab,
                     int max_slots, int H, void* y, hipStream_t s);
@@ -73,9 +76,10 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
                     int dh, int Kp, void* wt, hipStream_t s);
 void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const float* saved, const int* nchunks,
                        const Chunk* tab, int max_slots, int H, int Kp, float* partial, void* G, hipStream_t s);
+// gmax non-null: softmax key gate (ga holds logits; the gate is exp(s - gmax[seq][h]))
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
-                      hipStream_t s);
+                      const float* gmax, hipStream_t s);
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s);
 int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);

@@ -9,6 +9,8 @@
  *   x~      = causal depthwise Conv1d(x), kernel 4                (Eq. (4))
  *   q, k, v = x~ W_Q^h, x~ W_K^h, x~ W_V^h                       (Eq. (4), per-head weights)
  *   g_j     = sigmoid(x~_j . w_g^h + b_g^h)                      (key gate of Eq. (5))
+ *          or softmax over the sequence's tokens j of x~_j . w_g^h + b_g^h
+ *             (GBLA_GATE_SOFTMAX: the gate exactly as Eq. (5) writes it)
  *   S       = sum_j g_j phi(k_j) v_j^T,  z = sum_j g_j phi(k_j)  (Eq. (6), phi(u) = elu(u) + 1)
  *   y_i     = phi(q_i)^T S / phi(q_i)^T z                        (Eq. (5), state-first order of Eq. (3))
  *
@@ -65,7 +67,12 @@ typedef enum {
 } gbla_status;
 
 enum { GBLA_DTYPE_F32 = 0, GBLA_DTYPE_BF16 = 1 };
-enum { GBLA_GATE_SIGMOID = 0 };
+/* key gate of Eq. (5): per-token sigmoid, or softmax over the sequence. The
+ * output does not change if every gate of a sequence is scaled by the same
+ * factor, so the softmax gate is evaluated as exp(s_j - m) with m the
+ * sequence's largest logit, and its normaliser never needs to be formed; its
+ * bias gradient db_g is zero up to rounding (the softmax is shift invariant). */
+enum { GBLA_GATE_SIGMOID = 0, GBLA_GATE_SOFTMAX = 1 };
 
 typedef struct {
   int32_t num_seqs;     /* N >= 1 packed sequences (empty sequences allowed) */
@@ -74,7 +81,7 @@ typedef struct {
   int32_t num_heads;    /* H >= 1 */
   int32_t head_dim;     /* d_h: 32 or 64 */
   int32_t dtype;        /* GBLA_DTYPE_F32 or GBLA_DTYPE_BF16 */
-  int32_t gate;         /* GBLA_GATE_SIGMOID */
+  int32_t gate;         /* GBLA_GATE_SIGMOID or GBLA_GATE_SOFTMAX */
   int32_t conv_width;   /* must be 4 */
 } gbla_problem;
 
@@ -86,7 +93,11 @@ GBLA_API int gbla_version(void);
 
 /* Bytes of the `saved` buffer written by gbla_forward and read by
  * gbla_backward: N * H * (d_h*d_h + d_h) float32 values, laid out
- * [N][H][S (d_h x d_h, row i = key feature, column = value feature) | z (d_h)]. */
+ * [N][H][S (d_h x d_h, row i = key feature, column = value feature) | z (d_h)].
+ * With GBLA_GATE_SOFTMAX, S and z are built from the unnormalised gates
+ * exp(s_j - m) (so they are the softmax-gated states times sum_j exp(s_j - m))
+ * and N * H more floats follow: m, the largest gate logit of every (sequence,
+ * head), 0 for an empty sequence. */
 GBLA_API gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes);
 
 /* Bytes of device workspace needed by gbla_forward (backward = 0) or

@@ -171,7 +171,8 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
       dq = dq~ (.) phi'(q),  dk = dphi(k) (.) phi'(k),  ds = dg g (1 - g)  (sigmoid)
     then the projection and conv chain rule of Eq. (4).
 
-    Returns dict with dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g (float64).
+    Returns dict with dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g (float64) and
+    ds [T, H], the gradient with respect to the gate logits s.
     """
     x, w_q, w_k, w_v, w_g, b_g, dy = map(_f64, (x, w_q, w_k, w_v, w_g, b_g, dy))
     H = num_heads
@@ -180,6 +181,7 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
     dxt = np.zeros_like(xt)
     dw_q, dw_k, dw_v = np.zeros_like(w_q), np.zeros_like(w_k), np.zeros_like(w_v)
     dw_g, db_g = np.zeros_like(w_g), np.zeros_like(b_g)
+    ds_all = np.zeros((x.shape[0], H))
     for b in range(len(cu) - 1):
         s0, e0 = int(cu[b]), int(cu[b + 1])
         if e0 == s0:
@@ -215,7 +217,8 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
             dw_v[:, cols] += xb.T @ dv
             dw_g[h] += xb.T @ ds
             db_g[h] += ds.sum()
+            ds_all[s0:e0, h] = ds
             dxt[s0:e0] += dq @ w_q[:, cols].T + dk @ w_k[:, cols].T + dv @ w_v[:, cols].T \
                 + ds[:, None] * w_g[h][None, :]
     dx, dconv = causal_conv_backward(dxt, x, cu, conv_w)
-    return dict(dx=dx, dconv_w=dconv, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_g=dw_g, db_g=db_g)
+    return dict(dx=dx, dconv_w=dconv, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_g=dw_g, db_g=db_g, ds=ds_all)

@@ -62,11 +62,27 @@ def test_unsupported_gate_and_conv_width():
     lib = _lib.load()
     out = ctypes.c_size_t()
     p = _prob()
-    p.gate = 1
+    p.gate = 2
     assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 3
     p = _prob()
     p.conv_width = 3
     assert lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out)) == 3
+
+
+def test_softmax_gate_saved_size_adds_the_logit_maxima():
+    """The softmax gate's saved buffer holds the states and then one logit
+    maximum per (sequence, head)."""
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    p = _prob()
+    p.gate = _lib.GATE_SOFTMAX
+    assert lib.gbla_saved_size(ctypes.byref(p), ctypes.byref(out)) == 0
+    assert out.value == 4 * 2 * 2 * (64 * 64 + 64 + 1)
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    soft = out.value
+    p.gate = _lib.GATE_SIGMOID
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    assert soft >= out.value
 
 
 def test_size_queries_are_consistent():

@@ -41,17 +41,17 @@ def to_dev(inp):
                 b_g=torch.from_numpy(inp["b_g"]).float().to("cuda"), dy=t(inp["dy"]))
 
 
-def run_gpu(inp, backward, keep_act=True):
+def run_gpu(inp, backward, keep_act=True, gate="sigmoid"):
     """keep_act: pass forward's activation cache to the backward; False makes
     the backward recompute the activations from x."""
     d = to_dev(inp)
     H = inp["H"]
     y, saved, act = gb.forward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"], H,
-                               save_activations=keep_act)
+                               save_activations=keep_act, gate=gate)
     out = {"y": y, "saved": saved}
     if backward:
         out.update(gb.backward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"],
-                               saved, act, d["dy"], H))
+                               saved, act, d["dy"], H, gate=gate))
     torch.cuda.synchronize()
     return {k: v.float().cpu().numpy() for k, v in out.items()}
 
@@ -60,19 +60,47 @@ def oracle_args(inp):
     return [inp[k] for k in ("x", "cu_seqlens", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g")]
 
 
-def compare(inp, backward, tol=None, label="", keep_act=True):
+def gate_logit_max(inp):
+    """Largest gate logit of every (sequence, head), 0 for an empty sequence."""
+    xt = og.causal_conv(inp["x"], inp["cu_seqlens"], inp["conv_w"])
+    cu, H = inp["cu_seqlens"], inp["H"]
+    m = np.zeros((inp["N"], H))
+    for b in range(inp["N"]):
+        if cu[b + 1] > cu[b]:
+            m[b] = (xt[cu[b]:cu[b + 1]] @ np.asarray(inp["w_g"], np.float64).T + inp["b_g"]).max(axis=0)
+    return m
+
+
+def compare(inp, backward, tol=None, label="", keep_act=True, gate="sigmoid"):
+    """With the softmax gate the library keeps S and z built from exp(s - m),
+    a per-(sequence, head) multiple of the oracle's; they are compared after
+    dividing both by the sum of z, and the stored m against the largest logit.
+    db_g is zero in exact arithmetic there (shift invariance), so it is held to
+    tol times sum_t |ds_t|, the size of the terms that cancel."""
     tol = TOL[inp["dtype"]] if tol is None else tol
-    gpu = run_gpu(inp, backward, keep_act)
-    y, S, z = og.forward(*oracle_args(inp), inp["H"])
+    gpu = run_gpu(inp, backward, keep_act, gate)
+    y, S, z = og.forward(*oracle_args(inp), inp["H"], gate=gate)
     N, H, dh = inp["N"], inp["H"], inp["dh"]
-    sv = gpu["saved"].reshape(N, H, dh * dh + dh)
-    errs = {"y": rel_err(gpu["y"], y),
-            "S": rel_err(sv[:, :, :dh * dh].reshape(N, H, dh, dh), S),
-            "z": rel_err(sv[:, :, dh * dh:], z)}
+    E = dh * dh + dh
+    sv = gpu["saved"].reshape(-1)[:N * H * E].reshape(N, H, E)
+    gS, gz = sv[:, :, :dh * dh].reshape(N, H, dh, dh), sv[:, :, dh * dh:]
+    if gate == "softmax":
+        def unit(a, zz, axes):
+            tot = zz.sum(axis=-1)
+            return a / np.where(tot == 0, 1.0, tot).reshape(tot.shape + (1,) * axes)
+        gS, gz, S, z = unit(gS, gz, 2), unit(gz, gz, 1), unit(S, z, 2), unit(z, z, 1)
+    errs = {"y": rel_err(gpu["y"], y), "S": rel_err(gS, S), "z": rel_err(gz, z)}
+    if gate == "softmax":
+        m = gpu["saved"].reshape(-1)[N * H * E:].reshape(N, H)
+        errs["m"] = rel_err(m, gate_logit_max(inp))
     if backward:
-        g = og.backward(*oracle_args(inp), inp["dy"], inp["H"])
+        g = og.backward(*oracle_args(inp), inp["dy"], inp["H"], gate=gate)
         for k in GRADS:
-            errs[k] = rel_err(gpu[k], g[k])
+            if gate == "softmax" and k == "db_g":
+                scale = np.abs(g["ds"]).sum(axis=0)
+                errs[k] = float(np.max(np.abs(gpu[k] - g[k]) / np.maximum(scale, 1e-30)))
+            else:
+                errs[k] = rel_err(gpu[k], g[k])
     print(f"\n[{label}] T={inp['T']} N={N} d={inp['d']} H={H} dh={dh} {inp['dtype']}: "
           + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     bad = {k: v for k, v in errs.items() if not v <= tol}
@@ -200,3 +228,43 @@ def test_no_tokens():
     assert np.all(out["saved"] == 0)
     for k in ("dconv_w", "dw_q", "dw_k", "dw_v", "dw_g", "db_g"):
         assert np.all(out[k] == 0), k
+
+
+# ------------------------------------------------------------ softmax-over-the-sequence key gate
+
+@pytest.mark.parametrize("lengths,d,H,dh", [
+    ((3000, 1, 513, 0, 77), 96, 3, 64),      # several 256-token chunks per sequence, ragged tails
+    ((1100, 255, 2), 64, 2, 32),             # head_dim 32
+])
+def test_softmax_gate_f32_multi_chunk(lengths, d, H, dh):
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lengths, d_model=d, num_heads=H, head_dim=dh,
+                      dtype="f32", seed=31)
+    compare(make_inputs(w), backward=True, label="softmax f32 " + str(lengths), gate="softmax")
+
+
+def test_softmax_gate_bf16_long_history_recipe_small():
+    w = small_variant(WORKLOADS["gbla_bf16_B8_L8192_d512"], (2048, 1500), seed=32)
+    compare(make_inputs(w), backward=True, label="softmax bf16 long-history small", gate="softmax")
+
+
+def test_softmax_gate_wide_logits_do_not_overflow():
+    """Logits near 120 and spread over tens of units: exp(s) alone overflows
+    float32, exp(s - m) with the per-chunk and per-sequence maxima does not,
+    and most gates underflow to zero, as they do in the oracle."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (1500, 300, 40), d_model=64, num_heads=2, head_dim=64,
+                      dtype="f32", seed=33)
+    inp = make_inputs(w)
+    inp["w_g"] = inp["w_g"] * 8.0
+    inp["b_g"] = inp["b_g"] + 120.0
+    compare(inp, backward=True, label="softmax f32 wide logits", gate="softmax")
+
+
+def test_softmax_gate_recompute_path():
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (700, 300), d_model=64, num_heads=2, head_dim=64,
+                      dtype="f32", seed=34)
+    compare(make_inputs(w), backward=True, label="softmax f32 recompute", keep_act=False, gate="softmax")
+
+
+def test_softmax_gate_bf16_B8_L8192_d512_full():
+    w = WORKLOADS["gbla_bf16_B8_L8192_d512"]
+    compare(make_inputs(w), backward=True, label=w.name + " softmax", gate="softmax")
