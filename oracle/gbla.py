@@ -10,7 +10,9 @@ Source: "Gated Bidirectional Linear Attention for Generative Retrieval", section
   * 3. GBLA (2) key gating, Eq. (5)/(6): every key is scaled by a per-token
     scalar gate g_j before it enters the state S = sum_j g_j phi(k_j) v_j^T and
     the normaliser z = sum_j g_j phi(k_j).
-  * "多头" (multi-head): every head has its own W_Q^h, W_K^h, W_V^h, w_g^h.
+  * 3. GBLA (3) gated RMSNorm, Eq. (7): the attention output O of every head is
+    RMS-normalised and multiplied by SiLU(X~ W_R^h) (optional, `w_r`).
+  * "多头" (multi-head): every head has its own W_Q^h, W_K^h, W_V^h, w_g^h, W_R^h.
 
 Readings taken where the page leaves a step open (each is listed in the design doc):
   * conv: depthwise, causal, kernel 4, no bias; tap 3 multiplies the current
@@ -19,8 +21,11 @@ Readings taken where the page leaves a step open (each is listed in the design doc):
   * gate: sigmoid(x~_j . w_g^h + b_g^h) per token and head (the default); the
     page's literal softmax-over-the-sequence gate is available as gate="softmax".
   * no 1/sqrt(d_h) scale, no epsilon in the denominator, no projection biases;
-    the output is the concatenation of the heads (Eq. (7)'s RMSNorm gate is
-    not part of this layer's readout).
+    the output is the concatenation of the heads. Without `w_r` the readout
+    ends at O (Eq. (5)); with it, Eq. (7) is applied per head:
+    y_i = gamma (.) O_i / sqrt(mean_c O_ic^2 + eps) (.) SiLU(x~_i W_R^h), the
+    mean over the head's d_h features, eps added inside the root, and gamma
+    [d_h] the usual learnable RMSNorm scale, shared by the heads (None = 1).
   * packed variable-length input: rows [cu[b], cu[b+1]) form sequence b and
     every sum over j runs over that sequence only.
 
@@ -89,6 +94,39 @@ def causal_conv_backward(dxt, x, cu, conv_w):
     return dx, dw
 
 
+def silu(u):
+    return u * sigmoid(u)
+
+
+def dsilu(u):
+    sg = sigmoid(u)
+    return sg * (1.0 + u * (1.0 - sg))
+
+
+def output_gate(O, r, gamma, eps):
+    """Eq. (7) for one head: RmsNorm(O) (.) SiLU(r), O and r [L, d_h]."""
+    rms = np.sqrt(np.mean(O * O, axis=1, keepdims=True) + eps)
+    g = 1.0 if gamma is None else gamma[None, :]
+    return g * (O / rms) * silu(r)
+
+
+def output_gate_backward(O, r, gamma, eps, dy):
+    """Vector-Jacobian product of output_gate: returns (dO, dr, dgamma or None).
+
+    With rho = sqrt(mean(O^2) + eps), n = O / rho and a = gamma (.) SiLU(r):
+      dn = dy (.) a,  dO = (dn - n mean(n (.) dn)) / rho,
+      dr = dy (.) gamma (.) n (.) SiLU'(r),  dgamma = sum_i dy_i (.) n_i (.) SiLU(r_i)."""
+    dh = O.shape[1]
+    rho = np.sqrt(np.mean(O * O, axis=1, keepdims=True) + eps)
+    n = O / rho
+    g = np.ones(dh) if gamma is None else gamma
+    dn = dy * g[None, :] * silu(r)
+    dO = (dn - n * np.sum(n * dn, axis=1, keepdims=True) / dh) / rho
+    dr = dy * g[None, :] * n * dsilu(r)
+    dgamma = None if gamma is None else np.sum(dy * n * silu(r), axis=0)
+    return dO, dr, dgamma
+
+
 def _gate(s, gate):
     if gate == "sigmoid":
         return sigmoid(s)
@@ -107,12 +145,15 @@ def _heads(x_t, w_q, w_k, w_v, w_g, b_g, h, dh):
     return q, k, v, s
 
 
-def forward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="sigmoid"):
-    """GBLA forward, Eqs. (4)-(6), linear (state-first) order of Eq. (3).
+def forward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="sigmoid", w_r=None, gamma=None, eps=1e-6):
+    """GBLA forward, Eqs. (4)-(6), linear (state-first) order of Eq. (3), and
+    with w_r [d, H*d_h] the gated RMSNorm output of Eq. (7).
 
     Returns (y [T, H*d_h], S [N, H, d_h, d_h], z [N, H, d_h]).
     """
     x, w_q, w_k, w_v, w_g, b_g = map(_f64, (x, w_q, w_k, w_v, w_g, b_g))
+    w_r = None if w_r is None else _f64(w_r)
+    gamma = None if gamma is None else _f64(gamma)
     T = x.shape[0]
     H = num_heads
     dh = w_q.shape[1] // H
@@ -133,14 +174,19 @@ def forward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="sigmoid"):
             kt = g[:, None] * phi(k)            # K~ = g (.) phi(K), Eq. (6)
             S = kt.T @ v                        # sum_j g_j phi(k_j) v_j^T
             z = kt.sum(axis=0)                  # sum_j g_j phi(k_j)
-            y[s0:e0, h * dh:(h + 1) * dh] = (qf @ S) / (qf @ z)[:, None]
+            O = (qf @ S) / (qf @ z)[:, None]
+            if w_r is not None:
+                O = output_gate(O, xb @ w_r[:, h * dh:(h + 1) * dh], gamma, eps)
+            y[s0:e0, h * dh:(h + 1) * dh] = O
             S_all[b, h], z_all[b, h] = S, z
     return y, S_all, z_all
 
 
-def forward_quadratic(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="sigmoid"):
+def forward_quadratic(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="sigmoid", w_r=None, gamma=None,
+                      eps=1e-6):
     """Brute-force GBLA forward: Eq. (5) evaluated as an explicit L x L
-    similarity sim_ij = g_j phi(q_i)^T phi(k_j), row-normalised. Use for small L."""
+    similarity sim_ij = g_j phi(q_i)^T phi(k_j), row-normalised (then Eq. (7)
+    if w_r is given). Use for small L."""
     x, w_q, w_k, w_v, w_g, b_g = map(_f64, (x, w_q, w_k, w_v, w_g, b_g))
     H = num_heads
     dh = w_q.shape[1] // H
@@ -155,11 +201,16 @@ def forward_quadratic(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate="s
             q, k, v, s = _heads(xb, w_q, w_k, w_v, w_g, b_g, h, dh)
             g = _gate(s, gate)
             sim = (phi(q) @ phi(k).T) * g[None, :]
-            y[s0:e0, h * dh:(h + 1) * dh] = (sim @ v) / sim.sum(axis=1, keepdims=True)
+            O = (sim @ v) / sim.sum(axis=1, keepdims=True)
+            if w_r is not None:
+                O = output_gate(O, xb @ _f64(w_r)[:, h * dh:(h + 1) * dh], None if gamma is None else _f64(gamma),
+                                eps)
+            y[s0:e0, h * dh:(h + 1) * dh] = O
     return y
 
 
-def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoid"):
+def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoid", w_r=None, gamma=None,
+             eps=1e-6):
     """Gradients of sum(y * dy) for the layer of `forward`.
 
     Per sequence and head, with q~ = phi(q), k~ = g phi(k), num_i = q~_i^T S,
@@ -169,12 +220,19 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
       dk~_j  = dS v_j + dz,            dv_j = dS^T k~_j
       dphi(k)_j = g_j dk~_j,           dg_j = phi(k_j) . dk~_j
       dq = dq~ (.) phi'(q),  dk = dphi(k) (.) phi'(k),  ds = dg g (1 - g)  (sigmoid)
-    then the projection and conv chain rule of Eq. (4).
+    then the projection and conv chain rule of Eq. (4). With w_r, dy is first
+    taken back through Eq. (7) (output_gate_backward) to the gradient of O and
+    of r = x~ W_R^h.
 
-    Returns dict with dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g (float64) and
-    ds [T, H], the gradient with respect to the gate logits s.
+    Returns dict with dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g (float64),
+    ds [T, H], the gradient with respect to the gate logits s, and with w_r
+    also dw_r (and dgamma if gamma is given).
     """
     x, w_q, w_k, w_v, w_g, b_g, dy = map(_f64, (x, w_q, w_k, w_v, w_g, b_g, dy))
+    w_r = None if w_r is None else _f64(w_r)
+    gamma = None if gamma is None else _f64(gamma)
+    dw_r = None if w_r is None else np.zeros_like(w_r)
+    dgamma = None if gamma is None else np.zeros_like(gamma)
     H = num_heads
     dh = w_q.shape[1] // H
     xt = causal_conv(x, cu, conv_w)
@@ -197,6 +255,11 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
             den = qf @ z
             y = (qf @ S) / den[:, None]
             dyb = dy[s0:e0, cols]
+            if w_r is not None:          # Eq. (7): back to dO (dyb from here on) and dr
+                dyb, dr, dgam = output_gate_backward(y, xb @ w_r[:, cols], gamma, eps, dyb)
+                dw_r[:, cols] += xb.T @ dr
+                if gamma is not None:
+                    dgamma += dgam
             dn = dyb / den[:, None]
             dden = -np.sum(dyb * y, axis=1) / den
             dqf = dn @ S.T + dden[:, None] * z[None, :]
@@ -220,5 +283,12 @@ def backward(x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, dy, num_heads, gate="sigmoi
             ds_all[s0:e0, h] = ds
             dxt[s0:e0] += dq @ w_q[:, cols].T + dk @ w_k[:, cols].T + dv @ w_v[:, cols].T \
                 + ds[:, None] * w_g[h][None, :]
+            if w_r is not None:
+                dxt[s0:e0] += dr @ w_r[:, cols].T
     dx, dconv = causal_conv_backward(dxt, x, cu, conv_w)
-    return dict(dx=dx, dconv_w=dconv, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_g=dw_g, db_g=db_g, ds=ds_all)
+    out = dict(dx=dx, dconv_w=dconv, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_g=dw_g, db_g=db_g, ds=ds_all)
+    if w_r is not None:
+        out["dw_r"] = dw_r
+        if gamma is not None:
+            out["dgamma"] = dgamma
+    return out

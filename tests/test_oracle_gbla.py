@@ -261,3 +261,147 @@ def test_backward_gate_bias_gradient_vanishes_when_gate_cannot_matter():
     g = gbla.backward(p["x"], p["cu"], p["conv_w"], p["w_q"], p["w_k"], p["w_v"], p["w_g"],
                       p["b_g"], dy, H)
     np.testing.assert_allclose(g["db_g"], 0.0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- gated RMSNorm output (Eq. 7)
+
+def _gated(rng, p, H, dh, with_gamma=True):
+    d = p["x"].shape[1]
+    w_r = rng.standard_normal((d, H * dh)) / np.sqrt(d)
+    gamma = 1.0 + 0.3 * rng.standard_normal(dh) if with_gamma else None
+    return w_r, gamma
+
+
+@pytest.mark.parametrize("with_gamma", [True, False])
+@pytest.mark.parametrize("eps", [1e-6, 0.3])
+def test_output_gate_matches_torch_rms_norm(with_gamma, eps):
+    """Eq. (7) for one head == torch's rms_norm over the head dimension times
+    SiLU of the gate pre-activation (a library routine, not a retyped formula)."""
+    rng = np.random.default_rng(40)
+    O = rng.standard_normal((23, 8)) * 0.7
+    r = rng.standard_normal((23, 8)) * 2.0
+    gamma = rng.standard_normal(8) if with_gamma else None
+    got = gbla.output_gate(O, r, gamma, eps)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(O), (8,), weight=None if gamma is None else
+                                       torch.from_numpy(gamma), eps=eps) * torch.nn.functional.silu(torch.from_numpy(r))
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "softmax"])
+def test_output_gate_linear_form_equals_quadratic_brute_force(gate):
+    rng = np.random.default_rng(41)
+    p, H = _rand_problem(rng, [1, 5, 17, 40], d=16, H=2, dh=8)
+    w_r, gamma = _gated(rng, p, H, 8)
+    y, _, _ = _fwd(p, H, gate=gate, w_r=w_r, gamma=gamma, eps=1e-5)
+    yq = gbla.forward_quadratic(p["x"], p["cu"], p["conv_w"], p["w_q"], p["w_k"], p["w_v"], p["w_g"], p["b_g"], H,
+                                gate=gate, w_r=w_r, gamma=gamma, eps=1e-5)
+    np.testing.assert_allclose(y, yq, rtol=1e-12, atol=1e-13)
+
+
+def test_output_gate_rows_have_unit_rms_before_the_gate():
+    """With gamma = 1, y / SiLU(r) is O / rms(O): its mean square over a head's
+    features is mean(O^2) / (mean(O^2) + eps), exactly 1 for eps = 0."""
+    rng = np.random.default_rng(42)
+    p, H = _rand_problem(rng, [9, 30], d=8, H=2, dh=4)
+    w_r, _ = _gated(rng, p, H, 4)
+    y0, _, _ = _fwd(p, H)
+    xt = gbla.causal_conv(p["x"], p["cu"], p["conv_w"])
+    for eps in (0.0, 0.05):
+        y, _, _ = _fwd(p, H, w_r=w_r, eps=eps)
+        u = y / gbla.silu(xt @ w_r)
+        for h in range(H):
+            c = slice(4 * h, 4 * h + 4)
+            ms0 = np.mean(y0[:, c] ** 2, axis=1)
+            np.testing.assert_allclose(np.mean(u[:, c] ** 2, axis=1), ms0 / (ms0 + eps), rtol=1e-10)
+
+
+def test_output_gate_removes_the_value_scale():
+    """For eps = 0, y is homogeneous of degree 0 in W_V (O scales with W_V and
+    the RMSNorm removes it): scaling W_V leaves y unchanged and <W_V, dW_V> = 0;
+    y is linear in gamma, so <gamma, dgamma> = <y, dy>."""
+    rng = np.random.default_rng(43)
+    p, H = _rand_problem(rng, [10, 25], d=8, H=2, dh=4)
+    w_r, gamma = _gated(rng, p, H, 4)
+    dy = rng.standard_normal((35, 8))
+    y, _, _ = _fwd(p, H, w_r=w_r, gamma=gamma, eps=0.0)
+    y3, _, _ = _fwd(dict(p, w_v=3.0 * p["w_v"]), H, w_r=w_r, gamma=gamma, eps=0.0)
+    np.testing.assert_allclose(y3, y, rtol=1e-12, atol=1e-14)
+    g = gbla.backward(p["x"], p["cu"], p["conv_w"], p["w_q"], p["w_k"], p["w_v"], p["w_g"], p["b_g"], dy, H,
+                      w_r=w_r, gamma=gamma, eps=0.0)
+    assert abs(np.sum(p["w_v"] * g["dw_v"])) < 1e-12 * np.sum(np.abs(p["w_v"] * g["dw_v"]))
+    np.testing.assert_allclose(np.sum(gamma * g["dgamma"]), np.sum(y * dy), rtol=1e-12)
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "softmax"])
+def test_output_gate_backward_central_finite_differences(gate):
+    rng = np.random.default_rng(44)
+    p, H = _rand_problem(rng, [3, 6], d=6, H=2, dh=3, wscale=2.0)
+    w_r, gamma = _gated(rng, p, H, 3)
+    dy = rng.standard_normal((9, 6))
+    eps = 1e-3
+    kw = dict(gate=gate, eps=eps)
+
+    def loss(q, wr, gm):
+        return float(np.sum(_fwd(q, H, w_r=wr, gamma=gm, **kw)[0] * dy))
+
+    g = gbla.backward(p["x"], p["cu"], p["conv_w"], p["w_q"], p["w_k"], p["w_v"], p["w_g"], p["b_g"], dy, H,
+                      w_r=w_r, gamma=gamma, **kw)
+    h = 1e-6
+    names = dict(x="dx", conv_w="dconv_w", w_q="dw_q", w_k="dw_k", w_v="dw_v", w_g="dw_g", b_g="db_g")
+    for key, gkey in names.items():
+        base = p[key]
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            pp, pm = base.copy(), base.copy()
+            pp[idx] += h
+            pm[idx] -= h
+            num[idx] = (loss(dict(p, **{key: pp}), w_r, gamma) - loss(dict(p, **{key: pm}), w_r, gamma)) / (2 * h)
+        np.testing.assert_allclose(g[gkey], num, rtol=1e-6, atol=1e-8, err_msg=key)
+    for name, base in (("dw_r", w_r), ("dgamma", gamma)):
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            pp, pm = base.copy(), base.copy()
+            pp[idx] += h
+            pm[idx] -= h
+            if name == "dw_r":
+                num[idx] = (loss(p, pp, gamma) - loss(p, pm, gamma)) / (2 * h)
+            else:
+                num[idx] = (loss(p, w_r, pp) - loss(p, w_r, pm)) / (2 * h)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_output_gate_backward_matches_float64_autograd():
+    """An independent derivation: torch float64 autograd through Eqs. (4)-(7),
+    with torch's own rms_norm and silu."""
+    rng = np.random.default_rng(45)
+    lens = [17, 40]
+    p, H = _rand_problem(rng, lens, d=16, H=2, dh=8)
+    w_r, gamma = _gated(rng, p, H, 8)
+    dy = rng.standard_normal((57, 16))
+    eps = 1e-4
+    g = gbla.backward(p["x"], p["cu"], p["conv_w"], p["w_q"], p["w_k"], p["w_v"], p["w_g"], p["b_g"], dy, H,
+                      w_r=w_r, gamma=gamma, eps=eps)
+    t = {k: torch.tensor(v, requires_grad=True) for k, v in p.items() if k != "cu"}
+    t["w_r"] = torch.tensor(w_r, requires_grad=True)
+    t["gamma"] = torch.tensor(gamma, requires_grad=True)
+    F = torch.nn.functional
+    dh = 8
+    ys = []
+    for b in range(len(lens)):
+        s, e = int(p["cu"][b]), int(p["cu"][b + 1])
+        xt = F.conv1d(t["x"][s:e].T[None], t["conv_w"][:, None, :], padding=3, groups=16)[0, :, :e - s].T
+        heads = []
+        for h in range(H):
+            c = slice(h * dh, (h + 1) * dh)
+            q, k, v = xt @ t["w_q"][:, c], xt @ t["w_k"][:, c], xt @ t["w_v"][:, c]
+            gg = torch.sigmoid(xt @ t["w_g"][h] + t["b_g"][h])
+            fq, fk = F.elu(q) + 1, F.elu(k) + 1
+            kt = gg[:, None] * fk
+            O = (fq @ (kt.T @ v)) / (fq @ kt.sum(0))[:, None]
+            heads.append(F.rms_norm(O, (dh,), weight=t["gamma"], eps=eps) * F.silu(xt @ t["w_r"][:, c]))
+        ys.append(torch.cat(heads, 1))
+    (torch.cat(ys) * torch.from_numpy(dy)).sum().backward()
+    pairs = dict(x="dx", conv_w="dconv_w", w_q="dw_q", w_k="dw_k", w_v="dw_v", w_g="dw_g", b_g="db_g", w_r="dw_r",
+                 gamma="dgamma")
+    for k, gk in pairs.items():
+        np.testing.assert_allclose(g[gk], t[k].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=k)
