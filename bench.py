@@ -14,7 +14,8 @@ the timed region around that stage only (a pass before it, with events around
 every stage, gives stage_ms_per_step and picks the dominant stage), and the
 float64 CPU oracle timed on a bounded sample of the same workload.
 The same line carries secondary measurements: the same GBLA workload with the
-softmax-over-the-sequence key gate under "gbla_softmax", and the LION layers
+softmax-over-the-sequence key gate under "gbla_softmax" and with the gated
+RMSNorm output (Eq. (7)) under "gbla_gated_rmsnorm", and the LION layers
 (16 x 4096 tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under
 "lion_s", "lion_d" and "lion_lit" (selective, fixed per-head and no decay).
 
@@ -159,12 +160,13 @@ def copy_calibration(mib=1024, reps=3):
           flush=True)
 
 
-def gbla_setup(torch, gb, gate):
+def gbla_setup(torch, gb, gate, gated_output=False):
     """Device buffers and the step function of the GBLA workload (x and dy
-    rotate over three buffer sets)."""
+    rotate over three buffer sets); gated_output adds the gated RMSNorm output
+    (W_R, gamma)."""
     import numpy as np
 
-    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs
+    from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, make_output_gate
 
     w = WORKLOADS[WORKLOAD]
     inp = make_inputs(w)
@@ -183,7 +185,13 @@ def gbla_setup(torch, gb, gate):
     n_sets = 3
     xs = [t(inp["x"]) for _ in range(n_sets)]
     dys = [t(inp["dy"]) for _ in range(n_sets)]
-    p = gb.problem(N, T, d, H, dh, dt, gate)
+    p = gb.problem(N, T, d, H, dh, dt, gate, gated_output)
+    og = dict(w_r=None, gamma=None, dw_r=None, dgamma=None)
+    if gated_output:
+        o = make_output_gate(w)
+        og = dict(w_r=t(o["w_r"]), gamma=torch.from_numpy(o["gamma"]).float().to(dev),
+                  dw_r=torch.empty((d, D), dtype=torch.float32, device=dev),
+                  dgamma=torch.empty((dh,), dtype=torch.float32, device=dev))
     y = torch.empty((T, D), dtype=dt, device=dev)
     saved = torch.empty(gb.saved_size(p) // 4, dtype=torch.float32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -196,23 +204,26 @@ def gbla_setup(torch, gb, gate):
 
     def step(i):
         x, dy = xs[i % n_sets], dys[i % n_sets]
-        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws)
+        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws, w_r=og["w_r"],
+                        gamma=og["gamma"])
         gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
-                         dbg, ws)
+                         dbg, ws, **og)
 
     return dict(w=w, inp=inp, step=step, T=T, N=N, d=d, H=H, dh=dh, esz=esz)
 
 
-def gbla_softmax_leg(steps, warmup):
-    """The same GBLA workload with the softmax-over-the-sequence key gate."""
+def gbla_variant_leg(steps, warmup, gate="sigmoid", gated_output=False):
+    """The same GBLA workload with the softmax-over-the-sequence key gate or
+    the gated RMSNorm output."""
     import torch
 
     import bidirectional_linear_attention_amd as gb
 
-    g = gbla_setup(torch, gb, "softmax")
+    g = gbla_setup(torch, gb, gate, gated_output)
     elapsed, breakdown, _ = timed_passes(gb, torch, g["step"], steps, warmup, lambda br: [])
     T = g["T"]
-    return {"workload": g["w"].name, "gate": "softmax over the sequence", "tokens_per_step": T, "steps": steps,
+    return {"workload": g["w"].name, "key_gate": gate + (" over the sequence" if gate == "softmax" else ""),
+            "output": "gated RMSNorm (Eq. 7)" if gated_output else "plain", "tokens_per_step": T, "steps": steps,
             "warmup": warmup, "tokens_per_s": round(T * steps / elapsed, 1),
             "ms_per_step": round(1e3 * elapsed / steps, 4),
             "stage_ms_per_step": {k: round(v[0], 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])}}
@@ -343,7 +354,9 @@ def main():
     if args.lion_steps > 0:
         del g, step
         torch.cuda.empty_cache()
-        out["gbla_softmax"] = gbla_softmax_leg(args.lion_steps, min(args.warmup, 3))
+        out["gbla_softmax"] = gbla_variant_leg(args.lion_steps, min(args.warmup, 3), gate="softmax")
+        torch.cuda.empty_cache()
+        out["gbla_gated_rmsnorm"] = gbla_variant_leg(args.lion_steps, min(args.warmup, 3), gated_output=True)
         torch.cuda.empty_cache()
         out["lion_s"] = lion_leg(args.lion_steps, min(args.warmup, 3))
         for dec in ("d", "lit"):

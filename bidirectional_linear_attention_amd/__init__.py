@@ -11,14 +11,16 @@ Generative Retrieval" (core method): causal depthwise Conv1d (kernel 4), per-hea
 Q/K/V projections, phi = elu + 1, key gate (per-token sigmoid, or the softmax
 over the sequence that Eq. (5) writes), global state
 S = sum_j g_j phi(k_j) v_j^T, z = sum_j g_j phi(k_j), readout
-y_i = phi(q_i)^T S / phi(q_i)^T z, on packed variable-length sequences.
+O_i = phi(q_i)^T S / phi(q_i)^T z, optionally followed by the gated RMSNorm
+output of Eq. (7), y = gamma * RmsNorm(O) * SiLU(x~ W_R), on packed
+variable-length sequences.
 """
 from __future__ import annotations
 
 import ctypes
 
 from . import _lib
-from ._lib import DTYPE_BF16, DTYPE_F32, GATES, GblaError, GblaProblem
+from ._lib import DTYPE_BF16, DTYPE_F32, GATES, OUTPUT_GATED_RMSNORM, OUTPUT_PLAIN, GblaError, GblaProblem
 
 __all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "activation_size", "gbla_forward",
            "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "stage_names", "DTYPE_F32", "DTYPE_BF16"]
@@ -39,12 +41,13 @@ def _dtype_code(dt) -> int:
 
 
 def problem(num_seqs: int, total_tokens: int, d_model: int, num_heads: int, head_dim: int, dtype,
-            gate: str = "sigmoid") -> GblaProblem:
+            gate: str = "sigmoid", gated_output: bool = False, norm_eps: float = 1e-6) -> GblaProblem:
     """Problem descriptor; dtype is a torch dtype or a DTYPE_* code, gate
-    "sigmoid" or "softmax"."""
+    "sigmoid" or "softmax"; gated_output selects the gated RMSNorm output of
+    Eq. (7) with RMSNorm epsilon norm_eps."""
     code = dtype if isinstance(dtype, int) else _dtype_code(dtype)
     return GblaProblem(int(num_seqs), int(total_tokens), int(d_model), int(num_heads), int(head_dim), code,
-                       GATES[gate], 4)
+                       GATES[gate], 4, OUTPUT_GATED_RMSNORM if gated_output else OUTPUT_PLAIN, float(norm_eps))
 
 
 def saved_size(p: GblaProblem) -> int:
@@ -83,51 +86,61 @@ def _stream(stream):
 
 
 def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace,
-                 stream=None) -> None:
-    """Enqueue the forward pass (include/gbla.h: gbla_forward); act may be None."""
+                 stream=None, w_r=None, gamma=None) -> None:
+    """Enqueue the forward pass (include/gbla.h: gbla_forward); act may be None;
+    w_r (and optionally gamma) for the gated RMSNorm output."""
     st = _lib.load().gbla_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
-                                  _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(y), _ptr(saved), _ptr(act), _ptr(workspace),
+                                  _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(w_r), _ptr(gamma), _ptr(y), _ptr(saved),
+                                  _ptr(act), _ptr(workspace),
                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _lib.check(st, "gbla_forward")
 
 
 def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv_w,
-                  dw_q, dw_k, dw_v, dw_g, db_g, workspace, stream=None) -> None:
+                  dw_q, dw_k, dw_v, dw_g, db_g, workspace, stream=None, w_r=None, gamma=None, dw_r=None,
+                  dgamma=None) -> None:
     """Enqueue the backward pass (include/gbla.h: gbla_backward); act None recomputes."""
     st = _lib.load().gbla_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
-                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(saved), _ptr(act), _ptr(dy), _ptr(dx),
-                                   _ptr(dconv_w),
-                                   _ptr(dw_q), _ptr(dw_k), _ptr(dw_v), _ptr(dw_g), _ptr(db_g), _ptr(workspace),
+                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(w_r), _ptr(gamma), _ptr(saved), _ptr(act),
+                                   _ptr(dy), _ptr(dx), _ptr(dconv_w), _ptr(dw_q), _ptr(dw_k), _ptr(dw_v),
+                                   _ptr(dw_g), _ptr(db_g), _ptr(dw_r), _ptr(dgamma), _ptr(workspace),
                                    ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _lib.check(st, "gbla_backward")
 
 
-def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate):
+def _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate, w_r=None, gamma=None,
+                  norm_eps=1e-6):
     torch = _torch()
     T, d = x.shape
     D = w_q.shape[1]
     if D % num_heads:
         raise ValueError("w_q columns must be a multiple of num_heads")
-    for name, t, shape in (("conv_w", conv_w, (d, 4)), ("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)),
-                           ("w_v", w_v, (d, D)), ("w_g", w_g, (num_heads, d))):
+    mats = [("conv_w", conv_w, (d, 4)), ("w_q", w_q, (d, D)), ("w_k", w_k, (d, D)), ("w_v", w_v, (d, D)),
+            ("w_g", w_g, (num_heads, d))]
+    if w_r is not None:
+        mats.append(("w_r", w_r, (d, D)))
+    for name, t, shape in mats:
         if tuple(t.shape) != shape or t.dtype != x.dtype:
             raise ValueError(f"{name}: expected {shape} {x.dtype}, got {tuple(t.shape)} {t.dtype}")
     if b_g.dtype != torch.float32 or tuple(b_g.shape) != (num_heads,):
         raise ValueError("b_g must be float32 [num_heads]")
+    if gamma is not None and (w_r is None or gamma.dtype != torch.float32 or tuple(gamma.shape) != (D // num_heads,)):
+        raise ValueError("gamma must be float32 [head_dim] and needs w_r")
     if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be int32 [N+1]")
-    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype, gate)
+    return problem(cu_seqlens.numel() - 1, T, d, num_heads, D // num_heads, x.dtype, gate, w_r is not None, norm_eps)
 
 
 def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, workspace=None,
-            save_activations: bool = True, gate: str = "sigmoid"):
+            save_activations: bool = True, gate: str = "sigmoid", w_r=None, gamma=None, norm_eps: float = 1e-6):
     """Allocate y, saved, the activation cache (if save_activations) and the
-    workspace (unless given) and run gbla_forward.
+    workspace (unless given) and run gbla_forward; w_r [d, H*d_h] (and
+    optionally gamma [d_h] float32) selects the gated RMSNorm output.
     Returns (y [T, H*d_h], saved, act or None); saved is float32
     [N, H, d_h*d_h + d_h] for the sigmoid gate and flat (states, then the N*H
     logit maxima, as gbla_saved_size describes) for the softmax gate."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate)
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate, w_r, gamma, norm_eps)
     dev = x.device
     y = torch.empty((p.total_tokens, p.num_heads * p.head_dim), dtype=x.dtype, device=dev)
     E = p.head_dim * p.head_dim + p.head_dim
@@ -136,17 +149,18 @@ def forward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads: int, work
     act = torch.empty(activation_size(p), dtype=torch.uint8, device=dev) if save_activations else None
     if workspace is None:
         workspace = torch.empty(workspace_size(p, False), dtype=torch.uint8, device=dev)
-    gbla_forward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace)
+    gbla_forward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace, w_r=w_r, gamma=gamma)
     return y, saved, act
 
 
 def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num_heads: int,
-             workspace=None, gate: str = "sigmoid") -> dict:
+             workspace=None, gate: str = "sigmoid", w_r=None, gamma=None, norm_eps: float = 1e-6) -> dict:
     """Allocate the gradients (and the workspace unless given) and run
     gbla_backward; act is forward's activation cache or None (recompute).
-    Returns dict dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g."""
+    Returns dict dx, dconv_w, dw_q, dw_k, dw_v, dw_g, db_g, plus dw_r (and
+    dgamma) with the gated RMSNorm output."""
     torch = _torch()
-    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate)
+    p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate, w_r, gamma, norm_eps)
     if saved.numel() * 4 != saved_size(p):
         raise ValueError("saved does not match the problem (gate?)")
     dev = x.device
@@ -156,8 +170,13 @@ def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num
              dw_g=torch.empty(w_g.shape, **f32), db_g=torch.empty(b_g.shape, **f32))
     if workspace is None:
         workspace = torch.empty(workspace_size(p, True), dtype=torch.uint8, device=dev)
+    if w_r is not None:
+        g["dw_r"] = torch.empty(w_r.shape, **f32)
+    if gamma is not None:
+        g["dgamma"] = torch.empty(gamma.shape, **f32)
     gbla_backward(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, g["dx"], g["dconv_w"],
-                  g["dw_q"], g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace)
+                  g["dw_q"], g["dw_k"], g["dw_v"], g["dw_g"], g["db_g"], workspace, w_r=w_r, gamma=gamma,
+                  dw_r=g.get("dw_r"), dgamma=g.get("dgamma"))
     return g
 
 

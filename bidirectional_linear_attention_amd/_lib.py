@@ -18,6 +18,7 @@ LION_DECAY = {"s": 0, "d": 1, "lit": 2}  # selective, fixed per head, none
 GATE_SIGMOID = 0
 GATE_SOFTMAX = 1
 GATES = {"sigmoid": GATE_SIGMOID, "softmax": GATE_SOFTMAX}
+OUTPUT_PLAIN, OUTPUT_GATED_RMSNORM = 0, 1
 
 
 class GblaError(RuntimeError):
@@ -28,7 +29,8 @@ class GblaError(RuntimeError):
 
 class GblaProblem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "gate", "conv_width")]
+                ("num_seqs", "total_tokens", "d_model", "num_heads", "head_dim", "dtype", "gate", "conv_width",
+                 "output_gate")] + [("norm_eps", ctypes.c_float)]
 
 
 class LionProblem(ctypes.Structure):
@@ -47,8 +49,8 @@ _SIGNATURES = {
     "gbla_saved_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
     "gbla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
     "gbla_activation_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
-    "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 11 + [_vp, _sz, _vp]),
-    "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 18 + [_vp, _sz, _vp]),
+    "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 22 + [_vp, _sz, _vp]),
     "gbla_profile_begin": (ctypes.c_int, [ctypes.c_int]),
     "gbla_profile_begin_stages": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64]),
     "gbla_profile_end": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int),

@@ -3,6 +3,7 @@
 #include "gbla.h"
 
 #include <algorithm>
+#include <cmath>
 
 #include "internal.h"
 
@@ -23,13 +24,17 @@ struct Carver {
 struct Dims {
   int N, T, d, H, dh, D, E, NP, Kp, slots, nsplit, conv_rb;
   bool softmax;  // softmax key gate: the gate array holds logits, saved ends with the logit maxima
+  bool gated;    // gated RMSNorm output (Eq. (7)): a fourth projection segment R
+  float eps;     // its RMSNorm epsilon
   size_t esz;    // bytes per activation element
 };
 
 Dims dims_of(const gbla_problem* p) {
   Dims m;
   m.N = p->num_seqs; m.T = p->total_tokens; m.d = p->d_model; m.H = p->num_heads; m.dh = p->head_dim;
-  m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.NP = proj_cols(m.dh); m.Kp = grad_cols(m.H, m.dh);
+  m.gated = p->output_gate == GBLA_OUTPUT_GATED_RMSNORM;
+  m.eps = p->norm_eps;
+  m.D = m.H * m.dh; m.E = m.dh * m.dh + m.dh; m.NP = proj_cols(m.dh, m.gated); m.Kp = grad_cols(m.H, m.dh, m.gated);
   m.slots = max_chunks(m.T, m.N);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
   m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
@@ -39,8 +44,8 @@ Dims dims_of(const gbla_problem* p) {
   return m;
 }
 
-// activations kept from the forward for the backward
-struct Act { void* xt; void* qa; void* ka; void* va; float* ga; };
+// activations kept from the forward for the backward (ra: the gated output's R)
+struct Act { void* xt; void* qa; void* ka; void* va; float* ga; void* ra; };
 
 Act carve_act(const Dims& m, Carver& c, char* base) {
   Act a;
@@ -50,6 +55,7 @@ Act carve_act(const Dims& m, Carver& c, char* base) {
   a.ka = c.take<char>(base, TD);
   a.va = c.take<char>(base, TD);
   a.ga = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
+  a.ra = m.gated ? c.take<char>(base, TD) : nullptr;
   return a;
 }
 
@@ -64,7 +70,7 @@ struct FwdWs {
 };
 struct BwdWs {
   int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
-  void* G; void* dxt; float* dw_part; float* dconv_part; Act act;
+  float* dgam_part; void* G; void* dxt; float* dw_part; float* dconv_part; Act act;
 };
 
 // The workspace always has room for the activations, so it suffices whether or
@@ -94,6 +100,7 @@ size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
   t.dsz = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H * m.E);
   t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
+  t.dgam_part = m.gated ? c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.dh) : nullptr;
   t.G = c.take<char>(base, (size_t)m.T * m.Kp * m.esz);
   t.dxt = c.take<char>(base, m.esz * (size_t)m.T * m.d);
   t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
@@ -109,10 +116,14 @@ gbla_status check_problem(const gbla_problem* p) {
   if (p->head_dim != 32 && p->head_dim != 64) return GBLA_ERR_UNSUPPORTED;
   if ((p->gate != GBLA_GATE_SIGMOID && p->gate != GBLA_GATE_SOFTMAX) || p->conv_width != 4)
     return GBLA_ERR_UNSUPPORTED;
+  if (p->output_gate != GBLA_OUTPUT_PLAIN && p->output_gate != GBLA_OUTPUT_GATED_RMSNORM) return GBLA_ERR_UNSUPPORTED;
+  if (p->output_gate == GBLA_OUTPUT_GATED_RMSNORM && !(std::isfinite(p->norm_eps) && p->norm_eps >= 0.f))
+    return GBLA_ERR_BAD_SHAPE;
   if (p->num_seqs < 1 || p->total_tokens < 0 || p->num_heads < 1 || p->d_model < 8 || p->d_model % 8 != 0)
     return GBLA_ERR_BAD_SHAPE;
   const long long T = p->total_tokens;
-  const long long widest = std::max<long long>(p->d_model, grad_cols(p->num_heads, p->head_dim));
+  const long long widest =
+      std::max<long long>(p->d_model, grad_cols(p->num_heads, p->head_dim, p->output_gate != GBLA_OUTPUT_PLAIN));
   if (T * widest >= (1LL << 31) || (long long)p->num_heads * p->head_dim * 4 + 64 >= (1LL << 24) ||
       (long long)p->num_seqs >= (1LL << 24))
     return GBLA_ERR_BAD_SHAPE;
@@ -138,7 +149,7 @@ const char* gbla_status_string(int status) {
   }
 }
 
-int gbla_version(void) { return 3; }
+int gbla_version(void) { return 4; }
 
 gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes) {
   if (!bytes) return GBLA_ERR_NULL_ARG;
@@ -168,15 +179,18 @@ gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes) {
 
 gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                         void* y, float* saved, void* act, void* workspace, size_t workspace_bytes, void* stream) {
+                         const void* w_r, const float* gamma, void* y, float* saved, void* act, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
   if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !workspace) return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
-  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)y, (const void*)saved, (const void*)act,
+  const bool gated = p->output_gate == GBLA_OUTPUT_GATED_RMSNORM;
+  if (gated != (w_r != nullptr) || (!gated && gamma)) return GBLA_ERR_NULL_ARG;
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, w_r, (const void*)y, (const void*)saved, (const void*)act,
                         (const void*)workspace})
     if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
-  if (!aligned(b_g, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
+  if (!aligned(b_g, 4) || !aligned(gamma, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
   const Dims m = dims_of(p);
   FwdWs w;
   if (workspace_bytes < plan_fwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
@@ -190,35 +204,42 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
 
   (void)hipGetLastError();
   { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
+  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, s); }
   { StageScope ps(ST_CONV_FWD, s);
     launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
-  { StageScope ps(ST_PROJ_FWD, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
+  { StageScope ps(ST_PROJ_FWD, s);
+    launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
   { StageScope ps(ST_STATE_PARTIAL, s);
     launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, w.mpart, s); }
   { StageScope ps(ST_COMBINE_STATE, s);  // softmax gate: the logit maxima follow the N*H states
     launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
                    m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr); }
-  { StageScope ps(ST_READOUT, s); launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s); }
+  { StageScope ps(ST_READOUT, s);
+    launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s, A.ra, gamma, m.eps); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 
 gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                           const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                          const float* saved, const void* act, const void* dy, void* dx, float* dconv_w, float* dw_q,
-                          float* dw_k, float* dw_v, float* dw_g, float* db_g, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          const void* w_r, const float* gamma, const float* saved, const void* act, const void* dy,
+                          void* dx, float* dconv_w, float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g,
+                          float* dw_r, float* dgamma, void* workspace, size_t workspace_bytes, void* stream) {
   gbla_status st = check_problem(p);
   if (st != GBLA_OK) return st;
   if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !dconv_w || !dw_q || !dw_k ||
       !dw_v || !dw_g || !db_g || !workspace)
     return GBLA_ERR_NULL_ARG;
   if (p->total_tokens > 0 && (!x || !dy || !dx)) return GBLA_ERR_NULL_ARG;
-  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, (const void*)saved, act, dy, (const void*)dx,
-                        (const void*)dw_q, (const void*)dw_k, (const void*)dw_v, (const void*)dw_g,
+  const bool gated = p->output_gate == GBLA_OUTPUT_GATED_RMSNORM;
+  if (gated != (w_r != nullptr) || gated != (dw_r != nullptr) || (gamma != nullptr) != (dgamma != nullptr) ||
+      (!gated && gamma))
+    return GBLA_ERR_NULL_ARG;
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, w_r, (const void*)saved, act, dy, (const void*)dx,
+                        (const void*)dw_q, (const void*)dw_k, (const void*)dw_v, (const void*)dw_g, (const void*)dw_r,
                         (const void*)workspace})
     if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
-  if (!aligned(b_g, 4) || !aligned(db_g, 4) || !aligned(dconv_w, 4) || !aligned(cu_seqlens, 4))
+  if (!aligned(b_g, 4) || !aligned(db_g, 4) || !aligned(dconv_w, 4) || !aligned(cu_seqlens, 4) ||
+      !aligned(gamma, 4) || !aligned(dgamma, 4))
     return GBLA_ERR_MISALIGNED;
   const Dims m = dims_of(p);
   BwdWs w;
@@ -233,20 +254,25 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
 
   (void)hipGetLastError();
   { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s); }
+  { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_r, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s); }
   if (!act) {  // recompute x~, g, phi(q), phi(k), v into the workspace
-    { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, m.d, m.H, m.dh, w.wp, s); }
+    { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, s); }
     { StageScope ps(ST_CONV_RECOMPUTE, s);
       launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
-    { StageScope ps(ST_PROJ_RECOMPUTE, s); launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s); }
+    { StageScope ps(ST_PROJ_RECOMPUTE, s);
+      launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
   }
   { StageScope ps(ST_BWD_DSTATE, s);
-    launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s); }
+    launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s, A.ra,
+                      gamma, m.eps, gamma ? w.dgam_part : nullptr); }
   { StageScope ps(ST_COMBINE_DSTATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s); }
   { StageScope ps(ST_BWD_TOKEN, s);
-    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.G, w.dbg_part,
+    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, m.gated ? 4 : 3, w.G,
+                     w.dbg_part,
                      m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
-  { StageScope ps(ST_DBG_REDUCE, s); launch_sum_parts(w.dbg_part, m.H, 0, w.nchunks, db_g, s); }
+  { StageScope ps(ST_DBG_REDUCE, s);
+    launch_sum_parts(w.dbg_part, m.H, 0, w.nchunks, db_g, s);
+    if (gamma) launch_sum_parts(w.dgam_part, m.dh, 0, w.nchunks, dgamma, s, m.H); }
   if (m.T > 0) {
     { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }
     { StageScope ps(ST_CONV_BWD, s);
@@ -254,7 +280,7 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
   }
   { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, A.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
   { StageScope ps(ST_DW_REDUCE, s);
-    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_g, s); }
+    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_r, dw_g, s); }
   { StageScope ps(ST_DCONV_REDUCE, s); launch_sum_parts(w.dconv_part, 4 * m.d, m.conv_rb, nullptr, dconv_w, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }

@@ -28,32 +28,6 @@ namespace gbla {
 template <typename T> struct Parts { static constexpr int n = 2; };  // bf16: hi + lo split of fp32 matrices
 template <> struct Parts<float> { static constexpr int n = 1; };
 
-// fixed-order sum of per-wave dh x dh C-tile accumulators (+ a per-lane vector) into red[]
-template <int DH>
-__device__ __forceinline__ void wave_reduce_state(float* red, const f32x4 (&acc)[DH / 16][DH / 16],
-                                                  const float (&vec)[DH / 16], int w, int grp, int col) {
-  constexpr int FB = DH / 16;
-  for (int ww = 0; ww < 4; ++ww) {
-    if (w == ww) {
-#pragma unroll
-      for (int a = 0; a < FB; ++a) {
-#pragma unroll
-        for (int b = 0; b < FB; ++b)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int idx = (16 * a + 4 * grp + r) * DH + 16 * b + col;
-            red[idx] = ww == 0 ? acc[a][b][r] : red[idx] + acc[a][b][r];
-          }
-        if (grp == 0) {
-          const int idx = DH * DH + 16 * a + col;
-          red[idx] = ww == 0 ? vec[a] : red[idx] + vec[a];
-        }
-      }
-    }
-    __syncthreads();
-  }
-}
-
 // ============================================================== dS, dz and dq
 // Block = one chunk x one head; tiles of 64 tokens of q~ and dy are staged in
 // LDS with 16-byte loads, wave w works on tokens 16 w .. 16 w + 15 of a tile in
@@ -66,11 +40,19 @@ __device__ __forceinline__ void wave_reduce_state(float* red, const f32x4 (&acc)
 //   dq = dq~ (.) phi'(q) -> G             (8-byte stores)
 //   [dS | dz] += q~^T [dn | dden]         (MFMA over the tile's tokens; each wave
 //                                          owns a fixed set of output tiles)
-template <typename T, int DH>
+// GATED (gated RMSNorm output, Eq. (7)): dy is the gradient of
+// y = gamma (.) n (.) SiLU(r), n = O / rho, rho = sqrt(mean(O^2) + eps); with O
+// = num / den recomputed above, the gradient of O replaces dy:
+//   a = gamma (.) SiLU(r),  dO = (dy (.) a - n mean(n (.) dy (.) a)) / rho
+//   dr = dy (.) gamma (.) n (.) SiLU'(r) -> G's R columns,  dgamma += dy (.) n (.) SiLU(r)
+// (the means are row sums over the 4 lanes of a token, as for dy . y).
+template <typename T, int DH, bool GATED>
 __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, const T* __restrict__ dy,
                                                     const float* __restrict__ saved, const int* __restrict__ nchunks,
                                                     const Chunk* __restrict__ tab, int max_slots, int H, int Kp,
-                                                    float* __restrict__ partial, T* __restrict__ G) {
+                                                    float* __restrict__ partial, T* __restrict__ G,
+                                                    const T* __restrict__ ra, const float* __restrict__ gamma,
+                                                    float eps, float* __restrict__ dgam_part) {
   constexpr int FB = DH / 16, NB = FB + 1, NR = DH + 16;
   constexpr int PAD = 16 / (int)sizeof(T);
   constexpr int LD = DH + PAD, LDN = DH + 16 + PAD;
@@ -82,6 +64,8 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   __shared__ __align__(16) T qs[ST * LD];       // q~ tile (token-major)
   __shared__ __align__(16) T ys[ST * LD];       // dy tile
   __shared__ __align__(16) T dns[ST * LDN];     // [dn | dden | 0] (token-major)
+  __shared__ __align__(16) T rs[GATED ? ST * LD : 8];  // R tile (gated output)
+  __shared__ __align__(16) float gms[GATED ? DH : 4];   // gamma (gated output)
   __shared__ float zs[DH];
 
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
@@ -100,9 +84,16 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
 #pragma unroll
   for (int u = 0; u < TPW; ++u) accS[u] = zero4();
   const int r0 = 16 * w;
+  float dgam[FB][4];  // gated output: the lane's dgamma partial sums
+#pragma unroll
+  for (int nt = 0; nt < FB; ++nt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dgam[nt][r] = 0.f;
+  if constexpr (GATED)
+    for (int e = tid; e < DH; e += 256) gms[e] = gamma ? gamma[e] : 1.f;
 
   constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pq[NV], py[NV];
+  Frag8<T> pq[NV], py[NV], pr[NV];
   auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -111,6 +102,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
       pq[v] = ok ? frag_load(qa + o) : frag_zero<T>();
       py[v] = ok ? frag_load(dy + o) : frag_zero<T>();
+      if constexpr (GATED) pr[v] = ok ? frag_load(ra + o) : frag_zero<T>();
     }
   };
   fetch(ch.start);
@@ -121,6 +113,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       if (it < ST * V8) {
         frag_store(qs + r * LD + c, pq[v]);
         frag_store(ys + r * LD + c, py[v]);
+        if constexpr (GATED) frag_store(rs + r * LD + c, pr[v]);
       }
     }
     __syncthreads();
@@ -144,6 +137,50 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
     const bool ok = tb + tok < ch.end;
     const float den = __shfl(num[FB][0], col, 64);  // row dh (z) sits in group 0, element 0
     const float inv = ok ? fast_rcp(den) : 0.f;
+    if constexpr (GATED) {
+      // the gradient of O replaces dy in the staged tile (each lane rewrites
+      // its own token's features); O = num * inv and n = O * rinv are
+      // recomputed from the live accumulators rather than kept
+      float ss = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ss += num[nt][r] * num[nt][r];
+      ss *= inv * inv;
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      const float rinv = ok ? fast_rsqrt(ss * (1.f / DH) + eps) : 0.f;
+      const float nsc = inv * rinv;  // n = num * nsc
+      float ndot = 0.f, dnv[FB][4];
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) {
+        const Quad<T> q = quad_load(ys + tok * LD + 16 * nt + 4 * grp);
+        const Quad<T> rq = quad_load(rs + tok * LD + 16 * nt + 4 * grp);
+        const float4 g4 = *reinterpret_cast<const float4*>(gms + 16 * nt + 4 * grp);
+        const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
+        float dr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float dout = quad_get(q, r), rv = quad_get(rq, r), sg = sigmoidf_(rv), sl = rv * sg;
+          const float n = num[nt][r] * nsc, dg = dout * gv[r];
+          dnv[nt][r] = dg * sl;  // gradient of n
+          ndot += n * dnv[nt][r];
+          dr[r] = dg * n * sg * (1.f + rv * (1.f - sg));
+          dgam[nt][r] += dout * n * sl;
+        }
+        if (ok) quad_store(G + (size_t)(tb + tok) * Kp + 3 * D + h * DH + 16 * nt + 4 * grp, quad_from4<T>(dr));
+      }
+      ndot += __shfl_xor(ndot, 16, 64);
+      ndot += __shfl_xor(ndot, 32, 64);
+      const float c = ndot * (1.f / DH);
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = rinv * (dnv[nt][r] - num[nt][r] * nsc * c);
+        quad_store(ys + tok * LD + 16 * nt + 4 * grp, quad_from4<T>(v));
+      }
+    }
     float dyv[FB][4], pdot = 0.f;
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
@@ -212,13 +249,40 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       else if (col == 0) out[DH * DH + a] = accS[u][r];
     }
   }
+  if constexpr (GATED) {
+    if (dgam_part) {  // dgamma of the chunk: over the 16 tokens of a lane group, then over the 4 waves
+      float* red = reinterpret_cast<float*>(qs);  // the tiles are free after the last barrier
+#pragma unroll
+      for (int nt = 0; nt < FB; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = dgam[nt][r];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+          if (col == 0) red[w * DH + 16 * nt + 4 * grp + r] = v;
+        }
+      __syncthreads();
+      if (tid < DH)
+        dgam_part[((size_t)slot * H + h) * DH + tid] =
+            (red[tid] + red[DH + tid]) + (red[2 * DH + tid] + red[3 * DH + tid]);
+    }
+  }
 }
 
 void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const float* saved, const int* nchunks,
-                       const Chunk* tab, int max_slots, int H, int Kp, float* partial, void* G, hipStream_t s) {
+                       const Chunk* tab, int max_slots, int H, int Kp, float* partial, void* G, hipStream_t s,
+                       const void* ra, const float* gamma, float eps, float* dgam_part) {
   const dim3 grid(xcd_grid(max_slots * H));
-#define GBLA_BD(TT, DD) hipLaunchKernelGGL((k_bwd_dstate<TT, DD>), grid, dim3(256), 0, s, (const TT*)qa, \
-                                           (const TT*)dy, saved, nchunks, tab, max_slots, H, Kp, partial, (TT*)G)
+#define GBLA_BD(TT, DD)                                                                                           \
+  do {                                                                                                            \
+    if (ra)                                                                                                       \
+      hipLaunchKernelGGL((k_bwd_dstate<TT, DD, true>), grid, dim3(256), 0, s, (const TT*)qa, (const TT*)dy, saved, \
+                         nchunks, tab, max_slots, H, Kp, partial, (TT*)G, (const TT*)ra, gamma, eps, dgam_part);  \
+    else                                                                                                          \
+      hipLaunchKernelGGL((k_bwd_dstate<TT, DD, false>), grid, dim3(256), 0, s, (const TT*)qa, (const TT*)dy,       \
+                         saved, nchunks, tab, max_slots, H, Kp, partial, (TT*)G, (const TT*)ra, gamma, eps,       \
+                         dgam_part);                                                                              \
+  } while (0)
   if (dt == BF16) { if (dh == 64) GBLA_BD(bf16, 64); else GBLA_BD(bf16, 32); }
   else            { if (dh == 64) GBLA_BD(float, 64); else GBLA_BD(float, 32); }
 #undef GBLA_BD
@@ -234,7 +298,7 @@ template <typename T, int DH, bool SOFTMAX>
 __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, const T* __restrict__ va,
                                                    const float* __restrict__ ga, const float* __restrict__ dsz,
                                                    const int* __restrict__ nchunks, const Chunk* __restrict__ tab,
-                                                   int max_slots, int H, int Kp, T* __restrict__ G,
+                                                   int max_slots, int H, int Kp, int nseg, T* __restrict__ G,
                                                    float* __restrict__ dbg_part, const float* __restrict__ gmax) {
   constexpr int FB = DH / 16;
   constexpr int LD = DH + 16 / (int)sizeof(T);
@@ -261,7 +325,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
-  const int gcol0 = 3 * D + H;  // first zero-pad column of G
+  const int gs0 = nseg * D, gcol0 = gs0 + H;  // gate column of head 0; first zero-pad column of G
   const int r0 = 16 * w;
   constexpr int NV = (ST * V8 + 255) / 256;
   Frag8<T> pk[NV], pv[NV];
@@ -336,7 +400,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
       // invariant to the normaliser): dg g
       const float ds = SOFTMAX ? dg * g : dg * g * (1.f - g);
       if (ok && col == 0) {
-        G[(size_t)t * Kp + 3 * D + h] = from_f<T>(ds);
+        G[(size_t)t * Kp + gs0 + h] = from_f<T>(ds);
         dbg += ds;
       }
       if (ok && h == 0)
@@ -368,17 +432,17 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
 }
 
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
-                      const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
-                      const float* gmax, hipStream_t s) {
+                      const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, int nseg, void* G,
+                      float* dbg_part, const float* gmax, hipStream_t s) {
   const dim3 grid(xcd_grid(max_slots * H));
 #define GBLA_BT(TT, DD)                                                                                      \
   do {                                                                                                       \
     if (gmax)                                                                                                \
       hipLaunchKernelGGL((k_bwd_token<TT, DD, true>), grid, dim3(256), 0, s, (const TT*)ka, (const TT*)va, ga, \
-                         dsz, nchunks, tab, max_slots, H, Kp, (TT*)G, dbg_part, gmax);                       \
+                         dsz, nchunks, tab, max_slots, H, Kp, nseg, (TT*)G, dbg_part, gmax);                 \
     else                                                                                                     \
       hipLaunchKernelGGL((k_bwd_token<TT, DD, false>), grid, dim3(256), 0, s, (const TT*)ka, (const TT*)va,   \
-                         ga, dsz, nchunks, tab, max_slots, H, Kp, (TT*)G, dbg_part, gmax);                   \
+                         ga, dsz, nchunks, tab, max_slots, H, Kp, nseg, (TT*)G, dbg_part, gmax);             \
   } while (0)
   if (dt == BF16) { if (dh == 64) GBLA_BT(bf16, 64); else GBLA_BT(bf16, 32); }
   else            { if (dh == 64) GBLA_BT(float, 64); else GBLA_BT(float, 32); }
@@ -389,8 +453,9 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
 // wt[c][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | w_g[:,c] | 0]
 template <typename T>
 __global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
-                          const T* __restrict__ w_g, int d, int H, int dh, int Kp, T* __restrict__ wt) {
-  const int D = H * dh;
+                          const T* __restrict__ w_r, const T* __restrict__ w_g, int d, int H, int dh, int Kp,
+                          T* __restrict__ wt) {
+  const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
   const long total = (long)d * Kp;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
     const int c = (int)(e / Kp), n = (int)(e - (long)c * Kp);
@@ -398,21 +463,22 @@ __global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, 
     if (n < D) v = w_q[(long)c * D + n];
     else if (n < 2 * D) v = w_k[(long)c * D + n - D];
     else if (n < 3 * D) v = w_v[(long)c * D + n - 2 * D];
-    else if (n < 3 * D + H && w_g) v = w_g[(long)(n - 3 * D) * d + c];  // no w_g: zero rows
+    else if (n < GD) v = w_r[(long)c * D + n - 3 * D];
+    else if (n < GD + H && w_g) v = w_g[(long)(n - GD) * d + c];  // no w_g: zero rows
     wt[e] = v;
   }
 }
 
-void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_g, int d, int H,
-                    int dh, int Kp, void* wt, hipStream_t s) {
+void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
+                    int d, int H, int dh, int Kp, void* wt, hipStream_t s) {
   const long total = (long)d * Kp;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_g, d, H, dh, Kp, (bf16*)wt);
+                       (const bf16*)w_v, (const bf16*)w_r, (const bf16*)w_g, d, H, dh, Kp, (bf16*)wt);
   else
     hipLaunchKernelGGL(k_pack_wt<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_g, d, H, dh, Kp, (float*)wt);
+                       (const float*)w_v, (const float*)w_r, (const float*)w_g, d, H, dh, Kp, (float*)wt);
 }
 
 // ============================================================== dX~ = G Wt^T
@@ -558,26 +624,28 @@ void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp,
 
 __global__ void k_dw_reduce(const float* __restrict__ part, int nsplit, int d, int H, int dh, int Kp,
                             float* __restrict__ dw_q, float* __restrict__ dw_k, float* __restrict__ dw_v,
-                            float* __restrict__ dw_g) {
-  const int D = H * dh;
+                            float* __restrict__ dw_r, float* __restrict__ dw_g) {
+  const int D = H * dh, GD = (dw_r ? 4 : 3) * D;  // first gate column
   const long total = (long)d * Kp;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
     const int c = (int)(e / Kp), n = (int)(e - (long)c * Kp);
-    if (n >= 3 * D + H) continue;
+    if (n >= GD + H) continue;
     float s = 0.f;
     for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * total + e];
     if (n < D) dw_q[(long)c * D + n] = s;
     else if (n < 2 * D) dw_k[(long)c * D + n - D] = s;
     else if (n < 3 * D) dw_v[(long)c * D + n - 2 * D] = s;
-    else if (dw_g) dw_g[(long)(n - 3 * D) * d + c] = s;
+    else if (n < GD) dw_r[(long)c * D + n - 3 * D] = s;
+    else if (dw_g) dw_g[(long)(n - GD) * d + c] = s;
   }
 }
 
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
-                      float* dw_v, float* dw_g, hipStream_t s) {
+                      float* dw_v, float* dw_r, float* dw_g, hipStream_t s) {
   const long total = (long)d * Kp;
   const int grid = (int)std::min<long>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(256), 0, s, part, nsplit, d, H, dh, Kp, dw_q, dw_k, dw_v, dw_g);
+  hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(256), 0, s, part, nsplit, d, H, dh, Kp, dw_q, dw_k, dw_v, dw_r,
+                     dw_g);
 }
 
 // ============================================================== conv backward

@@ -79,31 +79,33 @@ void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, 
 }
 
 // ============================================================== weight packing
-// wp[h][n][c]: rows n < dh are W_Q[:, h*dh + n], then W_K, then W_V (k = c contiguous)
+// wp[h][n][c]: rows n < dh are W_Q[:, h*dh + n], then W_K, then W_V, then
+// (w_r non-null) W_R (k = c contiguous)
 template <typename T>
-__global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v, int d,
-                            int H, int dh, T* __restrict__ wp) {
-  const int NP = 3 * dh, D = H * dh;
+__global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
+                            const T* __restrict__ w_r, int d, int H, int dh, T* __restrict__ wp) {
+  const int NP = (w_r ? 4 : 3) * dh, D = H * dh;
   const long total = (long)H * NP * d;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
     const int c = (int)(e % d);
     const int n = (int)((e / d) % NP);
     const int h = (int)(e / ((long)d * NP));
-    const T* src = n < dh ? w_q : (n < 2 * dh ? w_k : w_v);
+    const int seg = n / dh;
+    const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
     wp[e] = src[(long)c * D + h * dh + (n % dh)];
   }
 }
 
-void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
-                      hipStream_t s) {
-  const long total = (long)H * proj_cols(dh) * d;
+void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
+                      int dh, void* wp, hipStream_t s) {
+  const long total = (long)H * proj_cols(dh, w_r != nullptr) * d;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, d, H, dh, (bf16*)wp);
+                       (const bf16*)w_v, (const bf16*)w_r, d, H, dh, (bf16*)wp);
   else
     hipLaunchKernelGGL(k_pack_proj<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, d, H, dh, (float*)wp);
+                       (const float*)w_v, (const float*)w_r, d, H, dh, (float*)wp);
 }
 
 // ============================================================== causal conv + gate
@@ -286,35 +288,48 @@ void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipSt
 }
 
 // ============================================================== projection GEMM
-// Block = 256 tokens x the [Q | K | V] columns (3 dh each) of HPB consecutive
-// heads (the packed per-head panels are contiguous, so HPB heads are one B
-// operand). bf16 runs the direct-to-LDS main loop, float the register-staged one.
-// Epilogue: phi on Q and K, identity on V.
-template <typename T, int DH> struct ProjCfg;
-template <> struct ProjCfg<bf16, 64> {
+// Block = 256 tokens x the [Q | K | V] columns (3 dh each; with the gated
+// RMSNorm output [Q | K | V | R], 4 dh) of HPB consecutive heads (the packed
+// per-head panels are contiguous, so HPB heads are one B operand). bf16 runs the
+// direct-to-LDS main loop, float the register-staged one.
+// Epilogue: phi on Q and K, identity on V and R.
+template <typename T, int DH, int NSEG> struct ProjCfg;
+template <> struct ProjCfg<bf16, 64, 3> {
   using S = DlShape<256, 384, 32, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
-template <> struct ProjCfg<bf16, 32> {
+template <> struct ProjCfg<bf16, 32, 3> {
   using S = DlShape<256, 192, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
-// float32 tiles stay within 64 KB of LDS
-template <> struct ProjCfg<float, 64> {
+template <> struct ProjCfg<bf16, 64, 4> {
+  using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
+};
+template <> struct ProjCfg<bf16, 32, 4> {
+  using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+};
+template <> struct ProjCfg<float, 64, 3> {
   using S = GemmShape<float, 32, 192, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
-template <> struct ProjCfg<float, 32> {
+template <> struct ProjCfg<float, 32, 3> {
   using S = GemmShape<float, 64, 96, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
+template <> struct ProjCfg<float, 64, 4> {
+  using S = GemmShape<float, 32, 256, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
+};
+template <> struct ProjCfg<float, 32, 4> {
+  using S = GemmShape<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
+};
 
-// PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION-s)
-template <typename T, int DH, bool PHI = true>
-__global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T* __restrict__ xt,
-                                                                      const T* __restrict__ wp, int T_, int d, int H,
-                                                                      T* __restrict__ q_out, T* __restrict__ k_out,
-                                                                      T* __restrict__ v_out) {
-  using S = typename ProjCfg<T, DH>::S;
-  constexpr bool DL = ProjCfg<T, DH>::DL;
-  constexpr int HPB = ProjCfg<T, DH>::HPB;
-  static_assert(S::BN == HPB * 3 * DH, "a block covers whole heads");
+// PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION)
+template <typename T, int DH, bool PHI, int NSEG>
+__global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS)) void k_proj(
+    const T* __restrict__ xt, const T* __restrict__ wp, int T_, int d, int H, T* __restrict__ q_out,
+    T* __restrict__ k_out, T* __restrict__ v_out, T* __restrict__ r_out) {
+  using Cfg = ProjCfg<T, DH, NSEG>;
+  using S = typename Cfg::S;
+  constexpr bool DL = Cfg::DL;
+  constexpr int HPB = Cfg::HPB;
+  constexpr int NP = NSEG * DH;  // weight rows per head
+  static_assert(S::BN == HPB * NP, "a block covers whole heads");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
   const int mtiles = (T_ + S::BM - 1) / S::BM, hgroups = (H + HPB - 1) / HPB;
@@ -322,13 +337,13 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
   if (lid >= mtiles * hgroups) return;
   const int mt = lid / hgroups, h0 = (lid - mt * hgroups) * HPB;
   const int m0 = mt * S::BM;
-  const int nb = min(HPB, H - h0) * 3 * DH;  // valid weight rows (a last odd head)
+  const int nb = min(HPB, H - h0) * NP;  // valid weight rows (a last odd head)
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
-    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * 3 * DH * d, d, nb, d, smem, smem1,
+    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d, smem, smem1,
                   smem1, smem1, acc);
   else
-    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * 3 * DH * d, d, nb, d,
+    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d,
                            smem, acc);
   // epilogue: phi on Q and K, staged per wave through LDS (the main loop ended
   // with a barrier, so smem is free) and written as 16-byte row vectors
@@ -345,7 +360,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
       const int n = wn * S::WTN + 16 * j;
-      const bool lin = !PHI || (n % (3 * DH)) / DH == 2;  // v columns (and everything without phi) stay linear
+      const bool lin = !PHI || (n % NP) / DH >= 2;  // v and r columns (and everything without phi) stay linear
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float v = acc[i][j][r];
@@ -357,28 +372,31 @@ __global__ __launch_bounds__((ProjCfg<T, DH>::S::NTHREADS)) void k_proj(const T*
       const int r = it / VPR, c = (it % VPR) * 8;
       const int t = m0 + wm * S::WTM + 16 * i + r;
       const int n = wn * S::WTN + c;
-      const int h = h0 + n / (3 * DH), nn = n % (3 * DH), kind = nn / DH;
-      T* out = kind == 0 ? q_out : (kind == 1 ? k_out : v_out);
+      const int h = h0 + n / NP, nn = n % NP, kind = nn / DH;
+      T* out = kind == 0 ? q_out : (kind == 1 ? k_out : (kind == 2 ? v_out : r_out));
       if (t < T_ && h < H) frag_store(out + (size_t)t * D + h * DH + (nn % DH), frag_load(ws + r * LDO + c));
     }
     __syncthreads();
   }
 }
 
-template <typename T, int DH, bool PHI>
-static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, hipStream_t s) {
-  using S = typename ProjCfg<T, DH>::S;
-  constexpr int HPB = ProjCfg<T, DH>::HPB;
+template <typename T, int DH, bool PHI, int NSEG>
+static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, void* r,
+                   hipStream_t s) {
+  using S = typename ProjCfg<T, DH, NSEG>::S;
+  constexpr int HPB = ProjCfg<T, DH, NSEG>::HPB;
   const int n = ((T_ + S::BM - 1) / S::BM) * ((H + HPB - 1) / HPB);
   if (n == 0) return;
-  hipLaunchKernelGGL((k_proj<T, DH, PHI>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
-                     (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v);
+  hipLaunchKernelGGL((k_proj<T, DH, PHI, NSEG>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
+                     (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v, (T*)r);
 }
 
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
-                 void* v_out, hipStream_t s, bool phi) {
-#define GBLA_PJ(TT, DD) (phi ? proj_t<TT, DD, true>(xt, wp, T, d, H, q_out, k_out, v_out, s) \
-                             : proj_t<TT, DD, false>(xt, wp, T, d, H, q_out, k_out, v_out, s))
+                 void* v_out, hipStream_t s, bool phi, void* r_out) {
+#define GBLA_PJ(TT, DD)                                                                \
+  (r_out ? proj_t<TT, DD, true, 4>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)      \
+         : (phi ? proj_t<TT, DD, true, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s) \
+                : proj_t<TT, DD, false, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)))
   if (dt == BF16) { if (dh == 64) GBLA_PJ(bf16, 64); else GBLA_PJ(bf16, 32); }
   else            { if (dh == 64) GBLA_PJ(float, 64); else GBLA_PJ(float, 32); }
 #undef GBLA_PJ
@@ -557,17 +575,17 @@ void launch_combine(const float* partial, const int* nchunks, const int* chunk_o
                      H, elems, mpart, out, mout);
 }
 
-// out[e] = sum over p < P of in[p * E + e], P = *P_dev if given else P_host.
+// out[e] = sum over p < P of in[p * E + e], P = *P_dev * p_mul if given else P_host.
 // A block covers EB elements with 256 / EB phases; each thread keeps eight
 // independent partial sums so its loads stay in flight. Fixed summation order.
 template <int EB>
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ in, int E, int P_host,
-                                                   const int* __restrict__ P_dev, float* __restrict__ out) {
+                                                   const int* __restrict__ P_dev, int p_mul, float* __restrict__ out) {
   constexpr int PH = 256 / EB;
   __shared__ float red[PH][EB];
   const int el = threadIdx.x % EB, ph = threadIdx.x / EB;
   const int e = blockIdx.x * EB + el;
-  const int P = P_dev ? *P_dev : P_host;
+  const int P = P_dev ? *P_dev * p_mul : P_host;
   float a[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) a[u] = 0.f;
@@ -587,11 +605,15 @@ __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ in,
   }
 }
 
-void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s) {
+void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s,
+                      int p_mul) {
   if (E <= 0) return;
 #define GBLA_SUMP(EB) hipLaunchKernelGGL(k_sum_parts<EB>, dim3((E + EB - 1) / EB), dim3(256), 0, s, in, E, P_host, \
-                                         P_dev, out)
-  if (E >= 64) GBLA_SUMP(64);
+                                         P_dev, p_mul, out)
+  // p_mul > 1 sums a long list of parts (one per chunk and head): narrower
+  // blocks give each element more threads (256 / EB) and the list more blocks
+  if (p_mul > 1) GBLA_SUMP(4);
+  else if (E >= 64) GBLA_SUMP(64);
   else if (E > 16) GBLA_SUMP(32);
   else if (E > 4) GBLA_SUMP(16);
   else GBLA_SUMP(4);
@@ -602,13 +624,17 @@ void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, floa
 // Stages [S | z] of the chunk's sequence in LDS as the B operand (column n of
 // S, column dh = z), split into a high and a low bfloat16 part for bf16 so the
 // state keeps ~16 mantissa bits; A = phi(q) rows straight from HBM.
+// GATED: the gated RMSNorm output of Eq. (7) in the epilogue; a token's d_h
+// outputs sit in the 16 lanes of one row group (FB per lane), so its mean
+// square is a 4-step butterfly; the R tile is staged beside phi(q).
 template <typename T> struct SplitState { static constexpr int parts = 2; };
 template <> struct SplitState<float> { static constexpr int parts = 1; };
 
-template <typename T, int DH>
+template <typename T, int DH, bool GATED>
 __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const float* __restrict__ saved,
                                                  const int* __restrict__ nchunks, const Chunk* __restrict__ tab,
-                                                 int max_slots, int H, T* __restrict__ y) {
+                                                 int max_slots, int H, T* __restrict__ y, const T* __restrict__ ra,
+                                                 const float* __restrict__ gamma, float eps) {
   constexpr int FB = DH / 16;
   constexpr int NR = DH + 16;
   constexpr int LD = DH + 16 / (int)sizeof(T);
@@ -617,6 +643,7 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   constexpr int ST = 64, V8 = DH / 8;
   __shared__ __align__(16) T Bs[P * NR * LD];
   __shared__ __align__(16) T qs[ST * LD];  // phi(q) tile, then y
+  __shared__ __align__(16) T rs[GATED ? ST * LD : 8];  // R tile (gated output)
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
@@ -627,15 +654,20 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
   stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid);
   const int r0 = 16 * w;
+  float gam[FB];  // RMSNorm scale of the lane's features 16 nt + col
+#pragma unroll
+  for (int nt = 0; nt < FB; ++nt) gam[nt] = GATED && gamma ? gamma[16 * nt + col] : 1.f;
 
   // the next tile's loads are issued before the current tile is processed
   constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pf[NV];
+  Frag8<T> pf[NV], pr[NV];
   auto fetch = [&](int tb) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
-      pf[v] = it < ST * V8 && t < ch.end ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>();
+      const bool ok = it < ST * V8 && t < ch.end;
+      pf[v] = ok ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>();
+      if constexpr (GATED) pr[v] = ok ? frag_load(ra + (size_t)t * D + h * DH + c) : frag_zero<T>();
     }
   };
   fetch(ch.start);
@@ -643,7 +675,10 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v;
-      if (it < ST * V8) frag_store(qs + (it / V8) * LD + (it % V8) * 8, pf[v]);
+      if (it < ST * V8) {
+        frag_store(qs + (it / V8) * LD + (it % V8) * 8, pf[v]);
+        if constexpr (GATED) frag_store(rs + (it / V8) * LD + (it % V8) * 8, pr[v]);
+      }
     }
     __syncthreads();
     if (tb + ST < ch.end) fetch(tb + ST);
@@ -662,10 +697,30 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      const int row = r0 + 4 * grp + r;
+      const bool ok = tb + row < ch.end;
       const float den = col0_bcast(acc[FB][r], lane);
-      const float inv = tb + r0 + 4 * grp + r < ch.end ? fast_rcp(den) : 0.f;
+      const float inv = ok ? fast_rcp(den) : 0.f;
+      if constexpr (GATED) {
+        // y = gamma (.) O / sqrt(mean(O^2) + eps) (.) SiLU(r)
+        float o[FB], ss = 0.f;
 #pragma unroll
-      for (int nt = 0; nt < FB; ++nt) qs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(acc[nt][r] * inv);
+        for (int nt = 0; nt < FB; ++nt) {
+          o[nt] = acc[nt][r] * inv;
+          ss += o[nt] * o[nt];
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        const float rinv = ok ? fast_rsqrt(ss * (1.f / DH) + eps) : 0.f;
+#pragma unroll
+        for (int nt = 0; nt < FB; ++nt) {
+          const float rv = to_f<T>(rs[row * LD + 16 * nt + col]);
+          qs[row * LD + 16 * nt + col] = from_f<T>(gam[nt] * o[nt] * rinv * rv * sigmoidf_(rv));
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < FB; ++nt) qs[row * LD + 16 * nt + col] = from_f<T>(acc[nt][r] * inv);
+      }
     }
     __syncthreads();
     for (int it = tid; it < ST * V8; it += 256) {
@@ -678,10 +733,17 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
 }
 
 void launch_readout(int dt, int dh, const void* qa, const float* saved, const int* nchunks, const Chunk* tab,
-                    int max_slots, int H, void* y, hipStream_t s) {
+                    int max_slots, int H, void* y, hipStream_t s, const void* ra, const float* gamma, float eps) {
   const dim3 grid(xcd_grid(max_slots * H));
-#define GBLA_RO(TT, DD) hipLaunchKernelGGL((k_readout<TT, DD>), grid, dim3(256), 0, s, (const TT*)qa, saved, \
-                                           nchunks, tab, max_slots, H, (TT*)y)
+#define GBLA_RO(TT, DD)                                                                                        \
+  do {                                                                                                         \
+    if (ra)                                                                                                    \
+      hipLaunchKernelGGL((k_readout<TT, DD, true>), grid, dim3(256), 0, s, (const TT*)qa, saved, nchunks, tab, \
+                         max_slots, H, (TT*)y, (const TT*)ra, gamma, eps);                                     \
+    else                                                                                                       \
+      hipLaunchKernelGGL((k_readout<TT, DD, false>), grid, dim3(256), 0, s, (const TT*)qa, saved, nchunks,     \
+                         tab, max_slots, H, (TT*)y, (const TT*)ra, gamma, eps);                                \
+  } while (0)
   if (dt == BF16) { if (dh == 64) GBLA_RO(bf16, 64); else GBLA_RO(bf16, 32); }
   else            { if (dh == 64) GBLA_RO(float, 64); else GBLA_RO(float, 32); }
 #undef GBLA_RO

@@ -39,22 +39,27 @@ constexpr int kChunk = 256;
 // upper bound on the number of chunks of `chunk` tokens for T tokens in N sequences
 inline int max_chunks(int T, int N, int chunk = kChunk) { return (T + chunk - 1) / chunk + N; }
 
-// rows of the packed per-head projection weights: Q, K and V features
-inline int proj_cols(int dh) { return 3 * dh; }
+// rows of the packed per-head projection weights: Q, K and V features, and with
+// the gated RMSNorm output also R (the gate pre-activation x~ W_R)
+inline int proj_cols(int dh, bool out_gate = false) { return (out_gate ? 4 : 3) * dh; }
 
-// columns of the gradient matrix [dQ | dK | dV | ds | 0-pad], padded to 64
-inline int grad_cols(int H, int dh) { return ((3 * H * dh + H) + 63) / 64 * 64; }
+// columns of the gradient matrix [dQ | dK | dV | (dR) | ds | 0-pad], padded to 64
+inline int grad_cols(int H, int dh, bool out_gate = false) {
+  return (((out_gate ? 4 : 3) * H * dh + H) + 63) / 64 * 64;
+}
 
 // ---- forward / shared
 void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
                      Chunk* tab, hipStream_t s);
-void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, int d, int H, int dh, void* wp,
-                      hipStream_t s);
+// w_r non-null: a fourth per-head segment (the gated RMSNorm output's W_R)
+void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
+                      int dh, void* wp, hipStream_t s);
 // g gets sigmoid(x~ w_g + b_g), or the logit itself for the softmax key gate
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
                      const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s);
+// r_out non-null: wp holds four segments per head and the fourth (linear) goes to r_out
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
-                 void* v_out, hipStream_t s, bool phi = true);
+                 void* v_out, hipStream_t s, bool phi = true, void* r_out = nullptr);
 void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
                       const float* b_lam, float* logl, hipStream_t s);
 // log lambda of every token for a decay that does not depend on the token:
@@ -66,28 +71,40 @@ void launch_state_partial(int dt, int dh, const void* ka, const void* va, const 
 // mpart non-null: rescale the partials to the sequence's largest chunk maximum (written to mout)
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
                     float* out, hipStream_t s, const float* mpart = nullptr, float* mout = nullptr);
-void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s);
+// out[e] = sum over the first P parts, P = (*P_dev) * p_mul if P_dev else P_host
+void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s,
+                      int p_mul = 1);
+// ra non-null: gated RMSNorm output, y = gamma (.) O / sqrt(mean(O^2) + eps) (.) SiLU(r)
+// per head (gamma null: no scale)
 void launch_readout(int dt, int dh, const void* qa, const float* saved, const int* nchunks, const Chunk* tab,
-                    int max_slots, int H, void* y, hipStream_t s);
+                    int max_slots, int H, void* y, hipStream_t s, const void* ra = nullptr,
+                    const float* gamma = nullptr, float eps = 0.f);
 
 // ---- backward
-// w_g may be null (its rows of Wt are zero)
-void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_g, int d, int H,
-                    int dh, int Kp, void* wt, hipStream_t s);
+// w_g may be null (its rows of Wt are zero); w_r non-null: the R segment
+// follows V ([W_Q | W_K | W_V | W_R | w_g^T])
+void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
+                    int d, int H, int dh, int Kp, void* wt, hipStream_t s);
+// ra non-null: gated RMSNorm output; dy is then the gradient of the gated
+// output, dR goes to G's R columns and per-(chunk, head) partials of dgamma
+// to dgam_part (gamma non-null)
 void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const float* saved, const int* nchunks,
-                       const Chunk* tab, int max_slots, int H, int Kp, float* partial, void* G, hipStream_t s);
+                       const Chunk* tab, int max_slots, int H, int Kp, float* partial, void* G, hipStream_t s,
+                       const void* ra = nullptr, const float* gamma = nullptr, float eps = 0.f,
+                       float* dgam_part = nullptr);
 // gmax non-null: softmax key gate (ga holds logits; the gate is exp(s - gmax[seq][h]))
+// G's gate column of head h is nseg * H * dh + h (nseg = 4 with the R segment)
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
-                      const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G, float* dbg_part,
-                      const float* gmax, hipStream_t s);
+                      const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, int nseg, void* G,
+                      float* dbg_part, const float* gmax, hipStream_t s);
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s);
 int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
-// dw_g may be null (its columns are not written)
+// dw_g may be null (its columns are not written); dw_r non-null: G has the R segment
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
-                      float* dw_v, float* dw_g, hipStream_t s);
+                      float* dw_v, float* dw_r, float* dw_g, hipStream_t s);
 void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,
                      const void* conv_w, void* dx, float* dconv_part, hipStream_t s);
 int conv_bwd_row_blocks(int T);

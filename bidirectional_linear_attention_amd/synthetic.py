@@ -20,6 +20,10 @@ Draw order (fixed, so a workload is a pure function of its seed):
   7. dY ~ N(0, 1)              [T, H*d_h]
 Values are then rounded to the storage dtype (round-to-nearest-even for bf16)
 and kept as float32 arrays holding exactly representable values.
+
+The gated RMSNorm output of the GBLA page's Eq. (7) draws its weights from a
+second stream (seed + 7919), so turning it on leaves the draws above intact:
+  W_R ~ N(0, 1/d) [d, H*d_h] (storage dtype), gamma ~ 1 + 0.1 N(0, 1) [d_h] (float32).
 """
 from __future__ import annotations
 
@@ -28,7 +32,7 @@ from typing import Optional
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "round_bf16", "small_variant"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_output_gate", "round_bf16", "small_variant"]
 
 
 def round_bf16(a: np.ndarray) -> np.ndarray:
@@ -149,3 +153,15 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     else:
         out["w_g"], out["b_g"] = w_g, b_g
     return out
+
+
+def make_output_gate(w: Workload, seed: Optional[int] = None) -> dict:
+    """Weights of the gated RMSNorm output for workload w: w_r [d, H*d_h]
+    (values exact in the workload's dtype) and gamma [d_h] (float32)."""
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 7919)
+    d, D = w.d_model, w.num_heads * w.head_dim
+    w_r = (rng.standard_normal((d, D)) / np.sqrt(d)).astype(np.float32)
+    gamma = (1.0 + 0.1 * rng.standard_normal(w.head_dim)).astype(np.float32)
+    if w.dtype == "bf16":
+        w_r = round_bf16(w_r)
+    return dict(w_r=w_r, gamma=gamma)

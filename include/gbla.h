@@ -12,7 +12,11 @@
  *          or softmax over the sequence's tokens j of x~_j . w_g^h + b_g^h
  *             (GBLA_GATE_SOFTMAX: the gate exactly as Eq. (5) writes it)
  *   S       = sum_j g_j phi(k_j) v_j^T,  z = sum_j g_j phi(k_j)  (Eq. (6), phi(u) = elu(u) + 1)
- *   y_i     = phi(q_i)^T S / phi(q_i)^T z                        (Eq. (5), state-first order of Eq. (3))
+ *   O_i     = phi(q_i)^T S / phi(q_i)^T z                        (Eq. (5), state-first order of Eq. (3))
+ *   y_i     = O_i, or with the gated RMSNorm output (component (3), Eq. (7))
+ *   y_i     = gamma (.) O_i / sqrt(mean_c O_ic^2 + eps) (.) SiLU(x~_i W_R^h)
+ *             (RMS over the head's d_h features, eps inside the root, gamma [d_h]
+ *             a learnable scale shared by the heads, or none)
  *
  * The conv restarts at every sequence start (zero left padding, tap 3 multiplies
  * the current token, tap k the token 3-k steps back) and S, z cover only the
@@ -35,9 +39,10 @@
  *    (outputs are unspecified but no memory outside the arguments is touched).
  *  - Results are deterministic: every reduction runs in a fixed order with no
  *    floating-point atomics, so repeated calls are bitwise identical.
- *  - Large arrays must be 16-byte aligned; b_g, db_g, dconv_w and cu_seqlens
- *    4-byte aligned.
- *  - Sizes: total_tokens * max(d_model, 3*H*d_h + H + 64) < 2^31.
+ *  - Large arrays must be 16-byte aligned; b_g, db_g, dconv_w, gamma, dgamma
+ *    and cu_seqlens 4-byte aligned.
+ *  - Sizes: total_tokens * max(d_model, S*H*d_h + H + 64) < 2^31, S = 3 (4 with
+ *    the gated output).
  *  - Calls that share a workspace must not overlap in time.
  */
 #ifndef GBLA_H_
@@ -73,6 +78,8 @@ enum { GBLA_DTYPE_F32 = 0, GBLA_DTYPE_BF16 = 1 };
  * sequence's largest logit, and its normaliser never needs to be formed; its
  * bias gradient db_g is zero up to rounding (the softmax is shift invariant). */
 enum { GBLA_GATE_SIGMOID = 0, GBLA_GATE_SOFTMAX = 1 };
+/* readout: O itself, or the gated RMSNorm output of Eq. (7) */
+enum { GBLA_OUTPUT_PLAIN = 0, GBLA_OUTPUT_GATED_RMSNORM = 1 };
 
 typedef struct {
   int32_t num_seqs;     /* N >= 1 packed sequences (empty sequences allowed) */
@@ -83,6 +90,8 @@ typedef struct {
   int32_t dtype;        /* GBLA_DTYPE_F32 or GBLA_DTYPE_BF16 */
   int32_t gate;         /* GBLA_GATE_SIGMOID or GBLA_GATE_SOFTMAX */
   int32_t conv_width;   /* must be 4 */
+  int32_t output_gate;  /* GBLA_OUTPUT_PLAIN or GBLA_OUTPUT_GATED_RMSNORM */
+  float norm_eps;       /* eps of the gated output's RMSNorm: finite, >= 0 (ignored when plain) */
 } gbla_problem;
 
 /* Human-readable name of a status code (static string). */
@@ -106,7 +115,8 @@ GBLA_API gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes);
 GBLA_API gbla_status gbla_workspace_size(const gbla_problem* p, int backward, size_t* bytes);
 
 /* Bytes of the optional activation cache `act`: the conv output, phi(q),
- * phi(k), v (dtype) and the gates (float32) of every token, kept by
+ * phi(k), v, with the gated output also x~ W_R (dtype), and the gates
+ * (float32) of every token, kept by
  * gbla_forward so that gbla_backward needs no recomputation. Its layout is
  * internal to the library. */
 GBLA_API gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes);
@@ -117,6 +127,10 @@ GBLA_API gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes);
  *   conv_w   [d, 4]        depthwise conv taps (dtype)
  *   w_q, w_k, w_v [d, H*d_h] projections; head h owns columns h*d_h.. (dtype)
  *   w_g      [H, d]        gate weights (dtype);  b_g [H] gate bias (float32)
+ *   w_r      [d, H*d_h]    Eq. (7) gate weights, head h in columns h*d_h.. (dtype);
+ *                          required with GBLA_OUTPUT_GATED_RMSNORM, NULL otherwise
+ *   gamma    [d_h]         Eq. (7) RMSNorm scale (float32), or NULL for none;
+ *                          must be NULL without the gated output
  *   y        [T, H*d_h]    output (dtype, overwritten)
  *   saved    see gbla_saved_size (float32, overwritten): the states S and z
  *   act      optional activation cache (gbla_activation_size bytes, overwritten)
@@ -124,8 +138,8 @@ GBLA_API gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes);
  *   workspace, workspace_bytes: at least gbla_workspace_size(p, 0) bytes */
 GBLA_API gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                                   const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                                  void* y, float* saved, void* act, void* workspace, size_t workspace_bytes,
-                                  void* stream);
+                                  const void* w_r, const float* gamma, void* y, float* saved, void* act,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass: gradients of sum(y * dy) for the forward above, obtained by
  * the chain rule through Eqs. (4)-(6). Inputs as in gbla_forward plus
@@ -136,11 +150,14 @@ GBLA_API gbla_status gbla_forward(const gbla_problem* p, const void* x, const in
  * Outputs (all overwritten, never accumulated):
  *   dx       [T, d] (dtype);  dconv_w [d, 4];  dw_q, dw_k, dw_v [d, H*d_h];
  *   dw_g     [H, d];  db_g [H]   (all float32)
+ *   dw_r     [d, H*d_h] (float32): required with the gated output, NULL otherwise
+ *   dgamma   [d_h] (float32): required exactly when gamma is given
  *   workspace, workspace_bytes: at least gbla_workspace_size(p, 1) bytes */
 GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
                                    const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
-                                   const float* saved, const void* act, const void* dy, void* dx, float* dconv_w,
-                                   float* dw_q, float* dw_k, float* dw_v, float* dw_g, float* db_g, void* workspace,
+                                   const void* w_r, const float* gamma, const float* saved, const void* act,
+                                   const void* dy, void* dx, float* dconv_w, float* dw_q, float* dw_k, float* dw_v,
+                                   float* dw_g, float* db_g, float* dw_r, float* dgamma, void* workspace,
                                    size_t workspace_bytes, void* stream);
 
 /* ---- Optional per-stage timing (benchmarking aid) ----------------------

@@ -41,15 +41,18 @@ def test_status_strings_and_version():
 
 
 def _prob(**kw):
-    base = dict(num_seqs=2, total_tokens=100, d_model=64, num_heads=2, head_dim=64, dtype=gb.DTYPE_BF16)
+    base = dict(num_seqs=2, total_tokens=100, d_model=64, num_heads=2, head_dim=64, dtype=gb.DTYPE_BF16,
+                output_gate=0, norm_eps=1e-6)
     base.update(kw)
     return gb.GblaProblem(base["num_seqs"], base["total_tokens"], base["d_model"], base["num_heads"],
-                          base["head_dim"], base["dtype"], 0, 4)
+                          base["head_dim"], base["dtype"], 0, 4, base["output_gate"], base["norm_eps"])
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(d_model=60), 2), (dict(num_seqs=0), 2),
     (dict(total_tokens=-1), 2), (dict(num_heads=0), 2), (dict(total_tokens=1 << 30), 2),
+    (dict(output_gate=2), 3), (dict(output_gate=1, norm_eps=-1.0), 2), (dict(output_gate=1, norm_eps=float("nan")), 2),
+    (dict(output_gate=1, norm_eps=float("inf")), 2),
 ])
 def test_size_queries_reject_bad_problems(kw, status):
     lib = _lib.load()
@@ -112,7 +115,9 @@ def test_forward_rejects_null_misaligned_and_small_workspace_without_launching()
     out = ctypes.c_size_t()
     lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out))
     need = out.value
-    a = [_fake(0x10000 + 0x1000 * i) for i in range(11)]
+    # x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, y, saved, act (w_r, gamma NULL: plain output)
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(13)]
+    a[8] = a[9] = None
     # NULL weight
     args = list(a)
     args[4] = None
@@ -126,6 +131,29 @@ def test_forward_rejects_null_misaligned_and_small_workspace_without_launching()
     # bad problem is reported first
     bad = _prob(head_dim=16)
     assert lib.gbla_forward(ctypes.byref(bad), *a, _fake(0x900000), need, None) == 3
+    # the plain output takes no W_R and no gamma
+    args = list(a)
+    args[9] = _fake(0x80000)
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+
+
+def test_forward_gated_output_argument_rules():
+    lib = _lib.load()
+    p = _prob(output_gate=1)
+    out = ctypes.c_size_t()
+    lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(13)]
+    args = list(a)
+    args[8] = None    # W_R is required
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    args = list(a)
+    args[8] = _fake(0x18008)   # misaligned W_R
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
+    args = list(a)
+    args[9] = _fake(0x19002)   # misaligned gamma
+    assert lib.gbla_forward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 4
+    assert lib.gbla_forward(ctypes.byref(p), *a, _fake(0x900000), need - 1, None) == 5
 
 
 def test_backward_rejects_null_and_small_workspace_without_launching():
@@ -134,11 +162,48 @@ def test_backward_rejects_null_and_small_workspace_without_launching():
     out = ctypes.c_size_t()
     lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
     need = out.value
-    a = [_fake(0x10000 + 0x1000 * i) for i in range(18)]
+    # x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, saved, act, dy, dx, dconv_w,
+    # dw_q, dw_k, dw_v, dw_g, db_g, dw_r, dgamma
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(22)]
+    a[8] = a[9] = a[20] = a[21] = None
     args = list(a)
-    args[17] = None   # db_g
+    args[19] = None   # db_g
     assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
     assert lib.gbla_backward(ctypes.byref(p), *a, _fake(0x900000), need - 256, None) == 5
+
+
+def test_backward_gated_output_argument_rules():
+    lib = _lib.load()
+    p = _prob(output_gate=1)
+    out = ctypes.c_size_t()
+    lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
+    need = out.value
+    a = [_fake(0x10000 + 0x1000 * i) for i in range(22)]
+    for idx in (8, 20):           # W_R and dW_R are required
+        args = list(a)
+        args[idx] = None
+        assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    args = list(a)
+    args[21] = None               # gamma given without dgamma
+    assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need, None) == 1
+    args[9] = None                # neither: no RMSNorm scale
+    assert lib.gbla_backward(ctypes.byref(p), *args, _fake(0x900000), need - 256, None) == 5
+
+
+def test_gated_output_sizes():
+    """The gated output adds the R segment: activations grow by T*H*d_h
+    elements, and so does the gradient matrix in the backward workspace."""
+    lib = _lib.load()
+    out = ctypes.c_size_t()
+    sizes = {}
+    for og in (0, 1):
+        p = _prob(output_gate=og)
+        lib.gbla_activation_size(ctypes.byref(p), ctypes.byref(out))
+        act = out.value
+        lib.gbla_workspace_size(ctypes.byref(p), 1, ctypes.byref(out))
+        sizes[og] = (act, out.value)
+    assert sizes[1][0] - sizes[0][0] >= 100 * 128 * 2
+    assert sizes[1][1] - sizes[0][1] >= 2 * (100 * 128 * 2)
 
 
 # ---------------------------------------------------------------- LION-s entry points

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import bidirectional_linear_attention_amd as gb
-from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, small_variant
+from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, make_output_gate, small_variant
 from oracle import gbla as og
 
 pytestmark = pytest.mark.gpu
@@ -41,17 +41,23 @@ def to_dev(inp):
                 b_g=torch.from_numpy(inp["b_g"]).float().to("cuda"), dy=t(inp["dy"]))
 
 
-def run_gpu(inp, backward, keep_act=True, gate="sigmoid"):
+def run_gpu(inp, backward, keep_act=True, gate="sigmoid", outg=None):
     """keep_act: pass forward's activation cache to the backward; False makes
-    the backward recompute the activations from x."""
+    the backward recompute the activations from x. outg: the gated RMSNorm
+    output's w_r, gamma (or None) and eps."""
     d = to_dev(inp)
     H = inp["H"]
+    kw = dict(gate=gate)
+    if outg is not None:
+        dt = d["x"].dtype
+        kw.update(w_r=torch.from_numpy(outg["w_r"]).to("cuda").to(dt).contiguous(), norm_eps=outg["eps"],
+                  gamma=None if outg["gamma"] is None else torch.from_numpy(outg["gamma"]).float().to("cuda"))
     y, saved, act = gb.forward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"], H,
-                               save_activations=keep_act, gate=gate)
+                               save_activations=keep_act, **kw)
     out = {"y": y, "saved": saved}
     if backward:
         out.update(gb.backward(d["x"], d["cu"], d["conv_w"], d["w_q"], d["w_k"], d["w_v"], d["w_g"], d["b_g"],
-                               saved, act, d["dy"], H, gate=gate))
+                               saved, act, d["dy"], H, **kw))
     torch.cuda.synchronize()
     return {k: v.float().cpu().numpy() for k, v in out.items()}
 
@@ -71,15 +77,16 @@ def gate_logit_max(inp):
     return m
 
 
-def compare(inp, backward, tol=None, label="", keep_act=True, gate="sigmoid"):
+def compare(inp, backward, tol=None, label="", keep_act=True, gate="sigmoid", outg=None):
     """With the softmax gate the library keeps S and z built from exp(s - m),
     a per-(sequence, head) multiple of the oracle's; they are compared after
     dividing both by the sum of z, and the stored m against the largest logit.
     db_g is zero in exact arithmetic there (shift invariance), so it is held to
     tol times sum_t |ds_t|, the size of the terms that cancel."""
     tol = TOL[inp["dtype"]] if tol is None else tol
-    gpu = run_gpu(inp, backward, keep_act, gate)
-    y, S, z = og.forward(*oracle_args(inp), inp["H"], gate=gate)
+    gpu = run_gpu(inp, backward, keep_act, gate, outg)
+    okw = {} if outg is None else dict(w_r=outg["w_r"], gamma=outg["gamma"], eps=outg["eps"])
+    y, S, z = og.forward(*oracle_args(inp), inp["H"], gate=gate, **okw)
     N, H, dh = inp["N"], inp["H"], inp["dh"]
     E = dh * dh + dh
     sv = gpu["saved"].reshape(-1)[:N * H * E].reshape(N, H, E)
@@ -94,8 +101,9 @@ def compare(inp, backward, tol=None, label="", keep_act=True, gate="sigmoid"):
         m = gpu["saved"].reshape(-1)[N * H * E:].reshape(N, H)
         errs["m"] = rel_err(m, gate_logit_max(inp))
     if backward:
-        g = og.backward(*oracle_args(inp), inp["dy"], inp["H"], gate=gate)
-        for k in GRADS:
+        g = og.backward(*oracle_args(inp), inp["dy"], inp["H"], gate=gate, **okw)
+        extra = () if outg is None else ("dw_r",) + (() if outg["gamma"] is None else ("dgamma",))
+        for k in GRADS + extra:
             if gate == "softmax" and k == "db_g":
                 scale = np.abs(g["ds"]).sum(axis=0)
                 errs[k] = float(np.max(np.abs(gpu[k] - g[k]) / np.maximum(scale, 1e-30)))
@@ -268,3 +276,49 @@ def test_softmax_gate_recompute_path():
 def test_softmax_gate_bf16_B8_L8192_d512_full():
     w = WORKLOADS["gbla_bf16_B8_L8192_d512"]
     compare(make_inputs(w), backward=True, label=w.name + " softmax", gate="softmax")
+
+
+# ------------------------------------------------------------ gated RMSNorm output (Eq. (7))
+
+def _outg(w, gamma=True, eps=1e-6):
+    o = make_output_gate(w)
+    return dict(w_r=o["w_r"], gamma=o["gamma"] if gamma else None, eps=eps)
+
+
+@pytest.mark.parametrize("lengths,d,H,dh,gamma", [
+    ((300, 1, 513, 0, 77), 96, 3, 64, True),   # several tiles, ragged tails, single-token and empty sequences
+    ((129, 255, 2), 64, 2, 32, True),          # head_dim 32 (two heads per projection block)
+    ((700,), 40, 1, 64, False),                # no RMSNorm scale; d not a multiple of the k chunk
+])
+def test_output_gate_f32_multi_tile(lengths, d, H, dh, gamma):
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lengths, d_model=d, num_heads=H, head_dim=dh,
+                      dtype="f32", seed=51)
+    compare(make_inputs(w), backward=True, label="gated f32 " + str(lengths), outg=_outg(w, gamma))
+
+
+def test_output_gate_f32_large_eps_and_softmax_key_gate():
+    """A large eps (the norm no longer removes the scale) with the softmax key gate."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (600, 301), d_model=64, num_heads=2, head_dim=64,
+                      dtype="f32", seed=52)
+    compare(make_inputs(w), backward=True, label="gated f32 eps 0.5 softmax", gate="softmax",
+            outg=_outg(w, eps=0.5))
+
+
+@pytest.mark.parametrize("dh", [64, 32])
+def test_output_gate_bf16_small(dh):
+    w = small_variant(WORKLOADS["gbla_bf16_B8_L8192_d512"], (2048, 1500, 3), head_dim=dh, seed=53)
+    compare(make_inputs(w), backward=True, label=f"gated bf16 dh={dh}", outg=_outg(w))
+
+
+def test_output_gate_recompute_path_matches_cache():
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (700, 300), seed=54)
+    inp, outg = make_inputs(w), _outg(w)
+    a = run_gpu(inp, True, True, outg=outg)
+    b = run_gpu(inp, True, False, outg=outg)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_output_gate_bf16_B8_L8192_d512_full():
+    w = WORKLOADS["gbla_bf16_B8_L8192_d512"]
+    compare(make_inputs(w), backward=True, label=w.name + " gated output", outg=_outg(w))
