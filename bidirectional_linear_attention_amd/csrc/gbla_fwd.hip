@@ -288,14 +288,16 @@ void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipSt
 }
 
 // ============================================================== projection GEMM
-// Block = 256 tokens x the [Q | K | V] columns (3 dh each; with the gated
+// Block = BM tokens x the [Q | K | V] columns (3 dh each; with the gated
 // RMSNorm output [Q | K | V | R], 4 dh) of HPB consecutive heads (the packed
 // per-head panels are contiguous, so HPB heads are one B operand). bf16 runs the
-// direct-to-LDS main loop, float the register-staged one.
+// direct-to-LDS main loop, float the register-staged one. For d_h = 64 the
+// 128 x 192 bf16 tile (8 waves of 32 x 96) leaves room for two blocks per CU,
+// so one block's output stores overlap another's main loop.
 // Epilogue: phi on Q and K, identity on V and R.
 template <typename T, int DH, int NSEG> struct ProjCfg;
 template <> struct ProjCfg<bf16, 64, 3> {
-  using S = DlShape<256, 384, 32, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+  using S = DlShape<128, 192, 64, 4, 2, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<bf16, 32, 3> {
   using S = DlShape<256, 192, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
@@ -319,9 +321,13 @@ template <> struct ProjCfg<float, 32, 4> {
   using S = GemmShape<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
 
+// pipeline depth of a main-loop shape (register-staged shapes have none)
+template <class S, class = void> struct NS_OF { static constexpr int n = 2; };
+template <class S> struct NS_OF<S, decltype(void(S::NS))> { static constexpr int n = S::NS; };
+
 // PHI = true: phi = elu + 1 on Q and K (GBLA); false: raw projections (LION)
 template <typename T, int DH, bool PHI, int NSEG>
-__global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS)) void k_proj(
+__global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS), 2) void k_proj(
     const T* __restrict__ xt, const T* __restrict__ wp, int T_, int d, int H, T* __restrict__ q_out,
     T* __restrict__ k_out, T* __restrict__ v_out, T* __restrict__ r_out) {
   using Cfg = ProjCfg<T, DH, NSEG>;
@@ -332,6 +338,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS)) void k_proj(
   static_assert(S::BN == HPB * NP, "a block covers whole heads");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
+  __shared__ __align__(16) T smem2[DL && NS_OF<S>::n > 2 ? S::STAGE : 8];
   const int mtiles = (T_ + S::BM - 1) / S::BM, hgroups = (H + HPB - 1) / HPB;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * hgroups);
   if (lid >= mtiles * hgroups) return;
@@ -341,7 +348,7 @@ __global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS)) void k_proj(
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
     gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d, smem, smem1,
-                  smem1, smem1, acc);
+                  smem2, smem2, acc);
   else
     gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d,
                            smem, acc);
