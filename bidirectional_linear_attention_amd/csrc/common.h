@@ -312,74 +312,81 @@ struct SeqCursor {
   }
 };
 
-// Stage a dh x dh float matrix M (row-major, read coalesced) and a vector z as
-// MFMA B operands in LDS, split into a high and a low part for bfloat16 (P = 2)
-// so the staged matrix keeps about 16 mantissa bits:
+// Stage a dh x dh float matrix M (row-major) and a vector z as MFMA B operands
+// in LDS, split into a high and a low part for bfloat16 (P = 2) so the staged
+// matrix keeps about 16 mantissa bits:
 //   MT[p][n][i] = M[i][n] for n < DH; row DH holds z, rows DH+1 .. NR-1 are 0
 //   MR[p][i][n] = M[i][n]
 // Either destination may be null; part 1 of MT starts NR rows after part 0,
-// part 1 of MR starts DH rows after part 0 (pitch ld elements, a multiple of 4).
-// M and z must be 16-byte aligned. Every thread of the NT-thread block issues
-// all of its 16-byte loads before its first LDS store.
+// part 1 of MR starts DH rows after part 0 (pitch ld elements; ld * sizeof(T)
+// a multiple of 16). M and z must be 16-byte aligned.
+// MT: a lane owns column n of M and a run of consecutive i, so its loads are
+// coalesced across the lanes (consecutive n) and its LDS stores are whole
+// 8- or 16-byte vectors along row n of MT (element-wise transposed stores
+// would put the lanes of a wave on a handful of banks). MR: float4 loads of a
+// row, stored as one vector each.
+// stores n consecutive values (n * sizeof(T) a multiple of 8) as whole vectors
+template <typename T, int N>
+__device__ __forceinline__ void lds_store_run(T* dst, const T (&v)[N]) {
+  constexpr int VE = 16 / (int)sizeof(T);
+  if constexpr (N % VE == 0) {
+#pragma unroll
+    for (int k = 0; k < N; k += VE) {
+      T tmp[VE];
+#pragma unroll
+      for (int j = 0; j < VE; ++j) tmp[j] = v[k + j];
+      *reinterpret_cast<uint4*>(dst + k) = __builtin_bit_cast(uint4, tmp);
+    }
+  } else {
+    static_assert(N * sizeof(T) == 8, "runs of 8 bytes or whole 16-byte vectors");
+    *reinterpret_cast<uint2*>(dst) = __builtin_bit_cast(uint2, v);
+  }
+}
+
 template <typename T, int DH, int NR, int NT = 256>
 __device__ __forceinline__ void stage_state(T* MT, T* MR, int ld, const float* __restrict__ M,
                                             const float* __restrict__ z, int tid) {
   constexpr bool SPLIT = sizeof(T) == 2;
-  constexpr int V4 = DH * DH / 4, PER = (V4 + NT - 1) / NT;
-  constexpr int XR = (NR - DH) * DH / 4;  // extra rows of MT, in 4-vectors
-  constexpr int XPER = XR > 0 ? (XR + NT - 1) / NT : 1;
-  float4 r[PER], x[XPER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e4 = tid + k * NT;
-    r[k] = e4 < V4 ? reinterpret_cast<const float4*>(M)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-#pragma unroll
-  for (int k = 0; k < XPER; ++k) {
-    const int e4 = tid + k * NT;
-    x[k] = MT && e4 < DH / 4 ? reinterpret_cast<const float4*>(z)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e4 = tid + k * NT;
-    if (e4 >= V4) continue;
-    const int i = (4 * e4) / DH, n = (4 * e4) % DH;
-    const float v[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
-    T hi[4], lo[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      hi[j] = from_f<T>(v[j]);
-      lo[j] = from_f<T>(v[j] - to_f<T>(hi[j]));
-    }
-    if (MT) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        MT[(n + j) * ld + i] = hi[j];
-        if (SPLIT) MT[NR * ld + (n + j) * ld + i] = lo[j];
-      }
-    }
-    if (MR) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        MR[i * ld + n + j] = hi[j];
-        if (SPLIT) MR[DH * ld + i * ld + n + j] = lo[j];
-      }
-    }
-  }
+  static_assert(NT % DH == 0 && (DH * DH) % NT == 0, "whole columns per thread group");
   if (MT) {
+    constexpr int IP = DH * DH / NT;  // consecutive i per thread
+    const int n = tid % DH, i0 = (tid / DH) * IP;
+    float v[IP];
 #pragma unroll
-    for (int k = 0; k < XPER; ++k) {  // rows DH.. of MT: z in row DH (from x), zeros below
+    for (int k = 0; k < IP; ++k) v[k] = M[(size_t)(i0 + k) * DH + n];
+    T hi[IP], lo[IP];
+#pragma unroll
+    for (int k = 0; k < IP; ++k) {
+      hi[k] = from_f<T>(v[k]);
+      lo[k] = from_f<T>(v[k] - to_f<T>(hi[k]));
+    }
+    lds_store_run(MT + n * ld + i0, hi);
+    if (SPLIT) lds_store_run(MT + NR * ld + n * ld + i0, lo);
+    for (int e = tid; e < (NR - DH) * DH; e += NT) {  // rows DH..: z in row DH, zeros below
+      const int r = DH + e / DH, i = e % DH;
+      const float u = r == DH ? z[i] : 0.f;
+      const T h = from_f<T>(u);
+      MT[r * ld + i] = h;
+      if (SPLIT) MT[NR * ld + r * ld + i] = from_f<T>(u - to_f<T>(h));
+    }
+  }
+  if (MR) {
+    constexpr int V4 = DH * DH / 4, PER = (V4 + NT - 1) / NT;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
       const int e4 = tid + k * NT;
-      if (e4 >= XR) continue;
-      const int n = DH + (4 * e4) / DH, i = (4 * e4) % DH;
-      const float v[4] = {x[k].x, x[k].y, x[k].z, x[k].w};
+      if (e4 >= V4) continue;
+      const int i = (4 * e4) / DH, n = (4 * e4) % DH;
+      const float4 r = reinterpret_cast<const float4*>(M)[e4];
+      const float v[4] = {r.x, r.y, r.z, r.w};
+      T hi[4], lo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float u = n == DH ? v[j] : 0.f;
-        const T hi = from_f<T>(u);
-        MT[n * ld + i + j] = hi;
-        if (SPLIT) MT[NR * ld + n * ld + i + j] = from_f<T>(u - to_f<T>(hi));
+        hi[j] = from_f<T>(v[j]);
+        lo[j] = from_f<T>(v[j] - to_f<T>(hi[j]));
       }
+      lds_store_run(MR + i * ld + n, hi);
+      if (SPLIT) lds_store_run(MR + DH * ld + i * ld + n, lo);
     }
   }
 }
