@@ -233,6 +233,16 @@ template <> __device__ __forceinline__ Quad<float> quad_kmajor<float>(const floa
 // ---------------------------------------------------------------- small helpers
 __device__ __forceinline__ float sigmoidf_(float s) { return fast_rcp(1.f + __expf(-s)); }
 // phi(u) = elu(u) + 1
+// Row order of a weight operand that is used as the A (row) side of a GEMM
+// whose output C[row][token] leaves straight from registers: in each group of
+// 32 rows, row p of the operand holds output feature tile_row_perm(p). A lane
+// (grp = lane / 16) holds C rows 4 grp .. 4 grp + 3 of the group's two 16-row
+// tiles, i.e. rows p = 16 u + 4 grp + r (u = 0, 1; r = 0..3), which are then
+// features 8 grp + 4 u + r: eight consecutive features, one vector store.
+__host__ __device__ __forceinline__ int tile_row_perm(int p) {
+  return (p & ~31) + 8 * ((p & 15) >> 2) + 4 * ((p >> 4) & 1) + (p & 3);
+}
+
 __device__ __forceinline__ float phi_elu1(float u) { return u > 0.f ? u + 1.f : __expf(u); }
 
 // Workgroup i runs on XCD i % 8. Give every XCD a contiguous range of logical

@@ -96,7 +96,7 @@ size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
-  t.wt = c.take<char>(base, (size_t)m.d * m.Kp * m.esz);
+  t.wt = c.take<char>(base, (size_t)wt_rows(m.d) * m.Kp * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
   t.dsz = c.take<float>(base, sizeof(float) * (size_t)m.N * m.H * m.E);
   t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);

@@ -450,17 +450,20 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
 }
 
 // ============================================================== weight packing for dX~
-// wt[c][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | w_g[:,c] | 0]
+// wt[p][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | (W_R[c,:]) | w_g[:,c] | 0] for
+// channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all)
 template <typename T>
 __global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
                           const T* __restrict__ w_r, const T* __restrict__ w_g, int d, int H, int dh, int Kp,
                           T* __restrict__ wt) {
   const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
-  const long total = (long)d * Kp;
+  const long total = (long)wt_rows(d) * Kp;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
-    const int c = (int)(e / Kp), n = (int)(e - (long)c * Kp);
+    const int p = (int)(e / Kp), n = (int)(e - (long)p * Kp);
+    const int c = tile_row_perm(p);
     T v = from_f<T>(0.f);
-    if (n < D) v = w_q[(long)c * D + n];
+    if (c >= d) v = from_f<T>(0.f);
+    else if (n < D) v = w_q[(long)c * D + n];
     else if (n < 2 * D) v = w_k[(long)c * D + n - D];
     else if (n < 3 * D) v = w_v[(long)c * D + n - 2 * D];
     else if (n < GD) v = w_r[(long)c * D + n - 3 * D];
@@ -471,7 +474,7 @@ __global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, 
 
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
                     int d, int H, int dh, int Kp, void* wt, hipStream_t s) {
-  const long total = (long)d * Kp;
+  const long total = (long)wt_rows(d) * Kp;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
@@ -482,10 +485,13 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
 }
 
 // ============================================================== dX~ = G Wt^T
-// C[M=T][N=d] = G[T][Kp] Wt[d][Kp]^T, fp32 output; 256 x 256 tiles, 8 waves.
+// Computed transposed, dX~^T = Wt G^T: A = the packed Wt (rows = channels in
+// tile_row_perm order), B = G (rows = tokens). A lane's tiles 2i and 2i+1 then
+// hold 8 consecutive channels of one token, stored as one vector straight from
+// registers (no LDS staging, no barrier).
 template <typename T> struct DxCfg;
-template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; };
-template <> struct DxCfg<float> { using S = GemmShape<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; };
+template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 2, 2>; static constexpr bool DL = true; };
+template <> struct DxCfg<float> { using S = GemmShape<float, 128, 64, 32, 2, 2>; static constexpr bool DL = false; };
 
 template <typename T>
 __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
@@ -493,53 +499,50 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
                                                                      T* __restrict__ dxt) {
   using S = typename DxCfg<T>::S;
   constexpr bool DL = DxCfg<T>::DL;
+  static_assert(S::BM % 32 == 0 && S::WTM % 32 == 0, "whole 32-row channel groups per wave");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
-  const int mtiles = (T_ + S::BM - 1) / S::BM, ntiles = (d + S::BN - 1) / S::BN;
+  const int dp = wt_rows(d);
+  const int mtiles = (T_ + S::BN - 1) / S::BN, ntiles = (dp + S::BM - 1) / S::BM;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * ntiles);
   if (lid >= mtiles * ntiles) return;
   const int mt = lid / ntiles, nt = lid - mt * ntiles;
-  const int m0 = mt * S::BM, n0 = nt * S::BN;
+  const int m0 = mt * S::BN, n0 = nt * S::BM;  // first token, first channel row
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
-    gemm_nt_dl<S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp, min(S::BN, d - n0), Kp,
+    gemm_nt_dl<S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp, min(S::BN, T_ - m0), Kp,
                   smem, smem1, smem1, smem1, acc);
   else
-    gemm_nt_mainloop<T, S>(G + (size_t)m0 * Kp, Kp, min(S::BM, T_ - m0), wt + (size_t)n0 * Kp, Kp,
-                           min(S::BN, d - n0), Kp, smem, acc);
-  // epilogue staged per wave through LDS, 16 rows at a time, 16-byte row stores
+    gemm_nt_mainloop<T, S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp,
+                           min(S::BN, T_ - m0), Kp, smem, acc);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
-  constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
-  constexpr int RP = 16, VPR = S::WTN / 8;
-  static_assert(S::NWAVES * RP * LDO <= S::STAGE, "epilogue staging must fit the main-loop LDS");
-  T* ws = smem + w * RP * LDO;
 #pragma unroll
-  for (int i = 0; i < S::FM; ++i) {
+  for (int i2 = 0; i2 < S::FM / 2; ++i2) {
+    const int c = n0 + wm * S::WTM + 32 * i2 + 8 * grp;  // the lane's 8 channels c .. c + 7 (d % 8 == 0)
 #pragma unroll
-    for (int j = 0; j < S::FN; ++j)
+    for (int j = 0; j < S::FN; ++j) {
+      const int t = m0 + wn * S::WTN + 16 * j + col;
+      float v[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ws[(4 * grp + r) * LDO + 16 * j + col] = from_f<T>(acc[i][j][r]);
-    __syncthreads();
-    for (int it = lane; it < RP * VPR; it += 64) {
-      const int r = it / VPR, c = (it % VPR) * 8;
-      const int m = m0 + wm * S::WTM + 16 * i + r;
-      const int n = n0 + wn * S::WTN + c;
-      if (m < T_ && n < d) frag_store(dxt + (size_t)m * d + n, frag_load(ws + r * LDO + c));
+      for (int r = 0; r < 4; ++r) {
+        v[r] = acc[2 * i2][j][r];
+        v[4 + r] = acc[2 * i2 + 1][j][r];
+      }
+      if (t < T_ && c < d) frag_store(dxt + (size_t)t * d + c, frag_from<T>(v));
     }
-    __syncthreads();
   }
 }
 
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s) {
   if (dt == BF16) {
     using S = DxCfg<bf16>::S;
-    const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
+    const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
     if (n) hipLaunchKernelGGL(k_gemm_dx<bf16>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const bf16*)G,
                               (const bf16*)wt, T, d, Kp, (bf16*)dxt);
   } else {
     using S = DxCfg<float>::S;
-    const int n = ((T + S::BM - 1) / S::BM) * ((d + S::BN - 1) / S::BN);
+    const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
     if (n) hipLaunchKernelGGL(k_gemm_dx<float>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const float*)G,
                               (const float*)wt, T, d, Kp, (float*)dxt);
   }

@@ -79,8 +79,10 @@ void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, 
 }
 
 // ============================================================== weight packing
-// wp[h][n][c]: rows n < dh are W_Q[:, h*dh + n], then W_K, then W_V, then
-// (w_r non-null) W_R (k = c contiguous)
+// wp[h][p][c] (k = c contiguous) holds column f = tile_row_perm(p) of the head's
+// [W_Q | W_K | W_V (| W_R)] block (f < dh: W_Q[:, h*dh + f], then W_K, W_V, W_R).
+// The row order within each 32-row group is what lets the projection epilogue
+// store 8 consecutive features per lane (see k_proj).
 template <typename T>
 __global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
                             const T* __restrict__ w_r, int d, int H, int dh, T* __restrict__ wp) {
@@ -88,8 +90,9 @@ __global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k
   const long total = (long)H * NP * d;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
     const int c = (int)(e % d);
-    const int n = (int)((e / d) % NP);
+    const int p = (int)((e / d) % NP);
     const int h = (int)(e / ((long)d * NP));
+    const int n = tile_row_perm(p);
     const int seg = n / dh;
     const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
     wp[e] = src[(long)c * D + h * dh + (n % dh)];
@@ -288,19 +291,22 @@ void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipSt
 }
 
 // ============================================================== projection GEMM
-// Block = BM tokens x the [Q | K | V] columns (3 dh each; with the gated
-// RMSNorm output [Q | K | V | R], 4 dh) of HPB consecutive heads (the packed
-// per-head panels are contiguous, so HPB heads are one B operand). bf16 runs the
-// direct-to-LDS main loop, float the register-staged one. For d_h = 64 the
-// 128 x 192 bf16 tile (8 waves of 32 x 96) leaves room for two blocks per CU,
-// so one block's output stores overlap another's main loop.
+// Block = the [Q | K | V] rows (3 dh each; with the gated RMSNorm output
+// [Q | K | V | R], 4 dh) of HPB consecutive heads x BN tokens, computed in the
+// transposed orientation: A = the packed weight panel (rows = features, the
+// per-head panels are contiguous, so HPB heads are one operand), B = the x~
+// tile (rows = tokens). A lane's C tiles then hold features of a single token,
+// and with the panel's row order (tile_row_perm) the tiles 2i and 2i+1 of a
+// lane hold 8 consecutive features, which leave as one 16-byte (bf16) store
+// straight from registers: no LDS staging and no barrier in the epilogue.
+// bf16 runs the direct-to-LDS main loop, float the register-staged one.
 // Epilogue: phi on Q and K, identity on V and R.
 template <typename T, int DH, int NSEG> struct ProjCfg;
 template <> struct ProjCfg<bf16, 64, 3> {
-  using S = DlShape<128, 192, 64, 4, 2, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
+  using S = DlShape<192, 128, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<bf16, 32, 3> {
-  using S = DlShape<256, 192, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+  using S = DlShape<192, 128, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
 template <> struct ProjCfg<bf16, 64, 4> {
   using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
@@ -309,16 +315,16 @@ template <> struct ProjCfg<bf16, 32, 4> {
   using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
 template <> struct ProjCfg<float, 64, 3> {
-  using S = GemmShape<float, 32, 192, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
+  using S = GemmShape<float, 192, 32, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<float, 32, 3> {
-  using S = GemmShape<float, 64, 96, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
+  using S = GemmShape<float, 96, 64, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<float, 64, 4> {
-  using S = GemmShape<float, 32, 256, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
+  using S = GemmShape<float, 256, 32, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<float, 32, 4> {
-  using S = GemmShape<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
+  using S = GemmShape<float, 128, 64, 32, 1, 4>; static constexpr bool DL = false; static constexpr int HPB = 1;
 };
 
 // pipeline depth of a main-loop shape (register-staged shapes have none)
@@ -335,55 +341,47 @@ __global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS), 2) void k_proj
   constexpr bool DL = Cfg::DL;
   constexpr int HPB = Cfg::HPB;
   constexpr int NP = NSEG * DH;  // weight rows per head
-  static_assert(S::BN == HPB * NP, "a block covers whole heads");
+  static_assert(S::BM == HPB * NP, "a block covers whole heads");
+  static_assert(S::WTM % 32 == 0 && NP % 32 == 0, "a wave's features are whole 32-row groups of one head");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
   __shared__ __align__(16) T smem2[DL && NS_OF<S>::n > 2 ? S::STAGE : 8];
-  const int mtiles = (T_ + S::BM - 1) / S::BM, hgroups = (H + HPB - 1) / HPB;
+  const int mtiles = (T_ + S::BN - 1) / S::BN, hgroups = (H + HPB - 1) / HPB;
   const int lid = xcd_logical_block(blockIdx.x, mtiles * hgroups);
   if (lid >= mtiles * hgroups) return;
   const int mt = lid / hgroups, h0 = (lid - mt * hgroups) * HPB;
-  const int m0 = mt * S::BM;
-  const int nb = min(HPB, H - h0) * NP;  // valid weight rows (a last odd head)
+  const int m0 = mt * S::BN;
+  const int nf = min(HPB, H - h0) * NP;  // valid weight rows (a last odd head)
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
-    gemm_nt_dl<S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d, smem, smem1,
+    gemm_nt_dl<S>(wp + (size_t)h0 * NP * d, d, nf, xt + (size_t)m0 * d, d, min(S::BN, T_ - m0), d, smem, smem1,
                   smem2, smem2, acc);
   else
-    gemm_nt_mainloop<T, S>(xt + (size_t)m0 * d, d, min(S::BM, T_ - m0), wp + (size_t)h0 * NP * d, d, nb, d,
+    gemm_nt_mainloop<T, S>(wp + (size_t)h0 * NP * d, d, nf, xt + (size_t)m0 * d, d, min(S::BN, T_ - m0), d,
                            smem, acc);
-  // epilogue: phi on Q and K, staged per wave through LDS (the main loop ended
-  // with a barrier, so smem is free) and written as 16-byte row vectors
+  // epilogue: lane (grp, col) holds, in tiles 2 i2 and 2 i2 + 1, features
+  // 8 grp .. 8 grp + 7 of the wave's 32-row group i2 for token col of tile j
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
   const int D = H * DH;
-  constexpr int LDO = S::WTN + 16 / (int)sizeof(T);
-  constexpr int RP = 16;                       // rows per pass
-  constexpr int VPR = S::WTN / 8;              // 8-element vectors per row
-  static_assert(S::NWAVES * RP * LDO <= S::STAGE, "epilogue staging must fit the main-loop LDS");
-  T* ws = smem + w * RP * LDO;
 #pragma unroll
-  for (int i = 0; i < S::FM; ++i) {
+  for (int i2 = 0; i2 < S::FM / 2; ++i2) {
+    const int n = wm * S::WTM + 32 * i2 + 8 * grp;  // block-relative feature of the lane's first element
+    const int h = h0 + n / NP, nn = n % NP, kind = nn / DH;
+    const bool lin = !PHI || kind >= 2;  // v and r columns (and everything without phi) stay linear
+    T* out = kind == 0 ? q_out : (kind == 1 ? k_out : (kind == 2 ? v_out : r_out));
+    const size_t fo = (size_t)h * DH + (nn % DH);
 #pragma unroll
     for (int j = 0; j < S::FN; ++j) {
-      const int n = wn * S::WTN + 16 * j;
-      const bool lin = !PHI || (n % NP) / DH >= 2;  // v and r columns (and everything without phi) stay linear
+      const int t = m0 + wn * S::WTN + 16 * j + col;
+      float v[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float v = acc[i][j][r];
-        ws[(4 * grp + r) * LDO + 16 * j + col] = from_f<T>(lin ? v : phi_elu1(v));
+        v[r] = lin ? acc[2 * i2][j][r] : phi_elu1(acc[2 * i2][j][r]);
+        v[4 + r] = lin ? acc[2 * i2 + 1][j][r] : phi_elu1(acc[2 * i2 + 1][j][r]);
       }
+      if (t < T_ && h < H) frag_store(out + (size_t)t * D + fo, frag_from<T>(v));
     }
-    __syncthreads();
-    for (int it = lane; it < RP * VPR; it += 64) {
-      const int r = it / VPR, c = (it % VPR) * 8;
-      const int t = m0 + wm * S::WTM + 16 * i + r;
-      const int n = wn * S::WTN + c;
-      const int h = h0 + n / NP, nn = n % NP, kind = nn / DH;
-      T* out = kind == 0 ? q_out : (kind == 1 ? k_out : (kind == 2 ? v_out : r_out));
-      if (t < T_ && h < H) frag_store(out + (size_t)t * D + h * DH + (nn % DH), frag_load(ws + r * LDO + c));
-    }
-    __syncthreads();
   }
 }
 
@@ -392,7 +390,7 @@ static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q
                    hipStream_t s) {
   using S = typename ProjCfg<T, DH, NSEG>::S;
   constexpr int HPB = ProjCfg<T, DH, NSEG>::HPB;
-  const int n = ((T_ + S::BM - 1) / S::BM) * ((H + HPB - 1) / HPB);
+  const int n = ((T_ + S::BN - 1) / S::BN) * ((H + HPB - 1) / HPB);
   if (n == 0) return;
   hipLaunchKernelGGL((k_proj<T, DH, PHI, NSEG>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const T*)xt,
                      (const T*)wp, T_, d, H, (T*)q, (T*)k, (T*)v, (T*)r);

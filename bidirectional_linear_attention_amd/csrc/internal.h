@@ -44,6 +44,9 @@ inline int max_chunks(int T, int N, int chunk = kChunk) { return (T + chunk - 1)
 inline int proj_cols(int dh, bool out_gate = false) { return (out_gate ? 4 : 3) * dh; }
 
 // columns of the gradient matrix [dQ | dK | dV | (dR) | ds | 0-pad], padded to 64
+// rows of the packed dX~ weight operand: d rounded up to whole 32-row groups
+// (its row order is tile_row_perm within each group; rows past d are zero)
+__host__ __device__ inline int wt_rows(int d) { return (d + 31) / 32 * 32; }
 inline int grad_cols(int H, int dh, bool out_gate = false) {
   return (((out_gate ? 4 : 3) * H * dh + H) + 63) / 64 * 64;
 }

@@ -82,7 +82,7 @@ size_t plan_bwd(const LDims& m, char* base, LBwdWs* w) {
   t.nchunks = c.take<int>(base, sizeof(int));
   t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
-  t.wt = c.take<char>(base, (size_t)m.d * m.Kp * m.esz);
+  t.wt = c.take<char>(base, (size_t)wt_rows(m.d) * m.Kp * m.esz);
   t.hst = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * 2 * m.E);
   t.dA_loc = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
   t.dA_tot = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
