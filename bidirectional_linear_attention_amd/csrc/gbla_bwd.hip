@@ -451,30 +451,41 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
 
 // ============================================================== weight packing for dX~
 // wt[p][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | (W_R[c,:]) | w_g[:,c] | 0] for
-// channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all)
+// channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all).
+// Thread = 8 consecutive columns n (16-byte loads and stores in the weight
+// column blocks, which start at multiples of 32; element-wise in the gate and
+// padding columns).
 template <typename T>
-__global__ void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
-                          const T* __restrict__ w_r, const T* __restrict__ w_g, int d, int H, int dh, int Kp,
-                          T* __restrict__ wt) {
+__global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k,
+                                                 const T* __restrict__ w_v, const T* __restrict__ w_r,
+                                                 const T* __restrict__ w_g, int d, int H, int dh, int Kp,
+                                                 T* __restrict__ wt) {
   const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
-  const long total = (long)wt_rows(d) * Kp;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
+  const long total = (long)wt_rows(d) * Kp / 8;
+  for (long e8 = blockIdx.x * (long)blockDim.x + threadIdx.x; e8 < total; e8 += (long)gridDim.x * blockDim.x) {
+    const long e = 8 * e8;
     const int p = (int)(e / Kp), n = (int)(e - (long)p * Kp);
     const int c = tile_row_perm(p);
-    T v = from_f<T>(0.f);
-    if (c >= d) v = from_f<T>(0.f);
-    else if (n < D) v = w_q[(long)c * D + n];
-    else if (n < 2 * D) v = w_k[(long)c * D + n - D];
-    else if (n < 3 * D) v = w_v[(long)c * D + n - 2 * D];
-    else if (n < GD) v = w_r[(long)c * D + n - 3 * D];
-    else if (n < GD + H && w_g) v = w_g[(long)(n - GD) * d + c];  // no w_g: zero rows
-    wt[e] = v;
+    Frag8<T> v = frag_zero<T>();
+    if (c < d) {
+      if (n < GD) {
+        const int seg = n / D;
+        const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
+        v = frag_load(src + (long)c * D + n - seg * D);
+      } else if (w_g) {  // no w_g: zero rows
+        float f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f[u] = n + u < GD + H ? to_f<T>(w_g[(long)(n + u - GD) * d + c]) : 0.f;
+        v = frag_from<T>(f);
+      }
+    }
+    frag_store(wt + e, v);
   }
 }
 
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
                     int d, int H, int dh, int Kp, void* wt, hipStream_t s) {
-  const long total = (long)wt_rows(d) * Kp;
+  const long total = (long)wt_rows(d) * Kp / 8;
   const int grid = (int)std::min<long>((total + 255) / 256, 4096);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
@@ -625,28 +636,41 @@ void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp,
                        (const float*)xt, (const float*)G, T, d, Kp, tps, nsplit, part);
 }
 
-__global__ void k_dw_reduce(const float* __restrict__ part, int nsplit, int d, int H, int dh, int Kp,
-                            float* __restrict__ dw_q, float* __restrict__ dw_k, float* __restrict__ dw_v,
-                            float* __restrict__ dw_r, float* __restrict__ dw_g) {
+// dW[c][n] = sum over the splits of part[k][c][n], four consecutive n per
+// thread (Kp % 4 == 0; the Q, K, V and R column blocks start at multiples of
+// 32, so a quad never straddles two of them), in split order (deterministic).
+__global__ __launch_bounds__(256) void k_dw_reduce(const float* __restrict__ part, int nsplit, int d, int H,
+                                                   int dh, int Kp, float* __restrict__ dw_q,
+                                                   float* __restrict__ dw_k, float* __restrict__ dw_v,
+                                                   float* __restrict__ dw_r, float* __restrict__ dw_g) {
   const int D = H * dh, GD = (dw_r ? 4 : 3) * D;  // first gate column
-  const long total = (long)d * Kp;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
+  const long total = (long)d * Kp, quads = total / 4;
+  for (long qi = blockIdx.x * (long)blockDim.x + threadIdx.x; qi < quads; qi += (long)gridDim.x * blockDim.x) {
+    const long e = 4 * qi;
     const int c = (int)(e / Kp), n = (int)(e - (long)c * Kp);
     if (n >= GD + H) continue;
-    float s = 0.f;
-    for (int k = 0; k < nsplit; ++k) s += part[(size_t)k * total + e];
-    if (n < D) dw_q[(long)c * D + n] = s;
-    else if (n < 2 * D) dw_k[(long)c * D + n - D] = s;
-    else if (n < 3 * D) dw_v[(long)c * D + n - 2 * D] = s;
-    else if (n < GD) dw_r[(long)c * D + n - 3 * D] = s;
-    else if (dw_g) dw_g[(long)(n - GD) * d + c] = s;
+    float4 s = *reinterpret_cast<const float4*>(part + e);
+    for (int k = 1; k < nsplit; ++k) {
+      const float4 p = *reinterpret_cast<const float4*>(part + (size_t)k * total + e);
+      s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+    }
+    if (n < GD) {
+      const int seg = n / D;
+      float* dst = seg == 0 ? dw_q : (seg == 1 ? dw_k : (seg == 2 ? dw_v : dw_r));
+      *reinterpret_cast<float4*>(dst + (long)c * D + n - seg * D) = s;
+    } else if (dw_g) {
+      const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (n + u < GD + H) dw_g[(long)(n + u - GD) * d + c] = v[u];
+    }
   }
 }
 
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_r, float* dw_g, hipStream_t s) {
-  const long total = (long)d * Kp;
-  const int grid = (int)std::min<long>((total + 255) / 256, 8192);
+  const long quads = (long)d * Kp / 4;
+  const int grid = (int)std::min<long>((quads + 255) / 256, 8192);
   hipLaunchKernelGGL(k_dw_reduce, dim3(grid), dim3(256), 0, s, part, nsplit, d, H, dh, Kp, dw_q, dw_k, dw_v, dw_r,
                      dw_g);
 }

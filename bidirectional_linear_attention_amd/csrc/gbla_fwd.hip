@@ -22,49 +22,63 @@
 namespace gbla {
 
 // ============================================================== schedule
+// One block of 1024 threads. Sequences are taken 1024 at a time: thread b
+// reads its offsets once, the chunk counts are prefix-summed with wave
+// shuffles plus one pass over the 16 wave totals, and the table entries of the
+// batch are then written by all threads in parallel (entry s finds its
+// sequence by binary search over the batch's offsets in LDS).
 __global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ cu, int N, int T, int chunk,
                                                    int max_slots, int* __restrict__ nchunks,
                                                    int* __restrict__ chunk_off, Chunk* __restrict__ tab) {
-  __shared__ int scan[1024];
-  __shared__ int bad;
-  const int tid = threadIdx.x;
+  __shared__ int off[1025];
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int bad = 0;
   if (tid == 0) bad = (cu[0] != 0) || (cu[N] != T);
-  __syncthreads();
   for (int b = tid; b < N; b += 1024)
     if (cu[b + 1] < cu[b]) bad = 1;
-  __syncthreads();
-  if (bad) {  // malformed offsets: schedule nothing, so no kernel reads outside [0, T)
+  if (__syncthreads_or(bad)) {  // malformed offsets: schedule nothing, so no kernel reads outside [0, T)
     for (int b = tid; b <= N; b += 1024) chunk_off[b] = 0;
     if (tid == 0) *nchunks = 0;
     return;
   }
   int carry = 0;
   for (int b0 = 0; b0 < N; b0 += 1024) {
-    const int b = b0 + tid;
-    int n = 0;
-    if (b < N) n = (cu[b + 1] - cu[b] + chunk - 1) / chunk;
-    scan[tid] = n;
+    const int b = b0 + tid, nb = min(1024, N - b0);
+    const int s0 = b < N ? cu[b] : 0, s1 = b < N ? cu[b + 1] : 0;
+    const int n = b < N ? (s1 - s0 + chunk - 1) / chunk : 0;
+    int inc = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wv] = inc;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int v = tid >= off ? scan[tid - off] : 0;
-      __syncthreads();
-      scan[tid] += v;
-      __syncthreads();
-    }
-    const int excl = carry + scan[tid] - n;
-    if (b < N) {
-      chunk_off[b] = excl;
-      const int s = cu[b], e = cu[b + 1];
-      for (int c = 0; c < n && excl + c < max_slots; ++c) {
-        Chunk ch;
-        ch.seq = b;
-        ch.start = s + c * chunk;
-        ch.end = min(s + (c + 1) * chunk, e);
-        ch.pad = 0;
-        tab[excl + c] = ch;
+    int wbase = 0;
+    for (int k = 0; k < wv; ++k) wbase += wsum[k];
+    const int excl = wbase + inc - n;  // within the batch
+    off[tid] = excl;
+    if (tid == 1023) off[1024] = excl + n;
+    if (b < N) chunk_off[b] = min(carry + excl, max_slots);
+    __syncthreads();
+    const int total = off[nb];
+    for (int e = tid; e < total && carry + e < max_slots; e += 1024) {
+      int lo = 0, hi = nb - 1;  // last sequence i with off[i] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= e) lo = mid; else hi = mid - 1;
       }
+      const int c = e - off[lo];
+      const int st = cu[b0 + lo] + c * chunk;
+      Chunk ch;
+      ch.seq = b0 + lo;
+      ch.start = st;
+      ch.end = min(st + chunk, cu[b0 + lo + 1]);
+      ch.pad = 0;
+      tab[carry + e] = ch;
     }
-    carry += scan[1023];
+    carry += total;
     __syncthreads();
   }
   if (tid == 0) {
@@ -83,26 +97,42 @@ void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, 
 // [W_Q | W_K | W_V (| W_R)] block (f < dh: W_Q[:, h*dh + f], then W_K, W_V, W_R).
 // The row order within each 32-row group is what lets the projection epilogue
 // store 8 consecutive features per lane (see k_proj).
+// Block = one 32-row group of one head x 64 channels c, transposed through
+// LDS: 16-byte loads of 8 consecutive features of one weight row, 16-byte
+// stores of 8 consecutive channels of one packed row. d % 8 == 0.
 template <typename T>
-__global__ void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k, const T* __restrict__ w_v,
-                            const T* __restrict__ w_r, int d, int H, int dh, T* __restrict__ wp) {
-  const int NP = (w_r ? 4 : 3) * dh, D = H * dh;
-  const long total = (long)H * NP * d;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < total; e += (long)gridDim.x * blockDim.x) {
-    const int c = (int)(e % d);
-    const int p = (int)((e / d) % NP);
-    const int h = (int)(e / ((long)d * NP));
-    const int n = tile_row_perm(p);
-    const int seg = n / dh;
-    const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
-    wp[e] = src[(long)c * D + h * dh + (n % dh)];
+__global__ __launch_bounds__(256) void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k,
+                                                   const T* __restrict__ w_v, const T* __restrict__ w_r, int d,
+                                                   int H, int dh, T* __restrict__ wp) {
+  __shared__ float tile[32][65];
+  const int NP = (w_r ? 4 : 3) * dh, D = H * dh, G = NP / 32;
+  const int cb = blockIdx.x % ((d + 63) / 64), rest = blockIdx.x / ((d + 63) / 64);
+  const int g = rest % G, h = rest / G;
+  const int c0 = 64 * cb, f0 = 32 * g, seg = f0 / dh;
+  const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
+  const int t = threadIdx.x;
+  {
+    const int c = t >> 2, fc = 8 * (t & 3);
+    if (c0 + c < d) {
+      const Frag8<T> v = frag_load(src + (size_t)(c0 + c) * D + h * dh + (f0 % dh) + fc);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[fc + j][c] = frag_get(v, j);
+    }
+  }
+  __syncthreads();
+  const int pr = t >> 3, cc = 8 * (t & 7);
+  if (c0 + cc < d) {
+    const int f = tile_row_perm(pr);  // pr < 32: the feature within the group
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = tile[f][cc + j];
+    frag_store(wp + ((size_t)h * NP + f0 + pr) * d + c0 + cc, frag_from<T>(v));
   }
 }
 
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
                       int dh, void* wp, hipStream_t s) {
-  const long total = (long)H * proj_cols(dh, w_r != nullptr) * d;
-  const int grid = (int)std::min<long>((total + 255) / 256, 4096);
+  const int grid = H * (proj_cols(dh, w_r != nullptr) / 32) * ((d + 63) / 64);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
                        (const bf16*)w_v, (const bf16*)w_r, d, H, dh, (bf16*)wp);
@@ -538,20 +568,20 @@ void launch_state_partial(int dt, int dh, const void* ka, const void* va, const 
 
 // ============================================================== combine
 // out[b][h][e] = sum of partial[c][h][e] over the chunks c of sequence b. A
-// block covers 64 elements of one (sequence, head); its four waves take every
-// fourth chunk and the four sums are added in a fixed order (deterministic).
-// With chunk maxima mpart (softmax key gate), partial c is scaled by
-// exp(mpart[c] - M), M the largest of the sequence's chunk maxima, which goes to
-// mout[b][h] (0 for an empty sequence).
+// block covers 256 elements (64 float4) of one (sequence, head); its four
+// waves take every fourth chunk and the four sums are added in a fixed order
+// (deterministic). E % 4 == 0. With chunk maxima mpart (softmax key gate),
+// partial c is scaled by exp(mpart[c] - M), M the largest of the sequence's
+// chunk maxima, which goes to mout[b][h] (0 for an empty sequence).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int* __restrict__ nchunks,
                                                  const int* __restrict__ chunk_off, int N, int H, int E,
                                                  const float* __restrict__ mpart, float* __restrict__ out,
                                                  float* __restrict__ mout) {
-  __shared__ float red[4][64];
-  const int eblocks = (E + 63) / 64;
+  __shared__ float4 red[4][64];
+  const int eblocks = (E + 255) / 256;
   const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
   const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int e = (blockIdx.x - bh * eblocks) * 64 + lane;
+  const int e = (blockIdx.x - bh * eblocks) * 256 + 4 * lane;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
   float M = 0.f;
@@ -563,20 +593,29 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
     if (c0 == c1) M = 0.f;
     if (mout && blockIdx.x == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
   }
-  float s = 0.f;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (e < E)
     for (int c = c0 + ph; c < c1; c += 4) {
-      const float p = partial[((size_t)c * H + h) * E + e];
-      s += mpart ? __expf(mpart[(size_t)c * H + h] - M) * p : p;
+      const float4 p = *reinterpret_cast<const float4*>(partial + ((size_t)c * H + h) * E + e);
+      const float f = mpart ? __expf(mpart[(size_t)c * H + h] - M) : 1.f;
+      s.x += f * p.x; s.y += f * p.y; s.z += f * p.z; s.w += f * p.w;
     }
   red[ph][lane] = s;
   __syncthreads();
-  if (ph == 0 && e < E) out[((size_t)b * H + h) * E + e] = (red[0][lane] + red[1][lane]) + (red[2][lane] + red[3][lane]);
+  if (ph == 0 && e < E) {
+    const float4 a = red[0][lane], b1 = red[1][lane], c2 = red[2][lane], d3 = red[3][lane];
+    float4 r;
+    r.x = (a.x + b1.x) + (c2.x + d3.x);
+    r.y = (a.y + b1.y) + (c2.y + d3.y);
+    r.z = (a.z + b1.z) + (c2.z + d3.z);
+    r.w = (a.w + b1.w) + (c2.w + d3.w);
+    *reinterpret_cast<float4*>(out + ((size_t)b * H + h) * E + e) = r;
+  }
 }
 
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
                     float* out, hipStream_t s, const float* mpart, float* mout) {
-  hipLaunchKernelGGL(k_combine, dim3(((elems + 63) / 64) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N,
+  hipLaunchKernelGGL(k_combine, dim3(((elems + 255) / 256) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N,
                      H, elems, mpart, out, mout);
 }
 
@@ -615,12 +654,10 @@ void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, floa
   if (E <= 0) return;
 #define GBLA_SUMP(EB) hipLaunchKernelGGL(k_sum_parts<EB>, dim3((E + EB - 1) / EB), dim3(256), 0, s, in, E, P_host, \
                                          P_dev, p_mul, out)
-  // p_mul > 1 sums a long list of parts (one per chunk and head): narrower
-  // blocks give each element more threads (256 / EB) and the list more blocks
-  if (p_mul > 1) GBLA_SUMP(4);
-  else if (E >= 64) GBLA_SUMP(64);
-  else if (E > 16) GBLA_SUMP(32);
-  else if (E > 4) GBLA_SUMP(16);
+  // the widest blocks that still make about 256 of them; p_mul > 1 sums a long
+  // list of parts (one per chunk and head), which wants many threads per element
+  if (p_mul == 1 && E >= 64 * 256) GBLA_SUMP(64);
+  else if (p_mul == 1 && E >= 16 * 256) GBLA_SUMP(16);
   else GBLA_SUMP(4);
 #undef GBLA_SUMP
 }
