@@ -499,9 +499,11 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
 // Computed transposed, dX~^T = Wt G^T: A = the packed Wt (rows = channels in
 // tile_row_perm order), B = G (rows = tokens). A lane's tiles 2i and 2i+1 then
 // hold 8 consecutive channels of one token, stored as one vector straight from
-// registers (no LDS staging, no barrier).
+// registers (no LDS staging, no barrier). bf16: 256 x 256 tiles of 16 waves of
+// 64 x 64 (one block per CU; a 64 x 64 wave tile keeps the LDS operand reads per
+// MFMA low, and 16 waves hide their latency).
 template <typename T> struct DxCfg;
-template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 2, 2>; static constexpr bool DL = true; };
+template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; };
 template <> struct DxCfg<float> { using S = GemmShape<float, 128, 64, 32, 2, 2>; static constexpr bool DL = false; };
 
 template <typename T>
@@ -561,9 +563,10 @@ void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp,
 
 // ============================================================== dW = X~^T G (split over tokens)
 // part[ks][m][n] = sum over the tokens of split ks of X~[t][m] G[t][n]; both
-// operands are token-major and are transposed while staged in LDS.
+// operands are token-major and are transposed while staged in LDS. bf16: 256 x
+// 256 tiles of 16 waves of 64 x 64, one block per CU.
 template <typename T> struct DwCfg;
-template <> struct DwCfg<bf16> { using S = DlShapeTN<128, 128, 64, 2, 2, 2>; static constexpr bool DL = true; };
+template <> struct DwCfg<bf16> { using S = DlShapeTN<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; };
 template <> struct DwCfg<float> { using S = GemmShapeTN<float, 64, 128, 32, 2, 2>; static constexpr bool DL = false; };
 
 int dw_tiles(int dt, int d, int Kp) {
@@ -575,11 +578,12 @@ int dw_tiles(int dt, int d, int Kp) {
   return ((d + S::BM - 1) / S::BM) * ((Kp + S::BN - 1) / S::BN);
 }
 
-// token splits of the dW GEMM: as many as fill two rounds of two resident
-// blocks on each of the 256 CUs, at least 1024 tokens per split, at most 64
+// token splits of the dW GEMM: bf16 (one 16-wave block per CU) as many as
+// fill one round of the 256 CUs, float as many as fill two rounds of two
+// resident blocks; at least 1024 tokens per split, at most 64
 int dw_splits(int dt, int d, int Kp, int T) {
   const int tiles = dw_tiles(dt, d, Kp);
-  int ns = std::max(1, 1024 / tiles);
+  int ns = std::max(1, (dt == BF16 ? 256 : 1024) / tiles);
   ns = std::min(ns, std::max(1, (T + 1023) / 1024));
   return std::max(1, std::min(ns, 64));
 }

@@ -329,7 +329,8 @@ void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipSt
 // and with the panel's row order (tile_row_perm) the tiles 2i and 2i+1 of a
 // lane hold 8 consecutive features, which leave as one 16-byte (bf16) store
 // straight from registers: no LDS staging and no barrier in the epilogue.
-// bf16 runs the direct-to-LDS main loop, float the register-staged one.
+// bf16 runs the direct-to-LDS main loop, float the register-staged one; the
+// four-segment panel (with R) runs 256 x 256 tiles of 16 waves of 64 x 64.
 // Epilogue: phi on Q and K, identity on V and R.
 template <typename T, int DH, int NSEG> struct ProjCfg;
 template <> struct ProjCfg<bf16, 64, 3> {
@@ -339,10 +340,10 @@ template <> struct ProjCfg<bf16, 32, 3> {
   using S = DlShape<192, 128, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
 template <> struct ProjCfg<bf16, 64, 4> {
-  using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
+  using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 1;
 };
 template <> struct ProjCfg<bf16, 32, 4> {
-  using S = DlShape<256, 256, 64, 2, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
+  using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; static constexpr int HPB = 2;
 };
 template <> struct ProjCfg<float, 64, 3> {
   using S = GemmShape<float, 192, 32, 32, 2, 2>; static constexpr bool DL = false; static constexpr int HPB = 1;
