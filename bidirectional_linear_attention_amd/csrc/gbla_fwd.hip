@@ -145,8 +145,8 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 // One wave per token row (16 consecutive rows per wave, 64 per block); lane l
 // owns channel groups c = 8 * (l + 64 m). The three previous rows slide in
 // registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
-// reduce-scatter butterfly: 8 head partials per lane become one head total per
-// 8 lanes in 4 + 2 + 1 + 3 shuffles.
+// reduce-scatter butterfly (butterfly8): 8 head partials per lane become one
+// head total per 8 lanes in 4 + 2 lane-half swaps and 4 DPP adds.
 constexpr int kConvRowsPerWave = 16;
 
 // sum of the 8 products of two fragments (bf16: four packed dot2 instructions)
@@ -168,25 +168,38 @@ template <> __device__ __forceinline__ float gate_dot8<bf16>(const Frag8<bf16>& 
   return s;
 }
 
+// DPP move of a float within rows of 16 lanes (ctrl: a DPP control code)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
+
+// Reduce-scatter of 8 per-lane values over the wave: lane l ends with the
+// wave total of value (l >> 3). Halving steps exchange the half a lane does not
+// keep: lanes 32-63 keep values 4-7 (v_permlane32_swap), then the odd 16-lane
+// rows keep the upper pair (v_permlane16_swap), then lanes with bit 3 set keep
+// the odd value (a rotate by 8 within the row); a mirror and two quad
+// permutations sum the 8 lanes of each group. All register-to-register.
 __device__ __forceinline__ float butterfly8(float (&v)[8], int lane) {
-  const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
   float u[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float mine = b5 ? v[4 + i] : v[i], other = b5 ? v[i] : v[4 + i];
-    u[i] = mine + __shfl_xor(other, 32, 64);
+  for (int i = 0; i < 4; ++i) {  // lanes 0-31: v[i] of both halves; lanes 32-63: v[4 + i]
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[4 + i]), false, false);
+    u[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
   float q[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float mine = b4 ? u[2 + i] : u[i], other = b4 ? u[i] : u[2 + i];
-    q[i] = mine + __shfl_xor(other, 16, 64);
+  for (int i = 0; i < 2; ++i) {  // even 16-lane rows: u[i] of the row pair; odd rows: u[2 + i]
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(u[i]), __float_as_uint(u[2 + i]), false, false);
+    q[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   }
-  float x = (b3 ? q[1] : q[0]) + __shfl_xor(b3 ? q[0] : q[1], 8, 64);
-  x += __shfl_xor(x, 4, 64);
-  x += __shfl_xor(x, 2, 64);
-  x += __shfl_xor(x, 1, 64);
-  return x;  // total of head (lane >> 3)
+  const bool b3 = lane & 8;
+  float x = (b3 ? q[1] : q[0]) + dpp_f<kDppRowRor8>(b3 ? q[0] : q[1]);  // partner: lane ^ 8
+  x += dpp_f<kDppHalfMirror>(x);  // lane i of an 8-lane group + lane 7 - i
+  x += dpp_f<kDppXor1>(x);
+  x += dpp_f<kDppXor2>(x);
+  return x;  // total of value (lane >> 3)
 }
 
 // log(sigmoid(z)) = -softplus(-z), stable for any z

@@ -242,10 +242,14 @@ struct DlShape {
   static constexpr int CPR = BK / 8;        // 16-byte chunks per LDS row
   static constexpr int RPL = 64 / CPR;      // rows written by one 1 KB wave load
   static constexpr int LA = BM / RPL, LB = BN / RPL;
-  static constexpr int LPW = (LA + LB) / NWAVES;  // wave loads per wave per chunk
+  // wave loads per wave per chunk; when they do not divide evenly, the last
+  // waves issue one fewer (only with two stages, whose waits are vmcnt(0))
+  static constexpr int LPW = (LA + LB + NWAVES - 1) / NWAVES;
+  static constexpr bool EVEN = (LA + LB) % NWAVES == 0;
   static constexpr int STAGE = (BM + BN) * BK;    // bf16 elements per stage
   static_assert(BK == 32 || BK == 64, "16 or 8 rows per wave load");
-  static_assert(BM % RPL == 0 && BN % RPL == 0 && (LA + LB) % NWAVES == 0, "whole wave loads per wave");
+  static_assert(BM % RPL == 0 && BN % RPL == 0, "whole wave loads");
+  static_assert(EVEN || NS_ == 2, "uneven wave loads need the two-stage pipeline");
   static_assert(WTM % 16 == 0 && WTN % 16 == 0 && NS >= 2 && NS <= 4, "tile shape");
   static_assert(LPW * (NS - 1) < 64, "vmcnt range");
 };
@@ -286,6 +290,7 @@ __device__ __forceinline__ void gemm_nt_dl(const bf16* __restrict__ A, int lda, 
 #pragma unroll
     for (int j = 0; j < S::LPW; ++j) {
       const int li = w + S::NWAVES * j;  // wave-uniform
+      if (!S::EVEN && li >= S::LA + S::LB) break;
       const bool isA = li < S::LA;
       const int r = (isA ? li : li - S::LA) * RPL + rr;
       const int c = dl_swizzle<CPR>(r, pp);

@@ -187,13 +187,16 @@ def backward_full(x, cu, w_q, w_k, w_v, w_lam, b_lam, dy, num_heads):
     """Gradients of sum(y * dy) for forward_full, through the projections of
     q, k, v and the decay logit a = x w_lam^h + b_lam^h.
 
-    Returns dict dx, dw_q, dw_k, dw_v, dw_lam, db_lam (float64)."""
+    Returns dict dx, dw_q, dw_k, dw_v, dw_lam, db_lam (float64), plus da [T, H],
+    the gradient of the decay logit a of every token and head (db_lam is its sum
+    over the tokens, dw_lam = x^T da)."""
     x, w_q, w_k, w_v, w_lam, b_lam, dy = map(_f64, (x, w_q, w_k, w_v, w_lam, b_lam, dy))
     H = num_heads
     dh = w_q.shape[1] // H
     dx = np.zeros_like(x)
     dw_q, dw_k, dw_v = np.zeros_like(w_q), np.zeros_like(w_k), np.zeros_like(w_v)
     dw_lam, db_lam = np.zeros_like(w_lam), np.zeros_like(b_lam)
+    da_all = np.zeros((x.shape[0], H))
     for b in range(len(cu) - 1):
         s0, e0 = int(cu[b]), int(cu[b + 1])
         if e0 == s0:
@@ -208,6 +211,7 @@ def backward_full(x, cu, w_q, w_k, w_v, w_lam, b_lam, dy, num_heads):
             dw_v[:, cols] += xb.T @ dv
             dw_lam[h] += xb.T @ da
             db_lam[h] += da.sum()
+            da_all[s0:e0, h] = da
             dx[s0:e0] += dq @ w_q[:, cols].T + dk @ w_k[:, cols].T + dv @ w_v[:, cols].T \
                 + da[:, None] * w_lam[h][None, :]
-    return dict(dx=dx, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_lam=dw_lam, db_lam=db_lam)
+    return dict(dx=dx, dw_q=dw_q, dw_k=dw_k, dw_v=dw_v, dw_lam=dw_lam, db_lam=db_lam, da=da_all)

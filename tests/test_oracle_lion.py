@@ -163,3 +163,22 @@ def test_euler_identity_in_value_weights():
     y = lion.forward_full(x, cu, *w, wl, bl, H)
     g = lion.backward_full(x, cu, *w, wl, bl, dy, H)
     np.testing.assert_allclose(np.sum(w[2] * g["dw_v"]), np.sum(y * dy), rtol=1e-11)
+
+
+def test_decay_logit_gradient_sums_to_the_bias_and_weight_gradients():
+    """The per-token logit gradient da that backward_full returns is the one its
+    weight gradients are built from: db_lam = sum_t da_t and dw_lam = x^T da
+    per head (a = x w_lam + b_lam is affine in both). db_lam and dw_lam are
+    themselves pinned by finite differences elsewhere in this file."""
+    rng = np.random.default_rng(71)
+    lens = [9, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    d, H, dh = 6, 2, 3
+    x = rng.standard_normal((cu[-1], d))
+    w = [rng.standard_normal((d, H * dh)) for _ in range(3)]
+    wl, bl = rng.standard_normal((H, d)), np.full(H, 1.5)
+    dy = rng.standard_normal((cu[-1], H * dh))
+    g = lion.backward_full(x, cu, *w, wl, bl, dy, H)
+    assert g["da"].shape == (cu[-1], H)
+    np.testing.assert_allclose(g["da"].sum(axis=0), g["db_lam"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(x.T @ g["da"], g["dw_lam"].T, rtol=1e-12, atol=1e-12)
