@@ -90,8 +90,9 @@ def traffic_for(stage):
     return rec["bytes_per_launch"]
 
 
-def cpu_baseline(inp, sample_seqs):
-    """Time the float64 oracle (fwd+bwd) on the first `sample_seqs` sequences."""
+def cpu_baseline(inp, sample_seqs, repeats=3):
+    """Time the float64 oracle (fwd+bwd) on the first `sample_seqs` sequences,
+    `repeats` times; the median run gives the rate."""
     import numpy as np
     from oracle import gbla as og
     try:
@@ -104,14 +105,18 @@ def cpu_baseline(inp, sample_seqs):
     T = int(cu[S])
     sub = dict(inp, x=inp["x"][:T], dy=inp["dy"][:T], cu_seqlens=cu[:S + 1].copy())
     args = [sub[k] for k in ("x", "cu_seqlens", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g")]
-    t0 = time.perf_counter()
-    og.forward(*args, inp["H"])
-    og.backward(*args, sub["dy"], inp["H"])
-    dt = time.perf_counter() - t0
+    runs = []
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        og.forward(*args, inp["H"])
+        og.backward(*args, sub["dy"], inp["H"])
+        runs.append(time.perf_counter() - t0)
+    dt = sorted(runs)[len(runs) // 2]
     del np
     return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"float64 numpy oracle forward+backward on the first {S} of {inp['N']} sequences "
-                      f"({T} tokens) of the same batch, timed once ({dt:.1f} s)"}
+                      f"({T} tokens) of the same batch, median of {repeats} runs "
+                      f"({', '.join(f'{r:.1f}' for r in runs)} s)"}
 
 
 def timed_passes(gb, torch, step, steps, warmup, stage_filter):
