@@ -290,7 +290,10 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 
 // ============================================================== dk, dv, ds
 // Same tiling as k_bwd_dstate: phi(k), v and g of 64 tokens are staged in LDS;
-//   dk~ = v dS^T + dz,  dv = k~ dS      (MFMA, A rows from LDS, k~ = g phi(k))
+//   dk~ = v dS^T + dz,  dv = k~ dS      (MFMA, A rows from LDS, k~ = g phi(k);
+//                                        dS is staged once, row-major, and read
+//                                        transposed for dv with the transposing
+//                                        LDS read, so three blocks fit per CU)
 //   dg = phi(k) . dk~,  dk = g dk~ (.) phi'(k),  ds = dg g (1 - g)
 // dk and dv are staged over the wave's own phi(k) and v rows and written to G
 // with 16-byte stores.
@@ -305,8 +308,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
   constexpr int ST = 64, V8 = DH / 8;
-  __shared__ __align__(16) T Srm[P * DH * LD];  // dS as B of v dS^T: Srm[i][n] = dS[i][n]
-  __shared__ __align__(16) T Str[P * DH * LD];  // dS as B of k~ dS:  Str[n][i] = dS[i][n]
+  __shared__ __align__(16) T Srm[P * DH * LD];  // dS[i][n]: B of v dS^T by rows, B of k~ dS by columns
   __shared__ __align__(16) T ks[ST * LD];       // phi(k) tile, then dk
   __shared__ __align__(16) T vs[ST * LD];       // v tile, then dv
   __shared__ float gs[ST];
@@ -321,7 +323,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = dsz + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, DH>(Str, Srm, LD, st, st + DH * DH, tid);
+  stage_state<T, DH, DH>(nullptr, Srm, LD, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
@@ -376,7 +378,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
 #pragma unroll
         for (int s = 0; s < DH / 32; ++s) {
           mma8(dkt[nt], vf[s], frag_load(Srm + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
-          mma8(dvv[nt], kf[s], frag_load(Str + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
+          mma8(dvv[nt], kf[s], frag_kmajor<T>(Srm + p * DH * LD, LD, 32 * s + 8 * grp, 16 * nt, lane));
         }
     }
     float dkv[FB][4];
