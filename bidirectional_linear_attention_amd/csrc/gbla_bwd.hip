@@ -463,10 +463,10 @@ __global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, cons
                                                  const T* __restrict__ w_g, int d, int H, int dh, int Kp,
                                                  T* __restrict__ wt) {
   const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
-  const long total = (long)wt_rows(d) * Kp / 8;
-  for (long e8 = blockIdx.x * (long)blockDim.x + threadIdx.x; e8 < total; e8 += (long)gridDim.x * blockDim.x) {
-    const long e = 8 * e8;
-    const int p = (int)(e / Kp), n = (int)(e - (long)p * Kp);
+  const int per_row = Kp / 8, total = wt_rows(d) * per_row;  // < 2^31 (checked on the host)
+  for (int e8 = blockIdx.x * blockDim.x + threadIdx.x; e8 < total; e8 += gridDim.x * blockDim.x) {
+    const int p = e8 / per_row, n = 8 * (e8 - p * per_row);
+    const size_t e = (size_t)p * Kp + n;
     const int c = tile_row_perm(p);
     Frag8<T> v = frag_zero<T>();
     if (c < d) {

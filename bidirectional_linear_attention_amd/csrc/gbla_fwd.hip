@@ -469,8 +469,10 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
   constexpr int FB = DH / 16, NB = FB + 1;     // key-feature blocks; value blocks + ones block
   constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
   constexpr int ST = 64;                       // tokens per staged tile
-  constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LDK = DH + PAD, LDV = 16 * NB + PAD;
+  // bf16 pitches of 40 or 24 dwords (8 banks apart mod 32): the four rows a
+  // transposing read touches per 16 lanes fall on disjoint banks
+  constexpr bool B16 = sizeof(T) == 2;
+  constexpr int LDK = DH + (B16 ? 16 : 4), LDV = 16 * NB + (B16 ? 0 : 4);
   constexpr int E = DH * DH + DH;
   __shared__ __align__(16) T ks[ST * LDK];
   __shared__ __align__(16) T vs[ST * LDV];

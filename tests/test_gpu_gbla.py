@@ -156,6 +156,15 @@ def test_bf16_odd_head_count(dh):
     compare(make_inputs(w), backward=True, label=f"bf16 H=3 dh={dh}")
 
 
+@pytest.mark.parametrize("d,H,dh", [(40, 1, 64), (72, 3, 32)])
+def test_bf16_d_model_not_a_multiple_of_32(d, H, dh):
+    """d % 32 != 0: the dX GEMM's packed weight operand is padded with zero rows
+    to whole 32-row groups, and the projection's k loop ends in a partial chunk."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (300, 77, 2), d_model=d, num_heads=H, head_dim=dh,
+                      seed=25)
+    compare(make_inputs(w), backward=True, label=f"bf16 d={d} H={H} dh={dh}")
+
+
 def test_bf16_small_ragged_recipe():
     rng = np.random.default_rng(23)
     lens = np.clip(np.rint(np.exp(rng.normal(np.log(600), 1.0, 12))), 16, 32768).astype(int)
