@@ -401,6 +401,35 @@ __device__ __forceinline__ void stage_state(T* MT, T* MR, int ld, const float* _
   }
 }
 
+// out[e] = sum over p < P of in[p * E + e] for the EB elements of virtual block
+// blk (256 threads: 256 / EB phases per element, eight independent partial sums
+// per thread so the loads stay in flight). Fixed summation order.
+template <int EB>
+__device__ __forceinline__ void sum_parts_block(const float* __restrict__ in, int E, int P, float* __restrict__ out,
+                                                int blk) {
+  constexpr int PH = 256 / EB;
+  __shared__ float red[PH][EB];
+  const int el = threadIdx.x % EB, ph = threadIdx.x / EB;
+  const int e = blk * EB + el;
+  float a[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a[u] = 0.f;
+  if (e < E) {
+    int p = ph;
+    for (; p + 7 * PH < P; p += 8 * PH)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[u] += in[(size_t)(p + u * PH) * E + e];
+    for (int u = 0; p < P; p += PH, ++u) a[u] += in[(size_t)p * E + e];
+  }
+  red[ph][el] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+  __syncthreads();
+  if (ph == 0 && e < E) {
+    float t = 0.f;
+    for (int q = 0; q < PH; ++q) t += red[q][el];
+    out[e] = t;
+  }
+}
+
 // chunk table entry: one run of <= chunk tokens inside one sequence
 struct Chunk { int seq, start, end, pad; };
 

@@ -272,18 +272,23 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
     launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, m.gated ? 4 : 3, w.G,
                      w.dbg_part,
                      m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
-  { StageScope ps(ST_DBG_REDUCE, s);
-    launch_sum_parts(w.dbg_part, m.H, 0, w.nchunks, db_g, s);
-    if (gamma) launch_sum_parts(w.dgam_part, m.dh, 0, w.nchunks, dgamma, s, m.H); }
   if (m.T > 0) {
     { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }
     { StageScope ps(ST_CONV_BWD, s);
       launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s); }
   }
   { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, A.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
-  { StageScope ps(ST_DW_REDUCE, s);
-    launch_dw_reduce(w.dw_part, m.nsplit, m.d, m.H, m.dh, m.Kp, dw_q, dw_k, dw_v, dw_r, dw_g, s); }
-  { StageScope ps(ST_DCONV_REDUCE, s); launch_sum_parts(w.dconv_part, 4 * m.d, m.conv_rb, nullptr, dconv_w, s); }
+  {
+    StageScope ps(ST_FINALIZE, s);
+    BwdFinalize f;
+    f.dw_part = w.dw_part; f.nsplit = m.nsplit; f.d = m.d; f.H = m.H; f.dh = m.dh; f.Kp = m.Kp;
+    f.dw_blocks = bwd_finalize_dw_blocks(m.d, m.Kp);
+    f.dw_q = dw_q; f.dw_k = dw_k; f.dw_v = dw_v; f.dw_r = dw_r; f.dw_g = dw_g;
+    f.dconv_part = w.dconv_part; f.conv_rb = m.conv_rb; f.dconv_w = dconv_w;
+    f.nchunks = w.nchunks; f.dbg_part = w.dbg_part; f.db_g = db_g;
+    f.dgam_part = gamma ? w.dgam_part : nullptr; f.dgamma = gamma ? dgamma : nullptr;
+    launch_bwd_finalize(f, s);
+  }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 

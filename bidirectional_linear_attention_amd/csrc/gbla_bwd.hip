@@ -681,6 +681,65 @@ void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int K
                      dw_g);
 }
 
+// ============================================================== the backward's final reductions
+// One launch for the three sums that close the backward, each over its own
+// range of blocks, each in a fixed order: the dW split-K partials (float4 per
+// thread, as k_dw_reduce), the conv-backward row-block partials of dconv_w,
+// and the per-chunk partials of db_g (and of dgamma with the gated output).
+__global__ __launch_bounds__(256) void k_bwd_finalize(BwdFinalize f) {
+  int b = blockIdx.x;
+  if (b < f.dw_blocks) {
+    const int D = f.H * f.dh, GD = (f.dw_r ? 4 : 3) * D;
+    const long total = (long)f.d * f.Kp, quads = total / 4;
+    for (long qi = b * 256L + threadIdx.x; qi < quads; qi += (long)f.dw_blocks * 256) {
+      const long e = 4 * qi;
+      const int c = (int)(e / f.Kp), n = (int)(e - (long)c * f.Kp);
+      if (n >= GD + f.H) continue;
+      float4 s = *reinterpret_cast<const float4*>(f.dw_part + e);
+      for (int k = 1; k < f.nsplit; ++k) {
+        const float4 p = *reinterpret_cast<const float4*>(f.dw_part + (size_t)k * total + e);
+        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+      }
+      if (n < GD) {
+        const int seg = n / D;
+        float* dst = seg == 0 ? f.dw_q : (seg == 1 ? f.dw_k : (seg == 2 ? f.dw_v : f.dw_r));
+        *reinterpret_cast<float4*>(dst + (long)c * D + n - seg * D) = s;
+      } else if (f.dw_g) {
+        const float v[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (n + u < GD + f.H) f.dw_g[(long)(n + u - GD) * f.d + c] = v[u];
+      }
+    }
+    return;
+  }
+  b -= f.dw_blocks;
+  const int dconv_blocks = f.d;  // 4 d elements, 4 per block
+  if (b < dconv_blocks) {
+    sum_parts_block<4>(f.dconv_part, 4 * f.d, f.conv_rb, f.dconv_w, b);
+    return;
+  }
+  b -= dconv_blocks;
+  const int nc = *f.nchunks;
+  const int dbg_blocks = (f.H + 3) / 4;
+  if (b < dbg_blocks) {
+    sum_parts_block<4>(f.dbg_part, f.H, nc, f.db_g, b);
+    return;
+  }
+  b -= dbg_blocks;
+  if (f.dgamma) sum_parts_block<4>(f.dgam_part, f.dh, nc * f.H, f.dgamma, b);
+}
+
+void launch_bwd_finalize(const BwdFinalize& f, hipStream_t s) {
+  const int grid = f.dw_blocks + f.d + (f.H + 3) / 4 + (f.dgamma ? (f.dh + 3) / 4 : 0);
+  hipLaunchKernelGGL(k_bwd_finalize, dim3(grid), dim3(256), 0, s, f);
+}
+
+int bwd_finalize_dw_blocks(int d, int Kp) {
+  const long quads = (long)d * Kp / 4;
+  return (int)std::min<long>((quads + 255) / 256, 8192);
+}
+
 // ============================================================== conv backward
 // Thread = 8 channels x kConvRun consecutive tokens; block = 64 channel groups
 // (512 channels) x 4 runs. Both windows slide in registers: dx~ rows u..u+3

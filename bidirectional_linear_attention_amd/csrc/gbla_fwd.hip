@@ -641,28 +641,7 @@ void launch_combine(const float* partial, const int* nchunks, const int* chunk_o
 template <int EB>
 __global__ __launch_bounds__(256) void k_sum_parts(const float* __restrict__ in, int E, int P_host,
                                                    const int* __restrict__ P_dev, int p_mul, float* __restrict__ out) {
-  constexpr int PH = 256 / EB;
-  __shared__ float red[PH][EB];
-  const int el = threadIdx.x % EB, ph = threadIdx.x / EB;
-  const int e = blockIdx.x * EB + el;
-  const int P = P_dev ? *P_dev * p_mul : P_host;
-  float a[8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) a[u] = 0.f;
-  if (e < E) {
-    int p = ph;
-    for (; p + 7 * PH < P; p += 8 * PH)
-#pragma unroll
-      for (int u = 0; u < 8; ++u) a[u] += in[(size_t)(p + u * PH) * E + e];
-    for (int u = 0; p < P; p += PH, ++u) a[u] += in[(size_t)p * E + e];
-  }
-  red[ph][el] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
-  __syncthreads();
-  if (ph == 0 && e < E) {
-    float t = 0.f;
-    for (int q = 0; q < PH; ++q) t += red[q][el];
-    out[e] = t;
-  }
+  sum_parts_block<EB>(in, E, P_dev ? *P_dev * p_mul : P_host, out, blockIdx.x);
 }
 
 void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s,

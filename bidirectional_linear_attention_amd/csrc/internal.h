@@ -16,7 +16,7 @@ enum StageId {
   ST_PACK_WT, ST_CONV_RECOMPUTE, ST_PROJ_RECOMPUTE, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN,
   ST_DBG_REDUCE, ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
   ST_LION_LOG_DECAY, ST_LION_PROJ, ST_LION_CHUNK_STATE, ST_LION_SCAN, ST_LION_READOUT,
-  ST_LION_BWD_STATE, ST_LION_BWD_SCAN, ST_LION_BWD_TOKEN, ST_LION_DA, ST_LION_DB_REDUCE,
+  ST_LION_BWD_STATE, ST_LION_BWD_SCAN, ST_LION_BWD_TOKEN, ST_LION_DA, ST_LION_DB_REDUCE, ST_FINALIZE,
   kNumStages
 };
 
@@ -106,6 +106,17 @@ int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
                     hipStream_t s);
 // dw_g may be null (its columns are not written); dw_r non-null: G has the R segment
+// the backward's closing sums (dW split-K partials, dconv_w row blocks, db_g and
+// dgamma chunk partials) in one launch
+struct BwdFinalize {
+  const float* dw_part; int nsplit, d, H, dh, Kp, dw_blocks;
+  float *dw_q, *dw_k, *dw_v, *dw_r, *dw_g;
+  const float* dconv_part; int conv_rb; float* dconv_w;
+  const int* nchunks; const float* dbg_part; float* db_g;
+  const float* dgam_part; float* dgamma;
+};
+int bwd_finalize_dw_blocks(int d, int Kp);
+void launch_bwd_finalize(const BwdFinalize& f, hipStream_t s);
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_r, float* dw_g, hipStream_t s);
 void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,

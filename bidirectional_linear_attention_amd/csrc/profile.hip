@@ -20,7 +20,7 @@ const char* kStageNames[kNumStages] = {
     "pack_wt", "conv_recompute", "proj_recompute", "bwd_dstate", "combine_dstate", "bwd_token",
     "dbg_reduce", "gemm_dx", "conv_bwd", "gemm_dw", "dw_reduce", "dconv_reduce",
     "lion_log_decay", "lion_proj", "lion_chunk_state", "lion_scan", "lion_readout",
-    "lion_bwd_state", "lion_bwd_scan", "lion_bwd_token", "lion_da", "lion_db_reduce",
+    "lion_bwd_state", "lion_bwd_scan", "lion_bwd_token", "lion_da", "lion_db_reduce", "finalize",
 };
 
 struct Profiler {
