@@ -167,8 +167,10 @@ void launch_lion_chunk_state(int dt, int dh, int mode, const void* rsrc, const v
 // ---------------------------------------------------------------- scan over chunks
 // For every (sequence, head, element e): replace U_c by SF_c (the state that
 // enters chunk c from the left) and W_c by SB_c (from the right), in chunk order.
-// The loads of kScanBatch chunks are issued together before the carry walks
-// over them, so the walk pays one memory latency per batch.
+// The two walks touch disjoint halves of each chunk's state, so they run
+// together: each round issues the loads of kScanBatch chunks of the forward
+// walk and of the backward walk before either carry advances, and the walk
+// pays one memory latency per round.
 constexpr int kScanBatch = 16;
 
 __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const float* __restrict__ lam,
@@ -183,39 +185,28 @@ __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
   const size_t cs = (size_t)H * 2 * E;  // stride between consecutive chunks
   float* base = st + (size_t)h * 2 * E + e;
-  float sf = 0.f;
-  for (int cb = c0; cb < c1; cb += B) {
-    float u[B], g[B];
+  float sf = 0.f, sb = 0.f;
+  for (int k = 0; c0 + k < c1; k += B) {
+    const int cf = c0 + k, cb = c1 - 1 - k;  // first chunk of the round: forward walk, backward walk
+    float u[B], gu[B], w[B], gw[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int c = cb + j;
+      const int c = cf + j, d = cb - j;
       u[j] = c < c1 ? base[(size_t)c * cs] : 0.f;
-      g[j] = c < c1 ? lam[(size_t)c * H + h] : 0.f;
+      gu[j] = c < c1 ? lam[(size_t)c * H + h] : 0.f;
+      w[j] = d >= c0 ? base[(size_t)d * cs + E] : 0.f;
+      gw[j] = d >= c0 ? lam[(size_t)d * H + h] : 0.f;
     }
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int c = cb + j;
+      const int c = cf + j, d = cb - j;
       if (c < c1) {
         base[(size_t)c * cs] = sf;
-        sf = __expf(g[j]) * sf + u[j];
+        sf = __expf(gu[j]) * sf + u[j];
       }
-    }
-  }
-  float sb = 0.f;
-  for (int cb = c1 - 1; cb >= c0; cb -= B) {
-    float w[B], g[B];
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int c = cb - j;
-      w[j] = c >= c0 ? base[(size_t)c * cs + E] : 0.f;
-      g[j] = c >= c0 ? lam[(size_t)c * H + h] : 0.f;
-    }
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int c = cb - j;
-      if (c >= c0) {
-        base[(size_t)c * cs + E] = sb;
-        sb = __expf(g[j]) * sb + w[j];
+      if (d >= c0) {
+        base[(size_t)d * cs + E] = sb;
+        sb = __expf(gw[j]) * sb + w[j];
       }
     }
   }
