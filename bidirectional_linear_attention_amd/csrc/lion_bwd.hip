@@ -77,12 +77,21 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
   __shared__ __align__(16) T Ks[C * LDR];   // phi(k); dq on output
   __shared__ __align__(16) T Vs[C * LDR];   // v; dv on output
   __shared__ __align__(16) T Gs[C * LDR];   // dy / r
-  __shared__ __align__(16) T Pt[C * LDP];   // P
-  __shared__ __align__(16) T Dt[C * LDP];   // dP (.) M
-  __shared__ __align__(16) T SFs[DH * LDR];  // SF, then HF: [n][a]
-  __shared__ __align__(16) T SBs[DH * LDR];  // SB, then HB: [n][a]
+  __shared__ __align__(16) T PD[2 * C * LDP];    // P, then dP (.) M; dq (float) at the output
+  __shared__ __align__(16) T SFB[2 * DH * LDR];  // SF then SB ([n][a]), later HF then HB; dk (float)
+  T* const Pt = PD;
+  T* const Dt = PD + C * LDP;
+  T* const SFs = SFB;
+  T* const SBs = SFB + DH * LDR;
+  // the gradients of phi(q) and phi(k), kept in float for the feature-map VJP
+  // at the output (both regions are free by then)
+  static_assert(2 * C * LDP * sizeof(T) >= (DH == 64 ? 1 : 2) * C * DH * sizeof(float) &&
+                    (DH != 64 || 2 * DH * LDR * sizeof(T) >= C * DH * sizeof(float)),
+                "room for the float gradients");
+  float* const dqf = reinterpret_cast<float*>(PD);
+  float* const dkf = DH == 64 ? reinterpret_cast<float*>(SFB) : reinterpret_cast<float*>(PD) + C * DH;
   __shared__ float xF[DH], xB[DH];          // extra columns of the staged states
-  __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C];
+  __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C], dotq[C], dotk[C];
   __shared__ float colpart[4][C];
   __shared__ float Ls;
 
@@ -221,16 +230,13 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = r0 + 4 * grp + r;
-      const int t = ch.start + i;
-      const bool ok = t < ch.end;
-      const float inv_n = fast_rcp(nq[i]);
+      const bool ok = ch.start + i < ch.end;
 #pragma unroll
-      for (int nt = 0; nt < FB; ++nt) {
-        const float u = ok ? to_f<T>(qr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;
-        const float p = to_f<T>(Qs[i * LDR + 16 * nt + col]);
-        dqo[nt][r] = ok ? phi_lion_vjp(u, p, inv_n, dq[nt][r], dot[r]) : 0.f;
+      for (int nt = 0; nt < FB; ++nt) dqo[nt][r] = dq[nt][r];  // the gradient of phi(q); its VJP runs at the output
+      if (col == 0) {
+        dAq[i] = ok ? sgn[r] + inter[r] : 0.f;
+        dotq[i] = dot[r];
       }
-      if (col == 0) dAq[i] = ok ? sgn[r] + inter[r] : 0.f;
     }
   }
   __syncthreads();  // every wave is done with SF / SB
@@ -297,16 +303,13 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int j = r0 + 4 * grp + r;
-      const int t = ch.start + j;
-      const bool ok = t < ch.end;
-      const float inv_n = fast_rcp(nk[j]);
+      const bool ok = ch.start + j < ch.end;
 #pragma unroll
-      for (int nt = 0; nt < FB; ++nt) {
-        const float u = ok ? to_f<T>(kr[(size_t)t * D + h * DH + 16 * nt + col]) : 0.f;
-        const float p = to_f<T>(Ks[j * LDR + 16 * nt + col]);
-        dko[nt][r] = ok ? phi_lion_vjp(u, p, inv_n, dk[nt][r], dot[r]) : 0.f;
+      for (int nt = 0; nt < FB; ++nt) dko[nt][r] = dk[nt][r];  // the gradient of phi(k); its VJP runs at the output
+      if (col == 0) {
+        dAk[j] = ok ? dAk[j] + inter[r] : 0.f;
+        dotk[j] = dot[r];
       }
-      if (col == 0) dAk[j] = ok ? dAk[j] + inter[r] : 0.f;
     }
   }
   __syncthreads();  // every wave is done reading the tiles; reuse them for the outputs
@@ -315,8 +318,8 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
     const int i = r0 + 4 * grp + r;
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
-      Ks[i * LDR + 16 * nt + col] = from_f<T>(dqo[nt][r]);
-      Qs[i * LDR + 16 * nt + col] = from_f<T>(dko[nt][r]);
+      dqf[i * DH + 16 * nt + col] = dqo[nt][r];
+      dkf[i * DH + 16 * nt + col] = dko[nt][r];
       Vs[i * LDR + 16 * nt + col] = from_f<T>(dv[nt][r]);
     }
   }
@@ -329,9 +332,20 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
     if (it >= C * V8) continue;
     const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
     if (t < ch.end) {
+      // feature-map VJP of 8 features of row r: raw q and k as 16-byte vectors
+      const size_t o = (size_t)t * D + h * DH + c;
+      const Frag8<T> uq = frag_load(qr + o), uk = frag_load(kr + o);
+      const Frag8<T> pq = frag_load(Qs + r * LDR + c), pk = frag_load(Ks + r * LDR + c);
+      const float inq = fast_rcp(nq[r]), ink = fast_rcp(nk[r]), dtq = dotq[r], dtk = dotk[r];
+      float oq[8], ok8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        oq[j] = phi_lion_vjp(frag_get(uq, j), frag_get(pq, j), inq, dqf[r * DH + c + j], dtq);
+        ok8[j] = phi_lion_vjp(frag_get(uk, j), frag_get(pk, j), ink, dkf[r * DH + c + j], dtk);
+      }
       T* g = G + (size_t)t * Kp + h * DH + c;
-      frag_store(g, frag_load(Ks + r * LDR + c));
-      frag_store(g + D, frag_load(Qs + r * LDR + c));
+      frag_store(g, frag_from<T>(oq));
+      frag_store(g + D, frag_from<T>(ok8));
       frag_store(g + 2 * D, frag_load(Vs + r * LDR + c));
     }
   }
