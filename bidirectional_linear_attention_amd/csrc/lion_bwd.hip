@@ -30,39 +30,52 @@ __device__ __forceinline__ float phi_lion_vjp(float u, float p, float inv_n, flo
   return (d - p * dot) * inv_n * (sg * (1.f + u * (1.f - sg)));
 }
 
-// stage a carried state, stored transposed ([n][a]: row n = column feature n,
-// dh values of the row feature a; row dh = the extra column), as the LDS tile
-// [n][a] for n < dh (pitch ld, a multiple of 4) plus the extra row as floats;
-// S is 16-byte aligned and every load is issued before the first LDS store
+// a carried state, stored transposed ([n][a]: row n = column feature n, dh
+// values of the row feature a; row dh = the extra column), staged as the LDS
+// tile [n][a] for n < dh (pitch ld, a multiple of 4) plus the extra row as
+// floats; S is 16-byte aligned. state_rows_load issues the loads into
+// registers, state_rows_store writes them (4 elements per 8- or 16-byte LDS
+// store), so the loads can be issued well before the tile is needed.
+template <int DH> struct StateRegs {
+  static constexpr int V4 = DH * DH / 4, PER = (V4 + 255) / 256;
+  float4 r[PER];
+  float x;
+};
+template <int DH>
+__device__ __forceinline__ void state_rows_load(StateRegs<DH>& g, const float* __restrict__ S, int tid) {
+#pragma unroll
+  for (int k = 0; k < StateRegs<DH>::PER; ++k) {
+    const int e4 = tid + 256 * k;
+    g.r[k] = e4 < StateRegs<DH>::V4 ? reinterpret_cast<const float4*>(S)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  g.x = tid < DH ? S[DH * DH + tid] : 0.f;
+}
+template <typename T, int DH>
+__device__ __forceinline__ void state_rows_store(const StateRegs<DH>& g, T* R, int ld, float* extra, int tid) {
+#pragma unroll
+  for (int k = 0; k < StateRegs<DH>::PER; ++k) {
+    const int e4 = tid + 256 * k;
+    if (e4 >= StateRegs<DH>::V4) continue;
+    const int n = (4 * e4) / DH, a = (4 * e4) % DH;
+    const float v[4] = {g.r[k].x, g.r[k].y, g.r[k].z, g.r[k].w};
+    quad_store(R + n * ld + a, quad_from4<T>(v));
+  }
+  if (tid < DH) extra[tid] = g.x;
+}
 template <typename T, int DH>
 __device__ __forceinline__ void stage_state_rows(T* R, int ld, float* extra, const float* __restrict__ S, int tid) {
-  constexpr int V4 = DH * DH / 4, PER = (V4 + 255) / 256;
-  float4 r[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e4 = tid + 256 * k;
-    r[k] = e4 < V4 ? reinterpret_cast<const float4*>(S)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  const float xv = tid < DH ? S[DH * DH + tid] : 0.f;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int e4 = tid + 256 * k;
-    if (e4 >= V4) continue;
-    const int n = (4 * e4) / DH, a = (4 * e4) % DH;
-    T* dst = R + n * ld + a;
-    dst[0] = from_f<T>(r[k].x);
-    dst[1] = from_f<T>(r[k].y);
-    dst[2] = from_f<T>(r[k].z);
-    dst[3] = from_f<T>(r[k].w);
-  }
-  if (tid < DH) extra[tid] = xv;
+  StateRegs<DH> g;
+  state_rows_load<DH>(g, S, tid);
+  state_rows_store<T, DH>(g, R, ld, extra, tid);
 }
 
 // Block = (chunk, head), 4 waves; wave w owns rows 16 w .. 16 w + 15 of the chunk
 // (query rows in phase 1, key rows in phase 2). The extra column of [v | 1] and
 // of g^ enters every contraction as a rank-1 term, so all MFMA widths are dh.
+// Two blocks per CU (the occupancy hint keeps the registers of the phase-2
+// state prefetch within 256 per lane).
 template <typename T, int DH>
-__global__ __launch_bounds__(256) void k_lion_bwd_token(
+__global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
     const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vr, const float* __restrict__ logl,
     const T* __restrict__ yv, const T* __restrict__ dy, const float* __restrict__ rsum, const float* __restrict__ st,
     const float* __restrict__ hst, const int* __restrict__ nchunks, const Chunk* __restrict__ tab, int max_slots,
@@ -152,6 +165,7 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
 
   // ---------------- phase 1: query rows i = r0 + 4 grp + r
   float dqo[FB][4];
+  StateRegs<DH> hreg[2];
   {
     Frag8<T> aq[DH / 32], ag[DH / 32];
 #pragma unroll
@@ -196,6 +210,9 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
 #pragma unroll
     for (int r = 0; r < 4; ++r) sgn[r] = row16_sum(sgn[r]);
     __syncthreads();  // Pt, Dt complete
+    // the states of phase 2 load while this phase finishes
+    state_rows_load<DH>(hreg[0], hst + ((size_t)slot * H + h) * 2 * E, tid);
+    state_rows_load<DH>(hreg[1], hst + ((size_t)slot * H + h) * 2 * E + E, tid);
 
     f32x4 dq[FB];
     float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
@@ -242,9 +259,8 @@ __global__ __launch_bounds__(256) void k_lion_bwd_token(
   __syncthreads();  // every wave is done with SF / SB
 
   // ---------------- phase 2: key rows j = r0 + 4 grp + r
-  const float* hp = hst + ((size_t)slot * H + h) * 2 * E;
-  stage_state_rows<T, DH>(SFs, LDR, xF, hp, tid);
-  stage_state_rows<T, DH>(SBs, LDR, xB, hp + E, tid);
+  state_rows_store<T, DH>(hreg[0], SFs, LDR, xF, tid);
+  state_rows_store<T, DH>(hreg[1], SBs, LDR, xB, tid);
   if (tid < C) dAk[tid] = (colpart[0][tid] + colpart[1][tid]) + (colpart[2][tid] + colpart[3][tid]);
   __syncthreads();
   float dko[FB][4];
