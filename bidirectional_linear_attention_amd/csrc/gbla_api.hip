@@ -273,7 +273,7 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
                      w.dbg_part,
                      m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
   if (m.T > 0) {
-    { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, w.dxt, s); }
+    { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, grad_cols_read(m.H, m.dh, m.gated), w.dxt, s); }
     { StageScope ps(ST_CONV_BWD, s);
       launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s); }
   }

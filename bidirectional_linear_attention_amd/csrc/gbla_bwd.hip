@@ -327,7 +327,8 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
-  const int gs0 = nseg * D, gcol0 = gs0 + H;  // gate column of head 0; first zero-pad column of G
+  const int gs0 = nseg * D, gcol0 = gs0 + H;  // gate column of head 0; first padding column of G
+  const int gcolr = (gcol0 + 7) / 8 * 8;       // padding columns the dX~ GEMM reads (zeroed)
   const int r0 = 16 * w;
   constexpr int NV = (ST * V8 + 255) / 256;
   Frag8<T> pk[NV], pv[NV];
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
         dbg += ds;
       }
       if (ok && h == 0)
-        for (int c = gcol0 + col; c < Kp; c += 16) G[(size_t)t * Kp + c] = from_f<T>(0.f);
+        for (int c = gcol0 + col; c < gcolr; c += 16) G[(size_t)t * Kp + c] = from_f<T>(0.f);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -508,10 +509,11 @@ template <typename T> struct DxCfg;
 template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; };
 template <> struct DxCfg<float> { using S = GemmShape<float, 128, 64, 32, 2, 2>; static constexpr bool DL = false; };
 
+// Kp is the row pitch of G and Wt; the k loop reads Kr <= Kp columns.
 template <typename T>
 __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
                                                                      const T* __restrict__ wt, int T_, int d, int Kp,
-                                                                     T* __restrict__ dxt) {
+                                                                     int Kr, T* __restrict__ dxt) {
   using S = typename DxCfg<T>::S;
   constexpr bool DL = DxCfg<T>::DL;
   static_assert(S::BM % 32 == 0 && S::WTM % 32 == 0, "whole 32-row channel groups per wave");
@@ -525,11 +527,11 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
   const int m0 = mt * S::BN, n0 = nt * S::BM;  // first token, first channel row
   f32x4 acc[S::FM][S::FN];
   if constexpr (DL)
-    gemm_nt_dl<S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp, min(S::BN, T_ - m0), Kp,
+    gemm_nt_dl<S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp, min(S::BN, T_ - m0), Kr,
                   smem, smem1, smem1, smem1, acc);
   else
     gemm_nt_mainloop<T, S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp,
-                           min(S::BN, T_ - m0), Kp, smem, acc);
+                           min(S::BN, T_ - m0), Kr, smem, acc);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
 #pragma unroll
@@ -549,17 +551,17 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
   }
 }
 
-void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s) {
+void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* dxt, hipStream_t s) {
   if (dt == BF16) {
     using S = DxCfg<bf16>::S;
     const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
     if (n) hipLaunchKernelGGL(k_gemm_dx<bf16>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const bf16*)G,
-                              (const bf16*)wt, T, d, Kp, (bf16*)dxt);
+                              (const bf16*)wt, T, d, Kp, Kr, (bf16*)dxt);
   } else {
     using S = DxCfg<float>::S;
     const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
     if (n) hipLaunchKernelGGL(k_gemm_dx<float>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const float*)G,
-                              (const float*)wt, T, d, Kp, (float*)dxt);
+                              (const float*)wt, T, d, Kp, Kr, (float*)dxt);
   }
 }
 

@@ -50,6 +50,11 @@ __host__ __device__ inline int wt_rows(int d) { return (d + 31) / 32 * 32; }
 inline int grad_cols(int H, int dh, bool out_gate = false) {
   return (((out_gate ? 4 : 3) * H * dh + H) + 63) / 64 * 64;
 }
+// columns of G the dX~ GEMM reads (its k extent): the used columns rounded up
+// to 8; only the padding columns below this bound are written (as zeros)
+inline int grad_cols_read(int H, int dh, bool out_gate = false) {
+  return (((out_gate ? 4 : 3) * H * dh + H) + 7) / 8 * 8;
+}
 
 // ---- forward / shared
 void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
@@ -100,7 +105,7 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, int nseg, void* G,
                       float* dbg_part, const float* gmax, hipStream_t s);
-void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, void* dxt, hipStream_t s);
+void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* dxt, hipStream_t s);
 int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,

@@ -221,7 +221,7 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
   }
   if (m.T > 0) {
     StageScope ps(ST_GEMM_DX, s);
-    launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, dx, s);
+    launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, grad_cols_read(m.H, m.dh), dx, s);
   }
   { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, x, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
   { StageScope ps(ST_DW_REDUCE, s);

@@ -398,7 +398,7 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
 //   k_lion_dsuffix  one wave per (sequence, head): chunk totals -> exclusive
 //                   suffix sums over the sequence's chunks, in place
 //   k_lion_da       one block per chunk: da for every token and head (written to G
-//                   when the decay depends on x, else 0), the zero padding of G,
+//                   when the decay depends on x, else 0), the padding columns of G the dX~ GEMM reads (zeroed),
 //                   and the chunk's per-head sum of da (db partial)
 __global__ __launch_bounds__(256) void k_lion_dsuffix(float* __restrict__ dA_tot, const int* __restrict__ nchunks,
                                                       const int* __restrict__ chunk_off, int N, int H) {
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl,
     for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
     if (lane == 0) db_part[(size_t)slot * H + h] = sum;
   }
-  const int g0 = 3 * D + H, P = Kp - g0;  // zero padding of G
+  const int g0 = 3 * D + H, P = (g0 + 7) / 8 * 8 - g0;  // the padding columns of G the dX~ GEMM reads
   for (int e = tid; e < C * P; e += 256) {
     const int r = e / P, c = g0 + e % P;
     if (ch.start + r < ch.end) G[(size_t)(ch.start + r) * Kp + c] = from_f<T>(0.f);
