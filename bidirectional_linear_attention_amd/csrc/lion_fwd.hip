@@ -129,20 +129,29 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
     }
   }
   // states are stored transposed, [n][a] (n = column feature, row n = dh is the
-  // extra column): this lane's 4 rows a of column n are contiguous
+  // extra column), so each state is one contiguous run of E floats: the tiles
+  // are gathered in LDS (a lane's 4 rows a of column n are one 16-byte store)
+  // and the run leaves as whole 1 KB wave stores, U then W
+  constexpr int LDO = DH + 4;
+  __shared__ __align__(16) float Ost[(DH + 1) * LDO];
   float* o = out + ((size_t)slot * H + h) * 2 * E;
   const int col = lane & 15;
 #pragma unroll
-  for (int u = 0; u < TPW; ++u) {
-    const int tile = w + 4 * u;
-    if (tile >= TILES) continue;
-    const int ib = tile / NB, nb = tile - ib * NB;
-    const int n = nb < FB ? 16 * nb + col : DH;
-    if (nb < FB || col == 0) {
-      float* p = o + n * DH + 16 * ib + 4 * grp;
-      *reinterpret_cast<float4*>(p) = make_float4(accU[u][0], accU[u][1], accU[u][2], accU[u][3]);
-      *reinterpret_cast<float4*>(p + E) = make_float4(accW[u][0], accW[u][1], accW[u][2], accW[u][3]);
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int u = 0; u < TPW; ++u) {
+      const int tile = w + 4 * u;
+      if (tile >= TILES) continue;
+      const int ib = tile / NB, nb = tile - ib * NB;
+      const int n = nb < FB ? 16 * nb + col : DH;
+      if (nb < FB || col == 0) *reinterpret_cast<f32x4*>(Ost + n * LDO + 16 * ib + 4 * grp) = half ? accW[u] : accU[u];
     }
+    __syncthreads();
+    for (int f = tid; f < E / 4; f += 256) {
+      const int n = f / (DH / 4), a = 4 * (f % (DH / 4));
+      *reinterpret_cast<float4*>(o + half * E + 4 * f) = *reinterpret_cast<const float4*>(Ost + n * LDO + a);
+    }
+    __syncthreads();
   }
   if (MODE == 0 && lam_out && tid == 0) lam_out[(size_t)slot * H + h] = Ls;
 }
