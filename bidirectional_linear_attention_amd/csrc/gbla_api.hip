@@ -205,8 +205,9 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
   const Act& A = w.act;
 
   (void)hipGetLastError();
-  { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, s); }
+  { StageScope ps(ST_PACK_PROJ, s);  // and the chunk table
+    launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp,
+                     Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
   { StageScope ps(ST_CONV_FWD, s);
     launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
   { StageScope ps(ST_PROJ_FWD, s);
@@ -255,10 +256,12 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
   const Act& A = w.act;
 
   (void)hipGetLastError();
-  { StageScope ps(ST_SCHEDULE, s); launch_schedule(cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_WT, s); launch_pack_wt(dt, w_q, w_k, w_v, w_r, w_g, m.d, m.H, m.dh, m.Kp, w.wt, s); }
+  { StageScope ps(ST_PACK_WT, s);  // and the chunk table
+    launch_pack_wt(dt, w_q, w_k, w_v, w_r, w_g, m.d, m.H, m.dh, m.Kp, w.wt,
+                   Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
   if (!act) {  // recompute x~, g, phi(q), phi(k), v into the workspace
-    { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, s); }
+    { StageScope ps(ST_PACK_PROJ, s);
+      launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, Sched{}, s); }
     { StageScope ps(ST_CONV_RECOMPUTE, s);
       launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
     { StageScope ps(ST_PROJ_RECOMPUTE, s);

@@ -457,15 +457,21 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
 // channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all).
 // Thread = 8 consecutive columns n (16-byte loads and stores in the weight
 // column blocks, which start at multiples of 32; element-wise in the gate and
-// padding columns).
+// padding columns). With a schedule (sc.cu non-null) the last block builds the
+// chunk table instead.
 template <typename T>
 __global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k,
                                                  const T* __restrict__ w_v, const T* __restrict__ w_r,
                                                  const T* __restrict__ w_g, int d, int H, int dh, int Kp,
-                                                 T* __restrict__ wt) {
+                                                 T* __restrict__ wt, Sched sc) {
+  const int nblk = gridDim.x - (sc.cu ? 1 : 0);  // packing blocks
+  if (sc.cu && blockIdx.x == nblk) {
+    schedule_block<256>(sc);
+    return;
+  }
   const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
   const int per_row = Kp / 8, total = wt_rows(d) * per_row;  // < 2^31 (checked on the host)
-  for (int e8 = blockIdx.x * blockDim.x + threadIdx.x; e8 < total; e8 += gridDim.x * blockDim.x) {
+  for (int e8 = blockIdx.x * blockDim.x + threadIdx.x; e8 < total; e8 += nblk * blockDim.x) {
     const int p = e8 / per_row, n = 8 * (e8 - p * per_row);
     const size_t e = (size_t)p * Kp + n;
     const int c = tile_row_perm(p);
@@ -487,15 +493,15 @@ __global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, cons
 }
 
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
-                    int d, int H, int dh, int Kp, void* wt, hipStream_t s) {
+                    int d, int H, int dh, int Kp, void* wt, const Sched& sc, hipStream_t s) {
   const long total = (long)wt_rows(d) * Kp / 8;
-  const int grid = (int)std::min<long>((total + 255) / 256, 4096);
+  const int grid = (int)std::min<long>((total + 255) / 256, 4096) + (sc.cu ? 1 : 0);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_r, (const bf16*)w_g, d, H, dh, Kp, (bf16*)wt);
+                       (const bf16*)w_v, (const bf16*)w_r, (const bf16*)w_g, d, H, dh, Kp, (bf16*)wt, sc);
   else
     hipLaunchKernelGGL(k_pack_wt<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_r, (const float*)w_g, d, H, dh, Kp, (float*)wt);
+                       (const float*)w_v, (const float*)w_r, (const float*)w_g, d, H, dh, Kp, (float*)wt, sc);
 }
 
 // ============================================================== dX~ = G Wt^T

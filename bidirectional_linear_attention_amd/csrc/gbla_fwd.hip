@@ -9,7 +9,8 @@
 //   y_i = phi(q_i)^T S / phi(q_i)^T z             (Eqs. (5)/(6) in the state-first order of Eq. (3))
 //
 // Kernels (all on the caller's stream, no host synchronisation):
-//   k_schedule      chunk table of <= kChunk-token runs inside each sequence, from cu_seqlens
+//   schedule_block  chunk table of <= kChunk-token runs inside each sequence, from cu_seqlens
+//                   (one extra block of the weight-packing launch)
 //   k_pack_proj     per-head packed weights [H][3*dh][d]: Q, K, V columns, k contiguous
 //   k_conv_fwd      causal conv -> x~, and the gates g = sigmoid(x~ w_g + b_g) of every head
 //   k_proj          projection GEMM x~ [W_Q|W_K|W_V]^h (pipelined MFMA) with phi epilogue
@@ -21,77 +22,6 @@
 
 namespace gbla {
 
-// ============================================================== schedule
-// One block of 1024 threads. Sequences are taken 1024 at a time: thread b
-// reads its offsets once, the chunk counts are prefix-summed with wave
-// shuffles plus one pass over the 16 wave totals, and the table entries of the
-// batch are then written by all threads in parallel (entry s finds its
-// sequence by binary search over the batch's offsets in LDS).
-__global__ __launch_bounds__(1024) void k_schedule(const int32_t* __restrict__ cu, int N, int T, int chunk,
-                                                   int max_slots, int* __restrict__ nchunks,
-                                                   int* __restrict__ chunk_off, Chunk* __restrict__ tab) {
-  __shared__ int off[1025];
-  __shared__ int wsum[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  int bad = 0;
-  if (tid == 0) bad = (cu[0] != 0) || (cu[N] != T);
-  for (int b = tid; b < N; b += 1024)
-    if (cu[b + 1] < cu[b]) bad = 1;
-  if (__syncthreads_or(bad)) {  // malformed offsets: schedule nothing, so no kernel reads outside [0, T)
-    for (int b = tid; b <= N; b += 1024) chunk_off[b] = 0;
-    if (tid == 0) *nchunks = 0;
-    return;
-  }
-  int carry = 0;
-  for (int b0 = 0; b0 < N; b0 += 1024) {
-    const int b = b0 + tid, nb = min(1024, N - b0);
-    const int s0 = b < N ? cu[b] : 0, s1 = b < N ? cu[b + 1] : 0;
-    const int n = b < N ? (s1 - s0 + chunk - 1) / chunk : 0;
-    int inc = n;  // inclusive scan within the wave
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int v = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += v;
-    }
-    if (lane == 63) wsum[wv] = inc;
-    __syncthreads();
-    int wbase = 0;
-    for (int k = 0; k < wv; ++k) wbase += wsum[k];
-    const int excl = wbase + inc - n;  // within the batch
-    off[tid] = excl;
-    if (tid == 1023) off[1024] = excl + n;
-    if (b < N) chunk_off[b] = min(carry + excl, max_slots);
-    __syncthreads();
-    const int total = off[nb];
-    for (int e = tid; e < total && carry + e < max_slots; e += 1024) {
-      int lo = 0, hi = nb - 1;  // last sequence i with off[i] <= e
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= e) lo = mid; else hi = mid - 1;
-      }
-      const int c = e - off[lo];
-      const int st = cu[b0 + lo] + c * chunk;
-      Chunk ch;
-      ch.seq = b0 + lo;
-      ch.start = st;
-      ch.end = min(st + chunk, cu[b0 + lo + 1]);
-      ch.pad = 0;
-      tab[carry + e] = ch;
-    }
-    carry += total;
-    __syncthreads();
-  }
-  if (tid == 0) {
-    chunk_off[N] = min(carry, max_slots);
-    *nchunks = min(carry, max_slots);
-  }
-}
-
-void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
-                     Chunk* tab, hipStream_t s) {
-  hipLaunchKernelGGL(k_schedule, dim3(1), dim3(1024), 0, s, cu, N, T, chunk, max_slots, nchunks, chunk_off, tab);
-}
-
 // ============================================================== weight packing
 // wp[h][p][c] (k = c contiguous) holds column f = tile_row_perm(p) of the head's
 // [W_Q | W_K | W_V (| W_R)] block (f < dh: W_Q[:, h*dh + f], then W_K, W_V, W_R).
@@ -99,11 +29,16 @@ void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, 
 // store 8 consecutive features per lane (see k_proj).
 // Block = one 32-row group of one head x 64 channels c, transposed through
 // LDS: 16-byte loads of 8 consecutive features of one weight row, 16-byte
-// stores of 8 consecutive channels of one packed row. d % 8 == 0.
+// stores of 8 consecutive channels of one packed row. d % 8 == 0. With a
+// schedule (sc.cu non-null) the last block builds the chunk table instead.
 template <typename T>
 __global__ __launch_bounds__(256) void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k,
                                                    const T* __restrict__ w_v, const T* __restrict__ w_r, int d,
-                                                   int H, int dh, T* __restrict__ wp) {
+                                                   int H, int dh, T* __restrict__ wp, Sched sc) {
+  if (sc.cu && blockIdx.x == gridDim.x - 1) {
+    schedule_block<256>(sc);
+    return;
+  }
   __shared__ float tile[32][65];
   const int NP = (w_r ? 4 : 3) * dh, D = H * dh, G = NP / 32;
   const int cb = blockIdx.x % ((d + 63) / 64), rest = blockIdx.x / ((d + 63) / 64);
@@ -131,14 +66,14 @@ __global__ __launch_bounds__(256) void k_pack_proj(const T* __restrict__ w_q, co
 }
 
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
-                      int dh, void* wp, hipStream_t s) {
-  const int grid = H * (proj_cols(dh, w_r != nullptr) / 32) * ((d + 63) / 64);
+                      int dh, void* wp, const Sched& sc, hipStream_t s) {
+  const int grid = H * (proj_cols(dh, w_r != nullptr) / 32) * ((d + 63) / 64) + (sc.cu ? 1 : 0);
   if (dt == BF16)
     hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_r, d, H, dh, (bf16*)wp);
+                       (const bf16*)w_v, (const bf16*)w_r, d, H, dh, (bf16*)wp, sc);
   else
     hipLaunchKernelGGL(k_pack_proj<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_r, d, H, dh, (float*)wp);
+                       (const float*)w_v, (const float*)w_r, d, H, dh, (float*)wp, sc);
 }
 
 // ============================================================== causal conv + gate

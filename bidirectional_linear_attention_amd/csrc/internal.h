@@ -12,7 +12,7 @@ enum DType { F32 = 0, BF16 = 1 };
 
 // stages timed by the optional profiling window (gbla_profile_begin/end)
 enum StageId {
-  ST_SCHEDULE, ST_PACK_PROJ, ST_CONV_FWD, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
+  ST_PACK_PROJ, ST_CONV_FWD, ST_PROJ_FWD, ST_STATE_PARTIAL, ST_COMBINE_STATE, ST_READOUT,
   ST_PACK_WT, ST_CONV_RECOMPUTE, ST_PROJ_RECOMPUTE, ST_BWD_DSTATE, ST_COMBINE_DSTATE, ST_BWD_TOKEN,
   ST_DBG_REDUCE, ST_GEMM_DX, ST_CONV_BWD, ST_GEMM_DW, ST_DW_REDUCE, ST_DCONV_REDUCE,
   ST_LION_LOG_DECAY, ST_LION_PROJ, ST_LION_CHUNK_STATE, ST_LION_SCAN, ST_LION_READOUT,
@@ -57,11 +57,88 @@ inline int grad_cols_read(int H, int dh, bool out_gate = false) {
 }
 
 // ---- forward / shared
-void launch_schedule(const int32_t* cu, int N, int T, int chunk, int max_slots, int* nchunks, int* chunk_off,
-                     Chunk* tab, hipStream_t s);
+// The chunk table (runs of <= chunk tokens inside each sequence, from cu) is
+// built by one extra block of a weight-packing launch, the first launch of each
+// pass (cu null: no table).
+struct Sched {
+  const int32_t* cu;
+  int N, T, chunk, max_slots;
+  int* nchunks;
+  int* chunk_off;
+  Chunk* tab;
+};
+
+// ---- the chunk table (run by one block of NT threads)
+// Sequences are taken NT at a time: thread b reads its offsets once, the chunk
+// counts are prefix-summed with wave shuffles plus one pass over the wave
+// totals, and the table entries of the batch are then written by all threads
+// in parallel (entry s finds its sequence by binary search over the batch's
+// offsets in LDS). Malformed offsets schedule nothing, so no kernel reads
+// outside [0, T).
+template <int NT>
+__device__ inline void schedule_block(const Sched& sc) {
+  static_assert(NT % 64 == 0, "whole waves");
+  __shared__ int off[NT + 1];
+  __shared__ int wsum[NT / 64];
+  const int32_t* cu = sc.cu;
+  const int N = sc.N, chunk = sc.chunk, max_slots = sc.max_slots;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  int bad = 0;
+  if (tid == 0) bad = (cu[0] != 0) || (cu[N] != sc.T);
+  for (int b = tid; b < N; b += NT)
+    if (cu[b + 1] < cu[b]) bad = 1;
+  if (__syncthreads_or(bad)) {
+    for (int b = tid; b <= N; b += NT) sc.chunk_off[b] = 0;
+    if (tid == 0) *sc.nchunks = 0;
+    return;
+  }
+  int carry = 0;
+  for (int b0 = 0; b0 < N; b0 += NT) {
+    const int b = b0 + tid, nb = min(NT, N - b0);
+    const int s0 = b < N ? cu[b] : 0, s1 = b < N ? cu[b + 1] : 0;
+    const int n = b < N ? (s1 - s0 + chunk - 1) / chunk : 0;
+    int inc = n;  // inclusive scan within the wave
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += v;
+    }
+    if (lane == 63) wsum[wv] = inc;
+    __syncthreads();
+    int wbase = 0;
+    for (int k = 0; k < wv; ++k) wbase += wsum[k];
+    const int excl = wbase + inc - n;  // within the batch
+    off[tid] = excl;
+    if (tid == NT - 1) off[NT] = excl + n;
+    if (b < N) sc.chunk_off[b] = min(carry + excl, max_slots);
+    __syncthreads();
+    const int total = off[nb];
+    for (int e = tid; e < total && carry + e < max_slots; e += NT) {
+      int lo = 0, hi = nb - 1;  // last sequence i with off[i] <= e
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= e) lo = mid; else hi = mid - 1;
+      }
+      const int c = e - off[lo];
+      const int st = cu[b0 + lo] + c * chunk;
+      Chunk ch;
+      ch.seq = b0 + lo;
+      ch.start = st;
+      ch.end = min(st + chunk, cu[b0 + lo + 1]);
+      ch.pad = 0;
+      sc.tab[carry + e] = ch;
+    }
+    carry += total;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    sc.chunk_off[N] = min(carry, max_slots);
+    *sc.nchunks = min(carry, max_slots);
+  }
+}
 // w_r non-null: a fourth per-head segment (the gated RMSNorm output's W_R)
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
-                      int dh, void* wp, hipStream_t s);
+                      int dh, void* wp, const Sched& sc, hipStream_t s);
 // g gets sigmoid(x~ w_g + b_g), or the logit itself for the softmax key gate
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
                      const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s);
@@ -92,7 +169,8 @@ void launch_readout(int dt, int dh, const void* qa, const float* saved, const in
 // w_g may be null (its rows of Wt are zero); w_r non-null: the R segment
 // follows V ([W_Q | W_K | W_V | W_R | w_g^T])
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
-                    int d, int H, int dh, int Kp, void* wt, hipStream_t s);
+                    int d, int H, int dh, int Kp, void* wt, const Sched& sc, hipStream_t s);
+
 // ra non-null: gated RMSNorm output; dy is then the gradient of the gated
 // output, dR goes to G's R columns and per-(chunk, head) partials of dgamma
 // to dgam_part (gamma non-null)

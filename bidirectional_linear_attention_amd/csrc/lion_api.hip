@@ -161,9 +161,9 @@ gbla_status lion_forward(const lion_problem* p, const void* x, const int32_t* cu
   const LAct& A = w.act;
 
   (void)hipGetLastError();
-  { StageScope ps(ST_SCHEDULE, s);
-    launch_schedule(cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_PROJ, s); launch_pack_proj(dt, w_q, w_k, w_v, nullptr, m.d, m.H, m.dh, w.wp, s); }
+  { StageScope ps(ST_PACK_PROJ, s);  // and the chunk table
+    launch_pack_proj(dt, w_q, w_k, w_v, nullptr, m.d, m.H, m.dh, w.wp,
+                     Sched{cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
   { StageScope ps(ST_LION_LOG_DECAY, s);
     if (sel) launch_log_decay(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, w_lam, b_lam, A.logl, s);
     else launch_const_log_decay(m.T, m.H, fixed ? b_lam : nullptr, A.logl, s); }
@@ -201,10 +201,9 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
 
   (void)hipGetLastError();
-  { StageScope ps(ST_SCHEDULE, s);
-    launch_schedule(cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab, s); }
-  { StageScope ps(ST_PACK_WT, s);
-    launch_pack_wt(dt, w_q, w_k, w_v, nullptr, sel ? w_lam : nullptr, m.d, m.H, m.dh, m.Kp, w.wt, s); }
+  { StageScope ps(ST_PACK_WT, s);  // and the chunk table
+    launch_pack_wt(dt, w_q, w_k, w_v, nullptr, sel ? w_lam : nullptr, m.d, m.H, m.dh, m.Kp, w.wt,
+                   Sched{cu_seqlens, m.N, m.T, kLionChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
   { StageScope ps(ST_LION_BWD_STATE, s);
     launch_lion_chunk_state(dt, m.dh, 1, A.q, dy, y, A.rsum, A.logl, w.nchunks, w.tab, m.slots, m.H, w.hst, nullptr,
                             s); }

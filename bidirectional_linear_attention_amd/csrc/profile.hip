@@ -16,7 +16,7 @@ namespace gbla {
 
 namespace {
 const char* kStageNames[kNumStages] = {
-    "schedule", "pack_proj", "conv_fwd", "proj_fwd", "state_partial", "combine_state", "readout",
+    "pack_proj", "conv_fwd", "proj_fwd", "state_partial", "combine_state", "readout",
     "pack_wt", "conv_recompute", "proj_recompute", "bwd_dstate", "combine_dstate", "bwd_token",
     "dbg_reduce", "gemm_dx", "conv_bwd", "gemm_dw", "dw_reduce", "dconv_reduce",
     "lion_log_decay", "lion_proj", "lion_chunk_state", "lion_scan", "lion_readout",
