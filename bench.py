@@ -21,6 +21,8 @@ RMSNorm output (Eq. (7)) under "gbla_gated_rmsnorm", and the LION layers
 
 --copy-calibration instead times a plain device-to-device copy of a known size
 (for scaling the FETCH_SIZE / WRITE_SIZE counters of rocprofv3 to bytes).
+--hbm-ceiling instead measures the practical HBM rate of a streaming copy (the
+context for the bandwidth-bound kernels' fraction of the 8 TB/s peak).
 """
 from __future__ import annotations
 
@@ -165,6 +167,41 @@ def copy_calibration(mib=1024, reps=3):
           flush=True)
 
 
+def hbm_ceiling(mib=64, reps=10):
+    """Rate of a device-to-device copy of `mib` MiB (bytes read + written over
+    the copy's time, HIP events on its stream). "cold": each timed copy follows
+    a read-only sum over a 1 GiB buffer, so the 256 MB last-level cache holds
+    none of the copy's operands (a write sweep would leave dirty lines whose
+    write-back the copy would pay for); "warm": the same copy repeated at once,
+    its operands cache-resident. Medians over `reps` pairs."""
+    import torch
+    n = mib * (1 << 20) // 2
+    src = torch.randn(n, device="cuda:0").to(torch.bfloat16)
+    dst = torch.empty_like(src)
+    sweep = torch.ones((1 << 30) // 4, device="cuda:0")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    cold, warm = [], []
+    for i in range(reps + 2):
+        torch.sum(sweep)
+        ev[0].record()
+        dst.copy_(src)
+        ev[1].record()
+        ev[2].record()
+        dst.copy_(src)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            cold.append(ev[0].elapsed_time(ev[1]) * 1e-3)
+            warm.append(ev[2].elapsed_time(ev[3]) * 1e-3)
+    moved = 2 * n * 2
+    med = lambda v: sorted(v)[len(v) // 2]
+    print(json.dumps({"hbm_ceiling": {
+        "copy_bytes_read_plus_written": moved, "pairs": reps,
+        "cold_tb_per_s": round(moved / med(cold) / 1e12, 3), "warm_tb_per_s": round(moved / med(warm) / 1e12, 3),
+        "cold_us": round(med(cold) * 1e6, 2), "warm_us": round(med(warm) * 1e6, 2),
+        "flush": "read-only sum over a 1 GiB buffer before each cold copy", "peak_tb_per_s": 8.0}}), flush=True)
+
+
 def gbla_setup(torch, gb, gate, gated_output=False):
     """Device buffers and the step function of the GBLA workload (x and dy
     rotate over three buffer sets); gated_output adds the gated RMSNorm output
@@ -296,6 +333,7 @@ def main():
     ap.add_argument("--lion-steps", type=int, default=10,
                     help="steps of each secondary leg (softmax-gate GBLA, Lion-s/d/lit) after the main run (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--hbm-ceiling", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -303,6 +341,9 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.hbm_ceiling:
+        hbm_ceiling()
         return
 
     import torch
