@@ -172,6 +172,18 @@ def test_bf16_small_ragged_recipe():
     compare(make_inputs(w), backward=True, label="bf16 ragged recipe small")
 
 
+def test_f32_many_sequences():
+    """More sequences than the schedule block has threads (256): the chunk table
+    is built in several batches, with empty and single-token sequences and
+    sequences of several chunks among them."""
+    rng = np.random.default_rng(26)
+    lens = rng.integers(0, 40, 700)
+    lens[rng.choice(700, 60, replace=False)] = 0
+    lens[[3, 257, 512, 699]] = (600, 1, 513, 300)
+    w = small_variant(WORKLOADS["gbla_f32_L256_d64"], lens, d_model=64, num_heads=2, head_dim=32, seed=26)
+    compare(make_inputs(w), backward=True, label="f32 700 sequences")
+
+
 # ------------------------------------------------------------ full-size workloads (the bench configuration)
 
 def test_bf16_B32_L1024_d256_full():

@@ -157,6 +157,17 @@ def _small_bf16():
     return make_inputs(small_variant(LION, (300, 65, 1, 0, 200), d_model=128, num_heads=2, seed=55))
 
 
+def test_f32_many_sequences():
+    """More sequences than the schedule block has threads (256): the chunk table
+    is built in several batches, with empty and single-token sequences among them."""
+    rng = np.random.default_rng(60)
+    lens = rng.integers(0, 30, 600)
+    lens[rng.choice(600, 50, replace=False)] = 0
+    lens[[5, 300, 599]] = (200, 1, 129)
+    w = small_variant(LION, lens, d_model=64, num_heads=2, dtype="f32", seed=60)
+    compare(make_inputs(w), label="f32 600 sequences")
+
+
 def test_bitwise_deterministic():
     inp = _small_bf16()
     a, b = run_gpu(inp), run_gpu(inp)
