@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, cons
                                                  const T* __restrict__ w_g, int d, int H, int dh, int Kp,
                                                  T* __restrict__ wt, Sched sc) {
   const int nblk = gridDim.x - (sc.cu ? 1 : 0);  // packing blocks
-  if (sc.cu && blockIdx.x == nblk) {
+  if (sc.cu && (int)blockIdx.x == nblk) {
     schedule_block<256>(sc);
     return;
   }

@@ -525,7 +525,7 @@ void launch_state_partial(int dt, int dh, const void* ka, const void* va, const 
 // partial c is scaled by exp(mpart[c] - M), M the largest of the sequence's
 // chunk maxima, which goes to mout[b][h] (0 for an empty sequence).
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int* __restrict__ nchunks,
-                                                 const int* __restrict__ chunk_off, int N, int H, int E,
+                                                 const int* __restrict__ chunk_off, int H, int E,
                                                  const float* __restrict__ mpart, float* __restrict__ out,
                                                  float* __restrict__ mout) {
   __shared__ float4 red[4][64];
@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     if (c0 == c1) M = 0.f;
-    if (mout && blockIdx.x == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
+    if (mout && (int)blockIdx.x == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
   }
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (e < E)
@@ -566,8 +566,8 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
 
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
                     float* out, hipStream_t s, const float* mpart, float* mout) {
-  hipLaunchKernelGGL(k_combine, dim3(((elems + 255) / 256) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, N,
-                     H, elems, mpart, out, mout);
+  hipLaunchKernelGGL(k_combine, dim3(((elems + 255) / 256) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, H,
+                     elems, mpart, out, mout);
 }
 
 // out[e] = sum over p < P of in[p * E + e], P = *P_dev * p_mul if given else P_host.
