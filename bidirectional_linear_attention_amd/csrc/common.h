@@ -255,15 +255,45 @@ __device__ __forceinline__ int xcd_logical_block(int bid, int n) {
 __host__ __device__ inline int xcd_grid(int n) { return ((n + 7) >> 3) << 3; }
 
 // sum over the 16 lanes that share lane / 16
-__device__ __forceinline__ float row16_sum(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  v += __shfl_xor(v, 4, 64);
-  v += __shfl_xor(v, 8, 64);
+// ---------------------------------------------------------------- cross-lane sums
+// Register to register: DPP moves within rows of 16 lanes, lane-half swaps
+// across rows. Each step adds the same two partial sums as the xor butterfly
+// (v += v[lane ^ m] for m = 1, 2, 4, ...), so the results equal it bit for bit
+// and are the same in every lane of a group. The whole wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// quad permutations (lane ^ 1, lane ^ 2), mirrors of an 8-lane half and of a row,
+// rotate a row by 8, broadcast lane 0 of the row
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppRowMirror = 0x140, kDppRowRor8 = 0x128,
+              kDppRowBcast0 = 0x150;
+
+// v summed over each aligned group of N lanes (N = 1, 2, 4, 8 or 16). Once the
+// 4-lane sums are uniform in a quad, the half mirror pairs each quad with the
+// other quad of its 8 lanes (as lane ^ 4 would), and once the 8-lane sums are
+// uniform, the row mirror pairs the two halves of the row (as lane ^ 8 would).
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "groups of 1 to 16 lanes");
+  if constexpr (N >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (N >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (N >= 16) v += dpp_f<kDppRowMirror>(v);
   return v;
 }
+__device__ __forceinline__ float row16_sum(float v) { return lane_group_sum<16>(v); }
+// v + v[lane ^ 16] and v + v[lane ^ 32]
+__device__ __forceinline__ float add_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // value held by lane 16 * (lane / 16) (column 0 of this lane's C-tile rows)
-__device__ __forceinline__ float col0_bcast(float v, int lane) { return __shfl(v, lane & 48, 64); }
+__device__ __forceinline__ float col0_bcast(float v) { return dpp_f<kDppRowBcast0>(v); }
 
 // position of token t inside its packed sequence (largest b with cu[b] <= t),
 // clamped so that t - pos >= 0 even for malformed offsets

@@ -147,8 +147,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
 #pragma unroll
         for (int r = 0; r < 4; ++r) ss += num[nt][r] * num[nt][r];
       ss *= inv * inv;
-      ss += __shfl_xor(ss, 16, 64);
-      ss += __shfl_xor(ss, 32, 64);
+      ss = add_xor32(add_xor16(ss));
       const float rinv = ok ? fast_rsqrt(ss * (1.f / DH) + eps) : 0.f;
       const float nsc = inv * rinv;  // n = num * nsc
       float ndot = 0.f, dnv[FB][4];
@@ -170,8 +169,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
         }
         if (ok) quad_store(G + (size_t)(tb + tok) * Kp + 3 * D + h * DH + 16 * nt + 4 * grp, quad_from4<T>(dr));
       }
-      ndot += __shfl_xor(ndot, 16, 64);
-      ndot += __shfl_xor(ndot, 32, 64);
+      ndot = add_xor32(add_xor16(ndot));
       const float c = ndot * (1.f / DH);
 #pragma unroll
       for (int nt = 0; nt < FB; ++nt) {
@@ -191,8 +189,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
         pdot += dyv[nt][r] * (num[nt][r] * inv);
       }
     }
-    pdot += __shfl_xor(pdot, 16, 64);
-    pdot += __shfl_xor(pdot, 32, 64);
+    pdot = add_xor32(add_xor16(pdot));
     const float dden = -pdot * inv;
     Quad<T> dnq[FB];
 #pragma unroll
@@ -257,8 +254,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           float v = dgam[nt][r];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) v += __shfl_xor(v, off, 64);
+          v = row16_sum(v);
           if (col == 0) red[w * DH + 16 * nt + 4 * grp + r] = v;
         }
       __syncthreads();
@@ -427,8 +423,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
     }
     __syncthreads();
   }
-  dbg += __shfl_xor(dbg, 16, 64);
-  dbg += __shfl_xor(dbg, 32, 64);
+  dbg = add_xor32(add_xor16(dbg));
   if (lane == 0) wsum[w] = dbg;
   __syncthreads();
   if (tid == 0) dbg_part[(size_t)slot * H + h] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);

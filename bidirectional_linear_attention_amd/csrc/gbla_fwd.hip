@@ -103,13 +103,6 @@ template <> __device__ __forceinline__ float gate_dot8<bf16>(const Frag8<bf16>& 
   return s;
 }
 
-// DPP move of a float within rows of 16 lanes (ctrl: a DPP control code)
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-constexpr int kDppRowRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor1 = 0xB1, kDppXor2 = 0x4E;
-
 // Reduce-scatter of 8 per-lane values over the wave: lane l ends with the
 // wave total of value (l >> 3). Halving steps exchange the half a lane does not
 // keep: lanes 32-63 keep values 4-7 (v_permlane32_swap), then the odd 16-lane
@@ -671,7 +664,7 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
     for (int r = 0; r < 4; ++r) {
       const int row = r0 + 4 * grp + r;
       const bool ok = tb + row < ch.end;
-      const float den = col0_bcast(acc[FB][r], lane);
+      const float den = col0_bcast(acc[FB][r]);
       const float inv = ok ? fast_rcp(den) : 0.f;
       if constexpr (GATED) {
         // y = gamma (.) O / sqrt(mean(O^2) + eps) (.) SiLU(r)
@@ -681,8 +674,7 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
           o[nt] = acc[nt][r] * inv;
           ss += o[nt] * o[nt];
         }
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) ss += __shfl_xor(ss, off, 64);
+        ss = row16_sum(ss);
         const float rinv = ok ? fast_rsqrt(ss * (1.f / DH) + eps) : 0.f;
 #pragma unroll
         for (int nt = 0; nt < FB; ++nt) {

@@ -152,8 +152,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       g[j] = frag_get(fd, j) * inv;
       dd += frag_get(fd, j) * frag_get(fy, j);
     }
-#pragma unroll
-    for (int m = 1; m < V8; m <<= 1) dd += __shfl_xor(dd, m, 64);
+    dd = lane_group_sum<V8>(dd);
     frag_store(Gs + r * LDR + c, frag_from<T>(g));
     if (c == 0) {
       gden[r] = -dd * inv;
@@ -203,8 +202,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
         sgn[r] += j < i ? e : (j > i ? -e : 0.f);  // towards dA_i
         cp += i < j ? e : (i > j ? -e : 0.f);      // towards dA_j
       }
-      cp += __shfl_xor(cp, 16, 64);
-      cp += __shfl_xor(cp, 32, 64);
+      cp = add_xor32(add_xor16(cp));
       if (grp == 0) colpart[w][j] = cp;
     }
 #pragma unroll

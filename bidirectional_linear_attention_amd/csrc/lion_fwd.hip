@@ -91,8 +91,7 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
         g[j] = frag_get(fd, j) * inv;
         dd += frag_get(fd, j) * frag_get(fy, j);
       }
-#pragma unroll
-      for (int m = 1; m < V8; m <<= 1) dd += __shfl_xor(dd, m, 64);
+      dd = lane_group_sum<V8>(dd);
       frag_store(Vs + r * LDC + c, frag_from<T>(g));
       if (c == 0) Vs[r * LDC + DH] = from_f<T>(-dd * inv);
     }
@@ -337,10 +336,8 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
         zf += q * zS[0][32 * s + 8 * grp + m];
         zb += q * zS[1][32 * s + 8 * grp + m];
       }
-    zf += __shfl_xor(zf, 16, 64);
-    zf += __shfl_xor(zf, 32, 64);
-    zb += __shfl_xor(zb, 16, 64);
-    zb += __shfl_xor(zb, 32, 64);
+    zf = add_xor32(add_xor16(zf));
+    zb = add_xor32(add_xor16(zb));
     if (grp == 0) {
       const float a = As[r0 + col];
       zpart[r0 + col] = __expf(a) * zf + __expf(L - a) * zb;

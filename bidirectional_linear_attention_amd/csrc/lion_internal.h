@@ -21,8 +21,7 @@ __device__ __forceinline__ float phi_lion8(const float (&u)[8], float (&out)[8],
     f[j] = u[j] * sigmoidf_(u[j]) + 0.5f;
     ss += f[j] * f[j];
   }
-#pragma unroll
-  for (int m = 1; m < V8; m <<= 1) ss += __shfl_xor(ss, m, 64);
+  ss = lane_group_sum<V8>(ss);
   const float rn = fast_rsqrt(ss);  // ss > 0: SiLU(u) + 0.5 >= 0.22 for every u
   const float n = ss * rn;
   const float inv = valid ? rn : 0.f;
