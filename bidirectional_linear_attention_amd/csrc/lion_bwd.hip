@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   const int r0 = 16 * w;
 
   // ---------------- phase 0: staging
-  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
+  const float la = chunk_decay_load<C>(logl, ch, H, h, tid);
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
   stage_state_rows<T, DH>(SFs, LDR, xF, sp, tid);
   stage_state_rows<T, DH>(SBs, LDR, xB, sp + E, tid);
@@ -159,6 +159,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       vone[r] = ok ? 1.f : 0.f;
     }
   }
+  chunk_decay_scan<C>(la, As, &Ls, tid);
   __syncthreads();
   const float L = Ls;
 

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, grp = lane >> 4;
   const int D = H * DH;
 
-  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
+  const float la = chunk_decay_load<C>(logl, ch, H, h, tid);
   for (int e = tid; e < C * 16; e += 256) {  // extra column block; in MODE 1 column dh is written below
     const int r = e >> 4, c = e & 15;
     if (MODE == 0 || c > 0) Vs[r * LDC + DH + c] = from_f<T>(MODE == 0 && c == 0 && ch.start + r < ch.end ? 1.f : 0.f);
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
       if (c == 0) Vs[r * LDC + DH] = from_f<T>(-dd * inv);
     }
   }
+  chunk_decay_scan<C>(la, As, &Ls, tid);
   __syncthreads();
   if (tid < C) {
     const bool ok = ch.start + tid < ch.end;
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const int ct = w / WPC, rt0 = (w % WPC) * RTW;
+  const float la = chunk_decay_load<C>(logl, ch, H, h, tid);
 
   // this wave's slice of the carried states: column n = 16 ct + col, rows a = 32 s + 8 grp .. + 7
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
@@ -297,7 +299,6 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
     const int dir = tid / (DH / 4), e4 = tid % (DH / 4);
     reinterpret_cast<float4*>(zS[dir])[e4] = reinterpret_cast<const float4*>(sp + dir * E + DH * DH)[e4];
   }
-  chunk_decay_prefix<C>(logl, ch, H, h, As, &Ls, tid);
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = tid + 256 * v;
@@ -318,6 +319,7 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
     frag_store(Ks + r * LDR + c, frag_from<T>(p));
     frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
   }
+  chunk_decay_scan<C>(la, As, &Ls, tid);
   __syncthreads();
   const float L = Ls;
 

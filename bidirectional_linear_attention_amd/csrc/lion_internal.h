@@ -30,16 +30,23 @@ __device__ __forceinline__ float phi_lion8(const float (&u)[8], float (&out)[8],
   return n;
 }
 
-// log-decay of the chunk's tokens -> inclusive prefix A~ (LDS), the chunk total
-// L (LDS), and validity; tokens past the chunk end count as log lambda = 0.
-// Called by all threads; uses wave 0.
+// Log-decay of the chunk's tokens -> inclusive prefix A~ (LDS) and the chunk
+// total L (LDS); tokens past the chunk end count as log lambda = 0. Split in
+// two so that the load is issued at block start and its latency hides behind
+// the tile loads: chunk_decay_load on every thread (wave 0 loads, the others
+// get 0), chunk_decay_scan on every thread before the barrier that publishes
+// the staged tiles (wave 0 scans and writes).
 template <int C>
-__device__ __forceinline__ void chunk_decay_prefix(const float* __restrict__ logl, const Chunk& ch, int H, int h,
-                                                   float* As, float* Ls, int tid) {
+__device__ __forceinline__ float chunk_decay_load(const float* __restrict__ logl, const Chunk& ch, int H, int h,
+                                                  int tid) {
   static_assert(C == 64, "one token per lane of wave 0");
+  const int t = ch.start + tid;
+  return tid < 64 && t < ch.end ? logl[(size_t)t * H + h] : 0.f;
+}
+
+template <int C>
+__device__ __forceinline__ void chunk_decay_scan(float a, float* As, float* Ls, int tid) {
   if (tid < 64) {
-    const int t = ch.start + tid;
-    float a = t < ch.end ? logl[(size_t)t * H + h] : 0.f;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const float o = __shfl_up(a, off, 64);
