@@ -77,12 +77,14 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 }
 
 // ============================================================== causal conv + gate
-// One wave per token row (16 consecutive rows per wave, 64 per block); lane l
-// owns channel groups c = 8 * (l + 64 m). The three previous rows slide in
-// registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
+// A wave owns 32 consecutive token rows (128 per block); lane l owns channel
+// groups c = 8 * (l + 64 m). The rows stream through two register batches of
+// 4 (the next batch loads while the current one is computed and stored), and
+// the three previous rows slide in registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
 // reduce-scatter butterfly (butterfly8): 8 head partials per lane become one
 // head total per 8 lanes in 4 + 2 lane-half swaps and 4 DPP adds.
-constexpr int kConvRowsPerWave = 16;
+constexpr int kConvRowsPerWave = 32;
+constexpr int kConvBatchRows = 4;
 
 // sum of the 8 products of two fragments (bf16: four packed dot2 instructions)
 template <typename T> __device__ __forceinline__ float gate_dot8(const Frag8<T>& a, const Frag8<T>& b);
@@ -143,10 +145,11 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
                                                   int gmode, T* __restrict__ xt, float* __restrict__ g_out) {
-  __shared__ float sacc[4][kConvRowsPerWave][8];
+  constexpr int RUN = kConvRowsPerWave, B = kConvBatchRows;
+  __shared__ float sacc[4][RUN][8];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int t_begin = (blockIdx.x * 4 + w) * kConvRowsPerWave;
-  const int t_end = min(t_begin + kConvRowsPerWave, T_);
+  const int t_begin = (blockIdx.x * 4 + w) * RUN;
+  const int t_end = min(t_begin + RUN, T_);
   const int ngroups = d / 8;
   for (int hg = 0; hg < H; hg += 8) {
     for (int g8 = lane; g8 < ((ngroups + 63) / 64) * 64; g8 += 64) {
@@ -169,44 +172,58 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         if (t_begin >= 2) xm2 = frag_load(x + (size_t)(t_begin - 2) * d + c);
         if (t_begin >= 3) xm3 = frag_load(x + (size_t)(t_begin - 3) * d + c);
       }
-      Frag8<T> xr[kConvRowsPerWave];  // every row of this wave, loaded together
+      // rows stream through two register batches: one is computed while the next loads
+      Frag8<T> xr[2][B];
+      auto fetch = [&](int buf, int tb) {
 #pragma unroll
-      for (int i = 0; i < kConvRowsPerWave; ++i)
-        xr[i] = okc && t_begin + i < t_end ? frag_load(x + (size_t)(t_begin + i) * d + c) : frag_zero<T>();
+        for (int i = 0; i < B; ++i)
+          xr[buf][i] = okc && tb + i < t_end ? frag_load(x + (size_t)(tb + i) * d + c) : frag_zero<T>();
+      };
       SeqCursor cur(cu, nseq, t_begin, T_);
+      auto compute = [&](int buf, int tb) {
 #pragma unroll
-      for (int i = 0; i < kConvRowsPerWave; ++i) {
-        const int t = t_begin + i;
-        if (t >= t_end) break;
-        const int pos = cur.pos(t);
-        const Frag8<T> x0 = xr[i];
-        float o[8];
+        for (int i = 0; i < B; ++i) {
+          const int t = tb + i;
+          if (t >= t_end) break;
+          const int pos = cur.pos(t);
+          const Frag8<T> x0 = xr[buf][i];
+          float o[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          float a = CONV ? wv[j][3] * frag_get(x0, j) : frag_get(x0, j);
-          if (CONV && pos >= 1) a += wv[j][2] * frag_get(xm1, j);
-          if (CONV && pos >= 2) a += wv[j][1] * frag_get(xm2, j);
-          if (CONV && pos >= 3) a += wv[j][0] * frag_get(xm3, j);
-          o[j] = a;
+          for (int j = 0; j < 8; ++j) {
+            float a = CONV ? wv[j][3] * frag_get(x0, j) : frag_get(x0, j);
+            if (CONV && pos >= 1) a += wv[j][2] * frag_get(xm1, j);
+            if (CONV && pos >= 2) a += wv[j][1] * frag_get(xm2, j);
+            if (CONV && pos >= 3) a += wv[j][0] * frag_get(xm3, j);
+            o[j] = a;
+          }
+          const Frag8<T> of = frag_from<T>(o);
+          if (CONV && okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
+          float sp[8];
+#pragma unroll
+          for (int hh = 0; hh < 8; ++hh) sp[hh] = gate_dot8<T>(of, wgf[hh]);  // the rounded x~ that Q, K, V see
+          const float tot = butterfly8(sp, lane);
+          if ((lane & 7) == 0) {
+            float& acc = sacc[w][t - t_begin][lane >> 3];
+            acc = g8 < 64 ? tot : acc + tot;
+          }
+          xm3 = xm2;
+          xm2 = xm1;
+          xm1 = x0;
         }
-        const Frag8<T> of = frag_from<T>(o);
-        if (CONV && okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
-        float sp[8];
-#pragma unroll
-        for (int hh = 0; hh < 8; ++hh) sp[hh] = gate_dot8<T>(of, wgf[hh]);  // the rounded x~ that Q, K, V see
-        const float tot = butterfly8(sp, lane);
-        if ((lane & 7) == 0) {
-          float& acc = sacc[w][i][lane >> 3];
-          acc = g8 < 64 ? tot : acc + tot;
+      };
+      if (t_begin < t_end) {
+        fetch(0, t_begin);
+        for (int tb = t_begin; tb < t_end; tb += 2 * B) {
+          if (tb + B < t_end) fetch(1, tb + B);
+          compute(0, tb);
+          if (tb + 2 * B < t_end) fetch(0, tb + 2 * B);
+          if (tb + B < t_end) compute(1, tb + B);
         }
-        xm3 = xm2;
-        xm2 = xm1;
-        xm1 = x0;
       }
     }
     __syncthreads();
     // sacc[w][row][hh] now holds the full logits of heads hg..hg+7 for this wave's rows
-    for (int e = lane; e < kConvRowsPerWave * 8; e += 64) {
+    for (int e = lane; e < RUN * 8; e += 64) {
       const int row = e >> 3, hh = e & 7;
       const int t = t_begin + row, h = hg + hh;
       if (t < t_end && h < H) {
