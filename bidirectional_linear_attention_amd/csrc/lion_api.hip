@@ -60,8 +60,8 @@ size_t act_bytes(const LDims& m) {
 
 struct LFwdWs { int* nchunks; int* chunk_off; Chunk* tab; void* wp; LAct act; };
 struct LBwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wt; float* hst; float* dA_loc; float* dA_tot; float* db_part;
-  void* G; float* dw_part;
+  int* nchunks; int* chunk_off; Chunk* tab; void* wt; float* hst; void* hrows; float* dA_loc; float* dA_tot;
+  float* db_part; void* G; float* dw_part;
 };
 
 size_t plan_fwd(const LDims& m, char* base, LFwdWs* w) {
@@ -84,6 +84,7 @@ size_t plan_bwd(const LDims& m, char* base, LBwdWs* w) {
   t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wt = c.take<char>(base, (size_t)wt_rows(m.d) * m.Kp * m.esz);
   t.hst = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * 2 * m.E);
+  t.hrows = c.take<char>(base, (size_t)m.slots * m.H * 2 * m.dh * m.dh * m.esz);
   t.dA_loc = c.take<float>(base, sizeof(float) * (size_t)m.T * m.H);
   t.dA_tot = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
   t.db_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
@@ -171,7 +172,8 @@ gbla_status lion_forward(const lion_problem* p, const void* x, const int32_t* cu
   { StageScope ps(ST_LION_CHUNK_STATE, s);
     launch_lion_chunk_state(dt, m.dh, 0, A.k, A.v, nullptr, nullptr, A.logl, w.nchunks, w.tab, m.slots, m.H, A.st,
                             A.lam, s); }
-  { StageScope ps(ST_LION_SCAN, s); launch_lion_scan(A.st, A.lam, w.nchunks, w.chunk_off, m.N, m.H, m.E, s); }
+  { StageScope ps(ST_LION_SCAN, s);
+    launch_lion_scan(A.st, A.lam, w.nchunks, w.chunk_off, m.N, m.H, m.E, dt, nullptr, m.dh, s); }
   { StageScope ps(ST_LION_READOUT, s);
     launch_lion_readout(dt, m.dh, A.q, A.k, A.v, A.logl, A.st, w.nchunks, w.tab, m.slots, m.H, y, A.rsum, s); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
@@ -207,10 +209,11 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
   { StageScope ps(ST_LION_BWD_STATE, s);
     launch_lion_chunk_state(dt, m.dh, 1, A.q, dy, y, A.rsum, A.logl, w.nchunks, w.tab, m.slots, m.H, w.hst, nullptr,
                             s); }
-  { StageScope ps(ST_LION_BWD_SCAN, s); launch_lion_scan(w.hst, A.lam, w.nchunks, w.chunk_off, m.N, m.H, m.E, s); }
+  { StageScope ps(ST_LION_BWD_SCAN, s);  // HF, HB: the dh x dh part leaves as the row image
+    launch_lion_scan(w.hst, A.lam, w.nchunks, w.chunk_off, m.N, m.H, m.E, dt, w.hrows, m.dh, s); }
   { StageScope ps(ST_LION_BWD_TOKEN, s);
-    launch_lion_bwd_token(dt, m.dh, A.q, A.k, A.v, A.logl, y, dy, A.rsum, A.st, w.hst, w.nchunks, w.tab, m.slots,
-                          m.H, m.Kp, w.G, w.dA_loc, w.dA_tot, s); }
+    launch_lion_bwd_token(dt, m.dh, A.q, A.k, A.v, A.logl, y, dy, A.rsum, A.st, w.hst, w.hrows, w.nchunks, w.tab,
+                          m.slots, m.H, m.Kp, w.G, w.dA_loc, w.dA_tot, s); }
   { StageScope ps(ST_LION_DA, s);
     launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.slots, m.H, m.D, m.Kp, dt, sel,
                    w.G, w.db_part, s); }

@@ -62,6 +62,32 @@ __device__ __forceinline__ void state_rows_store(const StateRegs<DH>& g, T* R, i
   }
   if (tid < DH) extra[tid] = g.x;
 }
+// the same staging from a state whose dh x dh part is already rounded to T
+// (the row image of the scan, rows [n][a] contiguous) and whose extra row is
+// the fp32 X: the loads move 4 T per lane and the LDS stores need no conversion
+template <typename T, int DH> struct ImageRegs {
+  static constexpr int V4 = DH * DH / 4, PER = (V4 + 255) / 256;
+  Quad<T> r[PER];
+  float x;
+};
+template <typename T, int DH>
+__device__ __forceinline__ void image_rows_load(ImageRegs<T, DH>& g, const T* __restrict__ S,
+                                                const float* __restrict__ X, int tid) {
+  static_assert(ImageRegs<T, DH>::V4 % 256 == 0, "every lane loads PER quads");
+#pragma unroll
+  for (int k = 0; k < ImageRegs<T, DH>::PER; ++k) g.r[k] = quad_load<T>(S + 4 * (tid + 256 * k));
+  g.x = tid < DH ? X[tid] : 0.f;
+}
+template <typename T, int DH>
+__device__ __forceinline__ void image_rows_store(const ImageRegs<T, DH>& g, T* R, int ld, float* extra, int tid) {
+#pragma unroll
+  for (int k = 0; k < ImageRegs<T, DH>::PER; ++k) {
+    const int e4 = tid + 256 * k;
+    const int n = (4 * e4) / DH, a = (4 * e4) % DH;
+    quad_store(R + n * ld + a, g.r[k]);
+  }
+  if (tid < DH) extra[tid] = g.x;
+}
 template <typename T, int DH>
 __device__ __forceinline__ void stage_state_rows(T* R, int ld, float* extra, const float* __restrict__ S, int tid) {
   StateRegs<DH> g;
@@ -78,8 +104,9 @@ template <typename T, int DH>
 __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
     const T* __restrict__ qr, const T* __restrict__ kr, const T* __restrict__ vr, const float* __restrict__ logl,
     const T* __restrict__ yv, const T* __restrict__ dy, const float* __restrict__ rsum, const float* __restrict__ st,
-    const float* __restrict__ hst, const int* __restrict__ nchunks, const Chunk* __restrict__ tab, int max_slots,
-    int H, int Kp, T* __restrict__ G, float* __restrict__ dA_loc, float* __restrict__ dA_tot) {
+    const float* __restrict__ hst, const T* __restrict__ hrows, const int* __restrict__ nchunks,
+    const Chunk* __restrict__ tab, int max_slots, int H, int Kp, T* __restrict__ G, float* __restrict__ dA_loc,
+    float* __restrict__ dA_tot) {
   constexpr int C = kLionChunk;
   constexpr int FB = DH / 16;
   constexpr int PAD = 16 / (int)sizeof(T);
@@ -165,7 +192,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
 
   // ---------------- phase 1: query rows i = r0 + 4 grp + r
   float dqo[FB][4];
-  StateRegs<DH> hreg[2];
+  ImageRegs<T, DH> hreg[2];
   {
     Frag8<T> aq[DH / 32], ag[DH / 32];
 #pragma unroll
@@ -210,8 +237,12 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
     for (int r = 0; r < 4; ++r) sgn[r] = row16_sum(sgn[r]);
     __syncthreads();  // Pt, Dt complete
     // the states of phase 2 load while this phase finishes
-    state_rows_load<DH>(hreg[0], hst + ((size_t)slot * H + h) * 2 * E, tid);
-    state_rows_load<DH>(hreg[1], hst + ((size_t)slot * H + h) * 2 * E + E, tid);
+    {
+      const T* img = hrows + ((size_t)slot * H + h) * 2 * (DH * DH);
+      const float* ext = hst + ((size_t)slot * H + h) * 2 * E + DH * DH;
+      image_rows_load<T, DH>(hreg[0], img, ext, tid);
+      image_rows_load<T, DH>(hreg[1], img + DH * DH, ext + E, tid);
+    }
 
     f32x4 dq[FB];
     float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
@@ -258,8 +289,8 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   __syncthreads();  // every wave is done with SF / SB
 
   // ---------------- phase 2: key rows j = r0 + 4 grp + r
-  state_rows_store<T, DH>(hreg[0], SFs, LDR, xF, tid);
-  state_rows_store<T, DH>(hreg[1], SBs, LDR, xB, tid);
+  image_rows_store<T, DH>(hreg[0], SFs, LDR, xF, tid);
+  image_rows_store<T, DH>(hreg[1], SBs, LDR, xB, tid);
   if (tid < C) dAk[tid] = (colpart[0][tid] + colpart[1][tid]) + (colpart[2][tid] + colpart[3][tid]);
   __syncthreads();
   float dko[FB][4];
@@ -379,12 +410,13 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
 
 void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
                            const void* y, const void* dy, const float* rsum, const float* st, const float* hst,
-                           const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G,
-                           float* dA_loc, float* dA_tot, hipStream_t s) {
+                           const void* hrows, const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp,
+                           void* G, float* dA_loc, float* dA_tot, hipStream_t s) {
   const dim3 grid(xcd_grid(max_slots * H));
 #define LION_BT(TT, DD) hipLaunchKernelGGL((k_lion_bwd_token<TT, DD>), grid, dim3(256), 0, s, (const TT*)q,         \
                                            (const TT*)k, (const TT*)v, logl, (const TT*)y, (const TT*)dy, rsum, st, \
-                                           hst, nchunks, tab, max_slots, H, Kp, (TT*)G, dA_loc, dA_tot)
+                                           hst, (const TT*)hrows, nchunks, tab, max_slots, H, Kp, (TT*)G,   \
+                                           dA_loc, dA_tot)
   if (dt == BF16) { if (dh == 64) LION_BT(bf16, 64); else LION_BT(bf16, 32); }
   else            { if (dh == 64) LION_BT(float, 64); else LION_BT(float, 32); }
 #undef LION_BT

@@ -180,11 +180,15 @@ void launch_lion_chunk_state(int dt, int dh, int mode, const void* rsrc, const v
 // together: each round issues the loads of kScanBatch chunks of the forward
 // walk and of the backward walk before either carry advances, and the walk
 // pays one memory latency per round.
+// With a row image (rows != null), the dh x dh part of each result (e < dh^2)
+// is written rounded to TO into rows [slot][H][2][dh^2] instead, for a consumer
+// that stages the state in TO anyway; the extra row stays in place in fp32.
 constexpr int kScanBatch = 16;
 
+template <typename TO>
 __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const float* __restrict__ lam,
                                                    const int* __restrict__ nchunks, const int* __restrict__ chunk_off,
-                                                   int N, int H, int E) {
+                                                   int N, int H, int E, TO* __restrict__ rows, int DD) {
   constexpr int B = kScanBatch;
   const int eblocks = (E + 255) / 256;
   const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
@@ -194,6 +198,9 @@ __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
   const size_t cs = (size_t)H * 2 * E;  // stride between consecutive chunks
   float* base = st + (size_t)h * 2 * E + e;
+  const bool img = rows != nullptr && e < DD;
+  const size_t rcs = (size_t)H * 2 * DD;  // chunk stride of the row image
+  TO* rbase = img ? rows + (size_t)h * 2 * DD + e : nullptr;
   float sf = 0.f, sb = 0.f;
   for (int k = 0; c0 + k < c1; k += B) {
     const int cf = c0 + k, cb = c1 - 1 - k;  // first chunk of the round: forward walk, backward walk
@@ -210,11 +217,13 @@ __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const
     for (int j = 0; j < B; ++j) {
       const int c = cf + j, d = cb - j;
       if (c < c1) {
-        base[(size_t)c * cs] = sf;
+        if (img) rbase[(size_t)c * rcs] = from_f<TO>(sf);
+        else base[(size_t)c * cs] = sf;
         sf = __expf(gu[j]) * sf + u[j];
       }
       if (d >= c0) {
-        base[(size_t)d * cs + E] = sb;
+        if (img) rbase[(size_t)d * rcs + DD] = from_f<TO>(sb);
+        else base[(size_t)d * cs + E] = sb;
         sb = __expf(gw[j]) * sb + w[j];
       }
     }
@@ -222,9 +231,14 @@ __global__ __launch_bounds__(256) void k_lion_scan(float* __restrict__ st, const
 }
 
 void launch_lion_scan(float* st, const float* lam, const int* nchunks, const int* chunk_off, int N, int H, int E,
-                      hipStream_t s) {
-  hipLaunchKernelGGL(k_lion_scan, dim3(((E + 255) / 256) * N * H), dim3(256), 0, s, st, lam, nchunks, chunk_off, N,
-                     H, E);
+                      int dt, void* rows, int dh, hipStream_t s) {
+  const dim3 grid(((E + 255) / 256) * N * H);
+  if (dt == BF16 && rows)
+    hipLaunchKernelGGL(k_lion_scan<bf16>, grid, dim3(256), 0, s, st, lam, nchunks, chunk_off, N, H, E, (bf16*)rows,
+                       dh * dh);
+  else
+    hipLaunchKernelGGL(k_lion_scan<float>, grid, dim3(256), 0, s, st, lam, nchunks, chunk_off, N, H, E,
+                       (float*)rows, dh * dh);
 }
 
 // ---------------------------------------------------------------- readout

@@ -60,15 +60,17 @@ __device__ __forceinline__ void chunk_decay_scan(float a, float* As, float* Ls, 
 void launch_lion_chunk_state(int dt, int dh, int mode, const void* rsrc, const void* vsrc, const void* ysrc,
                              const float* rsum, const float* logl, const int* nchunks, const Chunk* tab,
                              int max_slots, int H, float* out, float* lam_out, hipStream_t s);
+// rows: null (every element in place, fp32) or the row image of the scan (the
+// dh x dh part rounded to the data type dt, [slot][H][2][dh^2])
 void launch_lion_scan(float* st, const float* lam, const int* nchunks, const int* chunk_off, int N, int H, int E,
-                      hipStream_t s);
+                      int dt, void* rows, int dh, hipStream_t s);
 void launch_lion_readout(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
                          const float* st, const int* nchunks, const Chunk* tab, int max_slots, int H, void* y,
                          float* rsum, hipStream_t s);
 void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const void* v, const float* logl,
                            const void* y, const void* dy, const float* rsum, const float* st, const float* hst,
-                           const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, void* G,
-                           float* dA_loc, float* dA_tot, hipStream_t s);
+                           const void* hrows, const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp,
+                           void* G, float* dA_loc, float* dA_tot, hipStream_t s);
 // da into G (and its zero padding) and per-chunk partial sums of da [slot][H]
 // (sum them over the first *nchunks slots); dA_tot is overwritten
 void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
