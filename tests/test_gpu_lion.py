@@ -126,6 +126,13 @@ def test_bf16_small_ragged():
     compare(make_inputs(w), label="bf16 ragged chunks")
 
 
+def test_bf16_head_dim_32():
+    """head_dim 32 in bf16: one state quad per lane in the staging of the carried
+    states, two 16-wide column tiles per output, several chunks and ragged tails."""
+    w = small_variant(LION, (200, 64, 1, 130), d_model=96, num_heads=3, head_dim=32, seed=61)
+    compare(make_inputs(w), label="bf16 LION-s dh=32")
+
+
 # ------------------------------------------------------------ full size: 16 x 4096, d 512, 8 heads
 
 @pytest.mark.timeout(400)  # the float64 oracle needs about a minute for one 4096-token sequence
