@@ -129,6 +129,7 @@ def test_f32_L256_d64_forward_exact_workload():
     ((300, 1, 513, 77), 96, 3, 64),          # several tiles, ragged tails, a single-token sequence
     ((129, 0, 255, 40, 2), 64, 2, 32),       # empty sequence, head_dim 32
     ((700,), 40, 1, 64),                     # d not a multiple of the k chunk
+    ((300, 77, 2), 576, 10, 32),             # d > 512 and H > 8: second channel and head groups
 ])
 def test_f32_forward_backward_multi_tile(lengths, d, H, dh):
     w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lengths, d_model=d, num_heads=H, head_dim=dh,
@@ -163,6 +164,14 @@ def test_bf16_d_model_not_a_multiple_of_32(d, H, dh):
     w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (300, 77, 2), d_model=d, num_heads=H, head_dim=dh,
                       seed=25)
     compare(make_inputs(w), backward=True, label=f"bf16 d={d} H={H} dh={dh}")
+
+
+def test_bf16_wide_model_many_heads():
+    """d > 512 and H > 8 in bf16: two channel groups in the conv kernels, two
+    head groups of gate logits, and 9 k-chunks in the projection GEMM."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (300, 77, 2), d_model=576, num_heads=10, head_dim=32,
+                      seed=28)
+    compare(make_inputs(w), backward=True, label="bf16 d=576 H=10")
 
 
 def test_bf16_small_ragged_recipe():

@@ -92,6 +92,7 @@ def compare(inp, backward=True, tol=None, label=""):
     ((300, 1, 130, 64, 65), 96, 3, 64),     # several chunks, ragged tails, one-token and exact-chunk sequences
     ((129, 0, 255, 40, 2), 64, 2, 32),      # empty sequence, head_dim 32
     ((512,), 40, 1, 64),                    # d not a multiple of the GEMM k chunk
+    ((200, 65), 576, 10, 32),               # d > 512, H > 8: second channel and head groups of the decay logits
 ])
 def test_f32_forward_backward_multi_chunk(lengths, d, H, dh):
     w = small_variant(LION, lengths, d_model=d, num_heads=H, head_dim=dh, dtype="f32", seed=51)
