@@ -97,9 +97,20 @@ def cpu_baseline(inp, sample_seqs, repeats=3):
     `repeats` times; the median run gives the rate."""
     import numpy as np
     from oracle import gbla as og
+    host_cores = len(os.sched_getaffinity(0))
+    # the oracle's BLAS threads: the host cores this process may run on, capped
+    # by OMP_NUM_THREADS where the environment sets it (the GPU host's CPU share)
+    want = host_cores
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        want = max(1, min(want, int(os.environ["OMP_NUM_THREADS"])))
+    limiter, blas = None, "unknown"
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=want, user_api="blas")
+        info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in info] or [1])
+        blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '?')} threads)"
+                         for i in info) or "unknown"
     except Exception:
         threads = 1
     cu = inp["cu_seqlens"]
@@ -114,8 +125,11 @@ def cpu_baseline(inp, sample_seqs, repeats=3):
         og.backward(*args, sub["dy"], inp["H"])
         runs.append(time.perf_counter() - t0)
     dt = sorted(runs)[len(runs) // 2]
+    if limiter is not None:
+        limiter.restore_original_limits()
     del np
-    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": T / dt, "unit": "tokens/s", "cores": int(threads), "host_cores": host_cores, "blas": blas,
+            "kind": "oracle",
             "sample": f"float64 numpy oracle forward+backward on the first {S} of {inp['N']} sequences "
                       f"({T} tokens) of the same batch, median of {repeats} runs "
                       f"({', '.join(f'{r:.1f}' for r in runs)} s)"}

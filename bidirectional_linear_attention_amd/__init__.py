@@ -85,10 +85,34 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _check_common(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma) -> None:
+    """Sizes and dtypes of the arguments the forward and backward share, against p."""
+    torch = _torch()
+    dt = _lib._torch_dtype(p.dtype)
+    T, d, H, D = p.total_tokens, p.d_model, p.num_heads, p.num_heads * p.head_dim
+    _lib.need(x, "x", T * d, dt, required=T > 0)
+    _lib.need(cu_seqlens, "cu_seqlens", p.num_seqs + 1, torch.int32)
+    _lib.need(conv_w, "conv_w", d * 4, dt)
+    for name, w in (("w_q", w_q), ("w_k", w_k), ("w_v", w_v)):
+        _lib.need(w, name, d * D, dt)
+    _lib.need(w_g, "w_g", H * d, dt)
+    _lib.need(b_g, "b_g", H, torch.float32)
+    _lib.need(w_r, "w_r", d * D, dt, required=False)
+    _lib.need(gamma, "gamma", p.head_dim, torch.float32, required=False)
+
+
 def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, workspace,
                  stream=None, w_r=None, gamma=None) -> None:
     """Enqueue the forward pass (include/gbla.h: gbla_forward); act may be None;
-    w_r (and optionally gamma) for the gated RMSNorm output."""
+    w_r (and optionally gamma) for the gated RMSNorm output. Every tensor is
+    checked against p (dtype, device, size) before anything is enqueued."""
+    torch = _torch()
+    _check_common(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma)
+    _lib.need(y, "y", p.total_tokens * p.num_heads * p.head_dim, _lib._torch_dtype(p.dtype),
+              required=p.total_tokens > 0)
+    _lib.need(saved, "saved", saved_size(p) // 4, torch.float32)
+    _lib.need_bytes(act, "act", activation_size(p), required=False)
+    _lib.need_bytes(workspace, "workspace", 0)
     st = _lib.load().gbla_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
                                   _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(w_r), _ptr(gamma), _ptr(y), _ptr(saved),
                                   _ptr(act), _ptr(workspace),
@@ -99,7 +123,25 @@ def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g,
 def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv_w,
                   dw_q, dw_k, dw_v, dw_g, db_g, workspace, stream=None, w_r=None, gamma=None, dw_r=None,
                   dgamma=None) -> None:
-    """Enqueue the backward pass (include/gbla.h: gbla_backward); act None recomputes."""
+    """Enqueue the backward pass (include/gbla.h: gbla_backward); act None
+    recomputes. Every tensor is checked against p (dtype, device, size) before
+    anything is enqueued."""
+    torch = _torch()
+    dt = _lib._torch_dtype(p.dtype)
+    T, d, H, D = p.total_tokens, p.d_model, p.num_heads, p.num_heads * p.head_dim
+    _check_common(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma)
+    _lib.need(saved, "saved", saved_size(p) // 4, torch.float32)
+    _lib.need_bytes(act, "act", activation_size(p), required=False)
+    _lib.need(dy, "dy", T * D, dt, required=T > 0)
+    _lib.need(dx, "dx", T * d, dt, required=T > 0)
+    _lib.need(dconv_w, "dconv_w", d * 4, torch.float32)
+    for name, t in (("dw_q", dw_q), ("dw_k", dw_k), ("dw_v", dw_v)):
+        _lib.need(t, name, d * D, torch.float32)
+    _lib.need(dw_g, "dw_g", H * d, torch.float32)
+    _lib.need(db_g, "db_g", H, torch.float32)
+    _lib.need(dw_r, "dw_r", d * D, torch.float32, required=False)
+    _lib.need(dgamma, "dgamma", p.head_dim, torch.float32, required=False)
+    _lib.need_bytes(workspace, "workspace", 0)
     st = _lib.load().gbla_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q), _ptr(w_k),
                                    _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(w_r), _ptr(gamma), _ptr(saved), _ptr(act),
                                    _ptr(dy), _ptr(dx), _ptr(dconv_w), _ptr(dw_q), _ptr(dw_k), _ptr(dw_v),
@@ -161,8 +203,11 @@ def backward(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, num
     dgamma) with the gated RMSNorm output."""
     torch = _torch()
     p = _check_inputs(x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, num_heads, gate, w_r, gamma, norm_eps)
-    if saved.numel() * 4 != saved_size(p):
-        raise ValueError("saved does not match the problem (gate?)")
+    if saved.dtype != torch.float32 or saved.numel() * 4 != saved_size(p):
+        raise ValueError("saved does not match the problem (float32; gate?)")
+    if tuple(dy.shape) != (p.total_tokens, p.num_heads * p.head_dim) or dy.dtype != x.dtype:
+        raise ValueError(f"dy: expected {(p.total_tokens, p.num_heads * p.head_dim)} {x.dtype}, "
+                         f"got {tuple(dy.shape)} {dy.dtype}")
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty_like(x), dconv_w=torch.empty(conv_w.shape, **f32), dw_q=torch.empty(w_q.shape, **f32),

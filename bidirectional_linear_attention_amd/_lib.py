@@ -88,3 +88,37 @@ def load():
 def check(status: int, where: str):
     if status != 0:
         raise GblaError(status, where)
+
+
+def _torch_dtype(code: int):
+    import torch
+    return torch.bfloat16 if code == DTYPE_BF16 else torch.float32
+
+
+def need(t, name: str, nelem: int, dtype, required: bool = True) -> None:
+    """Host-side guard before a launch: tensor t (None allowed unless required)
+    must have the given torch dtype, live on the GPU, be contiguous and hold at
+    least nelem elements, so that no kernel reads or writes past its end."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous GPU tensor")
+    if t.numel() < nelem:
+        raise ValueError(f"{name}: needs at least {nelem} elements, got {t.numel()}")
+
+
+def need_bytes(t, name: str, nbytes: int, required: bool = True) -> None:
+    """As need(), for byte buffers (activation cache, workspace) of any dtype."""
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required")
+        return
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: must be a contiguous GPU tensor")
+    if t.numel() * t.element_size() < nbytes:
+        raise ValueError(f"{name}: needs at least {nbytes} bytes, got {t.numel() * t.element_size()}")
+

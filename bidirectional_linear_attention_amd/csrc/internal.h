@@ -20,7 +20,8 @@ enum StageId {
   kNumStages
 };
 
-// brackets the launches of one stage with events while a profiling window is open
+// brackets the launches of one stage with events while a profiling window is
+// open; without one it costs a single atomic load
 class StageScope {
  public:
   StageScope(int stage_id, hipStream_t s);
@@ -30,6 +31,7 @@ class StageScope {
 
  private:
   int rec_;
+  uint64_t gen_;
   hipStream_t s_;
 };
 

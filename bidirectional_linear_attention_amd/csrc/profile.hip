@@ -5,7 +5,10 @@
 // before and one after its kernel(s) on the caller's stream, so the elapsed time between the
 // two is that stage's device time on that stream. gbla_profile_end waits for
 // the recorded events and returns per-stage totals. The window is process-wide
-// state meant for benchmarking; it is not meant for concurrent callers.
+// state meant for benchmarking. An entry point called while no window is open
+// reads one atomic flag and takes no lock, so unprofiled calls share no state;
+// a stage whose window was closed or reopened while it ran records nothing.
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -25,6 +28,8 @@ const char* kStageNames[kNumStages] = {
 
 struct Profiler {
   std::mutex mu;
+  std::atomic<bool> open{false};  // mirrors `active`, read without the lock
+  uint64_t generation = 0;        // incremented by every begin and end
   bool active = false;
   uint64_t mask = ~0ull;  // stages that record events
   int capacity = 0;
@@ -38,11 +43,13 @@ Profiler& prof() {
 }
 }  // namespace
 
-StageScope::StageScope(int stage_id, hipStream_t s) : rec_(-1), s_(s) {
+StageScope::StageScope(int stage_id, hipStream_t s) : rec_(-1), gen_(0), s_(s) {
   Profiler& p = prof();
+  if (!p.open.load(std::memory_order_acquire)) return;  // no window: no lock, no shared state
   std::lock_guard<std::mutex> g(p.mu);
   if (!p.active || p.used >= p.capacity || !((p.mask >> stage_id) & 1ull)) return;
   rec_ = p.used++;
+  gen_ = p.generation;
   p.stage[rec_] = stage_id;
   (void)hipEventRecord(p.ev[2 * rec_], s_);
 }
@@ -51,6 +58,9 @@ StageScope::~StageScope() {
   if (rec_ < 0) return;
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
+  // the window this record belongs to may have been closed (events destroyed)
+  // or replaced by a new one since the constructor ran
+  if (!p.active || p.generation != gen_ || 2 * (size_t)rec_ + 1 >= p.ev.size()) return;
   (void)hipEventRecord(p.ev[2 * rec_ + 1], s_);
 }
 
@@ -66,6 +76,7 @@ GBLA_API gbla_status gbla_profile_begin_stages(int max_records, uint64_t stage_m
   if (max_records < 1 || max_records > (1 << 20)) return GBLA_ERR_BAD_SHAPE;
   Profiler& p = prof();
   std::lock_guard<std::mutex> g(p.mu);
+  ++p.generation;
   p.mask = stage_mask;
   for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
   p.ev.assign(2 * (size_t)max_records, nullptr);
@@ -73,11 +84,13 @@ GBLA_API gbla_status gbla_profile_begin_stages(int max_records, uint64_t stage_m
   for (auto& e : p.ev)
     if (hipEventCreate(&e) != hipSuccess) {
       p.active = false;
+      p.open.store(false, std::memory_order_release);
       return GBLA_ERR_HIP;
     }
   p.capacity = max_records;
   p.used = 0;
   p.active = true;
+  p.open.store(true, std::memory_order_release);
   return GBLA_OK;
 }
 
@@ -108,7 +121,9 @@ GBLA_API gbla_status gbla_profile_end(double* ms_per_stage, int* launches_per_st
   for (hipEvent_t e : p.ev) (void)hipEventDestroy(e);
   p.ev.clear();
   p.stage.clear();
+  ++p.generation;
   p.active = false;
+  p.open.store(false, std::memory_order_release);
   p.capacity = p.used = 0;
   *n_stages = kNumStages;
   return st;

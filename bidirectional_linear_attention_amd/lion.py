@@ -79,8 +79,28 @@ def _nbytes(t):
     return ctypes.c_size_t(t.numel() * t.element_size())
 
 
+def _check_common(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam) -> None:
+    """Sizes and dtypes of the arguments the forward and backward share, against p."""
+    torch = _torch()
+    dt = _lib._torch_dtype(p.dtype)
+    T, d, H, D = p.total_tokens, p.d_model, p.num_heads, p.num_heads * p.head_dim
+    _lib.need(x, "x", T * d, dt, required=T > 0)
+    _lib.need(cu_seqlens, "cu_seqlens", p.num_seqs + 1, torch.int32)
+    for name, w in (("w_q", w_q), ("w_k", w_k), ("w_v", w_v)):
+        _lib.need(w, name, d * D, dt)
+    _lib.need(w_lam, "w_lam", H * d, dt, required=False)
+    _lib.need(b_lam, "b_lam", H, torch.float32, required=False)
+
+
 def lion_forward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, y, act, workspace, stream=None) -> None:
-    """Enqueue the forward pass (include/lion.h: lion_forward); act may be None."""
+    """Enqueue the forward pass (include/lion.h: lion_forward); act may be None.
+    Every tensor is checked against p (dtype, device, size) before anything is
+    enqueued."""
+    _check_common(p, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam)
+    _lib.need(y, "y", p.total_tokens * p.num_heads * p.head_dim, _lib._torch_dtype(p.dtype),
+              required=p.total_tokens > 0)
+    _lib.need_bytes(act, "act", activation_size(p), required=False)
+    _lib.need_bytes(workspace, "workspace", 0)
     st = _lib.load().lion_forward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(w_q), _ptr(w_k), _ptr(w_v),
                                   _ptr(w_lam), _ptr(b_lam), _ptr(y), _ptr(act), _ptr(workspace), _nbytes(workspace),
                                   _stream(stream))
@@ -89,7 +109,21 @@ def lion_forward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, y, 
 
 def lion_backward(p: LionProblem, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, dx, dw_q, dw_k, dw_v,
                   dw_lam, db_lam, workspace, stream=None) -> None:
-    """Enqueue the backward pass (include/lion.h: lion_backward)."""
+    """Enqueue the backward pass (include/lion.h: lion_backward). Every tensor
+    is checked against p (dtype, device, size) before anything is enqueued."""
+    torch = _torch()
+    dt = _lib._torch_dtype(p.dtype)
+    T, d, H, D = p.total_tokens, p.d_model, p.num_heads, p.num_heads * p.head_dim
+    _check_common(p, x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam)
+    _lib.need_bytes(act, "act", activation_size(p))
+    _lib.need(y, "y", T * D, dt, required=T > 0)
+    _lib.need(dy, "dy", T * D, dt, required=T > 0)
+    _lib.need(dx, "dx", T * d, dt, required=T > 0)
+    for name, t in (("dw_q", dw_q), ("dw_k", dw_k), ("dw_v", dw_v)):
+        _lib.need(t, name, d * D, torch.float32)
+    _lib.need(dw_lam, "dw_lam", H * d, torch.float32, required=False)
+    _lib.need(db_lam, "db_lam", H, torch.float32, required=False)
+    _lib.need_bytes(workspace, "workspace", 0)
     st = _lib.load().lion_backward(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(w_q), _ptr(w_k), _ptr(w_v),
                                    _ptr(w_lam), _ptr(b_lam), _ptr(act), _ptr(y), _ptr(dy), _ptr(dx), _ptr(dw_q),
                                    _ptr(dw_k), _ptr(dw_v), _ptr(dw_lam), _ptr(db_lam), _ptr(workspace),
@@ -139,6 +173,10 @@ def backward(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, act, y, dy, num_heads: 
     them, dw_lam ("s") and db_lam ("s", "d")."""
     torch = _torch()
     p = _check_inputs(x, cu_seqlens, w_q, w_k, w_v, w_lam, b_lam, num_heads, decay)
+    TD = (p.total_tokens, p.num_heads * p.head_dim)
+    for name, t in (("y", y), ("dy", dy)):
+        if tuple(t.shape) != TD or t.dtype != x.dtype:
+            raise ValueError(f"{name}: expected {TD} {x.dtype}, got {tuple(t.shape)} {t.dtype}")
     dev = x.device
     f32 = dict(dtype=torch.float32, device=dev)
     g = dict(dx=torch.empty_like(x), dw_q=torch.empty(w_q.shape, **f32), dw_k=torch.empty(w_k.shape, **f32),

@@ -169,7 +169,10 @@ GBLA_API gbla_status gbla_backward(const gbla_problem* p, const void* x, const i
  * gbla_profile_end waits for those events, writes per-stage total device
  * milliseconds and launch counts for min(max_stages, *n_stages) stages
  * (names: gbla_profile_stage_name), and closes the window. Launches beyond
- * max_records are not timed. Not meant for concurrent callers.
+ * max_records are not timed. While no window is open the entry points touch
+ * no shared state (one atomic flag read per stage, no lock), so calls on
+ * separate workspaces and streams may run concurrently; opening and closing a
+ * window is not meant to race with itself.
  * Errors: GBLA_ERR_BAD_SHAPE (max_records out of [1, 2^20], or end without
  * begin), GBLA_ERR_NULL_ARG, GBLA_ERR_HIP (event creation/query failed). */
 GBLA_API gbla_status gbla_profile_begin(int max_records);

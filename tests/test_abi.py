@@ -299,3 +299,67 @@ def test_lion_fixed_and_no_decay_argument_rules(decay, null_ok, null_bad):
         bad = list(a)
         bad[i] = None
         assert lib.lion_forward(ctypes.byref(p), *bad, _fake(0x900000), need, None) == 1
+
+
+class _FakeDev:
+    """Stands in for a device tensor in the binding's host-side checks (no GPU here)."""
+
+    def __init__(self, n, dtype, cuda=True, contiguous=True, esz=None):
+        import torch
+        self._n, self.dtype, self.is_cuda, self._c = n, dtype, cuda, contiguous
+        self._esz = esz if esz is not None else torch.empty(0, dtype=dtype).element_size()
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._esz
+
+    def is_contiguous(self):
+        return self._c
+
+
+def test_binding_checks_dtype_device_and_size_before_launch():
+    """The Python binding refuses, before any launch, a tensor of the wrong dtype,
+    off the GPU, non-contiguous or smaller than the problem needs (a kernel would
+    otherwise read or write past its end)."""
+    import torch
+    _lib.need(_FakeDev(10, torch.bfloat16), "dy", 10, torch.bfloat16)
+    _lib.need(None, "w_r", 10, torch.bfloat16, required=False)
+    bad = [(_FakeDev(9, torch.bfloat16), torch.bfloat16), (_FakeDev(10, torch.float32), torch.bfloat16),
+           (_FakeDev(10, torch.bfloat16, cuda=False), torch.bfloat16),
+           (_FakeDev(10, torch.bfloat16, contiguous=False), torch.bfloat16), (None, torch.bfloat16)]
+    for t, dt in bad:
+        with pytest.raises(ValueError):
+            _lib.need(t, "dy", 10, dt)
+    _lib.need_bytes(_FakeDev(100, torch.uint8), "act", 100)
+    with pytest.raises(ValueError):
+        _lib.need_bytes(_FakeDev(99, torch.uint8), "act", 100)
+    with pytest.raises(ValueError):
+        _lib.need_bytes(None, "act", 1)
+    assert _lib._torch_dtype(_lib.DTYPE_BF16) == torch.bfloat16 and _lib._torch_dtype(_lib.DTYPE_F32) == torch.float32
+
+
+def test_gbla_binding_rejects_mismatched_gradient_buffers():
+    """gbla_backward's binding checks dy, saved and the activation cache against
+    the problem: a bf16/float32 mix-up, a narrower dy or a short cache raises
+    ValueError before the library is called."""
+    import torch
+    import bidirectional_linear_attention_amd as gb
+    p = gb.problem(2, 64, 32, 2, 32, torch.bfloat16)
+    T, d, D = 64, 32, 64
+    bf, f32 = torch.bfloat16, torch.float32
+    ok = dict(x=_FakeDev(T * d, bf), cu_seqlens=_FakeDev(3, torch.int32), conv_w=_FakeDev(d * 4, bf),
+              w_q=_FakeDev(d * D, bf), w_k=_FakeDev(d * D, bf), w_v=_FakeDev(d * D, bf), w_g=_FakeDev(2 * d, bf),
+              b_g=_FakeDev(2, f32), saved=_FakeDev(gb.saved_size(p) // 4, f32),
+              act=_FakeDev(gb.activation_size(p), torch.uint8), dy=_FakeDev(T * D, bf), dx=_FakeDev(T * d, bf),
+              dconv_w=_FakeDev(d * 4, f32), dw_q=_FakeDev(d * D, f32), dw_k=_FakeDev(d * D, f32),
+              dw_v=_FakeDev(d * D, f32), dw_g=_FakeDev(2 * d, f32), db_g=_FakeDev(2, f32))
+    for key, t in (("dy", _FakeDev(T * D, f32)), ("dy", _FakeDev(T * D - 1, bf)), ("saved", _FakeDev(10**6, bf)),
+                   ("act", _FakeDev(gb.activation_size(p) - 1, torch.uint8)), ("dx", _FakeDev(T * d, f32))):
+        kw = dict(ok)
+        kw[key] = t
+        with pytest.raises(ValueError, match=key):
+            gb.gbla_backward(p, kw["x"], kw["cu_seqlens"], kw["conv_w"], kw["w_q"], kw["w_k"], kw["w_v"],
+                             kw["w_g"], kw["b_g"], kw["saved"], kw["act"], kw["dy"], kw["dx"], kw["dconv_w"],
+                             kw["dw_q"], kw["dw_k"], kw["dw_v"], kw["dw_g"], kw["db_g"], workspace=None)
