@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import DTYPE_BF16, DTYPE_F32, GATES, OUTPUT_GATED_RMSNORM, OUTPUT_PLAIN, GblaError, GblaProblem
 
 __all__ = ["GblaProblem", "GblaError", "problem", "saved_size", "workspace_size", "activation_size", "gbla_forward",
-           "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "stage_names", "DTYPE_F32", "DTYPE_BF16"]
+           "gbla_forward_noalloc", "gbla_backward", "forward", "backward", "profile_begin", "profile_end", "stage_names", "DTYPE_F32", "DTYPE_BF16"]
 
 
 def _torch():
@@ -118,6 +118,24 @@ def gbla_forward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g,
                                   _ptr(act), _ptr(workspace),
                                   ctypes.c_size_t(workspace.numel() * workspace.element_size()), _stream(stream))
     _lib.check(st, "gbla_forward")
+
+
+def gbla_forward_noalloc(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act,
+                         stream=None, w_r=None, gamma=None) -> None:
+    """Enqueue the allocation-free forward (include/gbla.h: gbla_forward_noalloc):
+    gbla_forward without a workspace argument, its scratch being the library's
+    static device array. Calls on one GPU share that array, so calls that
+    overlap in time on one GPU race. Same checks as gbla_forward."""
+    torch = _torch()
+    _check_common(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma)
+    _lib.need(y, "y", p.total_tokens * p.num_heads * p.head_dim, _lib._torch_dtype(p.dtype),
+              required=p.total_tokens > 0)
+    _lib.need(saved, "saved", saved_size(p) // 4, torch.float32)
+    _lib.need_bytes(act, "act", activation_size(p), required=False)
+    st = _lib.load().gbla_forward_noalloc(ctypes.byref(p), _ptr(x), _ptr(cu_seqlens), _ptr(conv_w), _ptr(w_q),
+                                          _ptr(w_k), _ptr(w_v), _ptr(w_g), _ptr(b_g), _ptr(w_r), _ptr(gamma),
+                                          _ptr(y), _ptr(saved), _ptr(act), _stream(stream))
+    _lib.check(st, "gbla_forward_noalloc")
 
 
 def gbla_backward(p: GblaProblem, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv_w,

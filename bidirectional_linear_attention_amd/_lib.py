@@ -11,8 +11,10 @@ LIB_PATH = os.environ.get("GBLA_LIBRARY") or os.path.join(_PKG, "libgbla.so")
 
 STATUS = {
     0: "GBLA_OK", 1: "GBLA_ERR_NULL_ARG", 2: "GBLA_ERR_BAD_SHAPE", 3: "GBLA_ERR_UNSUPPORTED",
-    4: "GBLA_ERR_MISALIGNED", 5: "GBLA_ERR_WORKSPACE_TOO_SMALL", 6: "GBLA_ERR_HIP",
+    4: "GBLA_ERR_MISALIGNED", 5: "GBLA_ERR_WORKSPACE_TOO_SMALL", 6: "GBLA_ERR_HIP", 7: "GBLA_ERR_SCRATCH_LIMIT",
 }
+# bytes of the static scratch array of gbla_forward_noalloc (GBLA_STATIC_SCRATCH_BYTES in include/gbla.h)
+STATIC_SCRATCH_BYTES = 128 << 20
 DTYPE_F32, DTYPE_BF16 = 0, 1
 LION_DECAY = {"s": 0, "d": 1, "lit": 2}  # selective, fixed per head, none
 GATE_SIGMOID = 0
@@ -50,6 +52,7 @@ _SIGNATURES = {
     "gbla_workspace_size": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_sz)]),
     "gbla_activation_size": (ctypes.c_int, [_P, ctypes.POINTER(_sz)]),
     "gbla_forward": (ctypes.c_int, [_P] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "gbla_forward_noalloc": (ctypes.c_int, [_P] + [_vp] * 13 + [_vp]),
     "gbla_backward": (ctypes.c_int, [_P] + [_vp] * 22 + [_vp, _sz, _vp]),
     "gbla_profile_begin": (ctypes.c_int, [ctypes.c_int]),
     "gbla_profile_begin_stages": (ctypes.c_int, [ctypes.c_int, ctypes.c_uint64]),

@@ -3,7 +3,9 @@
 #include "gbla.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "internal.h"
 
@@ -73,9 +75,12 @@ struct BwdWs {
   float* dgam_part; void* G; void* dxt; float* dw_part; float* dconv_part; Act act;
 };
 
-// The workspace always has room for the activations, so it suffices whether or
-// not the caller passes an activation cache.
-size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
+// The workspace of gbla_forward always has room for the activations, so it
+// suffices whether or not the caller passes an activation cache; the
+// allocation-free forward reserves that region only when no cache is passed
+// (act_region). The activations are the last region, so the two sizes differ
+// by exactly act_bytes(m).
+size_t plan_fwd(const Dims& m, char* base, FwdWs* w, bool act_region = true) {
   Carver c;
   FwdWs t;
   t.nchunks = c.take<int>(base, sizeof(int));
@@ -84,7 +89,7 @@ size_t plan_fwd(const Dims& m, char* base, FwdWs* w) {
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
   t.mpart = m.softmax ? c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H) : nullptr;
-  t.act = carve_act(m, c, base);
+  t.act = act_region ? carve_act(m, c, base) : Act{};
   if (w) *w = t;
   return c.off;
 }
@@ -134,6 +139,77 @@ gbla_status check_problem(const gbla_problem* p) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
+// argument checks of the forward entry points (everything but the workspace)
+gbla_status check_forward_args(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                               const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                               const void* w_r, const float* gamma, const void* y, const float* saved,
+                               const void* act) {
+  gbla_status st = check_problem(p);
+  if (st != GBLA_OK) return st;
+  if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved) return GBLA_ERR_NULL_ARG;
+  if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
+  const bool gated = p->output_gate == GBLA_OUTPUT_GATED_RMSNORM;
+  if (gated != (w_r != nullptr) || (!gated && gamma)) return GBLA_ERR_NULL_ARG;
+  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, w_r, y, (const void*)saved, act})
+    if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
+  if (!aligned(b_g, 4) || !aligned(gamma, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
+  return GBLA_OK;
+}
+
+// the forward's launch sequence on a carved workspace w (w.act: the activations)
+gbla_status enqueue_forward(const gbla_problem* p, const Dims& m, const void* x, const int32_t* cu_seqlens,
+                            const void* conv_w, const void* w_q, const void* w_k, const void* w_v, const void* w_g,
+                            const float* b_g, const void* w_r, const float* gamma, void* y, float* saved,
+                            const FwdWs& w, hipStream_t s) {
+  const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
+  const Act& A = w.act;
+  (void)hipGetLastError();
+  { StageScope ps(ST_PACK_PROJ, s);  // and the chunk table
+    launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp,
+                     Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
+  { StageScope ps(ST_CONV_FWD, s);
+    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
+  { StageScope ps(ST_PROJ_FWD, s);
+    launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
+  { StageScope ps(ST_STATE_PARTIAL, s);
+    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, w.mpart, s); }
+  { StageScope ps(ST_COMBINE_STATE, s);  // softmax gate: the logit maxima follow the N*H states
+    launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
+                   m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr); }
+  { StageScope ps(ST_READOUT, s);
+    launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s, A.ra, gamma, m.eps); }
+  return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
+}
+
+// ---------------------------------------------------------------- static scratch
+// The allocation-free forward carves its workspace from this array. Every GPU
+// the library runs on holds its own copy, at its own address, until the process
+// ends. The array's name is a host-side stand-in in host code: its device
+// address is obtained once per device with hipGetSymbolAddress (with that
+// device current) and only that address is ever handed to kernels.
+__device__ __align__(256) char scratch[GBLA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<char*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// device address of the current device's scratch array (null on failure)
+char* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  char* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    ptr = static_cast<char*>(addr);
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,11 +223,13 @@ const char* gbla_status_string(int status) {
     case GBLA_ERR_MISALIGNED: return "GBLA_ERR_MISALIGNED: pointer alignment violated";
     case GBLA_ERR_WORKSPACE_TOO_SMALL: return "GBLA_ERR_WORKSPACE_TOO_SMALL: workspace below the size query";
     case GBLA_ERR_HIP: return "GBLA_ERR_HIP: a HIP launch failed";
+    case GBLA_ERR_SCRATCH_LIMIT:
+      return "GBLA_ERR_SCRATCH_LIMIT: the problem needs more than the allocation-free entry point's static scratch";
     default: return "unknown gbla_status";
   }
 }
 
-int gbla_version(void) { return 4; }
+int gbla_version(void) { return 5; }
 
 gbla_status gbla_saved_size(const gbla_problem* p, size_t* bytes) {
   if (!bytes) return GBLA_ERR_NULL_ARG;
@@ -183,16 +261,10 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
                          const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
                          const void* w_r, const float* gamma, void* y, float* saved, void* act, void* workspace,
                          size_t workspace_bytes, void* stream) {
-  gbla_status st = check_problem(p);
+  gbla_status st = check_forward_args(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, y, saved, act);
   if (st != GBLA_OK) return st;
-  if (!cu_seqlens || !conv_w || !w_q || !w_k || !w_v || !w_g || !b_g || !saved || !workspace) return GBLA_ERR_NULL_ARG;
-  if (p->total_tokens > 0 && (!x || !y)) return GBLA_ERR_NULL_ARG;
-  const bool gated = p->output_gate == GBLA_OUTPUT_GATED_RMSNORM;
-  if (gated != (w_r != nullptr) || (!gated && gamma)) return GBLA_ERR_NULL_ARG;
-  for (const void* a : {x, conv_w, w_q, w_k, w_v, w_g, w_r, (const void*)y, (const void*)saved, (const void*)act,
-                        (const void*)workspace})
-    if (!aligned(a, 16)) return GBLA_ERR_MISALIGNED;
-  if (!aligned(b_g, 4) || !aligned(gamma, 4) || !aligned(cu_seqlens, 4)) return GBLA_ERR_MISALIGNED;
+  if (!workspace) return GBLA_ERR_NULL_ARG;
+  if (!aligned(workspace, 16)) return GBLA_ERR_MISALIGNED;
   const Dims m = dims_of(p);
   FwdWs w;
   if (workspace_bytes < plan_fwd(m, static_cast<char*>(workspace), &w)) return GBLA_ERR_WORKSPACE_TOO_SMALL;
@@ -200,26 +272,29 @@ gbla_status gbla_forward(const gbla_problem* p, const void* x, const int32_t* cu
     Carver c;
     w.act = carve_act(m, c, static_cast<char*>(act));
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
-  const Act& A = w.act;
+  return enqueue_forward(p, m, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, y, saved, w,
+                         static_cast<hipStream_t>(stream));
+}
 
-  (void)hipGetLastError();
-  { StageScope ps(ST_PACK_PROJ, s);  // and the chunk table
-    launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp,
-                     Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
-  { StageScope ps(ST_CONV_FWD, s);
-    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
-  { StageScope ps(ST_PROJ_FWD, s);
-    launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
-  { StageScope ps(ST_STATE_PARTIAL, s);
-    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, w.mpart, s); }
-  { StageScope ps(ST_COMBINE_STATE, s);  // softmax gate: the logit maxima follow the N*H states
-    launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
-                   m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr); }
-  { StageScope ps(ST_READOUT, s);
-    launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s, A.ra, gamma, m.eps); }
-  return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
+gbla_status gbla_forward_noalloc(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,
+                                 const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
+                                 const void* w_r, const float* gamma, void* y, float* saved, void* act,
+                                 void* stream) {
+  gbla_status st = check_forward_args(p, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, y, saved, act);
+  if (st != GBLA_OK) return st;
+  const Dims m = dims_of(p);
+  // without a cache the activations live in the scratch too
+  if (plan_fwd(m, nullptr, nullptr, act == nullptr) > (size_t)GBLA_STATIC_SCRATCH_BYTES) return GBLA_ERR_SCRATCH_LIMIT;
+  char* base = scratch_for_current_device();
+  if (!base) return GBLA_ERR_HIP;
+  FwdWs w;
+  plan_fwd(m, base, &w, act == nullptr);
+  if (act) {
+    Carver c;
+    w.act = carve_act(m, c, static_cast<char*>(act));
+  }
+  return enqueue_forward(p, m, x, cu_seqlens, conv_w, w_q, w_k, w_v, w_g, b_g, w_r, gamma, y, saved, w,
+                         static_cast<hipStream_t>(stream));
 }
 
 gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* cu_seqlens, const void* conv_w,

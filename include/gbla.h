@@ -69,7 +69,8 @@ typedef enum {
   GBLA_ERR_UNSUPPORTED = 3,         /* dtype, head_dim, gate or conv width not supported */
   GBLA_ERR_MISALIGNED = 4,          /* pointer alignment violated */
   GBLA_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes below the size query */
-  GBLA_ERR_HIP = 6                  /* a HIP launch failed */
+  GBLA_ERR_HIP = 6,                 /* a HIP launch failed */
+  GBLA_ERR_SCRATCH_LIMIT = 7        /* gbla_forward_noalloc: problem larger than its static scratch */
 } gbla_status;
 
 enum { GBLA_DTYPE_F32 = 0, GBLA_DTYPE_BF16 = 1 };
@@ -141,6 +142,28 @@ GBLA_API gbla_status gbla_forward(const gbla_problem* p, const void* x, const in
                                   const void* w_q, const void* w_k, const void* w_v, const void* w_g, const float* b_g,
                                   const void* w_r, const float* gamma, void* y, float* saved, void* act,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- Allocation-free forward -------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * forward pass and results as gbla_forward (same kernels, bitwise equal), with
+ * no workspace argument. Its workspace is a static device array of
+ * GBLA_STATIC_SCRATCH_BYTES built into the library; every GPU the library runs
+ * on holds its own copy until the process ends. The call allocates nothing and
+ * calls no allocating routine.
+ * It needs gbla_workspace_size(p, 0) bytes of that array without an activation
+ * cache, and gbla_workspace_size(p, 0) - gbla_activation_size(p) bytes with one
+ * (the activations then go to `act`); a larger problem returns
+ * GBLA_ERR_SCRATCH_LIMIT before anything is enqueued. All calls on one GPU
+ * share its array and keep no state in it between calls (nothing is read
+ * before it is written), so calls that overlap in time on one GPU (on
+ * different streams or from different threads) race and must be ordered by
+ * the caller. Arguments, layouts and other errors as gbla_forward. */
+#define GBLA_STATIC_SCRATCH_BYTES (128u << 20)
+GBLA_API gbla_status gbla_forward_noalloc(const gbla_problem* p, const void* x, const int32_t* cu_seqlens,
+                                          const void* conv_w, const void* w_q, const void* w_k, const void* w_v,
+                                          const void* w_g, const float* b_g, const void* w_r, const float* gamma,
+                                          void* y, float* saved, void* act, void* stream);
 
 /* Backward pass: gradients of sum(y * dy) for the forward above, obtained by
  * the chain rule through Eqs. (4)-(6). Inputs as in gbla_forward plus

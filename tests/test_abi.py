@@ -363,3 +363,18 @@ def test_gbla_binding_rejects_mismatched_gradient_buffers():
             gb.gbla_backward(p, kw["x"], kw["cu_seqlens"], kw["conv_w"], kw["w_q"], kw["w_k"], kw["w_v"],
                              kw["w_g"], kw["b_g"], kw["saved"], kw["act"], kw["dy"], kw["dx"], kw["dconv_w"],
                              kw["dw_q"], kw["dw_k"], kw["dw_v"], kw["dw_g"], kw["db_g"], workspace=None)
+
+
+def test_noalloc_forward_refuses_problems_beyond_its_scratch_without_launching():
+    """gbla_forward_noalloc checks its static scratch limit on the host, before
+    touching the device: without an activation cache the activations count too."""
+    lib = _lib.load()
+    p = _prob(total_tokens=300_000)
+    out = ctypes.c_size_t()
+    assert lib.gbla_workspace_size(ctypes.byref(p), 0, ctypes.byref(out)) == 0
+    assert out.value > _lib.STATIC_SCRATCH_BYTES
+    args = [_fake(0x10000 + 0x1000 * i) for i in range(13)]
+    args[8] = args[9] = None  # w_r, gamma (plain output)
+    args[12] = None  # act
+    assert lib.gbla_forward_noalloc(ctypes.byref(p), *args, None) == 7
+    assert lib.gbla_status_string(7).decode().startswith("GBLA_ERR_SCRATCH_LIMIT")
