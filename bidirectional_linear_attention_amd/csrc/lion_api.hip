@@ -215,8 +215,8 @@ gbla_status lion_backward(const lion_problem* p, const void* x, const int32_t* c
     launch_lion_bwd_token(dt, m.dh, A.q, A.k, A.v, A.logl, y, dy, A.rsum, A.st, w.hst, w.hrows, w.nchunks, w.tab,
                           m.slots, m.H, m.Kp, w.G, w.dA_loc, w.dA_tot, s); }
   { StageScope ps(ST_LION_DA, s);
-    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.chunk_off, w.tab, m.N, m.slots, m.H, m.D, m.Kp, dt, sel,
-                   w.G, w.db_part, s); }
+    launch_lion_da(A.logl, w.dA_loc, w.dA_tot, w.nchunks, w.tab, m.slots, m.H, m.D, m.Kp, dt, sel, w.G, w.db_part,
+                   s); }
   if (sel || fixed) {
     StageScope ps(ST_LION_DB_REDUCE, s);
     launch_sum_parts(w.db_part, m.H, 0, w.nchunks, db_lam, s);

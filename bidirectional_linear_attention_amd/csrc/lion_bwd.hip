@@ -14,11 +14,23 @@
 // and dv; the inter-chunk parts of dA are dot products of q~ and k~ with those
 // inter-chunk gradients (e.g. sum_{j before c} E_tj = q~_t . dq~_t(from SF)).
 //
+// dlog lambda_t splits at the end e_c of t's chunk c: the suffix of dA inside
+// the chunk, plus sum_{u > e_c} dA_u. In that second sum every pair of tokens
+// both after e_c enters twice with opposite signs, so it equals the sum of F_uj
+// = E_uj + E_ju over the pairs u > e_c >= j that straddle the chunk end:
+//   Z'_c = sum_{j in c} Y_j + Z_c,   Y_j = sum_{u after c} F_uj,
+//   Z_c  = sum_{u after c, j before c} F_uj = e^{L_c} (<SF_c, HB_c> + <HF_c, SB_c>)
+// (Frobenius products of the states entering chunk c, L_c its total log decay).
+// Taking it in that form instead of summing dA over all later chunks keeps the
+// rounding error of dlog lambda independent of the sequence length: summed over
+// later chunks, the rounding residues of pairs that cancel in exact arithmetic
+// would accumulate with the number of chunks.
+//
 // k_lion_bwd_token   per (chunk, head): dq, dk, dv (through the feature-map
-//                    vector-Jacobian product) into G, and chunk-local suffix
-//                    sums of dA
-// k_lion_da          per (sequence, head): adds the suffix of later chunks,
-//                    writes da into G and a partial sum for db_lam
+//                    vector-Jacobian product) into G, chunk-local suffix sums
+//                    of dA and the chunk's straddling sum Z'_c
+// k_lion_da          per chunk: da = (local suffix + Z'_c)(1 - lambda) into G,
+//                    and a partial sum for db_lam
 #include "internal.h"
 #include "lion_internal.h"
 
@@ -88,6 +100,20 @@ __device__ __forceinline__ void image_rows_store(const ImageRegs<T, DH>& g, T* R
   }
   if (tid < DH) extra[tid] = g.x;
 }
+// this thread's share of the Frobenius product of a fp32 state and a state
+// image (the same elements of both: the quads e4 = tid + 256 k and extra entry tid)
+template <typename T, int DH>
+__device__ __forceinline__ float state_image_dot(const StateRegs<DH>& s, const ImageRegs<T, DH>& g, int tid) {
+  static_assert(StateRegs<DH>::PER == ImageRegs<T, DH>::PER, "same element split");
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < StateRegs<DH>::PER; ++k) {
+    const float4 a = s.r[k];
+    acc += a.x * quad_get(g.r[k], 0) + a.y * quad_get(g.r[k], 1) + a.z * quad_get(g.r[k], 2) +
+           a.w * quad_get(g.r[k], 3);
+  }
+  return acc + (tid < DH ? s.x * g.x : 0.f);
+}
 template <typename T, int DH>
 __device__ __forceinline__ void stage_state_rows(T* R, int ld, float* extra, const float* __restrict__ S, int tid) {
   StateRegs<DH> g;
@@ -131,9 +157,9 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   float* const dqf = reinterpret_cast<float*>(PD);
   float* const dkf = DH == 64 ? reinterpret_cast<float*>(SFB) : reinterpret_cast<float*>(PD) + C * DH;
   __shared__ float xF[DH], xB[DH];          // extra columns of the staged states
-  __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C], dotq[C], dotk[C];
+  __shared__ float As[C], nq[C], nk[C], gden[C], vone[C], dAq[C], dAk[C], dotq[C], dotk[C], Yq[C], Yk[C];
   __shared__ float colpart[4][C];
-  __shared__ float Ls;
+  __shared__ float Ls, zpart[4];
 
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
@@ -147,8 +173,27 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   // ---------------- phase 0: staging
   const float la = chunk_decay_load<C>(logl, ch, H, h, tid);
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
-  stage_state_rows<T, DH>(SFs, LDR, xF, sp, tid);
-  stage_state_rows<T, DH>(SBs, LDR, xB, sp + E, tid);
+  const T* img = hrows + ((size_t)slot * H + h) * 2 * (DH * DH);
+  const float* ext = hst + ((size_t)slot * H + h) * 2 * E + DH * DH;
+  float zdot = 0.f;  // this thread's terms of <SF, HB> + <HF, SB> (fp32 S; H as the scan rounded it)
+  {
+    StateRegs<DH> sf;
+    ImageRegs<T, DH> hb;
+    state_rows_load<DH>(sf, sp, tid);
+    image_rows_load<T, DH>(hb, img + DH * DH, ext + E, tid);
+    zdot += state_image_dot<T, DH>(sf, hb, tid);
+    state_rows_store<T, DH>(sf, SFs, LDR, xF, tid);
+  }
+  {
+    StateRegs<DH> sb;
+    ImageRegs<T, DH> hf;
+    state_rows_load<DH>(sb, sp + E, tid);
+    image_rows_load<T, DH>(hf, img, ext, tid);
+    zdot += state_image_dot<T, DH>(sb, hf, tid);
+    state_rows_store<T, DH>(sb, SBs, LDR, xB, tid);
+  }
+  zdot = add_xor32(add_xor16(row16_sum(zdot)));
+  if (lane == 0) zpart[w] = zdot;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = tid + 256 * v;
@@ -237,15 +282,11 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
     for (int r = 0; r < 4; ++r) sgn[r] = row16_sum(sgn[r]);
     __syncthreads();  // Pt, Dt complete
     // the states of phase 2 load while this phase finishes
-    {
-      const T* img = hrows + ((size_t)slot * H + h) * 2 * (DH * DH);
-      const float* ext = hst + ((size_t)slot * H + h) * 2 * E + DH * DH;
-      image_rows_load<T, DH>(hreg[0], img, ext, tid);
-      image_rows_load<T, DH>(hreg[1], img + DH * DH, ext + E, tid);
-    }
+    image_rows_load<T, DH>(hreg[0], img, ext, tid);
+    image_rows_load<T, DH>(hreg[1], img + DH * DH, ext + E, tid);
 
     f32x4 dq[FB];
-    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
+    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f}, later[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
       f32x4 in = zero4(), fw = zero4(), bw = zero4();
@@ -266,12 +307,14 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
         dq[nt][r] = in[r] + f + b;
         const float p = to_f<T>(Qs[i * LDR + 16 * nt + col]);
         inter[r] += p * (f - b);
+        later[r] += p * b;
         dot[r] += p * dq[nt][r];
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       inter[r] = row16_sum(inter[r]);
+      later[r] = row16_sum(later[r]);
       dot[r] = row16_sum(dot[r]);
     }
 #pragma unroll
@@ -282,6 +325,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       for (int nt = 0; nt < FB; ++nt) dqo[nt][r] = dq[nt][r];  // the gradient of phi(q); its VJP runs at the output
       if (col == 0) {
         dAq[i] = ok ? sgn[r] + inter[r] : 0.f;
+        Yq[i] = ok ? later[r] : 0.f;
         dotq[i] = dot[r];
       }
     }
@@ -311,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       oj[r] = vone[r0 + 4 * grp + r];
     }
     f32x4 dk[FB];
-    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f};
+    float inter[4] = {0.f, 0.f, 0.f, 0.f}, dot[4] = {0.f, 0.f, 0.f, 0.f}, later[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int nt = 0; nt < FB; ++nt) {
       f32x4 ik = zero4(), iv = zero4(), fk = zero4(), bk = zero4(), fv = zero4(), bv = zero4();
@@ -338,12 +382,14 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
         dv[nt][r] = iv[r] + ef[r] * fv[r] + eb[r] * bv[r];
         const float p = to_f<T>(Ks[j * LDR + 16 * nt + col]);
         inter[r] += p * (f - b);
+        later[r] += p * b;
         dot[r] += p * dk[nt][r];
       }
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       inter[r] = row16_sum(inter[r]);
+      later[r] = row16_sum(later[r]);
       dot[r] = row16_sum(dot[r]);
     }
 #pragma unroll
@@ -354,6 +400,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       for (int nt = 0; nt < FB; ++nt) dko[nt][r] = dk[nt][r];  // the gradient of phi(k); its VJP runs at the output
       if (col == 0) {
         dAk[j] = ok ? dAk[j] + inter[r] : 0.f;
+        Yk[j] = ok ? later[r] : 0.f;
         dotk[j] = dot[r];
       }
     }
@@ -395,7 +442,7 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       frag_store(g + 2 * D, frag_load(Vs + r * LDR + c));
     }
   }
-  if (tid < C) {  // chunk-local suffix sums of dA
+  if (tid < C) {  // chunk-local suffix sums of dA, and the chunk's straddling sum Z'_c
     const bool ok = ch.start + tid < ch.end;
     float a = ok ? dAq[tid] + dAk[tid] : 0.f;
 #pragma unroll
@@ -404,7 +451,11 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
       if (tid + off < 64) a += o;
     }
     if (ok) dA_loc[(size_t)(ch.start + tid) * H + h] = a;
-    if (tid == 0) dA_tot[(size_t)slot * H + h] = a;
+    float y = Yq[tid] + Yk[tid];  // 0 past the chunk's end
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) y += __shfl_xor(y, off, 64);
+    if (tid == 0)
+      dA_tot[(size_t)slot * H + h] = y + __expf(L) * ((zpart[0] + zpart[1]) + (zpart[2] + zpart[3]));
   }
 }
 
@@ -423,38 +474,11 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
 }
 
 // ---------------------------------------------------------------- decay gradient
-// dlog lambda_t = dA_loc[t] (the suffix inside t's chunk) + the dA of all later
-// chunks of t's sequence; da_t = dlog lambda_t (1 - lambda_t) goes to G column
-// 3 D + h. Two launches:
-//   k_lion_dsuffix  one wave per (sequence, head): chunk totals -> exclusive
-//                   suffix sums over the sequence's chunks, in place
-//   k_lion_da       one block per chunk: da for every token and head (written to G
-//                   when the decay depends on x, else 0), the padding columns of G the dX~ GEMM reads (zeroed),
-//                   and the chunk's per-head sum of da (db partial)
-__global__ __launch_bounds__(256) void k_lion_dsuffix(float* __restrict__ dA_tot, const int* __restrict__ nchunks,
-                                                      const int* __restrict__ chunk_off, int N, int H) {
-  const int lane = threadIdx.x & 63;
-  const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= N * H) return;
-  const int b = bh / H, h = bh - b * H;
-  const int nc = *nchunks;
-  const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
-  float carry = 0.f;
-  for (int top = c1; top > c0; top -= 64) {  // lane l takes chunk top - 1 - l
-    const int c = top - 1 - lane;
-    const bool ok = c >= c0;
-    const float v = ok ? dA_tot[(size_t)c * H + h] : 0.f;
-    float inc = v;  // inclusive sum over lanes <= l = chunks c .. top - 1
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float o = __shfl_up(inc, off, 64);
-      if (lane >= off) inc += o;
-    }
-    if (ok) dA_tot[(size_t)c * H + h] = carry + inc - v;
-    carry += __shfl(inc, 63, 64);
-  }
-}
-
+// dlog lambda_t = dA_loc[t] (the suffix of dA inside t's chunk) + Z'_c (the
+// chunk's straddling sum, dA_tot[slot]); da_t = dlog lambda_t (1 - lambda_t)
+// goes to G column 3 D + h when the decay depends on x (else 0). One block per
+// chunk also zeroes the padding columns of G the dX~ GEMM reads and writes the
+// chunk's per-head sum of da (db partial).
 template <typename T>
 __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl, const float* __restrict__ dA_loc,
                                                  const float* __restrict__ dA_tot, const int* __restrict__ nchunks,
@@ -486,10 +510,9 @@ __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl,
   }
 }
 
-void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
-                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G,
-                    float* db_part, hipStream_t s) {
-  hipLaunchKernelGGL(k_lion_dsuffix, dim3((N * H + 3) / 4), dim3(256), 0, s, dA_tot, nchunks, chunk_off, N, H);
+void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks, const Chunk* tab,
+                    int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G, float* db_part,
+                    hipStream_t s) {
   if (dt == BF16)
     hipLaunchKernelGGL(k_lion_da<bf16>, dim3(max_slots), dim3(256), 0, s, logl, dA_loc, dA_tot, nchunks, tab, H, D,
                        Kp, (int)write_da, (bf16*)G, db_part);

@@ -72,9 +72,9 @@ void launch_lion_bwd_token(int dt, int dh, const void* q, const void* k, const v
                            const void* hrows, const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp,
                            void* G, float* dA_loc, float* dA_tot, hipStream_t s);
 // da into G (and its zero padding) and per-chunk partial sums of da [slot][H]
-// (sum them over the first *nchunks slots); dA_tot is overwritten
-void launch_lion_da(const float* logl, const float* dA_loc, float* dA_tot, const int* nchunks, const int* chunk_off,
-                    const Chunk* tab, int N, int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G,
-                    float* db_part, hipStream_t s);
+// (sum them over the first *nchunks slots); dA_tot holds each chunk's straddling sum
+void launch_lion_da(const float* logl, const float* dA_loc, const float* dA_tot, const int* nchunks, const Chunk* tab,
+                    int max_slots, int H, int D, int Kp, int dt, bool write_da, void* G, float* db_part,
+                    hipStream_t s);
 
 }  // namespace gbla

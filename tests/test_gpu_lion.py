@@ -83,7 +83,9 @@ def grad_errors(gpu, g, keys, db_sum=False):
         errs[k] = rel_err(gpu[k], g[k])
         if k == "db_lam":
             errs["db_lam_sum"] = sum_err(gpu[k], g[k], g["da"])
-    bounded = {k: v for k, v in errs.items() if k != ("db_lam" if db_sum else "db_lam_sum")}
+            # how strongly the sum cancels: sum_t |da_t| over |sum_t da_t| (largest head)
+            errs["db_lam_cancel"] = float(np.max(np.abs(g["da"]).sum(axis=0)) / max(np.max(np.abs(g[k])), 1e-30))
+    bounded = {k: v for k, v in errs.items() if k not in ("db_lam_cancel", "db_lam" if db_sum else "db_lam_sum")}
     return errs, bounded
 
 
@@ -265,7 +267,7 @@ def run_gpu_decay(inp, decay, b):
     return {k: v.float().cpu().numpy() for k, v in out.items()}
 
 
-def compare_decay(inp, decay, label):
+def compare_decay(inp, decay, label, db_sum=False):
     """Lion-d is the oracle's selective form with w_lam = 0 (the logit is b_lam
     for every token: M_ij = lambda^|i-j|); Lion-lit is lambda = 1 (b_lam = +inf,
     M = 1). Compared: y, dx, dW_Q, dW_K, dW_V and, for Lion-d, db_lam."""
@@ -276,7 +278,7 @@ def compare_decay(inp, decay, label):
     args = [inp["x"], inp["cu_seqlens"], inp["w_q"], inp["w_k"], inp["w_v"], np.zeros_like(inp["w_lam"]), ob]
     errs = {"y": rel_err(gpu["y"], ol.forward_full(*args, H))}
     g = ol.backward_full(*args, inp["dy"], H)
-    e, bounded = grad_errors(gpu, g, ("dx", "dw_q", "dw_k", "dw_v") + (("db_lam",) if decay == "d" else ()))
+    e, bounded = grad_errors(gpu, g, ("dx", "dw_q", "dw_k", "dw_v") + (("db_lam",) if decay == "d" else ()), db_sum)
     errs.update(e)
     bounded.update({"y": errs["y"]})
     print(f"\n[Lion-{decay} {dtype} {label}] T={inp['T']}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()),
@@ -297,6 +299,9 @@ def test_fixed_and_no_decay_match_the_oracle(decay, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("decay", ["d", "lit"])
 def test_fixed_and_no_decay_many_chunks(decay, dtype):
-    """Lion-d and Lion-lit over 18 and 71 chunks (every scan and suffix round)."""
+    """Lion-d and Lion-lit over 18 and 71 chunks (every scan and suffix round).
+    With one decay per head, db_lam = sum_t da_t over 5600 tokens cancels by a
+    factor of about 350 here (printed as db_lam_cancel), so its bound is on the
+    error relative to the summed terms; the plain error is printed beside it."""
     w = small_variant(LION, (1100, 4500, 7), d_model=128, num_heads=2, dtype=dtype, seed=71)
-    compare_decay(make_inputs(w), decay, "18/71-chunk sequences")
+    compare_decay(make_inputs(w), decay, "18/71-chunk sequences", db_sum=decay == "d")
