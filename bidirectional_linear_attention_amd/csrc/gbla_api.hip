@@ -40,7 +40,7 @@ Dims dims_of(const gbla_problem* p) {
   m.slots = max_chunks(m.T, m.N);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
   m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
-  m.conv_rb = conv_bwd_row_blocks(m.T);
+  m.conv_rb = dx_token_tiles(p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32, m.T);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
   m.softmax = p->gate == GBLA_GATE_SOFTMAX;
   return m;
@@ -72,7 +72,7 @@ struct FwdWs {
 };
 struct BwdWs {
   int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
-  float* dgam_part; void* G; void* dxt; float* dw_part; float* dconv_part; Act act;
+  float* dgam_part; void* G; void* edge; float* dw_part; float* dconv_part; Act act;
 };
 
 // The workspace of gbla_forward always has room for the activations, so it
@@ -107,7 +107,7 @@ size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   t.dbg_part = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H);
   t.dgam_part = m.gated ? c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.dh) : nullptr;
   t.G = c.take<char>(base, (size_t)m.T * m.Kp * m.esz);
-  t.dxt = c.take<char>(base, m.esz * (size_t)m.T * m.d);
+  t.edge = c.take<char>(base, m.esz * (size_t)std::max(1, m.conv_rb) * 6 * m.d);
   t.dw_part = c.take<float>(base, sizeof(float) * (size_t)m.nsplit * m.d * m.Kp);
   t.dconv_part = c.take<float>(base, sizeof(float) * (size_t)std::max(1, m.conv_rb) * m.d * 4);
   t.act = carve_act(m, c, base);
@@ -350,21 +350,23 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
     launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, m.gated ? 4 : 3, w.G,
                      w.dbg_part,
                      m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
-  if (m.T > 0) {
-    { StageScope ps(ST_GEMM_DX, s); launch_gemm_dx(dt, w.G, w.wt, m.T, m.d, m.Kp, grad_cols_read(m.H, m.dh, m.gated), w.dxt, s); }
-    { StageScope ps(ST_CONV_BWD, s);
-      launch_conv_bwd(dt, w.dxt, x, cu_seqlens, m.N, m.T, m.d, conv_w, dx, w.dconv_part, s); }
+  if (m.T > 0) {  // dX~ = G Wt^T with the conv's vector-Jacobian product in its epilogue
+    StageScope ps(ST_GEMM_DX, s);
+    launch_gemm_dx_conv(dt, w.G, w.wt, m.T, m.d, m.Kp, grad_cols_read(m.H, m.dh, m.gated), x, cu_seqlens, m.N,
+                        conv_w, dx, w.dconv_part, w.edge, s);
   }
   { StageScope ps(ST_GEMM_DW, s); launch_gemm_dw(dt, A.xt, w.G, m.T, m.d, m.Kp, m.nsplit, w.dw_part, s); }
   {
     StageScope ps(ST_FINALIZE, s);
-    BwdFinalize f;
+    BwdFinalize f{};
     f.dw_part = w.dw_part; f.nsplit = m.nsplit; f.d = m.d; f.H = m.H; f.dh = m.dh; f.Kp = m.Kp;
     f.dw_blocks = bwd_finalize_dw_blocks(m.d, m.Kp);
     f.dw_q = dw_q; f.dw_k = dw_k; f.dw_v = dw_v; f.dw_r = dw_r; f.dw_g = dw_g;
     f.dconv_part = w.dconv_part; f.conv_rb = m.conv_rb; f.dconv_w = dconv_w;
     f.nchunks = w.nchunks; f.dbg_part = w.dbg_part; f.db_g = db_g;
     f.dgam_part = gamma ? w.dgam_part : nullptr; f.dgamma = gamma ? dgamma : nullptr;
+    f.dt = dt; f.tile_rows = dx_token_tile_rows(dt); f.nseq = m.N;
+    f.edge = m.T > 0 ? w.edge : nullptr; f.conv_w = conv_w; f.cu = cu_seqlens; f.dx = dx;
     launch_bwd_finalize(f, s);
   }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;

@@ -15,9 +15,12 @@
 //   (without an activation cache, k_conv_fwd + k_proj recompute x~, g, phi(q), phi(k), v)
 //   k_bwd_dstate  per (chunk, head): y, dn, dden, dq -> G; partial [dS | dz]
 //   k_bwd_token   per (chunk, head): dk, dv, ds -> G; partial db_g
-//   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA), stored in the activation dtype
-//   k_gemm_dw     split-token partials of X~^T G (pipelined MFMA), then k_dw_reduce
-//   k_conv_bwd    dx and per-block partial dconv_w (summed by k_sum_parts)
+//   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA); for GBLA its epilogue applies the
+//                 conv's chain rule to the tile (dx, dconv_w partials), so dX~
+//                 never reaches HBM; for LION dX~ is dx
+//   k_gemm_dw     split-token partials of X~^T G (pipelined MFMA)
+//   k_bwd_finalize the split-K sum of dW, the dconv_w / db_g / dgamma partial
+//                 sums and dx of the three tokens at each token-tile seam
 #include "gemm.h"
 #include <algorithm>
 
@@ -511,10 +514,158 @@ template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 4, 2>; stati
 template <> struct DxCfg<float> { using S = GemmShape<float, 128, 64, 32, 2, 2>; static constexpr bool DL = false; };
 
 // Kp is the row pitch of G and Wt; the k loop reads Kr <= Kp columns.
-template <typename T>
+//
+// CONV = false (LION): the tile of dX~ = dx is stored as it is.
+// CONV = true (GBLA): the epilogue applies the vector-Jacobian product of the
+// causal conv (Eq. (4)) to the block's tile of dX~ (BN tokens x BM channels),
+// which never goes to HBM:
+//   dx_u[c]       = sum_k w[c][k] dX~_{u+3-k}[c]    (u+3-k inside u's sequence)
+//   dconv_w[c][k] = sum_t dX~_t[c] x_{t-3+k}[c]     (t-3+k inside t's sequence)
+// The tile goes to LDS (rounded to the activation dtype, as dX~ would be
+// stored), then each thread slides a 4-row window over RL consecutive tokens of
+// one 8-channel group. dx of the tile's last three tokens needs the next tile's
+// first three rows of dX~, so every tile also writes its first and last three
+// rows to `edge` and dx of those three tokens is formed by k_bwd_finalize (the
+// last tile of the batch has no successor: its rows past T are zero and it
+// writes all of its dx). dconv_w gets one partial per token tile, summed in a
+// fixed order by k_bwd_finalize.
+constexpr float kZero4[4] = {0.f, 0.f, 0.f, 0.f};
+
+struct DxConv {
+  const void* x;           // [T][d] conv input (dtype)
+  const int32_t* cu;       // [N+1] sequence offsets
+  int nseq;
+  const void* conv_w;      // [d][4] (dtype)
+  float* dconv_part;       // [token tiles][d][4]
+  void* edge;              // [token tiles][6][d] (dtype): dX~ rows 0..2, then BN-3..BN-1 of every tile
+};
+
+template <typename T, class S>
+__device__ __forceinline__ void dx_conv_epilogue(const f32x4 (&acc)[S::FM][S::FN], T* lo, T* hi, int m0, int n0,
+                                                 int mt, int T_, int d, T* __restrict__ dx, const DxConv& cv) {
+  constexpr int BT = S::BN, BC = S::BM, CH = BC / 8, NT = S::NTHREADS;
+  constexpr int NQ = BC / 4, RUNS = NT / NQ, RL = BT / RUNS;  // 4-channel quads; token runs of RL
+  static_assert(NT % NQ == 0 && BT % RUNS == 0 && RL >= 4 && RL % 4 == 0, "thread runs tile the token axis");
+  constexpr int HALF = (BT / 2) * BC * (int)sizeof(T) / 4;  // floats in one token half of the tile
+  static_assert(RUNS * NQ * 16 <= 2 * HALF, "room for the dconv_w partials where the tile was");
+  const T* __restrict__ x = static_cast<const T*>(cv.x);
+  // row r of the dX~ tile (token m0 + r): chunk q (8 channels) at row(r) + 8 * (q ^ (r % CH))
+  auto row = [&](int r) -> T* { return r < BT / 2 ? lo + r * BC : hi + (r - BT / 2) * BC; };
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
+  const int wm = w / S::WGN, wn = w % S::WGN;
+#pragma unroll
+  for (int i2 = 0; i2 < S::FM / 2; ++i2) {
+    const int q = (wm * S::WTM + 32 * i2) / 8 + grp;
+#pragma unroll
+    for (int j = 0; j < S::FN; ++j) {
+      const int r = wn * S::WTN + 16 * j + col;
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = acc[2 * i2][j][e];
+        v[4 + e] = acc[2 * i2 + 1][j][e];
+      }
+      frag_store(row(r) + 8 * (q ^ (r % CH)), frag_from<T>(v));
+    }
+  }
+  __syncthreads();
+
+  // the tile's first and last three rows, for the dx of the previous tile's and
+  // this tile's last three tokens
+  for (int e = tid; e < 6 * CH; e += NT) {
+    const int er = e / CH, eq = e % CH, r = er < 3 ? er : BT - 6 + er;
+    if (n0 + 8 * eq < d)
+      frag_store(static_cast<T*>(cv.edge) + ((size_t)mt * 6 + er) * d + n0 + 8 * eq,
+                 frag_load(row(r) + 8 * (eq ^ (r % CH))));
+  }
+  const int qd = tid % NQ, run = tid / NQ;
+  const int c = n0 + 4 * qd, u0 = run * RL, t0 = m0 + u0;
+  const int qoff = 8 * ((qd >> 1)) + 4 * (qd & 1);  // before the row swizzle
+  const bool last_tile = m0 + BT >= T_;
+  float dw[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dw[j][k] = 0.f;
+  if (c < d && t0 < T_) {
+    // taps of the 4 channels: w[c + j][k] = element (4 j + k) % 8 of wf[(4 j + k) / 8]
+    Frag8<T> wf[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) wf[m] = frag_load(static_cast<const T*>(cv.conv_w) + (size_t)c * 4 + 8 * m);
+    auto wtap = [&](int j, int k) { return frag_get(wf[(4 * j + k) >> 3], (4 * j + k) & 7); };
+    // x rows slide through xw[0..3] = x_{t-3} .. x_t, loaded 4 rows ahead of use
+    auto xrow = [&](int t) { return t >= 0 && t < T_ ? quad_load(x + (size_t)t * d + c) : quad_from4<T>(kZero4); };
+    Quad<T> xw[4] = {quad_from4<T>(kZero4), xrow(t0 - 3), xrow(t0 - 2), xrow(t0 - 1)};
+    Quad<T> xb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xb[i] = xrow(t0 + i);
+    // the window g0..g3 = dX~ rows u .. u + 3 of the tile (zero past its end)
+    auto tile_row = [&](int r) {
+      return r < BT ? quad_load(row(r) + (qoff ^ (8 * (r % CH)))) : quad_from4<T>(kZero4);
+    };
+    Quad<T> g0 = tile_row(u0), g1 = tile_row(u0 + 1), g2 = tile_row(u0 + 2);
+    SeqCursor cur(cv.cu, cv.nseq, t0, T_);
+#pragma unroll
+    for (int i = 0; i < RL; ++i) {
+      const int u = u0 + i, t = m0 + u;
+      if (t >= T_) break;
+      xw[0] = xw[1];
+      xw[1] = xw[2];
+      xw[2] = xw[3];
+      xw[3] = xb[i % 4];
+      if (i % 4 == 3 && i + 1 < RL) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) xb[k] = xrow(t + 1 + k);
+      }
+      const Quad<T> g3 = tile_row(u + 3);
+      const int end = cur.end(t), pos = cur.pos(t);
+      if (u + 3 < BT || last_tile) {
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float a = t + 3 < end ? wtap(j, 0) * quad_get(g3, j) : 0.f;
+          if (t + 2 < end) a += wtap(j, 1) * quad_get(g2, j);
+          if (t + 1 < end) a += wtap(j, 2) * quad_get(g1, j);
+          a += wtap(j, 3) * quad_get(g0, j);
+          o[j] = a;
+        }
+        quad_store(dx + (size_t)t * d + c, quad_from4<T>(o));
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gv = quad_get(g0, j);
+        dw[j][3] += gv * quad_get(xw[3], j);
+        if (pos >= 1) dw[j][2] += gv * quad_get(xw[2], j);
+        if (pos >= 2) dw[j][1] += gv * quad_get(xw[1], j);
+        if (pos >= 3) dw[j][0] += gv * quad_get(xw[0], j);
+      }
+      g0 = g1;
+      g1 = g2;
+      g2 = g3;
+    }
+  }
+  __syncthreads();  // the tile is no longer read: its LDS takes the dconv_w partials [RUNS][NQ][16]
+  auto red_at = [&](int rr, int qq, int e) -> float& {
+    const int i = (rr * NQ + qq) * 16 + e;
+    return i < HALF ? reinterpret_cast<float*>(lo)[i] : reinterpret_cast<float*>(hi)[i - HALF];
+  };
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red_at(run, qd, j * 4 + k) = dw[j][k];
+  __syncthreads();
+  for (int e = tid; e < BC * 4; e += NT) {
+    const int cl = e >> 2, k = e & 3;
+    float sum = 0.f;
+    for (int rr = 0; rr < RUNS; ++rr) sum += red_at(rr, cl >> 2, (cl & 3) * 4 + k);
+    if (n0 + cl < d) cv.dconv_part[((size_t)mt * d + n0 + cl) * 4 + k] = sum;
+  }
+}
+
+template <typename T, bool CONV>
 __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
                                                                      const T* __restrict__ wt, int T_, int d, int Kp,
-                                                                     int Kr, T* __restrict__ dxt) {
+                                                                     int Kr, T* __restrict__ out, DxConv cv) {
   using S = typename DxCfg<T>::S;
   constexpr bool DL = DxCfg<T>::DL;
   static_assert(S::BM % 32 == 0 && S::WTM % 32 == 0, "whole 32-row channel groups per wave");
@@ -533,6 +684,13 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
   else
     gemm_nt_mainloop<T, S>(wt + (size_t)n0 * Kp, Kp, min(S::BM, dp - n0), G + (size_t)m0 * Kp, Kp,
                            min(S::BN, T_ - m0), Kr, smem, acc);
+  if constexpr (CONV) {
+    // the tile's token halves in the two stage buffers (bf16), or both in the one buffer (float)
+    static_assert(!DL || (S::BN / 2) * S::BM <= S::STAGE, "a token half of the tile fits one stage");
+    static_assert(DL || S::BN * S::BM <= 2 * S::STAGE, "the tile fits the stage buffer");
+    dx_conv_epilogue<T, S>(acc, smem, DL ? smem1 : smem + (S::BN / 2) * S::BM, m0, n0, mt, T_, d, out, cv);
+    return;
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, col = lane & 15, grp = lane >> 4;
   const int wm = w / S::WGN, wn = w % S::WGN;
 #pragma unroll
@@ -547,23 +705,42 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
         v[r] = acc[2 * i2][j][r];
         v[4 + r] = acc[2 * i2 + 1][j][r];
       }
-      if (t < T_ && c < d) frag_store(dxt + (size_t)t * d + c, frag_from<T>(v));
+      if (t < T_ && c < d) frag_store(out + (size_t)t * d + c, frag_from<T>(v));
     }
   }
 }
 
+int dx_token_tiles(int dt, int T) {
+  const int bn = dt == BF16 ? DxCfg<bf16>::S::BN : DxCfg<float>::S::BN;
+  return (T + bn - 1) / bn;
+}
+int dx_token_tile_rows(int dt) { return dt == BF16 ? DxCfg<bf16>::S::BN : DxCfg<float>::S::BN; }
+
+template <typename TT>
+static void gemm_dx_t(const void* G, const void* wt, int T, int d, int Kp, int Kr, void* out, const DxConv* cv,
+                      hipStream_t s) {
+  using S = typename DxCfg<TT>::S;
+  const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
+  if (n == 0) return;
+  if (cv)
+    hipLaunchKernelGGL((k_gemm_dx<TT, true>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
+                       (const TT*)wt, T, d, Kp, Kr, (TT*)out, *cv);
+  else
+    hipLaunchKernelGGL((k_gemm_dx<TT, false>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
+                       (const TT*)wt, T, d, Kp, Kr, (TT*)out, DxConv{});
+}
+
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* dxt, hipStream_t s) {
-  if (dt == BF16) {
-    using S = DxCfg<bf16>::S;
-    const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
-    if (n) hipLaunchKernelGGL(k_gemm_dx<bf16>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const bf16*)G,
-                              (const bf16*)wt, T, d, Kp, Kr, (bf16*)dxt);
-  } else {
-    using S = DxCfg<float>::S;
-    const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
-    if (n) hipLaunchKernelGGL(k_gemm_dx<float>, dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const float*)G,
-                              (const float*)wt, T, d, Kp, Kr, (float*)dxt);
-  }
+  if (dt == BF16) gemm_dx_t<bf16>(G, wt, T, d, Kp, Kr, dxt, nullptr, s);
+  else gemm_dx_t<float>(G, wt, T, d, Kp, Kr, dxt, nullptr, s);
+}
+
+void launch_gemm_dx_conv(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, const void* x,
+                         const int32_t* cu, int N, const void* conv_w, void* dx, float* dconv_part, void* edge,
+                         hipStream_t s) {
+  const DxConv cv{x, cu, N, conv_w, dconv_part, edge};
+  if (dt == BF16) gemm_dx_t<bf16>(G, wt, T, d, Kp, Kr, dx, &cv, s);
+  else gemm_dx_t<float>(G, wt, T, d, Kp, Kr, dx, &cv, s);
 }
 
 // ============================================================== dW = X~^T G (split over tokens)
@@ -689,6 +866,49 @@ void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int K
 // range of blocks, each in a fixed order: the dW split-K partials (float4 per
 // thread, as k_dw_reduce), the conv-backward row-block partials of dconv_w,
 // and the per-chunk partials of db_g (and of dgamma with the gated output).
+// dx of tokens u = m0 + BT - 3 + i (i < 3) of token tile mt: their conv window
+// dX~ rows u .. u + 3 straddles tiles mt and mt + 1, whose edge rows hold them
+// (tile mt's last three rows, then tile mt + 1's first three). Same arithmetic,
+// in the same order, as the dX~ GEMM's epilogue.
+template <typename T>
+__device__ void conv_tail_block(const BwdFinalize& f, int mt) {
+  const T* edge = static_cast<const T*>(f.edge);
+  const T* conv_w = static_cast<const T*>(f.conv_w);
+  const int BT = f.tile_rows, d = f.d, G8 = d / 8;
+  for (int e = threadIdx.x; e < 3 * G8; e += 256) {
+    const int i = e / G8, c = 8 * (e % G8);
+    const int t = mt * BT + BT - 3 + i;  // < T: tile mt is not the last
+    int lo = 0, hi = f.nseq;  // t's sequence: the last b with cu[b] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (f.cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int end = f.cu[lo + 1];
+    // window rows t + s, s = 0..3: edge row 3 + i + s of tile mt while inside it, else row i + s - 3 of tile mt + 1
+    Frag8<T> g[4];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) {
+      const int r = i + s2;
+      const size_t er = r < 3 ? (size_t)mt * 6 + 3 + r : (size_t)(mt + 1) * 6 + (r - 3);
+      g[s2] = frag_load(edge + er * d + c);
+    }
+    Frag8<T> wf[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) wf[m] = frag_load(conv_w + (size_t)c * 4 + 8 * m);
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      auto wtap = [&](int k) { return frag_get(wf[(4 * j + k) >> 3], (4 * j + k) & 7); };
+      float a = t + 3 < end ? wtap(0) * frag_get(g[3], j) : 0.f;
+      if (t + 2 < end) a += wtap(1) * frag_get(g[2], j);
+      if (t + 1 < end) a += wtap(2) * frag_get(g[1], j);
+      a += wtap(3) * frag_get(g[0], j);
+      o[j] = a;
+    }
+    frag_store(static_cast<T*>(f.dx) + (size_t)t * d + c, frag_from<T>(o));
+  }
+}
+
 __global__ __launch_bounds__(256) void k_bwd_finalize(BwdFinalize f) {
   int b = blockIdx.x;
   if (b < f.dw_blocks) {
@@ -730,152 +950,27 @@ __global__ __launch_bounds__(256) void k_bwd_finalize(BwdFinalize f) {
     return;
   }
   b -= dbg_blocks;
-  if (f.dgamma) sum_parts_block<4>(f.dgam_part, f.dh, nc * f.H, f.dgamma, b);
+  const int dgam_blocks = f.dgamma ? (f.dh + 3) / 4 : 0;
+  if (b < dgam_blocks) {
+    sum_parts_block<4>(f.dgam_part, f.dh, nc * f.H, f.dgamma, b);
+    return;
+  }
+  b -= dgam_blocks;
+  if (f.edge && b < f.conv_rb - 1) {  // dx of the last three tokens of token tile b (not the batch's last)
+    if (f.dt == BF16) conv_tail_block<bf16>(f, b);
+    else conv_tail_block<float>(f, b);
+  }
 }
 
 void launch_bwd_finalize(const BwdFinalize& f, hipStream_t s) {
-  const int grid = f.dw_blocks + f.d + (f.H + 3) / 4 + (f.dgamma ? (f.dh + 3) / 4 : 0);
+  const int grid = f.dw_blocks + f.d + (f.H + 3) / 4 + (f.dgamma ? (f.dh + 3) / 4 : 0) +
+                   (f.edge ? std::max(0, f.conv_rb - 1) : 0);
   hipLaunchKernelGGL(k_bwd_finalize, dim3(grid), dim3(256), 0, s, f);
 }
 
 int bwd_finalize_dw_blocks(int d, int Kp) {
   const long quads = (long)d * Kp / 4;
   return (int)std::min<long>((quads + 255) / 256, 8192);
-}
-
-// ============================================================== conv backward
-// Thread = 8 channels x kConvRun consecutive tokens; block = 64 channel groups
-// (512 channels) x 4 runs. Both windows slide in registers: dx~ rows u..u+3
-// (for dx) and x rows u-3..u (for dconv_w); sequence bounds come from a cursor.
-//   dx_u[c]       = sum_k w[c][k] dx~_{u+3-k}[c]      (u+3-k inside u's sequence)
-//   dconv_w[c][k] = sum_t dx~_t[c] x_{t-3+k}[c]       (t-3+k inside t's sequence)
-constexpr int kConvRun = 32;
-constexpr int kConvBatch = 4;  // tokens per unrolled, prefetched batch
-constexpr int kConvRows = 4 * kConvRun;
-int conv_bwd_row_blocks(int T) { return (T + kConvRows - 1) / kConvRows; }
-
-template <typename T>
-__device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
-  const Frag8<T> f = frag_load(p);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = frag_get(f, j);
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_conv_bwd(const T* __restrict__ dxt, const T* __restrict__ x,
-                                                  const int32_t* __restrict__ cu, int nseq, int T_, int d,
-                                                  const T* __restrict__ conv_w, T* __restrict__ dx,
-                                                  float* __restrict__ part) {
-  constexpr int B = kConvBatch, RP = 33;  // tokens per unrolled batch; padded pitch of red[]
-  __shared__ float red[4][64 * RP];
-  const int rb = blockIdx.x, cb = blockIdx.y;
-  const int tid = threadIdx.x, cg = tid & 63, run = tid >> 6;
-  const int c = cb * 512 + cg * 8;
-  float dw[8][4];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) dw[j][k] = 0.f;
-  const int u0 = rb * kConvRows + run * kConvRun;
-  const int u1 = min(u0 + kConvRun, T_);
-  if (c < d && u0 < u1) {
-    float wv[8][4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const Frag8<T> f = frag_load(conv_w + (size_t)c * 4 + 8 * m);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
-    }
-    // sliding windows: gw[s] = dx~_{u+s} (s = 0..2), xw[s] = x_{u-1-s} (s = 0..2); zero outside [0, T)
-    float gw[3][8], xw[3][8];
-#pragma unroll
-    for (int s = 0; s < 3; ++s) {
-      const int tg = u0 + s, tx = u0 - 1 - s;
-      if (tg < T_) load8f(dxt + (size_t)tg * d + c, gw[s]);
-      else
-#pragma unroll
-        for (int j = 0; j < 8; ++j) gw[s][j] = 0.f;
-      if (tx >= 0) load8f(x + (size_t)tx * d + c, xw[s]);
-      else
-#pragma unroll
-        for (int j = 0; j < 8; ++j) xw[s][j] = 0.f;
-    }
-    // the rows of a batch (dx~_{u+3}, x_u for its B tokens u) are loaded together, one batch ahead
-    Frag8<T> fa[2][B], fb[2][B];
-    auto fetch = [&](int buf, int ub) {
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int tg = ub + 3 + i, tx = ub + i;
-        fa[buf][i] = tg < T_ ? frag_load(dxt + (size_t)tg * d + c) : frag_zero<T>();
-        fb[buf][i] = tx < u1 ? frag_load(x + (size_t)tx * d + c) : frag_zero<T>();
-      }
-    };
-    SeqCursor cur(cu, nseq, u0, T_);
-    auto compute = [&](int buf, int ub) {
-#pragma unroll
-      for (int i = 0; i < B; ++i) {
-        const int u = ub + i;
-        if (u >= u1) break;
-        float g3[8], x0[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          g3[j] = frag_get(fa[buf][i], j);
-          x0[j] = frag_get(fb[buf][i], j);
-        }
-        const int end = cur.end(u), pos = cur.pos(u);
-        float o[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          // output token u + 3 - k reads x_u through tap k; token u read x_{u-sh} through tap 3 - sh
-          float a = u + 3 < end ? wv[j][0] * g3[j] : 0.f;
-          if (u + 2 < end) a += wv[j][1] * gw[2][j];
-          if (u + 1 < end) a += wv[j][2] * gw[1][j];
-          a += wv[j][3] * gw[0][j];
-          o[j] = a;
-          dw[j][3] += gw[0][j] * x0[j];
-          if (pos >= 1) dw[j][2] += gw[0][j] * xw[0][j];
-          if (pos >= 2) dw[j][1] += gw[0][j] * xw[1][j];
-          if (pos >= 3) dw[j][0] += gw[0][j] * xw[2][j];
-        }
-        frag_store(dx + (size_t)u * d + c, frag_from<T>(o));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          gw[0][j] = gw[1][j]; gw[1][j] = gw[2][j]; gw[2][j] = g3[j];
-          xw[2][j] = xw[1][j]; xw[1][j] = xw[0][j]; xw[0][j] = x0[j];
-        }
-      }
-    };
-    fetch(0, u0);
-    for (int ub = u0; ub < u1; ub += 2 * B) {
-      if (ub + B < u1) fetch(1, ub + B);
-      compute(0, ub);
-      if (ub + 2 * B < u1) fetch(0, ub + 2 * B);
-      if (ub + B < u1) compute(1, ub + B);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) red[run][cg * RP + j * 4 + k] = dw[j][k];
-  __syncthreads();
-  // 512 channels x 4 taps, summed over the 4 runs in a fixed order
-  for (int e = tid; e < 512 * 4; e += 256) {
-    const int cc = cb * 512 + (e >> 2);
-    const int li = (e >> 5) * RP + (e & 31);  // channel group e / 32, element (channel % 8) * 4 + tap
-    if (cc < d) part[((size_t)rb * d + cc) * 4 + (e & 3)] = (red[0][li] + red[1][li]) + (red[2][li] + red[3][li]);
-  }
-}
-
-void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,
-                     const void* conv_w, void* dx, float* dconv_part, hipStream_t s) {
-  const dim3 grid(conv_bwd_row_blocks(T), (d + 511) / 512);
-  if (grid.x == 0) return;
-  if (dt == BF16)
-    hipLaunchKernelGGL(k_conv_bwd<bf16>, grid, dim3(256), 0, s, (const bf16*)dxt, (const bf16*)x, cu, N, T, d,
-                       (const bf16*)conv_w, (bf16*)dx, dconv_part);
-  else
-    hipLaunchKernelGGL(k_conv_bwd<float>, grid, dim3(256), 0, s, (const float*)dxt, (const float*)x, cu, N, T, d,
-                       (const float*)conv_w, (float*)dx, dconv_part);
 }
 
 }  // namespace gbla

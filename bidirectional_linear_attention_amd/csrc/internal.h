@@ -185,7 +185,17 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const float* ga, const float* dsz,
                       const int* nchunks, const Chunk* tab, int max_slots, int H, int Kp, int nseg, void* G,
                       float* dbg_part, const float* gmax, hipStream_t s);
+// dx = G Wt^T (no conv: LION)
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* dxt, hipStream_t s);
+// dX~ = G Wt^T with the causal conv's VJP in the epilogue (GBLA): dx (but the
+// last three tokens of each token tile other than the last, left to
+// k_bwd_finalize), per-token-tile dconv_w partials [dx_token_tiles][d][4] and
+// the tiles' edge rows [dx_token_tiles][6][d]
+void launch_gemm_dx_conv(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, const void* x,
+                         const int32_t* cu, int N, const void* conv_w, void* dx, float* dconv_part, void* edge,
+                         hipStream_t s);
+int dx_token_tiles(int dt, int T);
+int dx_token_tile_rows(int dt);
 int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
@@ -193,19 +203,21 @@ void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp,
 // dw_g may be null (its columns are not written); dw_r non-null: G has the R segment
 // the backward's closing sums (dW split-K partials, dconv_w row blocks, db_g and
 // dgamma chunk partials) in one launch
+// With edge non-null (the conv VJP fused into the dX~ GEMM) it also forms dx of
+// the last three tokens of every token tile but the last (conv_rb tiles of
+// tile_rows tokens).
 struct BwdFinalize {
   const float* dw_part; int nsplit, d, H, dh, Kp, dw_blocks;
   float *dw_q, *dw_k, *dw_v, *dw_r, *dw_g;
   const float* dconv_part; int conv_rb; float* dconv_w;
   const int* nchunks; const float* dbg_part; float* db_g;
   const float* dgam_part; float* dgamma;
+  int dt, tile_rows, nseq;
+  const void* edge; const void* conv_w; const int32_t* cu; void* dx;
 };
 int bwd_finalize_dw_blocks(int d, int Kp);
 void launch_bwd_finalize(const BwdFinalize& f, hipStream_t s);
 void launch_dw_reduce(const float* part, int nsplit, int d, int H, int dh, int Kp, float* dw_q, float* dw_k,
                       float* dw_v, float* dw_r, float* dw_g, hipStream_t s);
-void launch_conv_bwd(int dt, const void* dxt, const void* x, const int32_t* cu, int N, int T, int d,
-                     const void* conv_w, void* dx, float* dconv_part, hipStream_t s);
-int conv_bwd_row_blocks(int T);
 
 }  // namespace gbla
