@@ -171,6 +171,30 @@ template <> __device__ __forceinline__ Frag8<float> frag_kmajor<float>(const flo
   return f;
 }
 
+// The same eight k values per lane as frag_kmajor for a 32-wide k step starting
+// at row k0, assigned so that 16-lane group g reads rows k0 + 4 g .. k0 + 4 g + 3
+// and k0 + 16 + 4 g .. k0 + 16 + 4 g + 3: each transposing read of the four
+// groups then covers 16 consecutive rows, which row pitches of 40 or 72 dwords
+// keep free of LDS bank conflicts (with rows k0 + 8 g .. as in frag_kmajor two
+// groups always share banks). Both operands of an MFMA must use the same form.
+template <typename T> __device__ __forceinline__ Frag8<T> frag_kmajor_4g(const T* tile, int ld, int k0, int cb, int lane);
+template <> __device__ __forceinline__ Frag8<bf16> frag_kmajor_4g<bf16>(const bf16* tile, int ld, int k0, int cb,
+                                                                        int lane) {
+  const int g = lane >> 4;
+  const uint2 lo = tr_read4(tile, ld, k0 + 4 * g, cb, lane), hi = tr_read4(tile, ld, k0 + 16 + 4 * g, cb, lane);
+  Frag8<bf16> f;
+  f.v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return f;
+}
+template <> __device__ __forceinline__ Frag8<float> frag_kmajor_4g<float>(const float* tile, int ld, int k0, int cb,
+                                                                          int lane) {
+  const float* p = tile + (k0 + 4 * (lane >> 4)) * ld + cb + (lane & 15);
+  Frag8<float> f;
+  f.lo = make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]);
+  f.hi = make_float4(p[16 * ld], p[17 * ld], p[18 * ld], p[19 * ld]);
+  return f;
+}
+
 // ---------------------------------------------------------------- 4-element quads (K = 16 MFMA operands)
 // Four consecutive k elements of one lane for a 16x16x16 MFMA (bf16: one 8-byte
 // register pair; float: four 16x16x4 MFMAs). With the C-reuse assignment

@@ -58,13 +58,22 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
                                                     float eps, float* __restrict__ dgam_part) {
   constexpr int FB = DH / 16, NB = FB + 1, NR = DH + 16;
   constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LD = DH + PAD, LDN = DH + 16 + PAD;
+  // pitches (elements): LD for the dy and R tiles (row reads only); LDT = DH + 16
+  // (40 dwords at d_h = 64, bf16) for the tiles that the transposing reads use:
+  // the state (read by 16-row groups) and q~, [dn | dden] (read by frag_kmajor_4g)
+  constexpr int LD = DH + PAD, LDT = DH + 16, LDN = DH + 16;
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
   constexpr int ST = 64, V8 = DH / 8, KS = DH / 32;
   constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
-  __shared__ __align__(16) T Sst[P * NR * LD];  // [S | z]^T: row n (row dh = z, rows > dh zero), column a
-  __shared__ __align__(16) T qs[ST * LD];       // q~ tile (token-major)
+  // One pool: [S | z]^T (row n = state row, row dh = z, rows > dh zero; the high
+  // part, then the low part) followed by the q~ tile. Rows dh + 1 .. of the low
+  // part overlap the q~ tile: they only feed output rows that are never used
+  // (num rows past dh), so they may hold anything.
+  constexpr int SST = (P * NR - (P - 1) * (NR - DH - 1)) * LDT, QS = ST * LDT;
+  __shared__ __align__(16) T pool[SST + QS];
+  T* const Sst = pool;
+  T* const qs = pool + SST;
   __shared__ __align__(16) T ys[ST * LD];       // dy tile
   __shared__ __align__(16) T dns[ST * LDN];     // [dn | dden | 0] (token-major)
   __shared__ __align__(16) T rs[GATED ? ST * LD : 8];  // R tile (gated output)
@@ -79,7 +88,8 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, NR>(Sst, nullptr, LD, st, st + DH * DH, tid);
+  stage_state<T, DH, NR>(Sst, nullptr, LDT, st, st + DH * DH, tid);
+  __syncthreads();  // the state's low-part rows past dh that overlap the q~ tile are written before it
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
   for (int e = tid; e < ST * 16; e += 256) dns[(e >> 4) * LDN + DH + (e & 15)] = from_f<T>(0.f);
 
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
       if (it < ST * V8) {
-        frag_store(qs + r * LD + c, pq[v]);
+        frag_store(qs + r * LDT + c, pq[v]);
         frag_store(ys + r * LD + c, py[v]);
         if constexpr (GATED) frag_store(rs + r * LD + c, pr[v]);
       }
@@ -125,7 +135,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
     // [num | den]^T for tokens r0 .. r0 + 15: C[4 grp + r][col] = num[token r0 + col][16 nt + 4 grp + r]
     Frag8<T> bq[KS];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) bq[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
+    for (int s = 0; s < KS; ++s) bq[s] = frag_load(qs + (r0 + col) * LDT + 32 * s + 8 * grp);
     f32x4 num[NB];
 #pragma unroll
     for (int nt = 0; nt < NB; ++nt) {
@@ -134,7 +144,7 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int s = 0; s < KS; ++s)
-          mma8(num[nt], frag_load(Sst + p * NR * LD + (16 * nt + col) * LD + 32 * s + 8 * grp), bq[s]);
+          mma8(num[nt], frag_load(Sst + p * NR * LDT + (16 * nt + col) * LDT + 32 * s + 8 * grp), bq[s]);
     }
     const int tok = r0 + col;
     const bool ok = tb + tok < ch.end;
@@ -213,8 +223,8 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       for (int nt = 0; nt < FB; ++nt)
 #pragma unroll
         for (int p = 0; p < P; ++p)
-          mma_q(dq, quad_kmajor<T>(Sst + p * NR * LD, LD, 16 * nt + 4 * grp, 16 * at, lane), dnq[nt]);
-      const Quad<T> qv = quad_load(qs + tok * LD + 16 * at + 4 * grp);
+          mma_q(dq, quad_kmajor<T>(Sst + p * NR * LDT, LDT, 16 * nt + 4 * grp, 16 * at, lane), dnq[nt]);
+      const Quad<T> qv = quad_load(qs + tok * LDT + 16 * at + 4 * grp);
       float o[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
@@ -231,8 +241,8 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
       const int ia = tile / NB, nb = tile - ia * NB;
 #pragma unroll
       for (int s = 0; s < ST / 32; ++s)
-        mma8(accS[u], frag_kmajor<T>(qs, LD, 32 * s + 8 * grp, 16 * ia, lane),
-             frag_kmajor<T>(dns, LDN, 32 * s + 8 * grp, 16 * nb, lane));
+        mma8(accS[u], frag_kmajor_4g<T>(qs, LDT, 32 * s, 16 * ia, lane),
+             frag_kmajor_4g<T>(dns, LDN, 32 * s, 16 * nb, lane));
     }
     __syncthreads();  // the tiles are rewritten next
   }
@@ -304,10 +314,11 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
                                                    float* __restrict__ dbg_part, const float* __restrict__ gmax) {
   constexpr int FB = DH / 16;
   constexpr int LD = DH + 16 / (int)sizeof(T);
+  constexpr int LDS_ = DH + 16;  // 40 dwords at d_h = 64 (bf16): conflict-free transposing reads of dS
   constexpr int P = Parts<T>::n;
   constexpr int E = DH * DH + DH;
   constexpr int ST = 64, V8 = DH / 8;
-  __shared__ __align__(16) T Srm[P * DH * LD];  // dS[i][n]: B of v dS^T by rows, B of k~ dS by columns
+  __shared__ __align__(16) T Srm[P * DH * LDS_];  // dS[i][n]: B of v dS^T by rows, B of k~ dS by columns
   __shared__ __align__(16) T ks[ST * LD];       // phi(k) tile, then dk
   __shared__ __align__(16) T vs[ST * LD];       // v tile, then dv
   __shared__ float gs[ST];
@@ -322,7 +333,7 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = dsz + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, DH>(nullptr, Srm, LD, st, st + DH * DH, tid);
+  stage_state<T, DH, DH>(nullptr, Srm, LDS_, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
@@ -358,14 +369,21 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
     __syncthreads();
     if (tb + ST < ch.end) fetch(tb + ST);
     const float gA = gs[r0 + col];
+    // kf: k~ of the lane's token with the k (feature) assignment of frag_kmajor_4g,
+    // features 32 s + 4 grp + e and 32 s + 16 + 4 grp + e (e < 4), the B side's
+    // transposing reads of dS then being conflict-free
     Frag8<T> vf[DH / 32], kf[DH / 32];
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) {
       vf[s] = frag_load(vs + (r0 + col) * LD + 32 * s + 8 * grp);
-      const Frag8<T> pk = frag_load(ks + (r0 + col) * LD + 32 * s + 8 * grp);
+      const Quad<T> k0 = quad_load(ks + (r0 + col) * LD + 32 * s + 4 * grp);
+      const Quad<T> k1 = quad_load(ks + (r0 + col) * LD + 32 * s + 16 + 4 * grp);
       float kt[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kt[e] = gA * frag_get(pk, e);
+      for (int e = 0; e < 4; ++e) {
+        kt[e] = gA * quad_get(k0, e);
+        kt[4 + e] = gA * quad_get(k1, e);
+      }
       kf[s] = frag_from<T>(kt);
     }
     f32x4 dkt[FB], dvv[FB];
@@ -377,8 +395,8 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
       for (int p = 0; p < P; ++p)
 #pragma unroll
         for (int s = 0; s < DH / 32; ++s) {
-          mma8(dkt[nt], vf[s], frag_load(Srm + p * DH * LD + (16 * nt + col) * LD + 32 * s + 8 * grp));
-          mma8(dvv[nt], kf[s], frag_kmajor<T>(Srm + p * DH * LD, LD, 32 * s + 8 * grp, 16 * nt, lane));
+          mma8(dkt[nt], vf[s], frag_load(Srm + p * DH * LDS_ + (16 * nt + col) * LDS_ + 32 * s + 8 * grp));
+          mma8(dvv[nt], kf[s], frag_kmajor_4g<T>(Srm + p * DH * LDS_, LDS_, 32 * s, 16 * nt, lane));
         }
     }
     float dkv[FB][4];

@@ -414,8 +414,8 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
   constexpr int FB = DH / 16, NB = FB + 1;     // key-feature blocks; value blocks + ones block
   constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
   constexpr int ST = 64;                       // tokens per staged tile
-  // bf16 pitches of 40 or 24 dwords (8 banks apart mod 32): the four rows a
-  // transposing read touches per 16 lanes fall on disjoint banks
+  // bf16 pitches of 40 (d_h = 64) or 24 dwords: with the 16-row groups of
+  // frag_kmajor_4g, the transposing reads of 40-dword rows are free of bank conflicts
   constexpr bool B16 = sizeof(T) == 2;
   constexpr int LDK = DH + (B16 ? 16 : 4), LDV = 16 * NB + (B16 ? 0 : 4);
   constexpr int E = DH * DH + DH;
@@ -486,8 +486,8 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
         const int ib = tile / NB, nb = tile - ib * NB;
 #pragma unroll
         for (int k0 = 0; k0 < ST; k0 += 32) {
-          const Frag8<T> a = frag_kmajor<T>(ks, LDK, k0 + 8 * grp, 16 * ib, lane);
-          const Frag8<T> b = frag_kmajor<T>(vs, LDV, k0 + 8 * grp, 16 * nb, lane);
+          const Frag8<T> a = frag_kmajor_4g<T>(ks, LDK, k0, 16 * ib, lane);
+          const Frag8<T> b = frag_kmajor_4g<T>(vs, LDV, k0, 16 * nb, lane);
           mma8(acc[u], a, b);
         }
       }
