@@ -13,9 +13,12 @@ measured live with the library's HIP events on the launch stream, recorded in
 the timed region around that stage only (a pass before it, with events around
 every stage, gives stage_ms_per_step and picks the dominant stage), and the
 float64 CPU oracle timed on a bounded sample of the same workload.
-The same line carries secondary measurements: the same GBLA workload with the
-softmax-over-the-sequence key gate under "gbla_softmax" and with the gated
-RMSNorm output (Eq. (7)) under "gbla_gated_rmsnorm", and the LION layers
+The same line carries secondary measurements: the GBLA layer on the 32 x 1024
+(d 256) and ragged 256-sequence workloads ("gbla_B32_L1024_d256",
+"gbla_ragged_N256_d512"), its forward-only latency at batch 8 and L = 8192 and
+32768 beside the pages' H100 figures ("forward_latency"), the main workload
+with the softmax-over-the-sequence key gate under "gbla_softmax" and with the
+gated RMSNorm output (Eq. (7)) under "gbla_gated_rmsnorm", and the LION layers
 (16 x 4096 tokens, d_model 512, 8 heads of 64, 64-token chunks, bf16) under
 "lion_s", "lion_d" and "lion_lit" (selective, fixed per-head and no decay).
 
@@ -216,15 +219,15 @@ def hbm_ceiling(mib=64, reps=10):
         "flush": "read-only sum over a 1 GiB buffer before each cold copy", "peak_tb_per_s": 8.0}}), flush=True)
 
 
-def gbla_setup(torch, gb, gate, gated_output=False):
-    """Device buffers and the step function of the GBLA workload (x and dy
-    rotate over three buffer sets); gated_output adds the gated RMSNorm output
-    (W_R, gamma)."""
+def gbla_setup(torch, gb, gate, gated_output=False, workload=WORKLOAD, n_sets=3):
+    """Device buffers and the step function of a GBLA workload (x and dy
+    rotate over n_sets buffer sets); gated_output adds the gated RMSNorm output
+    (W_R, gamma). Also returns fwd(i), the forward pass alone."""
     import numpy as np
 
     from bidirectional_linear_attention_amd.synthetic import WORKLOADS, make_inputs, make_output_gate
 
-    w = WORKLOADS[WORKLOAD]
+    w = WORKLOADS[workload]
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -238,7 +241,6 @@ def gbla_setup(torch, gb, gate, gated_output=False):
     cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
     conv_w, w_q, w_k, w_v, w_g = (t(inp[k]) for k in ("conv_w", "w_q", "w_k", "w_v", "w_g"))
     b_g = torch.from_numpy(inp["b_g"]).float().to(dev)
-    n_sets = 3
     xs = [t(inp["x"]) for _ in range(n_sets)]
     dys = [t(inp["dy"]) for _ in range(n_sets)]
     p = gb.problem(N, T, d, H, dh, dt, gate, gated_output)
@@ -258,14 +260,61 @@ def gbla_setup(torch, gb, gate, gated_output=False):
     ws = torch.empty(max(gb.workspace_size(p, False), gb.workspace_size(p, True)), dtype=torch.uint8, device=dev)
     act = torch.empty(gb.activation_size(p), dtype=torch.uint8, device=dev)
 
-    def step(i):
-        x, dy = xs[i % n_sets], dys[i % n_sets]
-        gb.gbla_forward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws, w_r=og["w_r"],
+    def fwd(i):
+        gb.gbla_forward(p, xs[i % n_sets], cu, conv_w, w_q, w_k, w_v, w_g, b_g, y, saved, act, ws, w_r=og["w_r"],
                         gamma=og["gamma"])
-        gb.gbla_backward(p, x, cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dy, dx, dconv, dwq, dwk, dwv, dwg,
-                         dbg, ws, **og)
 
-    return dict(w=w, inp=inp, step=step, T=T, N=N, d=d, H=H, dh=dh, esz=esz)
+    def step(i):
+        fwd(i)
+        gb.gbla_backward(p, xs[i % n_sets], cu, conv_w, w_q, w_k, w_v, w_g, b_g, saved, act, dys[i % n_sets], dx,
+                         dconv, dwq, dwk, dwv, dwg, dbg, ws, **og)
+
+    return dict(w=w, inp=inp, step=step, fwd=fwd, T=T, N=N, d=d, H=H, dh=dh, esz=esz)
+
+
+def gbla_workload_leg(steps, warmup, workload):
+    """GBLA forward+backward (sigmoid key gate, plain output) on another workload
+    of the recipe table: tokens/s and stage times."""
+    import torch
+
+    import bidirectional_linear_attention_amd as gb
+
+    g = gbla_setup(torch, gb, "sigmoid", workload=workload)
+    elapsed, breakdown, _ = timed_passes(gb, torch, g["step"], steps, warmup, lambda br: [])
+    T = g["T"]
+    return {"workload": workload, "sequences": g["N"], "tokens_per_step": T, "steps": steps, "warmup": warmup,
+            "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(1e3 * elapsed / steps, 4),
+            "stage_ms_per_step": {k: round(v[0], 4) for k, v in sorted(breakdown.items(), key=lambda kv: -kv[1][0])}}
+
+
+# forward-only single-layer latency of GBLA on an H100 in the GBLA page's
+# benchmark section (Table 5: batch 8, mean of 10 runs, precision and layer
+# boundary not stated); context for the forward latency legs, not a target
+PAGES_FORWARD_MS = {"gbla_bf16_B8_L8192_d512": 2.2, "gbla_bf16_B8_L32768_d512": 8.2}
+
+
+def forward_latency_leg(workload, runs=10, warmup=3):
+    """Forward-only latency of one layer call (batch 8, L = 8192 or 32768): the
+    mean of `runs` calls, each bracketed by synchronize, as the pages time it."""
+    import torch
+
+    import bidirectional_linear_attention_amd as gb
+
+    g = gbla_setup(torch, gb, "sigmoid", workload=workload, n_sets=2)
+    for i in range(warmup):
+        g["fwd"](i)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(runs):
+        t0 = time.perf_counter()
+        g["fwd"](i)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    ms = 1e3 * sum(times) / len(times)
+    return {"workload": workload, "tokens": g["T"], "forward_ms_mean": round(ms, 4), "runs": runs,
+            "forward_tokens_per_s": round(g["T"] / (ms / 1e3), 1),
+            "pages_h100_forward_ms": PAGES_FORWARD_MS.get(workload),
+            "note": "context only: the pages' figure is another machine, precision and layer boundary unstated"}
 
 
 def gbla_variant_leg(steps, warmup, gate="sigmoid", gated_output=False):
@@ -413,6 +462,15 @@ def main():
     }
     if args.lion_steps > 0:
         del g, step
+        torch.cuda.empty_cache()
+        out["gbla_B32_L1024_d256"] = gbla_workload_leg(args.lion_steps, min(args.warmup, 3),
+                                                        "gbla_bf16_B32_L1024_d256")
+        torch.cuda.empty_cache()
+        out["gbla_ragged_N256_d512"] = gbla_workload_leg(args.lion_steps, min(args.warmup, 3),
+                                                          "gbla_bf16_ragged_N256_d512")
+        torch.cuda.empty_cache()
+        out["forward_latency"] = [forward_latency_leg(wl) for wl in ("gbla_bf16_B8_L8192_d512",
+                                                                      "gbla_bf16_B8_L32768_d512")]
         torch.cuda.empty_cache()
         out["gbla_softmax"] = gbla_variant_leg(args.lion_steps, min(args.warmup, 3), gate="softmax")
         torch.cuda.empty_cache()

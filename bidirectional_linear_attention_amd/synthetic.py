@@ -84,6 +84,9 @@ WORKLOADS = {
     # long-history encoder: 8 x 8192 tokens, d=512, 8 heads, 10% repeated rows, gate bias +1
     "gbla_bf16_B8_L8192_d512": Workload("gbla_bf16_B8_L8192_d512", "gbla", "bf16", 512, 8, 64,
                                         lengths=(8192,) * 8, dup_frac=0.1, gate_bias=1.0, seed=2),
+    # the same recipe at the longest length of the latency benchmark: 8 x 32768 tokens
+    "gbla_bf16_B8_L32768_d512": Workload("gbla_bf16_B8_L32768_d512", "gbla", "bf16", 512, 8, 64,
+                                         lengths=(32768,) * 8, dup_frac=0.1, gate_bias=1.0, seed=5),
     # ragged packed batch: 256 lognormal lengths (median 600, sigma 1), clipped to [16, 32768]
     "gbla_bf16_ragged_N256_d512": Workload("gbla_bf16_ragged_N256_d512", "gbla", "bf16", 512, 8, 64,
                                            lengths=None, num_seqs=256, seed=3),
