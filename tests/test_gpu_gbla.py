@@ -137,6 +137,26 @@ def test_f32_forward_backward_multi_tile(lengths, d, H, dh):
     compare(make_inputs(w), backward=True, label="f32 " + str(lengths))
 
 
+def _seam_lengths(tile, tiles):
+    """Sequence lengths whose boundaries fall on every position from three tokens
+    before to two after each of `tiles` token-tile seams (multiples of `tile`),
+    plus a few longer sequences spanning whole tiles."""
+    bounds = sorted({k * tile + o for k in range(1, tiles + 1) for o in (-3, -2, -1, 0, 1, 2)})
+    cuts = [0] + bounds + [bounds[-1] + tile + 5]
+    return tuple(b - a for a, b in zip(cuts, cuts[1:]))
+
+
+@pytest.mark.parametrize("dtype,tile", [("f32", 64), ("bf16", 256)])
+def test_conv_backward_at_token_tile_seams(dtype, tile):
+    """The conv's backward runs in the dX~ GEMM's epilogue per token tile (64
+    tokens in float32, 256 in bf16); dx of a tile's last three tokens is formed
+    from the edge rows of two tiles. Sequence boundaries at every offset around
+    the seams check that the conv never reaches across a sequence there."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], _seam_lengths(tile, 3), d_model=96, num_heads=3,
+                      head_dim=32, dtype=dtype, seed=29)
+    compare(make_inputs(w), backward=True, label=f"{dtype} seams of {tile}-token tiles")
+
+
 # ------------------------------------------------------------ bf16, small versions of each workload
 
 def test_bf16_small_B32_recipe():
