@@ -21,6 +21,7 @@ typedef uint16_t bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
 

@@ -17,6 +17,9 @@
 //   k_state_partial split-L partial [S | z] per (chunk, head), MFMA over the token axis
 //   k_combine       fixed-order sum of the partials of each (sequence, head)
 //   k_readout       y = phi(Q) [S | z] (MFMA), divide
+#include <algorithm>
+#include <atomic>
+
 #include "gemm.h"
 #include "internal.h"
 
@@ -374,6 +377,106 @@ __global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS), 2) void k_proj
   }
 }
 
+// Persistent form for bf16: one block of 16 waves per CU walks 256 x 256 tiles
+// (256 rows of the packed panel of all heads x 256 tokens) with the k-chunk
+// pipeline running on from tile to tile (gemm_nt_dl_persistent). The tiles of
+// an XCD are consecutive logical ids, and consecutive ids share a token tile,
+// so the x~ tile is read from HBM once and its other row tiles hit the XCD's L2.
+// The epilogue stores through buffer stores (8 per wave per tile), which drop
+// rows past the last head and tokens past T.
+template <int DH, bool PHI, int NSEG>
+__global__ __launch_bounds__(512, 1) void k_proj_persistent(const bf16* __restrict__ xt, const bf16* __restrict__ wp,
+                                                             int T_, int d, int H, bf16* __restrict__ q_out,
+                                                             bf16* __restrict__ k_out, bf16* __restrict__ v_out,
+                                                             bf16* __restrict__ r_out) {
+  using S = DlShape<256, 256, 64, 2, 4, 2>;
+  constexpr int NP = NSEG * DH;
+  static_assert(S::WTM % 32 == 0 && NP % 32 == 0 && DH % 32 == 0, "32-row groups of one segment of one head");
+  __shared__ __align__(16) bf16 st0[S::STAGE];
+  __shared__ __align__(16) bf16 st1[S::STAGE];
+  const int R = H * NP, FT = (R + S::BM - 1) / S::BM, MT = (T_ + S::BN - 1) / S::BN, n = MT * FT;
+  const int D = H * DH;
+  auto coords = [&](int i, int& m0, int& f0) -> bool {
+    const int v = blockIdx.x + i * gridDim.x;  // gridDim.x % 8 == 0: the same XCD for every i
+    if (v >= xcd_grid(n)) return false;
+    const int l = xcd_logical_block(v, n);
+    if (l >= n) return false;
+    const int mt = l / FT;
+    m0 = mt * S::BN;
+    f0 = (l - mt * FT) * S::BM;
+    return true;
+  };
+  auto item = [&](int i, DlItem& it) -> bool {
+    int m0, f0;
+    if (!coords(i, m0, f0)) return false;
+    it.A = wp + (size_t)f0 * d;
+    it.ma = min(S::BM, R - f0);
+    it.B = xt + (size_t)m0 * d;
+    it.nb = min(S::BN, T_ - m0);
+    return true;
+  };
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / S::WGN, wn = w % S::WGN;
+  // lane (grp, col) holds, in tiles 2 i2 and 2 i2 + 1, features 8 grp .. 8 grp + 7
+  // of the wave's 32-row group i2 for token col of tile j
+  auto epi = [&](int i, f32x4(&acc)[S::FM][S::FN]) {
+    int m0 = 0, f0 = 0;
+    coords(i, m0, f0);
+    const int rows = min(S::BN, T_ - m0);
+#pragma unroll
+    for (int i2 = 0; i2 < S::FM / 2; ++i2) {
+      const int row = f0 + wm * S::WTM + 32 * i2;  // wave-uniform
+      const int h = row / NP, nn = row % NP, kind = nn / DH;
+      const bool lin = !PHI || kind >= 2;
+      bf16* out = kind == 0 ? q_out : (kind == 1 ? k_out : (kind == 2 ? v_out : r_out));
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(out + (size_t)m0 * D), 0, h < H ? rows * D * 2 : 0, kBufferRsrcWord3);
+      const int fo = h * DH + nn % DH + 8 * grp;
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j) {
+        const int t = wn * S::WTN + 16 * j + col;
+        float v[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = lin ? acc[2 * i2][j][r] : phi_elu1(acc[2 * i2][j][r]);
+          v[4 + r] = lin ? acc[2 * i2 + 1][j][r] : phi_elu1(acc[2 * i2 + 1][j][r]);
+        }
+        const uint4 u = frag_from<bf16>(v).v;
+        const u32x4 uv = {u.x, u.y, u.z, u.w};
+        __builtin_amdgcn_raw_buffer_store_b128(uv, ro, (t * D + fo) * 2, 0, 0);
+      }
+    }
+  };
+  gemm_nt_dl_persistent<S, S::FM / 2 * S::FN>(d, d, d, item, epi, st0, st1);
+}
+
+// compute units of the current device (cached per device)
+static int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// tiles of the persistent projection (256 tokens x 256 panel rows)
+static int proj_persistent_tiles(int T_, int rows) { return ((T_ + 255) / 256) * ((rows + 255) / 256); }
+
+template <int DH, bool PHI, int NSEG>
+static void proj_persistent(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, void* r,
+                            hipStream_t s) {
+  const int n = proj_persistent_tiles(T_, H * NSEG * DH);
+  if (n == 0) return;
+  const int grid = std::min(xcd_grid(n), std::max(8, device_cu_count() / 8 * 8));
+  hipLaunchKernelGGL((k_proj_persistent<DH, PHI, NSEG>), dim3(grid), dim3(512), 0, s, (const bf16*)xt,
+                     (const bf16*)wp, T_, d, H, (bf16*)q, (bf16*)k, (bf16*)v, (bf16*)r);
+}
+
 template <typename T, int DH, bool PHI, int NSEG>
 static void proj_t(const void* xt, const void* wp, int T_, int d, int H, void* q, void* k, void* v, void* r,
                    hipStream_t s) {
@@ -391,6 +494,19 @@ void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, i
   (r_out ? proj_t<TT, DD, true, 4>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)      \
          : (phi ? proj_t<TT, DD, true, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s) \
                 : proj_t<TT, DD, false, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)))
+  // the persistent form needs d % 128 == 0 (whole pairs of 64-deep chunks) and
+  // pays off from about three tiles per compute unit (with fewer, the last
+  // round leaves compute units idle; 192 x 128 tiles balance better there)
+  const int rows = H * (r_out ? 4 : 3) * dh;
+  if (dt == BF16 && d % 128 == 0 && proj_persistent_tiles(T, rows) >= 3 * device_cu_count()) {
+#define GBLA_PP(DD)                                                                                \
+  (r_out ? proj_persistent<DD, true, 4>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)            \
+         : (phi ? proj_persistent<DD, true, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)     \
+                : proj_persistent<DD, false, 3>(xt, wp, T, d, H, q_out, k_out, v_out, r_out, s)))
+    if (dh == 64) GBLA_PP(64); else GBLA_PP(32);
+#undef GBLA_PP
+    return;
+  }
   if (dt == BF16) { if (dh == 64) GBLA_PJ(bf16, 64); else GBLA_PJ(bf16, 32); }
   else            { if (dh == 64) GBLA_PJ(float, 64); else GBLA_PJ(float, 32); }
 #undef GBLA_PJ

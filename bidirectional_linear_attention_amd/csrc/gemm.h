@@ -341,6 +341,125 @@ __device__ __forceinline__ void gemm_nt_dl(const bf16* __restrict__ A, int lda, 
   __syncthreads();  // the stages may be reused by the caller
 }
 
+// ---------------------------------------------------------------- persistent NT loop, direct-to-LDS (bf16)
+// Operands of one work item (one C tile) of a persistent NT GEMM: A rows
+// [0, ma) and B rows [0, nb), k in [0, K); the pitches are fixed per launch.
+struct DlItem {
+  const bf16* A;
+  const bf16* B;
+  int ma, nb;
+};
+
+// One block per CU walks its work items in order (item(i, it) fills `it` and
+// returns false past the block's last item). The two-stage k-chunk pipeline of
+// gemm_nt_dl runs on across items: the first chunk of the next item is loaded
+// while the last chunk of the current one is multiplied and while the
+// epilogue's stores leave, so a tile pays no pipeline fill. Chunks go in pairs,
+// the first of a pair to st0, the second to st1: with compile-time stages the
+// wait-count pass sees that the loads in flight into one stage do not alias the
+// reads of the other. K % (2 BK) == 0 and K <= lda, ldb: a lane's offset within
+// a chunk is the same for every item and chunk (the chunk's k goes in the
+// scalar offset), and rows past ma / nb fall outside the buffer range and read
+// as zero. The epilogue, epi(i, acc), must issue exactly NST vector-memory
+// instructions per wave (buffer stores, whose range check drops what falls
+// outside): the wait for the next item's first chunk lets those NST complete later.
+template <class S, int NST, class ItemFn, class Epi>
+__device__ __forceinline__ void gemm_nt_dl_persistent(int K, int lda, int ldb, ItemFn item, Epi epi, bf16* st0,
+                                                      bf16* st1) {
+  static_assert(S::NS == 2, "two stages");
+  static_assert(NST < 64, "vmcnt range");
+  static_assert(S::LA % S::NWAVES == 0 && S::LB % S::NWAVES == 0, "whole wave loads of A and of B per wave");
+  constexpr int CPR = S::CPR, RPL = S::RPL, JA = S::LA / S::NWAVES, JB = S::LB / S::NWAVES;
+  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / S::WGN, wn = w % S::WGN;
+  unsigned offa[JA], offb[JB];  // this lane's byte offset in wave load j of a chunk at k = 0
+#pragma unroll
+  for (int j = 0; j < JA; ++j) {
+    const int r = (w + S::NWAVES * j) * RPL + lane / CPR;
+    offa[j] = (unsigned)(r * lda + 8 * dl_swizzle<CPR>(r, lane % CPR)) * 2u;
+  }
+#pragma unroll
+  for (int j = 0; j < JB; ++j) {
+    const int r = (w + S::NWAVES * j) * RPL + lane / CPR;
+    offb[j] = (unsigned)(r * ldb + 8 * dl_swizzle<CPR>(r, lane % CPR)) * 2u;
+  }
+  auto issue = [&](const DlItem& it, bf16* base, int k0) {
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)it.A, 0, it.ma * lda * 2, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)it.B, 0, it.nb * ldb * 2, kBufferRsrcWord3);
+#pragma unroll
+    for (int j = 0; j < JA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dl_lds_void*)(base + (w + S::NWAVES * j) * RPL * S::BK), 16,
+                                               offa[j], 2 * k0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (dl_lds_void*)(base + S::BM * S::BK + (w + S::NWAVES * j) * RPL * S::BK), 16, offb[j], 2 * k0, 0, 0);
+  };
+  f32x4 acc[S::FM][S::FN];
+  auto compute = [&](const bf16* buf) {
+    const bf16* As = buf;
+    const bf16* Bs = buf + S::BM * S::BK;
+#pragma unroll
+    for (int ks = 0; ks < S::BK / 32; ++ks) {
+      Frag8<bf16> a[S::FM];
+#pragma unroll
+      for (int i = 0; i < S::FM; ++i) {
+        const int r = wm * S::WTM + 16 * i + col;
+        a[i] = frag_load(As + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
+      }
+#pragma unroll
+      for (int j = 0; j < S::FN; ++j) {
+        const int r = wn * S::WTN + 16 * j + col;
+        const Frag8<bf16> b = frag_load(Bs + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
+#pragma unroll
+        for (int i = 0; i < S::FM; ++i) mma8(acc[i][j], a[i], b);
+      }
+    }
+  };
+
+  const int nk = K / S::BK;
+  DlItem cur, nxt;
+  if (nk == 0 || !item(0, cur)) return;
+  issue(cur, st0, 0);
+  __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
+  __syncthreads();
+  for (int i = 0;; ++i) {
+    const bool more = item(i + 1, nxt);
+#pragma unroll
+    for (int a = 0; a < S::FM; ++a)
+#pragma unroll
+      for (int b = 0; b < S::FN; ++b) acc[a][b] = zero4();
+    for (int c = 0; c < nk; c += 2) {
+      if (c > 0) {
+        __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));  // this wave's loads of chunk c are done
+        __syncthreads();  // every wave's loads of chunk c are in LDS; every wave is done with chunk c - 1
+      }
+      issue(cur, st1, (c + 1) * S::BK);
+      __builtin_amdgcn_sched_barrier(0);  // the loads leave before the multiplies, not after them
+      compute(st0);
+      __builtin_amdgcn_sched_barrier(0);  // and the multiplies stay ahead of the wait
+      __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
+      __syncthreads();
+      if (c + 2 < nk)
+        issue(cur, st0, (c + 2) * S::BK);
+      else if (more)
+        issue(nxt, st0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(st1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    epi(i, acc);
+    if (!more) break;
+    cur = nxt;
+    // the next item's first chunk is in: behind its loads only this item's NST stores may be in flight
+    __builtin_amdgcn_s_waitcnt(dl_vmcnt(NST));
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------- TN main loop, direct-to-LDS (bf16)
 // Same contract as gemm_tn_mainloop for bf16: A [K][lda] and B [K][ldb] are
 // k-major (token-major). LDS tiles keep that layout (row = k, BM or BN columns,

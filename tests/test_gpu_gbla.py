@@ -186,6 +186,19 @@ def test_bf16_d_model_not_a_multiple_of_32(d, H, dh):
     compare(make_inputs(w), backward=True, label=f"bf16 d={d} H={H} dh={dh}")
 
 
+@pytest.mark.parametrize("outg", [False, True])
+def test_bf16_projection_tiles_past_one_per_block(outg):
+    """d % 128 == 0 in bf16 with at least three 256 x 256 tiles per compute
+    unit runs the persistent projection: each block walks several tiles. 3
+    heads of 64 make 576 (or, with the gated output's R rows, 768) panel rows,
+    so the last row tile is partial when 576; 66003 tokens make 258 token
+    tiles, the last one partial."""
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], (40000, 1, 17001, 9001), d_model=128, num_heads=3,
+                      head_dim=64, seed=27)
+    compare(make_inputs(w), backward=True, label=f"bf16 persistent projection outg={outg}",
+            outg=_outg(w) if outg else None)
+
+
 def test_bf16_wide_model_many_heads():
     """d > 512 and H > 8 in bf16: two channel groups in the conv kernels, two
     head groups of gate logits, and 9 k-chunks in the projection GEMM."""
