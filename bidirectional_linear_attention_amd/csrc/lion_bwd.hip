@@ -175,23 +175,33 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
   const T* img = hrows + ((size_t)slot * H + h) * 2 * (DH * DH);
   const float* ext = hst + ((size_t)slot * H + h) * 2 * E + DH * DH;
-  float zdot = 0.f;  // this thread's terms of <SF, HB> + <HF, SB> (fp32 S; H as the scan rounded it)
-  {
-    StateRegs<DH> sf;
-    ImageRegs<T, DH> hb;
-    state_rows_load<DH>(sf, sp, tid);
-    image_rows_load<T, DH>(hb, img + DH * DH, ext + E, tid);
-    zdot += state_image_dot<T, DH>(sf, hb, tid);
-    state_rows_store<T, DH>(sf, SFs, LDR, xF, tid);
+  // every global load of the phase is issued before any of it is used: the
+  // token tiles, then the four states, so the phase pays one memory latency
+  Frag8<T> fq[NV], fk[NV], fv[NV], fd[NV], fy[NV];
+  float rinv[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int it = tid + 256 * v;
+    const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
+    const bool ok = it < C * V8 && t < ch.end;
+    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+    fq[v] = ok ? frag_load(qr + o) : frag_zero<T>();
+    fk[v] = ok ? frag_load(kr + o) : frag_zero<T>();
+    fv[v] = ok ? frag_load(vr + o) : frag_zero<T>();
+    fd[v] = ok ? frag_load(dy + o) : frag_zero<T>();
+    fy[v] = ok ? frag_load(yv + o) : frag_zero<T>();
+    rinv[v] = ok ? rsum[(size_t)t * H + h] : 1.f;
   }
-  {
-    StateRegs<DH> sb;
-    ImageRegs<T, DH> hf;
-    state_rows_load<DH>(sb, sp + E, tid);
-    image_rows_load<T, DH>(hf, img, ext, tid);
-    zdot += state_image_dot<T, DH>(sb, hf, tid);
-    state_rows_store<T, DH>(sb, SBs, LDR, xB, tid);
-  }
+  StateRegs<DH> sf, sb;
+  ImageRegs<T, DH> hb, hf;
+  state_rows_load<DH>(sf, sp, tid);
+  image_rows_load<T, DH>(hb, img + DH * DH, ext + E, tid);
+  state_rows_load<DH>(sb, sp + E, tid);
+  image_rows_load<T, DH>(hf, img, ext, tid);
+  // this thread's terms of <SF, HB> + <HF, SB> (fp32 S; H as the scan rounded it)
+  float zdot = state_image_dot<T, DH>(sf, hb, tid) + state_image_dot<T, DH>(sb, hf, tid);
+  state_rows_store<T, DH>(sf, SFs, LDR, xF, tid);
+  state_rows_store<T, DH>(sb, SBs, LDR, xB, tid);
   zdot = add_xor32(add_xor16(row16_sum(zdot)));
   if (lane == 0) zpart[w] = zdot;
 #pragma unroll
@@ -200,29 +210,24 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
     if (it >= C * V8) continue;
     const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
     const bool ok = t < ch.end;
-    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
     float u[8], p[8];
-    Frag8<T> f = ok ? frag_load(qr + o) : frag_zero<T>();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(fq[v], j);
     float n = phi_lion8<V8>(u, p, ok);
     frag_store(Qs + r * LDR + c, frag_from<T>(p));
     if (c == 0) nq[r] = ok ? n : 1.f;
-    f = ok ? frag_load(kr + o) : frag_zero<T>();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(fk[v], j);
     n = phi_lion8<V8>(u, p, ok);
     frag_store(Ks + r * LDR + c, frag_from<T>(p));
     if (c == 0) nk[r] = ok ? n : 1.f;
-    frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
-    const Frag8<T> fd = ok ? frag_load(dy + o) : frag_zero<T>();
-    const Frag8<T> fy = ok ? frag_load(yv + o) : frag_zero<T>();
-    const float inv = ok ? fast_rcp(rsum[(size_t)t * H + h]) : 0.f;
+    frag_store(Vs + r * LDR + c, fv[v]);
+    const float inv = ok ? fast_rcp(rinv[v]) : 0.f;
     float g[8], dd = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      g[j] = frag_get(fd, j) * inv;
-      dd += frag_get(fd, j) * frag_get(fy, j);
+      g[j] = frag_get(fd[v], j) * inv;
+      dd += frag_get(fd[v], j) * frag_get(fy[v], j);
     }
     dd = lane_group_sum<V8>(dd);
     frag_store(Gs + r * LDR + c, frag_from<T>(g));

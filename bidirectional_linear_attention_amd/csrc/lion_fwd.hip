@@ -66,30 +66,44 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
     const int r = e >> 4, c = e & 15;
     if (MODE == 0 || c > 0) Vs[r * LDC + DH + c] = from_f<T>(MODE == 0 && c == 0 && ch.start + r < ch.end ? 1.f : 0.f);
   }
+  // every load of the staging is issued before any of it is used
+  Frag8<T> fr[NV], fv[NV], fy[NV];
+  float rs[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int it = tid + 256 * v;
+    const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
+    const bool ok = it < C * V8 && t < ch.end;
+    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+    fr[v] = ok ? frag_load(rsrc + o) : frag_zero<T>();
+    fv[v] = ok ? frag_load(vsrc + o) : frag_zero<T>();
+    if (MODE == 1) {
+      fy[v] = ok ? frag_load(ysrc + o) : frag_zero<T>();
+      rs[v] = ok ? rsum[(size_t)t * H + h] : 1.f;
+    }
+  }
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int it = tid + 256 * v;
     if (it >= C * V8) continue;
     const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
     const bool ok = t < ch.end;
-    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
     float u[8], p[8];
-    const Frag8<T> fr = ok ? frag_load(rsrc + o) : frag_zero<T>();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = frag_get(fr, j);
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(fr[v], j);
     phi_lion8<V8>(u, p, ok);
     frag_store(Rs + r * LDR + c, frag_from<T>(p));
     if (MODE == 0) {
-      frag_store(Vs + r * LDC + c, ok ? frag_load(vsrc + o) : frag_zero<T>());
+      frag_store(Vs + r * LDC + c, fv[v]);
     } else {  // g^ from dy (vsrc), y (ysrc) and the row sum r
-      const Frag8<T> fd = ok ? frag_load(vsrc + o) : frag_zero<T>();
-      const Frag8<T> fy = ok ? frag_load(ysrc + o) : frag_zero<T>();
-      const float inv = ok ? fast_rcp(rsum[(size_t)t * H + h]) : 0.f;
+      const Frag8<T> fd = fv[v];
+      const Frag8<T> fy1 = fy[v];
+      const float inv = ok ? fast_rcp(rs[v]) : 0.f;
       float g[8], dd = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         g[j] = frag_get(fd, j) * inv;
-        dd += frag_get(fd, j) * frag_get(fy, j);
+        dd += frag_get(fd, j) * frag_get(fy1, j);
       }
       dd = lane_group_sum<V8>(dd);
       frag_store(Vs + r * LDC + c, frag_from<T>(g));
@@ -298,6 +312,19 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
   const int ct = w / WPC, rt0 = (w % WPC) * RTW;
   const float la = chunk_decay_load<C>(logl, ch, H, h, tid);
 
+  // the token tiles' loads are all issued first, then the states' (nothing
+  // waits on a load before every load of the staging is in flight)
+  Frag8<T> fq[NV], fk[NV], fv[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int it = tid + 256 * v;
+    const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
+    const bool ok = it < C * V8 && t < ch.end;
+    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+    fq[v] = ok ? frag_load(qr + o) : frag_zero<T>();
+    fk[v] = ok ? frag_load(kr + o) : frag_zero<T>();
+    fv[v] = ok ? frag_load(vr + o) : frag_zero<T>();
+  }
   // this wave's slice of the carried states: column n = 16 ct + col, rows a = 32 s + 8 grp .. + 7
   const float* sp = st + ((size_t)slot * H + h) * 2 * E;
   float4 sv[2][KS][2];
@@ -319,19 +346,16 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
     if (it >= C * V8) continue;
     const int r = it / V8, c = (it % V8) * 8, t = ch.start + r;
     const bool ok = t < ch.end;
-    const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
     float u[8], p[8];
-    Frag8<T> f = ok ? frag_load(qr + o) : frag_zero<T>();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(fq[v], j);
     phi_lion8<V8>(u, p, ok);
     frag_store(Qs + r * LDR + c, frag_from<T>(p));
-    f = ok ? frag_load(kr + o) : frag_zero<T>();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) u[j] = frag_get(f, j);
+    for (int j = 0; j < 8; ++j) u[j] = frag_get(fk[v], j);
     phi_lion8<V8>(u, p, ok);
     frag_store(Ks + r * LDR + c, frag_from<T>(p));
-    frag_store(Vs + r * LDR + c, ok ? frag_load(vr + o) : frag_zero<T>());
+    frag_store(Vs + r * LDR + c, fv[v]);
   }
   chunk_decay_scan<C>(la, As, &Ls, tid);
   __syncthreads();
