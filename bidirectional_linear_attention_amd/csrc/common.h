@@ -437,12 +437,18 @@ __device__ __forceinline__ void stage_state(T* MT, T* MR, int ld, const float* _
   }
   if (MR) {
     constexpr int V4 = DH * DH / 4, PER = (V4 + NT - 1) / NT;
+    float4 rv[PER];  // every load is issued before the first conversion
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int e4 = tid + k * NT;
+      rv[k] = e4 < V4 ? reinterpret_cast<const float4*>(M)[e4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int e4 = tid + k * NT;
       if (e4 >= V4) continue;
       const int i = (4 * e4) / DH, n = (4 * e4) % DH;
-      const float4 r = reinterpret_cast<const float4*>(M)[e4];
+      const float4 r = rv[k];
       const float v[4] = {r.x, r.y, r.z, r.w};
       T hi[4], lo[4];
 #pragma unroll

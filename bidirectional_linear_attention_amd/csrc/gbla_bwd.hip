@@ -83,11 +83,25 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
+  constexpr int NV = (ST * V8 + 255) / 256;
+  Frag8<T> pq[NV], py[NV], pr[NV];
+  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
+      const bool ok = it < ST * V8 && t < ch.end;
+      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
+      pq[v] = ok ? frag_load(qa + o) : frag_zero<T>();
+      py[v] = ok ? frag_load(dy + o) : frag_zero<T>();
+      if constexpr (GATED) pr[v] = ok ? frag_load(ra + o) : frag_zero<T>();
+    }
+  };
+  fetch(ch.start);  // the first tile loads while the state is staged
   stage_state<T, DH, NR>(Sst, nullptr, LDT, st, st + DH * DH, tid);
   __syncthreads();  // the state's low-part rows past dh that overlap the q~ tile are written before it
   for (int e = tid; e < DH; e += 256) zs[e] = st[DH * DH + e];
@@ -105,20 +119,6 @@ __global__ __launch_bounds__(256) void k_bwd_dstate(const T* __restrict__ qa, co
   if constexpr (GATED)
     for (int e = tid; e < DH; e += 256) gms[e] = gamma ? gamma[e] : 1.f;
 
-  constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pq[NV], py[NV], pr[NV];
-  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
-      const bool ok = it < ST * V8 && t < ch.end;
-      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      pq[v] = ok ? frag_load(qa + o) : frag_zero<T>();
-      py[v] = ok ? frag_load(dy + o) : frag_zero<T>();
-      if constexpr (GATED) pr[v] = ok ? frag_load(ra + o) : frag_zero<T>();
-    }
-  };
-  fetch(ch.start);
   for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -328,13 +328,11 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = dsz + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, DH>(nullptr, Srm, LDS_, st, st + DH * DH, tid);
-  for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
 
   float dbg = 0.f;
   const int gs0 = nseg * D, gcol0 = gs0 + H;  // gate column of head 0; first padding column of G
@@ -354,8 +352,10 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
     }
     if (tid < ST) pg = tb + tid < ch.end ? ga[(size_t)(tb + tid) * H + h] : 0.f;  // gate or softmax logit
   };
-  fetch(ch.start);
+  fetch(ch.start);  // the first tile loads while dS is staged
   const float gm = SOFTMAX ? gmax[(size_t)ch.seq * H + h] : 0.f;  // softmax gate: exp(s - largest logit)
+  stage_state<T, DH, DH>(nullptr, Srm, LDS_, st, st + DH * DH, tid);
+  for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
   for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {

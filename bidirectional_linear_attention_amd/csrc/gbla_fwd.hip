@@ -383,10 +383,11 @@ __global__ __launch_bounds__((ProjCfg<T, DH, NSEG>::S::NTHREADS), 2) void k_proj
 // an XCD are consecutive logical ids, and consecutive ids share a token tile,
 // so the x~ tile is read from HBM once and its other row tiles hit the XCD's L2.
 // The epilogue stores through buffer stores (16 per wave per tile), which drop
-// rows past the last head and tokens past T. They are non-temporal: otherwise
-// the tile's 128 KB of outputs push the x~ tiles that the other row tiles of
-// the same token tile are about to read out of the XCD's L2 (x~ was read 2.3
-// times from beyond the L2, 1.3 times with these stores).
+// rows past the last head and tokens past T. (The tiles' outputs push x~ tiles
+// out of the XCD's L2 before every row tile of them has read them: x~ is read
+// 2.3 times from beyond the L2. Non-temporal stores cut that to 1.3 but made
+// the kernel slower, 513 -> 590 us on a 267k-token batch: the half-line stores
+// of a wave then reach memory uncombined.)
 template <int DH, bool PHI, int NSEG>
 __global__ __launch_bounds__(512, 1) void k_proj_persistent(const bf16* __restrict__ xt, const bf16* __restrict__ wp,
                                                              int T_, int d, int H, bf16* __restrict__ q_out,
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(512, 1) void k_proj_persistent(const bf16* __restri
         }
         const uint4 u = frag_from<bf16>(v).v;
         const u32x4 uv = {u.x, u.y, u.z, u.w};
-        __builtin_amdgcn_raw_buffer_store_b128(uv, ro, (t * D + fo) * 2, 0, kBufferNonTemporal);
+        __builtin_amdgcn_raw_buffer_store_b128(uv, ro, (t * D + fo) * 2, 0, 0);
       }
     }
   };
@@ -543,8 +544,8 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   for (int e = tid; e < ST * 16; e += 256) {  // ones column (z) and zero padding of the last block
@@ -748,12 +749,11 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const float* st = saved + ((size_t)ch.seq * H + h) * E;
-  stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid);
   const int r0 = 16 * w;
   float gam[FB];  // RMSNorm scale of the lane's features 16 nt + col
 #pragma unroll
@@ -771,7 +771,8 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
       if constexpr (GATED) pr[v] = ok ? frag_load(ra + (size_t)t * D + h * DH + c) : frag_zero<T>();
     }
   };
-  fetch(ch.start);
+  fetch(ch.start);  // the first tile loads while the state is staged
+  stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid);
   for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {

@@ -263,8 +263,6 @@ __host__ __device__ constexpr int dl_vmcnt(int n) { return (n & 15) | (7 << 4) |
 
 typedef __attribute__((address_space(3))) void dl_lds_void;
 constexpr int kBufferRsrcWord3 = 0x00020000;
-// cache-policy operand of a buffer store: non-temporal (streaming) data
-constexpr int kBufferNonTemporal = 2;
 
 // st[s] are NS distinct LDS arrays of S::STAGE elements (distinct objects let the
 // compiler tell the stages apart when it orders LDS reads after LDS-DMA loads)

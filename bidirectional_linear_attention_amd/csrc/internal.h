@@ -70,6 +70,16 @@ struct Sched {
   Chunk* tab;
 };
 
+// The chunk of a (chunk, head) block: the count and the entry are loaded
+// together rather than one after the other (slot < max_slots, the table's
+// size, so the entry load stays inside the table even past the count).
+__device__ __forceinline__ bool block_chunk(const int* __restrict__ nchunks, const Chunk* __restrict__ tab, int slot,
+                                            Chunk& ch) {
+  const int nc = *nchunks;
+  ch = tab[slot];
+  return slot < nc;
+}
+
 // ---- the chunk table (run by one block of NT threads)
 // Sequences are taken NT at a time: thread b reads its offsets once, the chunk
 // counts are prefix-summed with wave shuffles plus one pass over the wave

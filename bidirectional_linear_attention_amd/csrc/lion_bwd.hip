@@ -164,8 +164,8 @@ __global__ __launch_bounds__(256, 2) void k_lion_bwd_token(
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const int r0 = 16 * w;
@@ -491,8 +491,8 @@ __global__ __launch_bounds__(256) void k_lion_da(const float* __restrict__ logl,
                                                  int write_da, T* __restrict__ G, float* __restrict__ db_part) {
   constexpr int C = kLionChunk;
   const int slot = blockIdx.x;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t = ch.start + lane;
   const bool ok = t < ch.end;

@@ -56,8 +56,8 @@ __global__ __launch_bounds__(256) void k_lion_chunk_state(const T* __restrict__ 
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, grp = lane >> 4;
   const int D = H * DH;
 
@@ -305,8 +305,8 @@ __global__ __launch_bounds__(256) void k_lion_readout(const T* __restrict__ qr, 
   const int lid = xcd_logical_block(blockIdx.x, max_slots * H);
   if (lid >= max_slots * H) return;
   const int slot = lid / H, h = lid - slot * H;
-  if (slot >= *nchunks) return;
-  const Chunk ch = tab[slot];
+  Chunk ch;
+  if (!block_chunk(nchunks, tab, slot, ch)) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, col = lane & 15, grp = lane >> 4;
   const int D = H * DH;
   const int ct = w / WPC, rt0 = (w % WPC) * RTW;
