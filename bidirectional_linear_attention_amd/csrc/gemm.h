@@ -341,112 +341,6 @@ __device__ __forceinline__ void gemm_nt_dl(const bf16* __restrict__ A, int lda, 
   __syncthreads();  // the stages may be reused by the caller
 }
 
-// ---------------------------------------------------------------- NT main loop, direct-to-LDS, software-pipelined reads
-// Same contract as gemm_nt_dl with two 64-deep stages, for wave tiles large
-// enough that the LDS operand reads, not the MFMAs, would otherwise set the
-// pace (128 x 64 per wave: a quarter fewer LDS bytes per MFMA than 64 x 64).
-// The operand reads of each 32-deep k-step are issued one k-step ahead, into a
-// second register set, so they run under the MFMAs of the step before:
-//   k-step 0 of chunk c: read k-step 1 of c; multiply k-step 0;
-//   then wait for chunk c + 1's loads and barrier (every wave has read all of
-//   chunk c's stage), issue chunk c + 2 into that stage, read k-step 0 of c + 1;
-//   k-step 1 of chunk c: multiply.
-// The chunk loop is unrolled by two so that both stages are compile-time
-// arrays (the wait-count pass then sees that the loads in flight into one
-// stage do not alias the reads of the other).
-template <class S>
-__device__ __forceinline__ void gemm_nt_dl_pipe(const bf16* __restrict__ A, int lda, int ma, const bf16* __restrict__ B,
-                                                int ldb, int nb, int K, bf16* st0, bf16* st1,
-                                                f32x4 (&acc)[S::FM][S::FN]) {
-  static_assert(S::NS == 2 && S::BK == 64, "two 64-deep stages");
-  constexpr int CPR = S::CPR, RPL = S::RPL;
-  const int lane = threadIdx.x & 63, col = lane & 15, grp = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = w / S::WGN, wn = w % S::WGN;
-#pragma unroll
-  for (int i = 0; i < S::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j) acc[i][j] = zero4();
-
-  const __amdgpu_buffer_rsrc_t ra =
-      __builtin_amdgcn_make_buffer_rsrc((void*)A, 0, ma > 0 ? (ma - 1) * lda * 2 + K * 2 : 0, kBufferRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)B, 0, nb > 0 ? (nb - 1) * ldb * 2 + K * 2 : 0, kBufferRsrcWord3);
-  const int rr = lane / CPR, pp = lane % CPR;
-  auto issue = [&](bf16* base, int k0) {
-#pragma unroll
-    for (int j = 0; j < S::LPW; ++j) {
-      const int li = w + S::NWAVES * j;  // wave-uniform
-      if (!S::EVEN && li >= S::LA + S::LB) break;
-      const bool isA = li < S::LA;
-      const int r = (isA ? li : li - S::LA) * RPL + rr;
-      const int k = k0 + 8 * dl_swizzle<CPR>(r, pp);
-      const int ld = isA ? lda : ldb, rows = isA ? ma : nb;
-      const unsigned off = (r < rows && k < K) ? (unsigned)(r * ld + k) * 2u : 0x80000000u;
-      bf16* dst = base + (isA ? li * RPL * S::BK : S::BM * S::BK + (li - S::LA) * RPL * S::BK);
-      if (isA)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (dl_lds_void*)dst, 16, off, 0, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (dl_lds_void*)dst, 16, off, 0, 0, 0);
-    }
-  };
-  auto read = [&](const bf16* buf, int ks, Frag8<bf16> (&a)[S::FM], Frag8<bf16> (&b)[S::FN]) {
-    const bf16* As = buf;
-    const bf16* Bs = buf + S::BM * S::BK;
-#pragma unroll
-    for (int i = 0; i < S::FM; ++i) {
-      const int r = wm * S::WTM + 16 * i + col;
-      a[i] = frag_load(As + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
-    }
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j) {
-      const int r = wn * S::WTN + 16 * j + col;
-      b[j] = frag_load(Bs + r * S::BK + 8 * dl_swizzle<CPR>(r, 4 * ks + grp));
-    }
-  };
-  auto mma = [&](const Frag8<bf16> (&a)[S::FM], const Frag8<bf16> (&b)[S::FN]) {
-#pragma unroll
-    for (int j = 0; j < S::FN; ++j)
-#pragma unroll
-      for (int i = 0; i < S::FM; ++i) mma8(acc[i][j], a[i], b[j]);
-  };
-
-  const int nk = (K + S::BK - 1) / S::BK;
-  if (nk == 0) return;
-  Frag8<bf16> a0[S::FM], b0[S::FN], a1[S::FM], b1[S::FN];
-  issue(st0, 0);
-  if (nk > 1) {
-    issue(st1, S::BK);
-    __builtin_amdgcn_s_waitcnt(dl_vmcnt(S::LPW));  // chunk 0's loads of this wave are done
-  } else {
-    __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));
-  }
-  __syncthreads();
-  read(st0, 0, a0, b0);
-  // one chunk: x = its stage, y = the other; on entry chunk c is visible in x
-  // and its k-step 0 operands are in (a0, b0)
-  auto step = [&](bf16* x, bf16* y, int c) {
-    read(x, 1, a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a0, b0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < nk) {
-      __builtin_amdgcn_s_waitcnt(dl_vmcnt(0));  // this wave's loads of chunk c + 1 are done
-      __syncthreads();  // every wave's loads of c + 1 are in LDS; every wave has read all of chunk c
-      if (c + 2 < nk) issue(x, (c + 2) * S::BK);
-      read(y, 0, a0, b0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    mma(a1, b1);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  for (int c = 0; c < nk; c += 2) {
-    step(st0, st1, c);
-    if (c + 1 < nk) step(st1, st0, c + 1);
-  }
-  __syncthreads();  // the stages may be reused by the caller
-}
-
 // ---------------------------------------------------------------- persistent NT loop, direct-to-LDS (bf16)
 // Operands of one work item (one C tile) of a persistent NT GEMM: A rows
 // [0, ma) and B rows [0, nb), k in [0, K); the pitches are fixed per launch.
