@@ -243,6 +243,13 @@ def test_bf16_ragged_N256_d512_full():
     compare(make_inputs(w), backward=True, label=w.name)
 
 
+def test_bf16_B8_L8192_head_dim_32_full():
+    """The long-history batch with 16 heads of 32: the persistent projection
+    with the panels of 16 heads in six 256-row tiles (1536 tiles, six per compute unit)."""
+    w = small_variant(WORKLOADS["gbla_bf16_B8_L8192_d512"], (8192,) * 8, num_heads=16, head_dim=32, seed=33)
+    compare(make_inputs(w), backward=True, label="bf16 B=8 L=8192 d=512 H=16 dh=32")
+
+
 # ------------------------------------------------------------ properties of the GPU path itself
 
 def _small_bf16():
