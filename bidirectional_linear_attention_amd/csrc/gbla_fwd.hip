@@ -739,7 +739,10 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
                                                  const float* __restrict__ gamma, float eps) {
   constexpr int FB = DH / 16;
   constexpr int NR = DH + 16;
-  constexpr int LD = DH + 16 / (int)sizeof(T);
+  // 40-dword rows for bf16 (d_h = 64): the 16-byte operand reads of 16
+  // consecutive rows hit distinct banks (at 36 dwords, 61% of the kernel's LDS
+  // cycles were bank conflicts)
+  constexpr int LD = sizeof(T) == 2 ? DH + 16 : DH + 4;
   constexpr int P = SplitState<T>::parts;
   constexpr int E = DH * DH + DH;
   constexpr int ST = 64, V8 = DH / 8;
