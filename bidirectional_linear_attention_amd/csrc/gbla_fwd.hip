@@ -80,14 +80,19 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 }
 
 // ============================================================== causal conv + gate
-// A wave owns 32 consecutive token rows (128 per block); lane l owns channel
+// A wave owns RUN consecutive token rows (4 RUN per block); lane l owns channel
 // groups c = 8 * (l + 64 m). The rows stream through two register batches of
 // 4 (the next batch loads while the current one is computed and stored), and
 // the three previous rows slide in registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
 // reduce-scatter butterfly (butterfly8): 8 head partials per lane become one
 // head total per 8 lanes in 4 + 2 lane-half swaps and 4 DPP adds.
-constexpr int kConvRowsPerWave = 32;
+// RUN = 32 rows per wave; with fewer than 2048 such waves (T < 65 536), 8 rows,
+// so that a small batch still puts several waves on every SIMD
+constexpr int kConvRowsPerWave = 32, kConvRowsPerWaveSmall = 8;
 constexpr int kConvBatchRows = 4;
+inline int conv_rows_per_wave(int T) {
+  return (T + kConvRowsPerWave - 1) / kConvRowsPerWave >= 2048 ? kConvRowsPerWave : kConvRowsPerWaveSmall;
+}
 
 // sum of the 8 products of two fragments (bf16: four packed dot2 instructions)
 template <typename T> __device__ __forceinline__ float gate_dot8(const Frag8<T>& a, const Frag8<T>& b);
@@ -143,12 +148,12 @@ __device__ __forceinline__ float log_sigmoidf_(float z) { return fminf(z, 0.f) -
 // sigmoid key gate), z itself (gmode 1, the logit of the softmax key gate) or
 // log sigmoid(z) (gmode 2, the LION-s log decay).
 enum GateMode { kGateSigmoid = 0, kGateLogit = 1, kGateLogSigmoid = 2 };
-template <typename T, bool CONV = true>
+template <typename T, bool CONV, int RUN>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
                                                   int gmode, T* __restrict__ xt, float* __restrict__ g_out) {
-  constexpr int RUN = kConvRowsPerWave, B = kConvBatchRows;
+  constexpr int B = kConvBatchRows;
   __shared__ float sacc[4][RUN][8];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t_begin = (blockIdx.x * 4 + w) * RUN;
@@ -242,29 +247,35 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
                      const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s) {
   const int gmode = softmax_gate ? kGateLogit : kGateSigmoid;
-  const int rows = 4 * kConvRowsPerWave;
-  const dim3 grid((T + rows - 1) / rows);
   if (T == 0) return;
-  if (dt == BF16)
-    hipLaunchKernelGGL((k_conv_fwd<bf16, true>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
-                       (const bf16*)conv_w, (const bf16*)w_g, b_g, gmode, (bf16*)xt, g);
-  else
-    hipLaunchKernelGGL((k_conv_fwd<float, true>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
-                       (const float*)conv_w, (const float*)w_g, b_g, gmode, (float*)xt, g);
+  const int run = conv_rows_per_wave(T);
+  const dim3 grid((T + 4 * run - 1) / (4 * run));
+#define GBLA_CF(TT, RR)                                                                                  \
+  hipLaunchKernelGGL((k_conv_fwd<TT, true, RR>), grid, dim3(256), 0, s, (const TT*)x, cu, N, T, d, H,  \
+                     (const TT*)conv_w, (const TT*)w_g, b_g, gmode, (TT*)xt, g)
+  if (dt == BF16) {
+    if (run == kConvRowsPerWave) GBLA_CF(bf16, kConvRowsPerWave); else GBLA_CF(bf16, kConvRowsPerWaveSmall);
+  } else {
+    if (run == kConvRowsPerWave) GBLA_CF(float, kConvRowsPerWave); else GBLA_CF(float, kConvRowsPerWaveSmall);
+  }
+#undef GBLA_CF
 }
 
 void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* w_lam,
                       const float* b_lam, float* logl, hipStream_t s) {
-  const int rows = 4 * kConvRowsPerWave;
-  const dim3 grid((T + rows - 1) / rows);
   if (T == 0) return;
+  const int run = conv_rows_per_wave(T);
+  const dim3 grid((T + 4 * run - 1) / (4 * run));
   // no conv in this mode: the conv-tap pointer is never dereferenced
-  if (dt == BF16)
-    hipLaunchKernelGGL((k_conv_fwd<bf16, false>), grid, dim3(256), 0, s, (const bf16*)x, cu, N, T, d, H,
-                       (const bf16*)w_lam, (const bf16*)w_lam, b_lam, (int)kGateLogSigmoid, (bf16*)nullptr, logl);
-  else
-    hipLaunchKernelGGL((k_conv_fwd<float, false>), grid, dim3(256), 0, s, (const float*)x, cu, N, T, d, H,
-                       (const float*)w_lam, (const float*)w_lam, b_lam, (int)kGateLogSigmoid, (float*)nullptr, logl);
+#define GBLA_LD(TT, RR)                                                                                  \
+  hipLaunchKernelGGL((k_conv_fwd<TT, false, RR>), grid, dim3(256), 0, s, (const TT*)x, cu, N, T, d, H, \
+                     (const TT*)w_lam, (const TT*)w_lam, b_lam, (int)kGateLogSigmoid, (TT*)nullptr, logl)
+  if (dt == BF16) {
+    if (run == kConvRowsPerWave) GBLA_LD(bf16, kConvRowsPerWave); else GBLA_LD(bf16, kConvRowsPerWaveSmall);
+  } else {
+    if (run == kConvRowsPerWave) GBLA_LD(float, kConvRowsPerWave); else GBLA_LD(float, kConvRowsPerWaveSmall);
+  }
+#undef GBLA_LD
 }
 
 __global__ __launch_bounds__(256) void k_const_log_decay(int T_, int H, const float* __restrict__ b_lam,
