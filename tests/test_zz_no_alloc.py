@@ -81,3 +81,41 @@ def test_noalloc_forward_rejects_a_problem_beyond_its_scratch():
         gb.gbla_forward_noalloc(p, x, cu, torch.zeros((512, 4), dtype=torch.bfloat16, device="cuda"), w, w, w,
                                 torch.zeros((8, 512), dtype=torch.bfloat16, device="cuda"),
                                 torch.zeros(8, dtype=torch.float32, device="cuda"), y, saved, None)
+
+
+def test_noalloc_forward_replays_under_graph_capture():
+    """The allocation-free forward captured into a graph (torch.cuda.graph)
+    and replayed three times, new inputs copied into the captured buffers
+    before each replay; every replay is compared bitwise with an eager call of
+    the same entry point on the same inputs, made between the replays."""
+    w = small_variant(BASE, (1200, 333, 900), d_model=256, num_heads=4, seed=83)
+    inps = [make_inputs(w, seed=83 + i) for i in range(3)]
+    bufs = _dev(inps[0])
+    p = gb.problem(inps[0]["N"], inps[0]["T"], inps[0]["d"], inps[0]["H"], inps[0]["dh"], bufs["x"].dtype)
+    y = torch.zeros((p.total_tokens, p.num_heads * p.head_dim), dtype=bufs["x"].dtype, device="cuda")
+    saved = torch.zeros(gb.saved_size(p) // 4, dtype=torch.float32, device="cuda")
+    args = (p, bufs["x"], bufs["cu"], bufs["conv_w"], bufs["w_q"], bufs["w_k"], bufs["w_v"], bufs["w_g"],
+            bufs["b_g"], y, saved, None)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager call first, off the capture
+        gb.gbla_forward_noalloc(*args)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gb.gbla_forward_noalloc(*args)
+    n_saved = p.num_seqs * p.num_heads * (p.head_dim * p.head_dim + p.head_dim)
+    for i, inp in enumerate(inps):
+        new = _dev(inp)
+        for k in ("x", "conv_w", "w_q", "w_k", "w_v", "w_g", "b_g"):
+            bufs[k].copy_(new[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_y, got_s = y.float().cpu().numpy(), saved.cpu().numpy()[:n_saved]
+        ref = _run(inp, noalloc=True, with_act=False)
+        assert np.array_equal(got_y, ref["y"]), i
+        assert np.array_equal(got_s, ref["saved"][:n_saved]), i
+        print(f"\n[graph replay {i}] T={inp['T']} d={inp['d']} H={inp['H']}: bitwise equal to the eager call",
+              flush=True)
