@@ -399,8 +399,8 @@ def main():
     ap.add_argument("--hbm-ceiling", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(multi-GPU sharding is a design note, not an implemented path)", file=sys.stderr)
+        print(f"bench.py: the GBLA/LION path here runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is designed but not implemented)", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
