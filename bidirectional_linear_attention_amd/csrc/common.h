@@ -22,6 +22,7 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
 
@@ -78,6 +79,45 @@ template <> __device__ __forceinline__ void frag_store<bf16>(bf16* p, const Frag
 }
 template <> __device__ __forceinline__ void frag_store<float>(float* p, const Frag8<float>& f) {
   reinterpret_cast<float4*>(p)[0] = f.lo; reinterpret_cast<float4*>(p)[1] = f.hi;
+}
+
+// Rows [0, n) of a row-major array (pitch ld elements), `width` elements of each
+// from `base` on, seen through a buffer resource: a fragment load from a row at
+// or past n returns zeros and a store there is dropped. Tile loops use it so that
+// no branch surrounds their memory operations: around a branch the compiler's
+// wait-count pass loses track of the loads in flight and waits for all of them
+// at the next use, which leaves one tile in flight instead of two. Offsets are
+// 32-bit (n * ld * sizeof(T) < 2^31); width % 8 == 0.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+template <typename T> struct RowBuf {
+  __amdgpu_buffer_rsrc_t r;
+  int ld;
+  __device__ __forceinline__ RowBuf(const T* base, int n, int ld_, int width) : ld(ld_) {
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), 0,
+                                          n > 0 ? ((n - 1) * ld_ + width) * (int)sizeof(T) : 0, kBufferRsrcWord3);
+  }
+  __device__ __forceinline__ Frag8<T> load(int row, int col) const;
+  __device__ __forceinline__ void store(int row, int col, const Frag8<T>& f) const;
+};
+template <> __device__ __forceinline__ Frag8<bf16> RowBuf<bf16>::load(int row, int col) const {
+  Frag8<bf16> f;
+  f.v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (row * ld + col) * 2, 0, 0));
+  return f;
+}
+template <> __device__ __forceinline__ Frag8<float> RowBuf<float>::load(int row, int col) const {
+  const int o = (row * ld + col) * 4;
+  Frag8<float> f;
+  f.lo = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0));
+  f.hi = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, o + 16, 0, 0));
+  return f;
+}
+template <> __device__ __forceinline__ void RowBuf<bf16>::store(int row, int col, const Frag8<bf16>& f) const {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.v), r, (row * ld + col) * 2, 0, 0);
+}
+template <> __device__ __forceinline__ void RowBuf<float>::store(int row, int col, const Frag8<float>& f) const {
+  const int o = (row * ld + col) * 4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.lo), r, o, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, f.hi), r, o + 16, 0, 0);
 }
 
 // element access of a fragment as float
@@ -231,6 +271,26 @@ template <> __device__ __forceinline__ void quad_store<bf16>(bf16* p, const Quad
 template <> __device__ __forceinline__ void quad_store<float>(float* p, const Quad<float>& q) {
   *reinterpret_cast<float4*>(p) = q.v;
 }
+// 4 elements at (row, col) of a RowBuf (col % 4 == 0); dropped past its rows
+__device__ __forceinline__ void rowbuf_store_quad(const RowBuf<bf16>& b, int row, int col, const Quad<bf16>& q) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, q.v), b.r, (row * b.ld + col) * 2, 0, 0);
+}
+__device__ __forceinline__ void rowbuf_store_quad(const RowBuf<float>& b, int row, int col, const Quad<float>& q) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, q.v), b.r, (row * b.ld + col) * 4, 0, 0);
+}
+// One float per row (pitch ld floats) of rows [0, n) from base, through a
+// buffer resource: rows at or past n read as 0.
+struct RowScalar {
+  __amdgpu_buffer_rsrc_t r;
+  int ld;
+  __device__ __forceinline__ RowScalar(const float* base, int n, int ld_) : ld(ld_) {
+    r = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, n > 0 ? ((n - 1) * ld_ + 1) * 4 : 0,
+                                          kBufferRsrcWord3);
+  }
+  __device__ __forceinline__ float load(int row) const {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, row * ld * 4, 0, 0));
+  }
+};
 // acc += A(16x16) B(16x16) with this lane's quads of A (row lane % 16) and B (column lane % 16)
 __device__ __forceinline__ void mma_q(f32x4& acc, const Quad<bf16>& a, const Quad<bf16>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_v, a.v), __builtin_bit_cast(s16x4_v, b.v),

@@ -306,12 +306,13 @@ void launch_bwd_dstate(int dt, int dh, const void* qa, const void* dy, const flo
 //   dg = phi(k) . dk~,  dk = g dk~ (.) phi'(k),  ds = dg g (1 - g)
 // dk and dv are staged over the wave's own phi(k) and v rows and written to G
 // with 16-byte stores.
+constexpr int kBwdTokenSets = 2;
 template <typename T, int DH, bool SOFTMAX>
-__global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, const T* __restrict__ va,
-                                                   const float* __restrict__ ga, const float* __restrict__ dsz,
-                                                   const int* __restrict__ nchunks, const Chunk* __restrict__ tab,
-                                                   int max_slots, int H, int Kp, int nseg, T* __restrict__ G,
-                                                   float* __restrict__ dbg_part, const float* __restrict__ gmax) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))  // two tile sets within 168 registers
+void k_bwd_token(const T* __restrict__ ka, const T* __restrict__ va, const float* __restrict__ ga,
+                 const float* __restrict__ dsz, const int* __restrict__ nchunks, const Chunk* __restrict__ tab,
+                 int max_slots, int H, int Kp, int nseg, T* __restrict__ G, float* __restrict__ dbg_part,
+                 const float* __restrict__ gmax) {
   constexpr int FB = DH / 16;
   constexpr int LD = DH + 16 / (int)sizeof(T);
   constexpr int LDS_ = DH + 16;  // 40 dwords at d_h = 64 (bf16): conflict-free transposing reads of dS
@@ -338,36 +339,48 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
   const int gs0 = nseg * D, gcol0 = gs0 + H;  // gate column of head 0; first padding column of G
   const int gcolr = (gcol0 + 7) / 8 * 8;       // padding columns the dX~ GEMM reads (zeroed)
   const int r0 = 16 * w;
-  constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pk[NV], pv[NV];
-  float pg = 0.f;
-  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
+  // The tile walk is unrolled (a chunk has at most kChunk / ST tiles); SETS
+  // tiles are in flight, each in a register set of its own, and rows past the
+  // chunk read as zeros (stores there are dropped) through buffer range checks:
+  // no branch surrounds a tile load, so each tile's wait leaves the later
+  // tiles' loads in flight.
+  constexpr int NV = ST * V8 / 256, TILES = kChunk / ST, SETS = kBwdTokenSets;
+  static_assert(ST * V8 % 256 == 0 && kChunk % ST == 0, "whole vectors per thread, whole tiles per chunk");
+  const int n = ch.end - ch.start;
+  const size_t o0 = (size_t)ch.start * D + h * DH;
+  const RowBuf<T> kb(ka + o0, n, D, DH), vb(va + o0, n, D, DH);
+  const RowBuf<T> gb(G + (size_t)ch.start * Kp, n, Kp, Kp);
+  const RowScalar gate(ga + (size_t)ch.start * H + h, n, H);
+  Frag8<T> pk[SETS][NV], pv[SETS][NV];
+  float pg[SETS];
+  auto fetch = [&](int i) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
-      const bool ok = it < ST * V8 && t < ch.end;
-      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
-      pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
+      const int it = tid + 256 * v, r = ST * i + it / V8, c = (it % V8) * 8;
+      pk[i % SETS][v] = kb.load(r, c);
+      pv[i % SETS][v] = vb.load(r, c);
     }
-    if (tid < ST) pg = tb + tid < ch.end ? ga[(size_t)(tb + tid) * H + h] : 0.f;  // gate or softmax logit
+    pg[i % SETS] = gate.load(ST * i + (tid & (ST - 1)));  // gate or softmax logit (used by tid < ST)
   };
-  fetch(ch.start);  // the first tile loads while dS is staged
+#pragma unroll
+  for (int i = 0; i < SETS; ++i) fetch(i);  // the first tiles load while dS is staged
   const float gm = SOFTMAX ? gmax[(size_t)ch.seq * H + h] : 0.f;  // softmax gate: exp(s - largest logit)
   stage_state<T, DH, DH>(nullptr, Srm, LDS_, st, st + DH * DH, tid);
   for (int e = tid; e < DH; e += 256) dzs[e] = st[DH * DH + e];
-  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    if (ST * i >= n) break;  // uniform (barriers inside)
+    const int tb = ch.start + ST * i;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
-      if (it < ST * V8) {
-        frag_store(ks + r * LD + c, pk[v]);
-        frag_store(vs + r * LD + c, pv[v]);
-      }
+      frag_store(ks + r * LD + c, pk[i % SETS][v]);
+      frag_store(vs + r * LD + c, pv[i % SETS][v]);
     }
-    if (tid < ST) gs[tid] = SOFTMAX ? (tb + tid < ch.end ? __expf(pg - gm) : 0.f) : pg;
+    const float pgv = pg[i % SETS];
+    if (tid < ST) gs[tid] = SOFTMAX ? (tb + tid < ch.end ? __expf(pgv - gm) : 0.f) : pgv;
     __syncthreads();
-    if (tb + ST < ch.end) fetch(tb + ST);
+    if (i + SETS < TILES) fetch(i + SETS);
     const float gA = gs[r0 + col];
     // kf: k~ of the lane's token with the k (feature) assignment of frag_kmajor_4g,
     // features 32 s + 4 grp + e and 32 s + 16 + 4 grp + e (e < 4), the B side's
@@ -434,13 +447,11 @@ __global__ __launch_bounds__(256) void k_bwd_token(const T* __restrict__ ka, con
         vs[(r0 + 4 * grp + r) * LD + 16 * nt + col] = from_f<T>(dvv[nt][r]);
       }
     __syncthreads();
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      if (t < ch.end) {
-        frag_store(G + (size_t)t * Kp + D + h * DH + c, frag_load(ks + r * LD + c));
-        frag_store(G + (size_t)t * Kp + 2 * D + h * DH + c, frag_load(vs + r * LD + c));
-      }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {  // rows past the chunk are dropped
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      gb.store(ST * i + r, D + h * DH + c, frag_load(ks + r * LD + c));
+      gb.store(ST * i + r, 2 * D + h * DH + c, frag_load(vs + r * LD + c));
     }
     __syncthreads();
   }

@@ -543,7 +543,7 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
                                                        const Chunk* __restrict__ tab, int max_slots, int H,
                                                        float* __restrict__ partial, float* __restrict__ mpart) {
   constexpr int FB = DH / 16, NB = FB + 1;     // key-feature blocks; value blocks + ones block
-  constexpr int TILES = FB * NB, TPW = (TILES + 3) / 4;
+  constexpr int TILES_S = FB * NB, TPW = (TILES_S + 3) / 4;
   constexpr int ST = 64;                       // tokens per staged tile
   // bf16 pitches of 40 (d_h = 64) or 24 dwords: with the 16-row groups of
   // frag_kmajor_4g, the transposing reads of 40-dword rows are free of bank conflicts
@@ -567,23 +567,31 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
 #pragma unroll
   for (int u = 0; u < TPW; ++u) acc[u] = zero4();
 
+  // The tile walk is unrolled (a chunk has at most kChunk / ST tiles); SETS
+  // tiles are in flight, each in a register set of its own, and rows past the
+  // chunk read as zeros through buffer range checks (no branch around a load,
+  // so each tile's wait leaves the later tiles' loads in flight).
   constexpr int V8 = DH / 8;  // 8-feature vectors per token row
-  constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pk[NV], pv[NV];
-  float pg[NV];
-  auto fetch = [&](int tb) {  // the next tile's loads are issued before the current tile is processed
+  constexpr int NV = ST * V8 / 256, TILES = kChunk / ST, SETS = 2;
+  static_assert(ST * V8 % 256 == 0 && kChunk % ST == 0, "whole vectors per thread, whole tiles per chunk");
+  const int n = ch.end - ch.start;
+  const size_t o0 = (size_t)ch.start * D + h * DH;
+  const RowBuf<T> kb(ka + o0, n, D, DH), vb(va + o0, n, D, DH);
+  const RowScalar gb(ga + (size_t)ch.start * H + h, n, H);
+  Frag8<T> pk[SETS][NV], pv[SETS][NV];
+  float pg[SETS][NV];
+  auto fetch = [&](int i) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
-      const bool ok = it < ST * V8 && t < ch.end;
-      const size_t o = (size_t)(ok ? t : ch.start) * D + h * DH + c;
-      pg[v] = ok ? ga[(size_t)t * H + h] : 0.f;  // the gate, or the softmax gate's logit
-      pk[v] = ok ? frag_load(ka + o) : frag_zero<T>();
-      pv[v] = ok ? frag_load(va + o) : frag_zero<T>();
+      const int it = tid + 256 * v, r = ST * i + it / V8, c = (it % V8) * 8;
+      pg[i % SETS][v] = gb.load(r);  // the gate, or the softmax gate's logit
+      pk[i % SETS][v] = kb.load(r, c);
+      pv[i % SETS][v] = vb.load(r, c);
     }
   };
-  fetch(ch.start);
-  float gmax = 0.f;  // softmax gate: largest logit of the chunk (reduced while the first tile loads)
+#pragma unroll
+  for (int i = 0; i < SETS; ++i) fetch(i);
+  float gmax = 0.f;  // softmax gate: largest logit of the chunk (reduced while the first tiles load)
   if constexpr (SOFTMAX) {
     __shared__ float wmax[4];
     float m = -INFINITY;
@@ -595,25 +603,26 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
     gmax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
     if (tid == 0) mpart[(size_t)slot * H + h] = gmax;
   }
-  for (int tb = ch.start; tb < ch.end; tb += ST) {
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    if (ST * i >= n) break;  // uniform (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
-      if (it < ST * V8) {
-        const float g = SOFTMAX ? (tb + r < ch.end ? __expf(pg[v] - gmax) : 0.f) : pg[v];
-        float kt[8];
+      const float pgv = pg[i % SETS][v];
+      const float g = SOFTMAX ? (ST * i + r < n ? __expf(pgv - gmax) : 0.f) : pgv;
+      float kt[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) kt[j] = g * frag_get(pk[v], j);  // rounded once, used by S and z alike
-        frag_store(ks + r * LDK + c, frag_from<T>(kt));
-        frag_store(vs + r * LDV + c, pv[v]);
-      }
+      for (int j = 0; j < 8; ++j) kt[j] = g * frag_get(pk[i % SETS][v], j);  // rounded once, used by S and z alike
+      frag_store(ks + r * LDK + c, frag_from<T>(kt));
+      frag_store(vs + r * LDV + c, pv[i % SETS][v]);
     }
     __syncthreads();
-    if (tb + ST < ch.end) fetch(tb + ST);
+    if (i + SETS < TILES) fetch(i + SETS);
 #pragma unroll
     for (int u = 0; u < TPW; ++u) {
       const int tile = w + 4 * u;
-      if (tile < TILES) {
+      if (tile < TILES_S) {
         const int ib = tile / NB, nb = tile - ib * NB;
 #pragma unroll
         for (int k0 = 0; k0 < ST; k0 += 32) {
@@ -629,7 +638,7 @@ __global__ __launch_bounds__(256) void k_state_partial(const T* __restrict__ ka,
 #pragma unroll
   for (int u = 0; u < TPW; ++u) {
     const int tile = w + 4 * u;
-    if (tile < TILES) {
+    if (tile < TILES_S) {
       const int ib = tile / NB, nb = tile - ib * NB;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -773,31 +782,42 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
 #pragma unroll
   for (int nt = 0; nt < FB; ++nt) gam[nt] = GATED && gamma ? gamma[16 * nt + col] : 1.f;
 
-  // the next tile's loads are issued before the current tile is processed
-  constexpr int NV = (ST * V8 + 255) / 256;
-  Frag8<T> pf[NV], pr[NV];
-  auto fetch = [&](int tb) {
+  // A chunk has at most kChunk / ST tiles: the tile walk is unrolled, and the
+  // first SETS tiles' loads are issued at the start (while the state is
+  // staged), each into a register set of its own; tile i + SETS reuses tile i's
+  // set once tile i is in LDS. Rows past the chunk read as zeros and their
+  // stores are dropped (buffer range checks), so no branch surrounds a memory
+  // operation and each tile's wait leaves the later tiles' loads in flight.
+  constexpr int NV = ST * V8 / 256, TILES = kChunk / ST;
+  constexpr int SETS = sizeof(T) == 2 && !(GATED && DH == 64) ? TILES : 2;  // within the register budget
+  static_assert(ST * V8 % 256 == 0 && kChunk % ST == 0, "whole vectors per thread, whole tiles per chunk");
+  const int n = ch.end - ch.start;
+  const size_t o0 = (size_t)ch.start * D + h * DH;
+  const RowBuf<T> qb(qa + o0, n, D, DH), yb(y + o0, n, D, DH), rb(GATED ? ra + o0 : qa + o0, n, D, DH);
+  Frag8<T> pf[SETS][NV], pr[SETS][NV];
+  auto fetch = [&](int i) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8, t = tb + r;
-      const bool ok = it < ST * V8 && t < ch.end;
-      pf[v] = ok ? frag_load(qa + (size_t)t * D + h * DH + c) : frag_zero<T>();
-      if constexpr (GATED) pr[v] = ok ? frag_load(ra + (size_t)t * D + h * DH + c) : frag_zero<T>();
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      pf[i % SETS][v] = qb.load(ST * i + r, c);
+      if constexpr (GATED) pr[i % SETS][v] = rb.load(ST * i + r, c);
     }
   };
-  fetch(ch.start);  // the first tile loads while the state is staged
+#pragma unroll
+  for (int i = 0; i < SETS; ++i) fetch(i);
   stage_state<T, DH, NR>(Bs, nullptr, LD, st, st + DH * DH, tid);
-  for (int tb = ch.start; tb < ch.end; tb += ST) {  // uniform trip count (barriers inside)
+#pragma unroll
+  for (int i = 0; i < TILES; ++i) {
+    if (ST * i >= n) break;  // uniform (barriers inside)
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int it = tid + 256 * v;
-      if (it < ST * V8) {
-        frag_store(qs + (it / V8) * LD + (it % V8) * 8, pf[v]);
-        if constexpr (GATED) frag_store(rs + (it / V8) * LD + (it % V8) * 8, pr[v]);
-      }
+      frag_store(qs + (it / V8) * LD + (it % V8) * 8, pf[i % SETS][v]);
+      if constexpr (GATED) frag_store(rs + (it / V8) * LD + (it % V8) * 8, pr[i % SETS][v]);
     }
     __syncthreads();
-    if (tb + ST < ch.end) fetch(tb + ST);
+    if (i + SETS < TILES) fetch(i + SETS);
+    const int tb = ch.start + ST * i;
     Frag8<T> a[DH / 32];
 #pragma unroll
     for (int s = 0; s < DH / 32; ++s) a[s] = frag_load(qs + (r0 + col) * LD + 32 * s + 8 * grp);
@@ -838,10 +858,10 @@ __global__ __launch_bounds__(256) void k_readout(const T* __restrict__ qa, const
       }
     }
     __syncthreads();
-    for (int it = tid; it < ST * V8; it += 256) {
-      const int r = it / V8, c = (it % V8) * 8;
-      const int t = tb + r;
-      if (t < ch.end) frag_store(y + (size_t)t * D + h * DH + c, frag_load(qs + r * LD + c));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int it = tid + 256 * v, r = it / V8, c = (it % V8) * 8;
+      yb.store(ST * i + r, c, frag_load(qs + r * LD + c));  // rows past the chunk are dropped
     }
     __syncthreads();
   }

@@ -262,7 +262,6 @@ __device__ __forceinline__ int dl_swizzle(int r, int c) { return c ^ ((r / (16 /
 __host__ __device__ constexpr int dl_vmcnt(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
 typedef __attribute__((address_space(3))) void dl_lds_void;
-constexpr int kBufferRsrcWord3 = 0x00020000;
 
 // st[s] are NS distinct LDS arrays of S::STAGE elements (distinct objects let the
 // compiler tell the stages apart when it orders LDS reads after LDS-DMA loads)
