@@ -83,7 +83,7 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 // A wave owns RUN consecutive token rows (4 RUN per block); lane l owns channel
 // groups c = 8 * (l + 64 m). The rows stream through two register batches of
 // 4 (the next batch loads while the current one is computed and stored), and
-// the three previous rows slide in registers. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
+// the three previous rows slide in registers. The row walk is unrolled. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
 // reduce-scatter butterfly (butterfly8): 8 head partials per lane become one
 // head total per 8 lanes in 4 + 2 lane-half swaps and 4 DPP adds.
 // RUN = 32 rows per wave; with fewer than 2048 such waves (T < 65 536), 8 rows,
@@ -153,48 +153,73 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
                                                   int gmode, T* __restrict__ xt, float* __restrict__ g_out) {
-  constexpr int B = kConvBatchRows;
+  constexpr int B = kConvBatchRows, NB = RUN / B;
+  static_assert(RUN % B == 0 && RUN <= 32, "whole batches; 2 bits per row position in 64");
   __shared__ float sacc[4][RUN][8];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int t_begin = (blockIdx.x * 4 + w) * RUN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t_begin = (blockIdx.x * 4 + w) * RUN;  // wave-uniform
   const int t_end = min(t_begin + RUN, T_);
   const int ngroups = d / 8;
+  // position of each row of the run in its sequence, capped at 3 (2 bits per
+  // row), looked up before any row load is in flight: the lookup's loads are
+  // wave-uniform, and a wait for them then holds up nothing else
+  unsigned long long posbits = 0;
+  if (CONV && t_begin < t_end) {
+    SeqCursor cur(cu, nseq, t_begin, T_);
+    for (int i = 0; i < RUN && t_begin + i < t_end; ++i)
+      posbits |= (unsigned long long)min(cur.pos(t_begin + i), 3) << (2 * i);
+  }
+  // x rows max(t_begin - 3, 0) .. t_end - 1 and the run's x~ rows through buffer
+  // range checks: rows past the run read as zeros and their stores are dropped,
+  // so no branch surrounds a row load or store and each batch's wait leaves the
+  // next batch's loads in flight
+  const int x0r = max(t_begin - 3, 0), nx = max(t_end - x0r, 0), nrun = max(t_end - t_begin, 0);
+  const RowBuf<T> xb(x + (size_t)x0r * d, nx, d, d);
+  const RowBuf<T> xtb(CONV ? xt + (size_t)t_begin * d : x, CONV ? nrun : 0, d, d);
   for (int hg = 0; hg < H; hg += 8) {
     for (int g8 = lane; g8 < ((ngroups + 63) / 64) * 64; g8 += 64) {
       const bool okc = g8 < ngroups;
       const int c = g8 * 8;
-      float wv[8][4];
-      Frag8<T> wgf[8];
+      const int cx = okc ? c : (nx + 3) * d, cs = okc ? c : nrun * d;  // out of range for lanes past d
+      // every load is issued before any is used: the weights, the three rows
+      // before the run (zeros before row 0; sequence starts are cut by the
+      // positions) and the first two row batches
+      Frag8<T> cwf[4], wgf[8];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const Frag8<T> f = CONV && okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
-#pragma unroll
-        for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(f, e);
-      }
+      for (int m = 0; m < 4; ++m)
+        cwf[m] = CONV && okc ? frag_load(conv_w + (size_t)c * 4 + 8 * m) : frag_zero<T>();
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh)
         wgf[hh] = okc && hg + hh < H ? frag_load(w_g + (size_t)(hg + hh) * d + c) : frag_zero<T>();
+      const int r0 = t_begin - x0r;  // the run's first row in xb
       Frag8<T> xm1 = frag_zero<T>(), xm2 = frag_zero<T>(), xm3 = frag_zero<T>();
-      if (CONV && okc && t_begin < t_end) {
-        if (t_begin >= 1) xm1 = frag_load(x + (size_t)(t_begin - 1) * d + c);
-        if (t_begin >= 2) xm2 = frag_load(x + (size_t)(t_begin - 2) * d + c);
-        if (t_begin >= 3) xm3 = frag_load(x + (size_t)(t_begin - 3) * d + c);
+      if (CONV) {
+        xm1 = xb.load(r0 - 1, cx);
+        xm2 = xb.load(r0 - 2, cx);
+        xm3 = xb.load(r0 - 3, cx);
       }
       // rows stream through two register batches: one is computed while the next loads
       Frag8<T> xr[2][B];
-      auto fetch = [&](int buf, int tb) {
+      auto fetch = [&](int bi) {
 #pragma unroll
-        for (int i = 0; i < B; ++i)
-          xr[buf][i] = okc && tb + i < t_end ? frag_load(x + (size_t)(tb + i) * d + c) : frag_zero<T>();
+        for (int i = 0; i < B; ++i) xr[bi % 2][i] = xb.load(r0 + B * bi + i, cx);
       };
-      SeqCursor cur(cu, nseq, t_begin, T_);
-      auto compute = [&](int buf, int tb) {
+      fetch(0);
+      if (NB > 1) fetch(1);
+      __builtin_amdgcn_sched_barrier(0);  // the conversions below stay behind the loads
+      float wv[8][4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wv[(8 * m + e) >> 2][(8 * m + e) & 3] = frag_get(cwf[m], e);
+#pragma unroll
+      for (int bi = 0; bi < NB; ++bi) {
 #pragma unroll
         for (int i = 0; i < B; ++i) {
-          const int t = tb + i;
-          if (t >= t_end) break;
-          const int pos = cur.pos(t);
-          const Frag8<T> x0 = xr[buf][i];
+          const int u = B * bi + i;  // row of the run
+          const int pos = (int)(posbits >> (2 * u)) & 3;
+          const Frag8<T> x0 = xr[bi % 2][i];
           float o[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -205,28 +230,20 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
             o[j] = a;
           }
           const Frag8<T> of = frag_from<T>(o);
-          if (CONV && okc && hg == 0) frag_store(xt + (size_t)t * d + c, of);
+          if (CONV && hg == 0) xtb.store(u, cs, of);
           float sp[8];
 #pragma unroll
           for (int hh = 0; hh < 8; ++hh) sp[hh] = gate_dot8<T>(of, wgf[hh]);  // the rounded x~ that Q, K, V see
           const float tot = butterfly8(sp, lane);
           if ((lane & 7) == 0) {
-            float& acc = sacc[w][t - t_begin][lane >> 3];
+            float& acc = sacc[w][u][lane >> 3];
             acc = g8 < 64 ? tot : acc + tot;
           }
           xm3 = xm2;
           xm2 = xm1;
           xm1 = x0;
         }
-      };
-      if (t_begin < t_end) {
-        fetch(0, t_begin);
-        for (int tb = t_begin; tb < t_end; tb += 2 * B) {
-          if (tb + B < t_end) fetch(1, tb + B);
-          compute(0, tb);
-          if (tb + 2 * B < t_end) fetch(0, tb + 2 * B);
-          if (tb + B < t_end) compute(1, tb + B);
-        }
+        if (bi + 2 < NB) fetch(bi + 2);
       }
     }
     __syncthreads();
