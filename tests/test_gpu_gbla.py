@@ -207,6 +207,17 @@ def test_bf16_wide_model_many_heads():
     compare(make_inputs(w), backward=True, label="bf16 d=576 H=10")
 
 
+def test_bf16_short_sequences_in_32_row_runs():
+    """At least 65 536 tokens give every wave of the forward conv 32 rows, whose
+    positions in their sequences are looked up once per run. 3000 sequences of
+    1 to 7 tokens mixed with longer ones put sequence starts at every offset
+    inside those runs, inside the 256-token chunks and across the dX~ GEMM's
+    token-tile seams."""
+    lens = [1, 2, 3, 4, 5, 6, 7, 29, 64, 100] * 300  # 66 300 tokens
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lens, d_model=64, num_heads=2, head_dim=32, seed=35)
+    compare(make_inputs(w), backward=True, label="bf16 short sequences in 32-row conv runs")
+
+
 def test_bf16_small_ragged_recipe():
     rng = np.random.default_rng(23)
     lens = np.clip(np.rint(np.exp(rng.normal(np.log(600), 1.0, 12))), 16, 32768).astype(int)
