@@ -105,7 +105,9 @@ gbla_status check_problem(const lion_problem* p) {
     return GBLA_ERR_BAD_SHAPE;
   const long long T = p->total_tokens;
   const long long widest = std::max<long long>(p->d_model, grad_cols(p->num_heads, p->head_dim));
-  if (T * widest >= (1LL << 31) || (long long)p->num_heads * p->head_dim * 4 + 64 >= (1LL << 24) ||
+  // widest < 2^21: a run of rows of the widest array fits the kernels' 32-bit buffer offsets
+  if (T * widest >= (1LL << 31) || widest >= (1LL << 21) ||
+      (long long)p->num_heads * p->head_dim * 4 + 64 >= (1LL << 24) ||
       (long long)p->num_seqs >= (1LL << 24) ||
       (long long)wt_rows(p->d_model) * grad_cols(p->num_heads, p->head_dim) >= (1LL << 31))
     return GBLA_ERR_BAD_SHAPE;

@@ -41,7 +41,8 @@
  *    floating-point atomics, so repeated calls are bitwise identical.
  *  - Large arrays must be 16-byte aligned; b_g, db_g, dconv_w, gamma, dgamma
  *    and cu_seqlens 4-byte aligned.
- *  - Sizes: total_tokens * max(d_model, S*H*d_h + H + 64) < 2^31 and
+ *  - Sizes: total_tokens * max(d_model, S*H*d_h + H + 64) < 2^31,
+ *    max(d_model, S*H*d_h + H + 64) < 2^21 and
  *    ceil32(d_model) * (S*H*d_h + H + 64) < 2^31, S = 3 (4 with the gated
  *    output); otherwise GBLA_ERR_BAD_SHAPE.
  *  - Calls that share a workspace must not overlap in time.

@@ -30,7 +30,8 @@
  * returned as gbla_status before anything is enqueued; cu_seqlens read on the
  * device only (malformed offsets schedule no token); deterministic results;
  * large arrays 16-byte aligned, b_lam, db_lam and cu_seqlens 4-byte aligned;
- * total_tokens * max(d_model, 3*H*d_h + H + 64) < 2^31 and
+ * total_tokens * max(d_model, 3*H*d_h + H + 64) < 2^31,
+ * max(d_model, 3*H*d_h + H + 64) < 2^21 and
  * ceil32(d_model) * (3*H*d_h + H + 64) < 2^31; calls that share a
  * workspace or an activation cache must not overlap in time.
  */

@@ -54,6 +54,7 @@ def _prob(**kw):
     (dict(output_gate=2), 3), (dict(output_gate=1, norm_eps=-1.0), 2), (dict(output_gate=1, norm_eps=float("nan")), 2),
     (dict(output_gate=1, norm_eps=float("inf")), 2),
     (dict(total_tokens=1, d_model=1 << 22, num_heads=8), 2),  # packed dX weights past 2^31 elements
+    (dict(total_tokens=1, d_model=1 << 21, num_heads=1, head_dim=32), 2),  # rows past 32-bit buffer offsets
 ])
 def test_size_queries_reject_bad_problems(kw, status):
     lib = _lib.load()
@@ -220,6 +221,7 @@ def _lprob(**kw):
     (dict(head_dim=48), 3), (dict(dtype=7), 3), (dict(chunk=32), 3), (dict(decay=3), 3), (dict(decay=-1), 3),
     (dict(d_model=60), 2), (dict(num_seqs=0), 2), (dict(total_tokens=-1), 2), (dict(num_heads=0), 2),
     (dict(total_tokens=1 << 30), 2), (dict(total_tokens=1, d_model=1 << 22, num_heads=8), 2),
+    (dict(total_tokens=1, d_model=1 << 21, num_heads=1, head_dim=32), 2),
 ])
 def test_lion_size_queries_reject_bad_problems(kw, status):
     lib = _lib.load()
