@@ -194,10 +194,10 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
         wgf[hh] = okc && hg + hh < H ? frag_load(w_g + (size_t)(hg + hh) * d + c) : frag_zero<T>();
       const int r0 = t_begin - x0r;  // the run's first row in xb
       Frag8<T> xm1 = frag_zero<T>(), xm2 = frag_zero<T>(), xm3 = frag_zero<T>();
-      if (CONV) {
-        xm1 = xb.load(r0 - 1, cx);
-        xm2 = xb.load(r0 - 2, cx);
-        xm3 = xb.load(r0 - 3, cx);
+      if (CONV) {  // rows before row 0 are read at row nx, past the range (zeros)
+        xm1 = xb.load(r0 >= 1 ? r0 - 1 : nx, cx);
+        xm2 = xb.load(r0 >= 2 ? r0 - 2 : nx, cx);
+        xm3 = xb.load(r0 >= 3 ? r0 - 3 : nx, cx);
       }
       // rows stream through two register batches: one is computed while the next loads
       Frag8<T> xr[2][B];
