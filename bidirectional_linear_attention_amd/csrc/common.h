@@ -22,7 +22,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_v;
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_v;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float bf2f(bf16 v) { return __uint_as_float(((uint32_t)v) << 16); }
 
@@ -271,13 +270,6 @@ template <> __device__ __forceinline__ void quad_store<bf16>(bf16* p, const Quad
 template <> __device__ __forceinline__ void quad_store<float>(float* p, const Quad<float>& q) {
   *reinterpret_cast<float4*>(p) = q.v;
 }
-// 4 elements at (row, col) of a RowBuf (col % 4 == 0); dropped past its rows
-__device__ __forceinline__ void rowbuf_store_quad(const RowBuf<bf16>& b, int row, int col, const Quad<bf16>& q) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, q.v), b.r, (row * b.ld + col) * 2, 0, 0);
-}
-__device__ __forceinline__ void rowbuf_store_quad(const RowBuf<float>& b, int row, int col, const Quad<float>& q) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, q.v), b.r, (row * b.ld + col) * 4, 0, 0);
-}
 // One float per row (pitch ld floats) of rows [0, n) from base, through a
 // buffer resource: rows at or past n read as 0.
 struct RowScalar {
@@ -380,31 +372,10 @@ __device__ __forceinline__ float add_xor32(float v) {
 // value held by lane 16 * (lane / 16) (column 0 of this lane's C-tile rows)
 __device__ __forceinline__ float col0_bcast(float v) { return dpp_f<kDppRowBcast0>(v); }
 
-// position of token t inside its packed sequence (largest b with cu[b] <= t),
-// clamped so that t - pos >= 0 even for malformed offsets
-__device__ __forceinline__ int pos_in_seq(const int32_t* __restrict__ cu, int nseq, int t) {
-  int lo = 0, hi = nseq;  // invariant: cu[lo] <= t < cu[hi] for well-formed offsets
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  int p = t - cu[lo];
-  return p < 0 ? 0 : (p > t ? t : p);
-}
-// end (exclusive) of token t's sequence, clamped to [t + 1, T]
-__device__ __forceinline__ int seq_end_of(const int32_t* __restrict__ cu, int nseq, int t, int T) {
-  int lo = 0, hi = nseq;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (cu[mid] <= t) lo = mid; else hi = mid;
-  }
-  int e = cu[lo + 1];
-  return e <= t ? t + 1 : (e > T ? T : e);
-}
-
-// Walks consecutive tokens t0, t0+1, ... tracking their sequence: pos(t) and
-// end(t) as pos_in_seq / seq_end_of, with one binary search at t0 and an
-// advance over the offsets only where a sequence boundary is crossed.
+// Walks consecutive tokens t0, t0+1, ... tracking their sequence: pos(t) is
+// t's position in its sequence and end(t) the sequence's end (exclusive,
+// clamped to [t + 1, T]), with one binary search at t0 and an advance over the
+// offsets only where a sequence boundary is crossed.
 // Must be queried with non-decreasing t.
 struct SeqCursor {
   const int32_t* cu;
