@@ -40,7 +40,7 @@ Dims dims_of(const gbla_problem* p) {
   m.slots = max_chunks(m.T, m.N);
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
   m.nsplit = dw_splits(dt, m.d, m.Kp, m.T);
-  m.conv_rb = dx_token_tiles(p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32, m.T);
+  m.conv_rb = dx_token_tiles(p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32, m.T, m.d);
   m.esz = p->dtype == GBLA_DTYPE_BF16 ? 2 : 4;
   m.softmax = p->gate == GBLA_GATE_SOFTMAX;
   return m;
@@ -367,7 +367,7 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
     f.dconv_part = w.dconv_part; f.conv_rb = m.conv_rb; f.dconv_w = dconv_w;
     f.nchunks = w.nchunks; f.dbg_part = w.dbg_part; f.db_g = db_g;
     f.dgam_part = gamma ? w.dgam_part : nullptr; f.dgamma = gamma ? dgamma : nullptr;
-    f.dt = dt; f.tile_rows = dx_token_tile_rows(dt); f.nseq = m.N;
+    f.dt = dt; f.tile_rows = dx_token_tile_rows(dt, m.T, m.d); f.nseq = m.N;
     f.edge = m.T > 0 ? w.edge : nullptr; f.conv_w = conv_w; f.cu = cu_seqlens; f.dx = dx;
     launch_bwd_finalize(f, s);
   }

@@ -538,9 +538,17 @@ void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, c
 // registers (no LDS staging, no barrier). bf16: 256 x 256 tiles of 16 waves of
 // 64 x 64 (one block per CU; a 64 x 64 wave tile keeps the LDS operand reads per
 // MFMA low, and 16 waves hide their latency).
-template <typename T> struct DxCfg;
-template <> struct DxCfg<bf16> { using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; };
-template <> struct DxCfg<float> { using S = GemmShape<float, 128, 64, 32, 2, 2>; static constexpr bool DL = false; };
+// A batch whose 256-token tiles would leave compute units idle (fewer tiles than
+// 256; the B = 32, L = 1024, d = 256 workload has 128) takes 128-token tiles
+// of 8 waves instead (SMALL), so that every compute unit gets a block.
+template <typename T, bool SMALL = false> struct DxCfg;
+template <> struct DxCfg<bf16, false> { using S = DlShape<256, 256, 64, 4, 4, 2>; static constexpr bool DL = true; };
+template <> struct DxCfg<bf16, true> { using S = DlShape<256, 128, 64, 4, 2, 2>; static constexpr bool DL = true; };
+template <bool SMALL> struct DxCfg<float, SMALL> {
+  using S = GemmShape<float, 128, 64, 32, 2, 2>;
+  static constexpr bool DL = false;
+};
+constexpr int kDxFillTiles = 256;  // compute units of the MI355X
 
 // Kp is the row pitch of G and Wt; the k loop reads Kr <= Kp columns.
 //
@@ -691,12 +699,13 @@ __device__ __forceinline__ void dx_conv_epilogue(const f32x4 (&acc)[S::FM][S::FN
   }
 }
 
-template <typename T, bool CONV>
-__global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
-                                                                     const T* __restrict__ wt, int T_, int d, int Kp,
-                                                                     int Kr, T* __restrict__ out, DxConv cv) {
-  using S = typename DxCfg<T>::S;
-  constexpr bool DL = DxCfg<T>::DL;
+template <typename T, bool CONV, bool SMALL>
+__global__ __launch_bounds__((DxCfg<T, SMALL>::S::NTHREADS)) void k_gemm_dx(const T* __restrict__ G,
+                                                                            const T* __restrict__ wt, int T_, int d,
+                                                                            int Kp, int Kr, T* __restrict__ out,
+                                                                            DxConv cv) {
+  using S = typename DxCfg<T, SMALL>::S;
+  constexpr bool DL = DxCfg<T, SMALL>::DL;
   static_assert(S::BM % 32 == 0 && S::WTM % 32 == 0, "whole 32-row channel groups per wave");
   __shared__ __align__(16) T smem[DL ? S::STAGE : 2 * S::STAGE];
   __shared__ __align__(16) T smem1[DL ? S::STAGE : 8];
@@ -739,37 +748,50 @@ __global__ __launch_bounds__((DxCfg<T>::S::NTHREADS)) void k_gemm_dx(const T* __
   }
 }
 
-int dx_token_tiles(int dt, int T) {
-  const int bn = dt == BF16 ? DxCfg<bf16>::S::BN : DxCfg<float>::S::BN;
+static bool dx_small(int dt, int T, int d) {
+  using S = DxCfg<bf16, false>::S;
+  return dt == BF16 && (long)((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM) < kDxFillTiles;
+}
+int dx_token_tile_rows(int dt, int T, int d) {
+  if (dt != BF16) return DxCfg<float>::S::BN;
+  return dx_small(dt, T, d) ? DxCfg<bf16, true>::S::BN : DxCfg<bf16, false>::S::BN;
+}
+int dx_token_tiles(int dt, int T, int d) {
+  const int bn = dx_token_tile_rows(dt, T, d);
   return (T + bn - 1) / bn;
 }
-int dx_token_tile_rows(int dt) { return dt == BF16 ? DxCfg<bf16>::S::BN : DxCfg<float>::S::BN; }
 
-template <typename TT>
+template <typename TT, bool SMALL>
 static void gemm_dx_t(const void* G, const void* wt, int T, int d, int Kp, int Kr, void* out, const DxConv* cv,
                       hipStream_t s) {
-  using S = typename DxCfg<TT>::S;
+  using S = typename DxCfg<TT, SMALL>::S;
   const int n = ((T + S::BN - 1) / S::BN) * ((wt_rows(d) + S::BM - 1) / S::BM);
   if (n == 0) return;
   if (cv)
-    hipLaunchKernelGGL((k_gemm_dx<TT, true>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
+    hipLaunchKernelGGL((k_gemm_dx<TT, true, SMALL>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
                        (const TT*)wt, T, d, Kp, Kr, (TT*)out, *cv);
   else
-    hipLaunchKernelGGL((k_gemm_dx<TT, false>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
+    hipLaunchKernelGGL((k_gemm_dx<TT, false, SMALL>), dim3(xcd_grid(n)), dim3(S::NTHREADS), 0, s, (const TT*)G,
                        (const TT*)wt, T, d, Kp, Kr, (TT*)out, DxConv{});
+}
+template <typename TT>
+static void gemm_dx_any(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* out,
+                        const DxConv* cv, hipStream_t s) {
+  if (dx_small(dt, T, d)) gemm_dx_t<TT, true>(G, wt, T, d, Kp, Kr, out, cv, s);
+  else gemm_dx_t<TT, false>(G, wt, T, d, Kp, Kr, out, cv, s);
 }
 
 void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, void* dxt, hipStream_t s) {
-  if (dt == BF16) gemm_dx_t<bf16>(G, wt, T, d, Kp, Kr, dxt, nullptr, s);
-  else gemm_dx_t<float>(G, wt, T, d, Kp, Kr, dxt, nullptr, s);
+  if (dt == BF16) gemm_dx_any<bf16>(dt, G, wt, T, d, Kp, Kr, dxt, nullptr, s);
+  else gemm_dx_t<float, false>(G, wt, T, d, Kp, Kr, dxt, nullptr, s);
 }
 
 void launch_gemm_dx_conv(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, const void* x,
                          const int32_t* cu, int N, const void* conv_w, void* dx, float* dconv_part, void* edge,
                          hipStream_t s) {
   const DxConv cv{x, cu, N, conv_w, dconv_part, edge};
-  if (dt == BF16) gemm_dx_t<bf16>(G, wt, T, d, Kp, Kr, dx, &cv, s);
-  else gemm_dx_t<float>(G, wt, T, d, Kp, Kr, dx, &cv, s);
+  if (dt == BF16) gemm_dx_any<bf16>(dt, G, wt, T, d, Kp, Kr, dx, &cv, s);
+  else gemm_dx_t<float, false>(G, wt, T, d, Kp, Kr, dx, &cv, s);
 }
 
 // ============================================================== dW = X~^T G (split over tokens)
@@ -791,11 +813,11 @@ int dw_tiles(int dt, int d, int Kp) {
 
 // token splits of the dW GEMM: bf16 (one 16-wave block per CU) as many as
 // fill one round of the 256 CUs, float as many as fill two rounds of two
-// resident blocks; at least 1024 tokens per split, at most 64
+// resident blocks; at least 512 tokens per split, at most 64
 int dw_splits(int dt, int d, int Kp, int T) {
   const int tiles = dw_tiles(dt, d, Kp);
   int ns = std::max(1, (dt == BF16 ? 256 : 1024) / tiles);
-  ns = std::min(ns, std::max(1, (T + 1023) / 1024));
+  ns = std::min(ns, std::max(1, (T + 511) / 512));
   return std::max(1, std::min(ns, 64));
 }
 
@@ -947,10 +969,20 @@ __global__ __launch_bounds__(256) void k_bwd_finalize(BwdFinalize f) {
       const long e = 4 * qi;
       const int c = (int)(e / f.Kp), n = (int)(e - (long)c * f.Kp);
       if (n >= GD + f.H) continue;
+      // split k in order; the loads go out U at a time (one memory latency per U splits)
+      constexpr int U = 8;
       float4 s = *reinterpret_cast<const float4*>(f.dw_part + e);
-      for (int k = 1; k < f.nsplit; ++k) {
-        const float4 p = *reinterpret_cast<const float4*>(f.dw_part + (size_t)k * total + e);
-        s.x += p.x; s.y += p.y; s.z += p.z; s.w += p.w;
+      for (int kb = 1; kb < f.nsplit; kb += U) {
+        float4 p[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          p[u] = kb + u < f.nsplit ? *reinterpret_cast<const float4*>(f.dw_part + (size_t)(kb + u) * total + e)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if (kb + u >= f.nsplit) break;
+          s.x += p[u].x; s.y += p[u].y; s.z += p[u].z; s.w += p[u].w;
+        }
       }
       if (n < GD) {
         const int seg = n / D;

@@ -204,8 +204,8 @@ void launch_gemm_dx(int dt, const void* G, const void* wt, int T, int d, int Kp,
 void launch_gemm_dx_conv(int dt, const void* G, const void* wt, int T, int d, int Kp, int Kr, const void* x,
                          const int32_t* cu, int N, const void* conv_w, void* dx, float* dconv_part, void* edge,
                          hipStream_t s);
-int dx_token_tiles(int dt, int T);
-int dx_token_tile_rows(int dt);
+int dx_token_tiles(int dt, int T, int d);
+int dx_token_tile_rows(int dt, int T, int d);
 int dw_tiles(int dt, int d, int Kp);
 int dw_splits(int dt, int d, int Kp, int T);
 void launch_gemm_dw(int dt, const void* xt, const void* G, int T, int d, int Kp, int nsplit, float* part,
