@@ -146,14 +146,19 @@ def _seam_lengths(tile, tiles):
     return tuple(b - a for a, b in zip(cuts, cuts[1:]))
 
 
-@pytest.mark.parametrize("dtype,tile", [("f32", 64), ("bf16", 256)])
+@pytest.mark.parametrize("dtype,tile", [("f32", 64), ("bf16", 128), ("bf16", 256)])
 def test_conv_backward_at_token_tile_seams(dtype, tile):
     """The conv's backward runs in the dX~ GEMM's epilogue per token tile (64
-    tokens in float32, 256 in bf16); dx of a tile's last three tokens is formed
-    from the edge rows of two tiles. Sequence boundaries at every offset around
-    the seams check that the conv never reaches across a sequence there."""
-    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], _seam_lengths(tile, 3), d_model=96, num_heads=3,
-                      head_dim=32, dtype=dtype, seed=29)
+    tokens in float32; in bf16 256, or 128 when the batch has fewer than 256
+    tiles of 256); dx of a tile's last three tokens is formed from the edge rows
+    of two tiles. Sequence boundaries at every offset around the seams check
+    that the conv never reaches across a sequence there. For 256-token tiles a
+    long last sequence brings the batch past 65 536 tokens."""
+    lens = _seam_lengths(tile, 3)
+    if tile == 256:
+        lens = lens + (65536,)
+    w = small_variant(WORKLOADS["gbla_bf16_B32_L1024_d256"], lens, d_model=96, num_heads=3, head_dim=32,
+                      dtype=dtype, seed=29)
     compare(make_inputs(w), backward=True, label=f"{dtype} seams of {tile}-token tiles")
 
 
