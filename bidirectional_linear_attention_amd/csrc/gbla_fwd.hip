@@ -83,9 +83,10 @@ void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v,
 // A wave owns RUN consecutive token rows (4 RUN per block); lane l owns channel
 // groups c = 8 * (l + 64 m). The rows stream through two register batches of
 // 4 (the next batch loads while the current one is computed and stored), and
-// the three previous rows slide in registers. The row walk is unrolled. The gate logits s_h = x~ . w_g^h are reduced over the wave with a
-// reduce-scatter butterfly (butterfly8): 8 head partials per lane become one
-// head total per 8 lanes in 4 + 2 lane-half swaps and 4 DPP adds.
+// the three previous rows slide in registers; the row walk is unrolled. The
+// gate logits s_h = x~ . w_g^h are reduced over the wave with a reduce-scatter
+// butterfly (butterfly8): 8 head partials per lane become one head total per 8
+// lanes in 4 + 2 lane-half swaps and 4 DPP adds.
 // RUN = 32 rows per wave; with fewer than 2048 such waves (T < 65 536), 8 rows,
 // so that a small batch still puts several waves on every SIMD
 constexpr int kConvRowsPerWave = 32, kConvRowsPerWaveSmall = 8;
