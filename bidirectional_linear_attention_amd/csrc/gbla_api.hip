@@ -46,12 +46,19 @@ Dims dims_of(const gbla_problem* p) {
   return m;
 }
 
-// activations kept from the forward for the backward (ra: the gated output's R)
-struct Act { void* xt; void* qa; void* ka; void* va; float* ga; void* ra; };
+// activations kept from the forward for the backward (ra: the gated output's R),
+// with the batch's chunk table, which the backward then need not rebuild
+struct Act {
+  int* nchunks; int* chunk_off; Chunk* tab;
+  void* xt; void* qa; void* ka; void* va; float* ga; void* ra;
+};
 
 Act carve_act(const Dims& m, Carver& c, char* base) {
   Act a;
   const size_t TD = (size_t)m.T * m.D * m.esz;
+  a.nchunks = c.take<int>(base, sizeof(int));
+  a.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
+  a.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   a.xt = c.take<char>(base, (size_t)m.T * m.d * m.esz);
   a.qa = c.take<char>(base, TD);
   a.ka = c.take<char>(base, TD);
@@ -68,10 +75,10 @@ size_t act_bytes(const Dims& m) {
 }
 
 struct FwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wp; float* partial; float* mpart; Act act;
+  void* wp; float* partial; float* mpart; Act act;
 };
 struct BwdWs {
-  int* nchunks; int* chunk_off; Chunk* tab; void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
+  void* wp; void* wt; float* partial; float* dsz; float* dbg_part;
   float* dgam_part; void* G; void* edge; float* dw_part; float* dconv_part; Act act;
 };
 
@@ -83,9 +90,6 @@ struct BwdWs {
 size_t plan_fwd(const Dims& m, char* base, FwdWs* w, bool act_region = true) {
   Carver c;
   FwdWs t;
-  t.nchunks = c.take<int>(base, sizeof(int));
-  t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
-  t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
   t.mpart = m.softmax ? c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H) : nullptr;
@@ -97,9 +101,6 @@ size_t plan_fwd(const Dims& m, char* base, FwdWs* w, bool act_region = true) {
 size_t plan_bwd(const Dims& m, char* base, BwdWs* w) {
   Carver c;
   BwdWs t;
-  t.nchunks = c.take<int>(base, sizeof(int));
-  t.chunk_off = c.take<int>(base, sizeof(int) * (m.N + 1));
-  t.tab = c.take<Chunk>(base, sizeof(Chunk) * m.slots);
   t.wp = c.take<char>(base, (size_t)m.H * m.NP * m.d * m.esz);
   t.wt = c.take<char>(base, (size_t)wt_rows(m.d) * m.Kp * m.esz);
   t.partial = c.take<float>(base, sizeof(float) * (size_t)m.slots * m.H * m.E);
@@ -166,20 +167,19 @@ gbla_status enqueue_forward(const gbla_problem* p, const Dims& m, const void* x,
   const int dt = p->dtype == GBLA_DTYPE_BF16 ? BF16 : F32;
   const Act& A = w.act;
   (void)hipGetLastError();
-  { StageScope ps(ST_PACK_PROJ, s);  // and the chunk table
-    launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp,
-                     Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
-  { StageScope ps(ST_CONV_FWD, s);
-    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
+  const ProjPackArgs pack{w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp};
+  { StageScope ps(ST_CONV_FWD, s);  // with the projection's weight packing and the chunk table
+    launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s, &pack,
+                    Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, A.nchunks, A.chunk_off, A.tab}); }
   { StageScope ps(ST_PROJ_FWD, s);
     launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
   { StageScope ps(ST_STATE_PARTIAL, s);
-    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, w.nchunks, w.tab, m.slots, m.H, w.partial, w.mpart, s); }
+    launch_state_partial(dt, m.dh, A.ka, A.va, A.ga, A.nchunks, A.tab, m.slots, m.H, w.partial, w.mpart, s); }
   { StageScope ps(ST_COMBINE_STATE, s);  // softmax gate: the logit maxima follow the N*H states
-    launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
+    launch_combine(w.partial, A.nchunks, A.chunk_off, m.N, m.H, m.E, saved, s, w.mpart,
                    m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr); }
   { StageScope ps(ST_READOUT, s);
-    launch_readout(dt, m.dh, A.qa, saved, w.nchunks, w.tab, m.slots, m.H, y, s, A.ra, gamma, m.eps); }
+    launch_readout(dt, m.dh, A.qa, saved, A.nchunks, A.tab, m.slots, m.H, y, s, A.ra, gamma, m.eps); }
   return hipGetLastError() == hipSuccess ? GBLA_OK : GBLA_ERR_HIP;
 }
 
@@ -333,23 +333,24 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
   const Act& A = w.act;
 
   (void)hipGetLastError();
-  { StageScope ps(ST_PACK_WT, s);  // and the chunk table
-    launch_pack_wt(dt, w_q, w_k, w_v, w_r, w_g, m.d, m.H, m.dh, m.Kp, w.wt,
-                   Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, w.nchunks, w.chunk_off, w.tab}, s); }
+  // with an activation cache the chunk table is the forward's; without one,
+  // the recomputation's conv launch builds it in the workspace
   if (!act) {  // recompute x~, g, phi(q), phi(k), v into the workspace
-    { StageScope ps(ST_PACK_PROJ, s);
-      launch_pack_proj(dt, w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp, Sched{}, s); }
-    { StageScope ps(ST_CONV_RECOMPUTE, s);
-      launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s); }
+    const ProjPackArgs pack{w_q, w_k, w_v, w_r, m.d, m.H, m.dh, w.wp};
+    { StageScope ps(ST_CONV_RECOMPUTE, s);  // with the projection's weight packing and the chunk table
+      launch_conv_fwd(dt, x, cu_seqlens, m.N, m.T, m.d, m.H, conv_w, w_g, b_g, m.softmax, A.xt, A.ga, s, &pack,
+                      Sched{cu_seqlens, m.N, m.T, kChunk, m.slots, A.nchunks, A.chunk_off, A.tab}); }
     { StageScope ps(ST_PROJ_RECOMPUTE, s);
       launch_proj(dt, m.dh, A.xt, w.wp, m.T, m.d, m.H, A.qa, A.ka, A.va, s, true, A.ra); }
   }
   { StageScope ps(ST_BWD_DSTATE, s);
-    launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, w.nchunks, w.tab, m.slots, m.H, m.Kp, w.partial, w.G, s, A.ra,
+    launch_bwd_dstate(dt, m.dh, A.qa, dy, saved, A.nchunks, A.tab, m.slots, m.H, m.Kp, w.partial, w.G, s, A.ra,
                       gamma, m.eps, gamma ? w.dgam_part : nullptr); }
-  { StageScope ps(ST_COMBINE_DSTATE, s); launch_combine(w.partial, w.nchunks, w.chunk_off, m.N, m.H, m.E, w.dsz, s); }
+  { StageScope ps(ST_COMBINE_DSTATE, s);  // with the packing of the dX~ GEMM's weights
+    const WtPackArgs pack{w_q, w_k, w_v, w_r, w_g, m.d, m.H, m.dh, m.Kp, w.wt};
+    launch_combine(w.partial, A.nchunks, A.chunk_off, m.N, m.H, m.E, w.dsz, s, nullptr, nullptr, &pack, dt); }
   { StageScope ps(ST_BWD_TOKEN, s);
-    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, w.nchunks, w.tab, m.slots, m.H, m.Kp, m.gated ? 4 : 3, w.G,
+    launch_bwd_token(dt, m.dh, A.ka, A.va, A.ga, w.dsz, A.nchunks, A.tab, m.slots, m.H, m.Kp, m.gated ? 4 : 3, w.G,
                      w.dbg_part,
                      m.softmax ? saved + (size_t)m.N * m.H * m.E : nullptr, s); }
   if (m.T > 0) {  // dX~ = G Wt^T with the conv's vector-Jacobian product in its epilogue
@@ -365,7 +366,7 @@ gbla_status gbla_backward(const gbla_problem* p, const void* x, const int32_t* c
     f.dw_blocks = bwd_finalize_dw_blocks(m.d, m.Kp);
     f.dw_q = dw_q; f.dw_k = dw_k; f.dw_v = dw_v; f.dw_r = dw_r; f.dw_g = dw_g;
     f.dconv_part = w.dconv_part; f.conv_rb = m.conv_rb; f.dconv_w = dconv_w;
-    f.nchunks = w.nchunks; f.dbg_part = w.dbg_part; f.db_g = db_g;
+    f.nchunks = A.nchunks; f.dbg_part = w.dbg_part; f.db_g = db_g;
     f.dgam_part = gamma ? w.dgam_part : nullptr; f.dgamma = gamma ? dgamma : nullptr;
     f.dt = dt; f.tile_rows = dx_token_tile_rows(dt, m.T, m.d); f.nseq = m.N;
     f.edge = m.T > 0 ? w.edge : nullptr; f.conv_w = conv_w; f.cu = cu_seqlens; f.dx = dx;

@@ -14,6 +14,8 @@
 // Kernels:
 //   (without an activation cache, k_conv_fwd + k_proj recompute x~, g, phi(q), phi(k), v)
 //   k_bwd_dstate  per (chunk, head): y, dn, dden, dq -> G; partial [dS | dz]
+//   k_combine     the sum of those partials; its extra blocks pack the dX~ weights
+//                 (pack_wt_range; k_pack_wt is the same as a launch of its own, for LION)
 //   k_bwd_token   per (chunk, head): dk, dv, ds -> G; partial db_g
 //   k_gemm_dx     dX~ = G Wt^T (pipelined MFMA); for GBLA its epilogue applies the
 //                 conv's chain rule to the tile (dx, dconv_w partials), so dX~
@@ -480,55 +482,23 @@ void launch_bwd_token(int dt, int dh, const void* ka, const void* va, const floa
 }
 
 // ============================================================== weight packing for dX~
-// wt[p][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | (W_R[c,:]) | w_g[:,c] | 0] for
-// channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all).
-// Thread = 8 consecutive columns n (16-byte loads and stores in the weight
-// column blocks, which start at multiples of 32; element-wise in the gate and
-// padding columns). With a schedule (sc.cu non-null) the last block builds the
-// chunk table instead.
+// as a launch of its own (LION-s); the GBLA backward runs pack_wt_range as
+// extra blocks of the combine launch instead
 template <typename T>
-__global__ __launch_bounds__(256) void k_pack_wt(const T* __restrict__ w_q, const T* __restrict__ w_k,
-                                                 const T* __restrict__ w_v, const T* __restrict__ w_r,
-                                                 const T* __restrict__ w_g, int d, int H, int dh, int Kp,
-                                                 T* __restrict__ wt, Sched sc) {
-  const int nblk = gridDim.x - (sc.cu ? 1 : 0);  // packing blocks
-  if (sc.cu && (int)blockIdx.x == nblk) {
+__global__ __launch_bounds__(256) void k_pack_wt(WtPack<T> pk, Sched sc) {
+  if (sc.cu && (int)blockIdx.x == pk.blocks) {
     schedule_block<256>(sc);
     return;
   }
-  const int D = H * dh, GD = (w_r ? 4 : 3) * D;  // first gate column
-  const int per_row = Kp / 8, total = wt_rows(d) * per_row;  // < 2^31 (checked on the host)
-  for (int e8 = blockIdx.x * blockDim.x + threadIdx.x; e8 < total; e8 += nblk * blockDim.x) {
-    const int p = e8 / per_row, n = 8 * (e8 - p * per_row);
-    const size_t e = (size_t)p * Kp + n;
-    const int c = tile_row_perm(p);
-    Frag8<T> v = frag_zero<T>();
-    if (c < d) {
-      if (n < GD) {
-        const int seg = n / D;
-        const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
-        v = frag_load(src + (long)c * D + n - seg * D);
-      } else if (w_g) {  // no w_g: zero rows
-        float f[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) f[u] = n + u < GD + H ? to_f<T>(w_g[(long)(n + u - GD) * d + c]) : 0.f;
-        v = frag_from<T>(f);
-      }
-    }
-    frag_store(wt + e, v);
-  }
+  pack_wt_range(pk, blockIdx.x);
 }
 
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
                     int d, int H, int dh, int Kp, void* wt, const Sched& sc, hipStream_t s) {
-  const long total = (long)wt_rows(d) * Kp / 8;
-  const int grid = (int)std::min<long>((total + 255) / 256, 4096) + (sc.cu ? 1 : 0);
-  if (dt == BF16)
-    hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_r, (const bf16*)w_g, d, H, dh, Kp, (bf16*)wt, sc);
-  else
-    hipLaunchKernelGGL(k_pack_wt<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_r, (const float*)w_g, d, H, dh, Kp, (float*)wt, sc);
+  const WtPackArgs a{w_q, w_k, w_v, w_r, w_g, d, H, dh, Kp, wt};
+  const int grid = wt_pack_blocks(d, Kp) + (sc.cu ? 1 : 0);
+  if (dt == BF16) hipLaunchKernelGGL(k_pack_wt<bf16>, dim3(grid), dim3(256), 0, s, wt_pack_of<bf16>(a), sc);
+  else hipLaunchKernelGGL(k_pack_wt<float>, dim3(grid), dim3(256), 0, s, wt_pack_of<float>(a), sc);
 }
 
 // ============================================================== dX~ = G Wt^T

@@ -9,10 +9,11 @@
 //   y_i = phi(q_i)^T S / phi(q_i)^T z             (Eqs. (5)/(6) in the state-first order of Eq. (3))
 //
 // Kernels (all on the caller's stream, no host synchronisation):
-//   schedule_block  chunk table of <= kChunk-token runs inside each sequence, from cu_seqlens
-//                   (one extra block of the weight-packing launch)
-//   k_pack_proj     per-head packed weights [H][3*dh][d]: Q, K, V columns, k contiguous
-//   k_conv_fwd      causal conv -> x~, and the gates g = sigmoid(x~ w_g + b_g) of every head
+//   k_conv_fwd      causal conv -> x~, and the gates g = sigmoid(x~ w_g + b_g) of every head;
+//                   its extra blocks pack the per-head weights [H][3*dh][d] (Q, K, V
+//                   columns, k contiguous; pack_proj_block) and build the chunk table of
+//                   <= kChunk-token runs inside each sequence from cu_seqlens (schedule_block)
+//   k_pack_proj     the same packing (and table) as a launch of its own (LION-s)
 //   k_proj          projection GEMM x~ [W_Q|W_K|W_V]^h (pipelined MFMA) with phi epilogue
 //   k_state_partial split-L partial [S | z] per (chunk, head), MFMA over the token axis
 //   k_combine       fixed-order sum of the partials of each (sequence, head)
@@ -32,22 +33,27 @@ namespace gbla {
 // store 8 consecutive features per lane (see k_proj).
 // Block = one 32-row group of one head x 64 channels c, transposed through
 // LDS: 16-byte loads of 8 consecutive features of one weight row, 16-byte
-// stores of 8 consecutive channels of one packed row. d % 8 == 0. With a
-// schedule (sc.cu non-null) the last block builds the chunk table instead.
+// stores of 8 consecutive channels of one packed row. d % 8 == 0. The blocks
+// run on their own (k_pack_proj, whose last block builds the chunk table when
+// given a schedule) or as the leading blocks of the conv launch.
 template <typename T>
-__global__ __launch_bounds__(256) void k_pack_proj(const T* __restrict__ w_q, const T* __restrict__ w_k,
-                                                   const T* __restrict__ w_v, const T* __restrict__ w_r, int d,
-                                                   int H, int dh, T* __restrict__ wp, Sched sc) {
-  if (sc.cu && blockIdx.x == gridDim.x - 1) {
-    schedule_block<256>(sc);
-    return;
-  }
+struct ProjPack {
+  const T* w_q; const T* w_k; const T* w_v; const T* w_r;  // w_r null: three segments per head
+  int d, H, dh;
+  T* wp;
+  int blocks;  // proj_pack_blocks(); 0: no packing in this launch
+};
+inline int proj_pack_blocks(int d, int H, int dh, bool four) { return H * (proj_cols(dh, four) / 32) * ((d + 63) / 64); }
+
+template <typename T>
+__device__ __forceinline__ void pack_proj_block(const ProjPack<T>& pk, int blk) {
   __shared__ float tile[32][65];
-  const int NP = (w_r ? 4 : 3) * dh, D = H * dh, G = NP / 32;
-  const int cb = blockIdx.x % ((d + 63) / 64), rest = blockIdx.x / ((d + 63) / 64);
+  const int d = pk.d, dh = pk.dh;
+  const int NP = (pk.w_r ? 4 : 3) * dh, D = pk.H * dh, G = NP / 32;
+  const int cb = blk % ((d + 63) / 64), rest = blk / ((d + 63) / 64);
   const int g = rest % G, h = rest / G;
   const int c0 = 64 * cb, f0 = 32 * g, seg = f0 / dh;
-  const T* src = seg == 0 ? w_q : (seg == 1 ? w_k : (seg == 2 ? w_v : w_r));
+  const T* src = seg == 0 ? pk.w_q : (seg == 1 ? pk.w_k : (seg == 2 ? pk.w_v : pk.w_r));
   const int t = threadIdx.x;
   {
     const int c = t >> 2, fc = 8 * (t & 3);
@@ -64,19 +70,31 @@ __global__ __launch_bounds__(256) void k_pack_proj(const T* __restrict__ w_q, co
     float v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = tile[f][cc + j];
-    frag_store(wp + ((size_t)h * NP + f0 + pr) * d + c0 + cc, frag_from<T>(v));
+    frag_store(pk.wp + ((size_t)h * NP + f0 + pr) * d + c0 + cc, frag_from<T>(v));
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_pack_proj(ProjPack<T> pk, Sched sc) {
+  if (sc.cu && (int)blockIdx.x == pk.blocks) {
+    schedule_block<256>(sc);
+    return;
+  }
+  pack_proj_block(pk, blockIdx.x);
+}
+
+template <typename T>
+ProjPack<T> proj_pack_of(const ProjPackArgs& a) {
+  return ProjPack<T>{(const T*)a.w_q, (const T*)a.w_k, (const T*)a.w_v, (const T*)a.w_r, a.d, a.H, a.dh, (T*)a.wp,
+                     proj_pack_blocks(a.d, a.H, a.dh, a.w_r != nullptr)};
 }
 
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
                       int dh, void* wp, const Sched& sc, hipStream_t s) {
-  const int grid = H * (proj_cols(dh, w_r != nullptr) / 32) * ((d + 63) / 64) + (sc.cu ? 1 : 0);
-  if (dt == BF16)
-    hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, (const bf16*)w_q, (const bf16*)w_k,
-                       (const bf16*)w_v, (const bf16*)w_r, d, H, dh, (bf16*)wp, sc);
-  else
-    hipLaunchKernelGGL(k_pack_proj<float>, dim3(grid), dim3(256), 0, s, (const float*)w_q, (const float*)w_k,
-                       (const float*)w_v, (const float*)w_r, d, H, dh, (float*)wp, sc);
+  const ProjPackArgs a{w_q, w_k, w_v, w_r, d, H, dh, wp};
+  const int grid = proj_pack_blocks(d, H, dh, w_r != nullptr) + (sc.cu ? 1 : 0);
+  if (dt == BF16) hipLaunchKernelGGL(k_pack_proj<bf16>, dim3(grid), dim3(256), 0, s, proj_pack_of<bf16>(a), sc);
+  else hipLaunchKernelGGL(k_pack_proj<float>, dim3(grid), dim3(256), 0, s, proj_pack_of<float>(a), sc);
 }
 
 // ============================================================== causal conv + gate
@@ -148,14 +166,27 @@ __device__ __forceinline__ float log_sigmoidf_(float z) { return fminf(z, 0.f) -
 // (nothing stored). With z = x~ w_g + b_g, g_out gets sigmoid(z) (gmode 0, the
 // sigmoid key gate), z itself (gmode 1, the logit of the softmax key gate) or
 // log sigmoid(z) (gmode 2, the LION-s log decay).
+// The conv's blocks may be followed by the projection's weight-packing blocks
+// (pk.blocks of them) and then one block that builds the chunk table (sc.cu
+// non-null): the projection needs the packed weights and the per-chunk kernels
+// the table, and neither needs the conv, so they ride along instead of taking a
+// launch of their own. They come last so that the conv's blocks are spread
+// evenly over the compute units first.
 enum GateMode { kGateSigmoid = 0, kGateLogit = 1, kGateLogSigmoid = 2 };
 template <typename T, bool CONV, int RUN>
 __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const int32_t* __restrict__ cu, int nseq,
                                                   int T_, int d, int H, const T* __restrict__ conv_w,
                                                   const T* __restrict__ w_g, const float* __restrict__ b_g,
-                                                  int gmode, T* __restrict__ xt, float* __restrict__ g_out) {
+                                                  int gmode, T* __restrict__ xt, float* __restrict__ g_out,
+                                                  ProjPack<T> pk, Sched sc) {
   constexpr int B = kConvBatchRows, NB = RUN / B;
   static_assert(RUN % B == 0 && RUN <= 32, "whole batches; 2 bits per row position in 64");
+  const int nconv = (int)gridDim.x - pk.blocks - (sc.cu ? 1 : 0);
+  if ((int)blockIdx.x >= nconv) {
+    if ((int)blockIdx.x - nconv < pk.blocks) pack_proj_block(pk, blockIdx.x - nconv);
+    else schedule_block<256>(sc);
+    return;
+  }
   __shared__ float sacc[4][RUN][8];
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -263,14 +294,17 @@ __global__ __launch_bounds__(256) void k_conv_fwd(const T* __restrict__ x, const
 }
 
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
-                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s) {
+                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s,
+                     const ProjPackArgs* pack, const Sched& sc) {
   const int gmode = softmax_gate ? kGateLogit : kGateSigmoid;
-  if (T == 0) return;
   const int run = conv_rows_per_wave(T);
-  const dim3 grid((T + 4 * run - 1) / (4 * run));
-#define GBLA_CF(TT, RR)                                                                                  \
-  hipLaunchKernelGGL((k_conv_fwd<TT, true, RR>), grid, dim3(256), 0, s, (const TT*)x, cu, N, T, d, H,  \
-                     (const TT*)conv_w, (const TT*)w_g, b_g, gmode, (TT*)xt, g)
+  const int pre = (pack ? proj_pack_blocks(pack->d, pack->H, pack->dh, pack->w_r != nullptr) : 0) + (sc.cu ? 1 : 0);
+  const int grid = (T + 4 * run - 1) / (4 * run) + pre;
+  if (grid == 0) return;
+#define GBLA_CF(TT, RR)                                                                                     \
+  hipLaunchKernelGGL((k_conv_fwd<TT, true, RR>), dim3(grid), dim3(256), 0, s, (const TT*)x, cu, N, T, d, H, \
+                     (const TT*)conv_w, (const TT*)w_g, b_g, gmode, (TT*)xt, g,                             \
+                     pack ? proj_pack_of<TT>(*pack) : ProjPack<TT>{}, sc)
   if (dt == BF16) {
     if (run == kConvRowsPerWave) GBLA_CF(bf16, kConvRowsPerWave); else GBLA_CF(bf16, kConvRowsPerWaveSmall);
   } else {
@@ -287,7 +321,8 @@ void launch_log_decay(int dt, const void* x, const int32_t* cu, int N, int T, in
   // no conv in this mode: the conv-tap pointer is never dereferenced
 #define GBLA_LD(TT, RR)                                                                                  \
   hipLaunchKernelGGL((k_conv_fwd<TT, false, RR>), grid, dim3(256), 0, s, (const TT*)x, cu, N, T, d, H, \
-                     (const TT*)w_lam, (const TT*)w_lam, b_lam, (int)kGateLogSigmoid, (TT*)nullptr, logl)
+                     (const TT*)w_lam, (const TT*)w_lam, b_lam, (int)kGateLogSigmoid, (TT*)nullptr, logl,   \
+                     ProjPack<TT>{}, Sched{})
   if (dt == BF16) {
     if (run == kConvRowsPerWave) GBLA_LD(bf16, kConvRowsPerWave); else GBLA_LD(bf16, kConvRowsPerWaveSmall);
   } else {
@@ -692,15 +727,24 @@ void launch_state_partial(int dt, int dh, const void* ka, const void* va, const 
 // (deterministic). E % 4 == 0. With chunk maxima mpart (softmax key gate),
 // partial c is scaled by exp(mpart[c] - M), M the largest of the sequence's
 // chunk maxima, which goes to mout[b][h] (0 for an empty sequence).
+// The launch may end with pk.blocks blocks that pack the dX~ weights (the
+// combine of dS leaves most compute units idle).
+template <typename T>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ partial, const int* __restrict__ nchunks,
                                                  const int* __restrict__ chunk_off, int H, int E,
                                                  const float* __restrict__ mpart, float* __restrict__ out,
-                                                 float* __restrict__ mout) {
+                                                 float* __restrict__ mout, WtPack<T> pk) {
+  const int ncomb = (int)gridDim.x - pk.blocks;
+  if ((int)blockIdx.x >= ncomb) {
+    pack_wt_range(pk, blockIdx.x - ncomb);
+    return;
+  }
   __shared__ float4 red[4][64];
+  const int blk = blockIdx.x;
   const int eblocks = (E + 255) / 256;
-  const int bh = blockIdx.x / eblocks, b = bh / H, h = bh - b * H;
+  const int bh = blk / eblocks, b = bh / H, h = bh - b * H;
   const int lane = threadIdx.x & 63, ph = threadIdx.x >> 6;
-  const int e = (blockIdx.x - bh * eblocks) * 256 + 4 * lane;
+  const int e = (blk - bh * eblocks) * 256 + 4 * lane;
   const int nc = *nchunks;
   const int c0 = min(chunk_off[b], nc), c1 = min(chunk_off[b + 1], nc);
   float M = 0.f;
@@ -710,7 +754,7 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     if (c0 == c1) M = 0.f;
-    if (mout && (int)blockIdx.x == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
+    if (mout && blk == bh * eblocks && threadIdx.x == 0) mout[(size_t)b * H + h] = M;
   }
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   if (e < E)
@@ -733,9 +777,15 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ parti
 }
 
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
-                    float* out, hipStream_t s, const float* mpart, float* mout) {
-  hipLaunchKernelGGL(k_combine, dim3(((elems + 255) / 256) * N * H), dim3(256), 0, s, partial, nchunks, chunk_off, H,
-                     elems, mpart, out, mout);
+                    float* out, hipStream_t s, const float* mpart, float* mout, const WtPackArgs* pack, int dt) {
+  const int grid = ((elems + 255) / 256) * N * H;
+  if (pack && dt == BF16)
+    hipLaunchKernelGGL(k_combine<bf16>, dim3(grid + wt_pack_blocks(pack->d, pack->Kp)), dim3(256), 0, s, partial,
+                       nchunks, chunk_off, H, elems, mpart, out, mout, wt_pack_of<bf16>(*pack));
+  else
+    hipLaunchKernelGGL(k_combine<float>, dim3(grid + (pack ? wt_pack_blocks(pack->d, pack->Kp) : 0)), dim3(256), 0,
+                       s, partial, nchunks, chunk_off, H, elems, mpart, out, mout,
+                       pack ? wt_pack_of<float>(*pack) : WtPack<float>{});
 }
 
 // out[e] = sum over p < P of in[p * E + e], P = *P_dev * p_mul if given else P_host.

@@ -148,12 +148,73 @@ __device__ inline void schedule_block(const Sched& sc) {
     *sc.nchunks = min(carry, max_slots);
   }
 }
+
+// wt[p][n] = [W_Q[c,:] | W_K[c,:] | W_V[c,:] | (W_R[c,:]) | w_g[:,c] | 0] for
+// channel c = tile_row_perm(p) (zero rows for c >= d; wt_rows(d) rows in all).
+// Thread = 8 consecutive columns n (16-byte loads and stores in the weight
+// column blocks, which start at multiples of 32; element-wise in the gate and
+// padding columns); `blocks` blocks stride over the array.
+struct WtPackArgs {
+  const void* w_q; const void* w_k; const void* w_v; const void* w_r; const void* w_g;  // w_r, w_g may be null
+  int d, H, dh, Kp;
+  void* wt;
+};
+template <typename T>
+struct WtPack {
+  const T* w_q; const T* w_k; const T* w_v; const T* w_r; const T* w_g;
+  int d, H, dh, Kp;
+  T* wt;
+  int blocks;  // 0: no packing in this launch
+};
+inline int wt_pack_blocks(int d, int Kp) {
+  const long total = (long)wt_rows(d) * Kp / 8;
+  return (int)(total < 4096L * 256 ? (total + 255) / 256 : 4096);
+}
+template <typename T>
+WtPack<T> wt_pack_of(const WtPackArgs& a) {
+  return WtPack<T>{(const T*)a.w_q, (const T*)a.w_k, (const T*)a.w_v, (const T*)a.w_r, (const T*)a.w_g,
+                   a.d, a.H, a.dh, a.Kp, (T*)a.wt, wt_pack_blocks(a.d, a.Kp)};
+}
+template <typename T>
+__device__ __forceinline__ void pack_wt_range(const WtPack<T>& pk, int blk) {
+  const int d = pk.d, D = pk.H * pk.dh, GD = (pk.w_r ? 4 : 3) * D;  // first gate column
+  const int per_row = pk.Kp / 8, total = wt_rows(d) * per_row;  // < 2^31 (checked on the host)
+  for (int e8 = blk * 256 + (int)threadIdx.x; e8 < total; e8 += pk.blocks * 256) {
+    const int p = e8 / per_row, n = 8 * (e8 - p * per_row);
+    const size_t e = (size_t)p * pk.Kp + n;
+    const int c = tile_row_perm(p);
+    Frag8<T> v = frag_zero<T>();
+    if (c < d) {
+      if (n < GD) {
+        const int seg = n / D;
+        const T* src = seg == 0 ? pk.w_q : (seg == 1 ? pk.w_k : (seg == 2 ? pk.w_v : pk.w_r));
+        v = frag_load(src + (long)c * D + n - seg * D);
+      } else if (pk.w_g) {  // no w_g: zero rows
+        float f[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) f[u] = n + u < GD + pk.H ? to_f<T>(pk.w_g[(long)(n + u - GD) * d + c]) : 0.f;
+        v = frag_from<T>(f);
+      }
+    }
+    frag_store(pk.wt + e, v);
+  }
+}
+
 // w_r non-null: a fourth per-head segment (the gated RMSNorm output's W_R)
 void launch_pack_proj(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, int d, int H,
                       int dh, void* wp, const Sched& sc, hipStream_t s);
-// g gets sigmoid(x~ w_g + b_g), or the logit itself for the softmax key gate
+// the operands of the projection's weight packing (w_r null: three segments)
+struct ProjPackArgs {
+  const void* w_q; const void* w_k; const void* w_v; const void* w_r;
+  int d, H, dh;
+  void* wp;
+};
+// g gets sigmoid(x~ w_g + b_g), or the logit itself for the softmax key gate.
+// pack non-null: the same launch also packs the projection weights; sc.cu
+// non-null: it also builds the chunk table.
 void launch_conv_fwd(int dt, const void* x, const int32_t* cu, int N, int T, int d, int H, const void* conv_w,
-                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s);
+                     const void* w_g, const float* b_g, bool softmax_gate, void* xt, float* g, hipStream_t s,
+                     const ProjPackArgs* pack = nullptr, const Sched& sc = Sched{});
 // r_out non-null: wp holds four segments per head and the fourth (linear) goes to r_out
 void launch_proj(int dt, int dh, const void* xt, const void* wp, int T, int d, int H, void* q_out, void* k_out,
                  void* v_out, hipStream_t s, bool phi = true, void* r_out = nullptr);
@@ -166,8 +227,10 @@ void launch_const_log_decay(int T, int H, const float* b_lam, float* logl, hipSt
 void launch_state_partial(int dt, int dh, const void* ka, const void* va, const float* ga, const int* nchunks,
                           const Chunk* tab, int max_slots, int H, float* partial, float* mpart, hipStream_t s);
 // mpart non-null: rescale the partials to the sequence's largest chunk maximum (written to mout)
+// pack non-null: the same launch also packs the dX~ weights (dtype dt)
 void launch_combine(const float* partial, const int* nchunks, const int* chunk_off, int N, int H, int elems,
-                    float* out, hipStream_t s, const float* mpart = nullptr, float* mout = nullptr);
+                    float* out, hipStream_t s, const float* mpart = nullptr, float* mout = nullptr,
+                    const WtPackArgs* pack = nullptr, int dt = F32);
 // out[e] = sum over the first P parts, P = (*P_dev) * p_mul if P_dev else P_host
 void launch_sum_parts(const float* in, int E, int P_host, const int* P_dev, float* out, hipStream_t s,
                       int p_mul = 1);
@@ -182,6 +245,7 @@ void launch_readout(int dt, int dh, const void* qa, const float* saved, const in
 // follows V ([W_Q | W_K | W_V | W_R | w_g^T])
 void launch_pack_wt(int dt, const void* w_q, const void* w_k, const void* w_v, const void* w_r, const void* w_g,
                     int d, int H, int dh, int Kp, void* wt, const Sched& sc, hipStream_t s);
+
 
 // ra non-null: gated RMSNorm output; dy is then the gradient of the gated
 // output, dR goes to G's R columns and per-(chunk, head) partials of dgamma

@@ -119,8 +119,8 @@ GBLA_API gbla_status gbla_workspace_size(const gbla_problem* p, int backward, si
 
 /* Bytes of the optional activation cache `act`: the conv output, phi(q),
  * phi(k), v, with the gated output also x~ W_R (dtype), and the gates
- * (float32) of every token, kept by
- * gbla_forward so that gbla_backward needs no recomputation. Its layout is
+ * (float32) of every token, and the batch's table of 256-token chunks, kept
+ * by gbla_forward so that gbla_backward needs no recomputation. Its layout is
  * internal to the library. */
 GBLA_API gbla_status gbla_activation_size(const gbla_problem* p, size_t* bytes);
 
